@@ -1,0 +1,246 @@
+/*
+ * CPU ORACLE for the Switch FFN layer forward pass -- TEST INFRASTRUCTURE.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load or call this library.  The HIP product path never links or calls it,
+ * and it includes none of the product's headers: the two share no code.
+ *
+ * It is the plain definition of what the layer computes, evaluated in double
+ * precision from the exact input values (bf16 and fp32 inputs widen exactly),
+ * one step after another, with no blocking, fusion or reordering beyond what
+ * each definition states.  OpenMP only splits independent tokens (or
+ * independent experts) across threads; every sum keeps its natural order.
+ *
+ * Pages cited (all describe the Switch Transformers paper, Fedus, Zoph and
+ * Shazeer):
+ *   [MS]  "Switch Transformer - Scaling to Trillion Parameter Models with Simple
+ *          and Efficient Sparsity" (Incredible.AI blog): sections "Expert
+ *          Capacity", "Differentiable Load Balancing Loss", "MoE Layer".
+ *   [KB]  "Switch Transformerとは？巨大モデルを効率化するMoE" (kasblo
+ *          explainer): sections "Top-1 Routingを数式で追う",
+ *          "tokenをExpertへ送って戻すforward pass", "Expert Capacityは
+ *          tokenの受付上限", "16 token、4 Expertで考える",
+ *          "補助負荷分散lossは何を均等にするのか",
+ *          "Routerだけfloat32で計算するSelective Precision".
+ *   [BH]  "Switch Transformer by Hand" (byhand.ai): walkthrough steps [5]-[13].
+ *   [LP]  "精读 06 | Switch Transformers" (llm-papers-study close reading):
+ *          sections 3.1 (router logits and softmax), 3.2 (switch routing),
+ *          3.3 (load-balancing loss), 3.4 (capacity factor, dropped tokens),
+ *          part 六 (architecture diagram).
+ *
+ * Readings taken where the pages are silent or disagree (listed with reasons
+ * in the design notes):
+ *   - capacity C = ceil(c * T / N) with T = every token of the call;
+ *   - argmax over the logits, lowest index on an exact tie;
+ *   - f_i counts tokens before the capacity cut;
+ *   - the expert FFN is relu(x W_in^T) W_out^T without biases;
+ *   - out = x + gate * E(x) inside the layer; a dropped token leaves unchanged.
+ *
+ * Parity pins: every function here is pinned by the -m "not gpu" tests
+ * (worked examples of the pages, closed forms, brute force, a library matmul
+ * for the dense special case).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define NT(n) ((n) > 0 ? (n) : 1)
+
+/*
+ * O-4  Expert capacity.  [LP 3.4] expert capacity = (tokens per batch /
+ * number of experts) x capacity factor; [KB "Expert Capacityはtokenの受付上限"]
+ * rounds it to an integer.  Reading: round up, over all T tokens of the call.
+ * A positive override replaces the formula (worked examples that print C).
+ */
+int64_t oracle_capacity(int64_t T, int64_t N, double c, int64_t capacity_override) {
+  if (capacity_override > 0) return capacity_override;
+  if (N <= 0) return 0;
+  double v = ceil((c * (double)T) / (double)N);
+  return v < 0.0 ? 0 : (int64_t)v;
+}
+
+/*
+ * O-1  Router logits h(x) = W_r . x  ([LP 3.1]; [MS] "Expert Capacity" recap of
+ * MoE routing), plus an optional per-expert bias.  W_r is [N, d] (one row per
+ * expert), x is [T, d]; h is [T, N].  Accumulated in double in k order.
+ */
+void oracle_logits(const float* x, const float* W_r, const float* b_r, int64_t T, int64_t d,
+                   int64_t N, double* h, int nthreads) {
+#pragma omp parallel for schedule(static) num_threads(NT(nthreads))
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t i = 0; i < N; ++i) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < d; ++k) acc += (double)x[t * d + k] * (double)W_r[i * d + k];
+      if (b_r) acc += (double)b_r[i];
+      h[t * N + i] = acc;
+    }
+  }
+}
+
+/* Logits of selected tokens only (large workloads are checked on samples). */
+void oracle_logits_rows(const float* x_rows /* [n, d] */, int64_t n, const float* W_r,
+                        const float* b_r, int64_t d, int64_t N, double* h /* [n, N] */,
+                        int nthreads) {
+  oracle_logits(x_rows, W_r, b_r, n, d, N, h, nthreads);
+}
+
+/*
+ * O-2, O-3  Softmax gate and top-1 choice for one token.
+ * [LP 3.1] p_i(x) = exp(h_i) / sum_j exp(h_j); [LP 3.2] the chosen expert is
+ * argmax_i p_i(x) and the output is scaled by p of that expert; [KB
+ * "Top-1 Routingを数式で追う"] the router scores every expert and runs one.
+ * The max is subtracted before exponentiating (same value in exact
+ * arithmetic).  Returns i*, writes gate = p_{i*}, max m and sum S.
+ */
+static int32_t route_token(const double* h, int64_t N, double* gate, double* m_out, double* S_out) {
+  int32_t best = 0;
+  double m = h[0];
+  for (int64_t i = 1; i < N; ++i)
+    if (h[i] > m) { m = h[i]; best = (int32_t)i; }
+  double S = 0.0;
+  for (int64_t i = 0; i < N; ++i) S += exp(h[i] - m);
+  *gate = exp(h[best] - m) / S;
+  *m_out = m;
+  *S_out = S;
+  return best;
+}
+
+/*
+ * O-2 .. O-6  Routing stage of the layer, applied to given logits h [T, N]
+ * (the oracle's own, or the GPU's fp32 logits widened to double).
+ *
+ *   expert_idx[t], gate[t]         top-1 and its softmax probability
+ *   position[t]                    rank of t among the tokens routed to the
+ *                                  same expert, in token order
+ *                                  ([MS] "MoE Layer": an expert keeps the first
+ *                                  `capacity` of its tokens in flattened token
+ *                                  order; [KB "16 token、4 Expertで考える"];
+ *                                  [BH] step 7: Z5 arrives after Expert C is
+ *                                  full)
+ *   drop[t] = position[t] >= C     overflow tokens skip the expert
+ *                                  ([LP 3.4]; [KB "Expert Capacityは..."])
+ *   load[e]                        tokens routed to e, before the capacity cut
+ *   P[e] = (1/T) sum_t p_e(t)      mean router probability ([LP 3.3])
+ *   aux = alpha N sum_e f_e P_e,   f_e = load[e] / T ([LP 3.3]; [KB
+ *                                  "補助負荷分散lossは何を均等にするのか"])
+ *
+ * P_out may be NULL.  Returns the capacity C.
+ */
+int64_t oracle_route(const double* h, int64_t T, int64_t N, double c, int64_t capacity_override,
+                     double alpha, int32_t* expert_idx, double* gate, int32_t* position,
+                     uint8_t* drop, int32_t* load, double* P_out, double* aux, int nthreads) {
+  int64_t C = oracle_capacity(T, N, c, capacity_override);
+  double* m = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+  double* S = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+  double* P = (double*)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+
+#pragma omp parallel for schedule(static) num_threads(NT(nthreads))
+  for (int64_t t = 0; t < T; ++t)
+    expert_idx[t] = route_token(h + t * N, N, &gate[t], &m[t], &S[t]);
+
+  /* one sequential pass in token order */
+  for (int64_t e = 0; e < N; ++e) load[e] = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    int32_t e = expert_idx[t];
+    position[t] = load[e];
+    load[e] += 1;
+    drop[t] = (uint8_t)((int64_t)position[t] >= C);
+  }
+
+  /* P_e = (1/T) sum over tokens of p_e(t); each expert's sum runs in token order */
+#pragma omp parallel for schedule(static) num_threads(NT(nthreads))
+  for (int64_t e = 0; e < N; ++e) {
+    double acc = 0.0;
+    for (int64_t t = 0; t < T; ++t) acc += exp(h[t * N + e] - m[t]) / S[t];
+    P[e] = T > 0 ? acc / (double)T : 0.0;
+  }
+
+  double sum = 0.0;
+  for (int64_t e = 0; e < N; ++e) {
+    double f = T > 0 ? (double)load[e] / (double)T : 0.0;
+    sum += f * P[e];
+  }
+  *aux = alpha * (double)N * sum;
+  if (P_out) memcpy(P_out, P, sizeof(double) * (size_t)N);
+  free(m);
+  free(S);
+  free(P);
+  return C;
+}
+
+/*
+ * O-7  One expert's FFN on one token: E = W_out . relu(W_in . x)
+ * (the dense FFN the Switch layer replaces, [KB "TransformerのどこへSwitch
+ * layerが入るのか"]; no biases).  W_in is [F, d], W_out is [d, F].
+ * Double accumulation, no intermediate rounding.
+ */
+static void expert_ffn(const float* x, const float* W_in, const float* W_out, int64_t d, int64_t F,
+                       double* u /* [F] scratch */, double* E /* [d] */) {
+  for (int64_t j = 0; j < F; ++j) {
+    double acc = 0.0;
+    for (int64_t k = 0; k < d; ++k) acc += (double)W_in[j * d + k] * (double)x[k];
+    u[j] = acc > 0.0 ? acc : 0.0;
+  }
+  for (int64_t i = 0; i < d; ++i) {
+    double acc = 0.0;
+    for (int64_t j = 0; j < F; ++j) acc += (double)W_out[i * F + j] * u[j];
+    E[i] = acc;
+  }
+}
+
+/*
+ * O-7, O-8  Output row of one token.  [LP 3.2] y = p_{i*}(x) E_{i*}(x);
+ * part 六 adds the residual; [LP 3.4] and [BH] step 13: a dropped token is
+ * passed through unchanged.  `W_in_e`/`W_out_e` are the chosen expert's
+ * weights.  out[k] = x[k] + gate * E[k] (kept) or x[k] (dropped).
+ */
+void oracle_token_output(const float* x, int32_t dropped, double gate, const float* W_in_e,
+                         const float* W_out_e, int64_t d, int64_t F, double* out,
+                         double* E_out /* [d] or NULL: the expert output itself */) {
+  if (dropped) {
+    for (int64_t k = 0; k < d; ++k) out[k] = (double)x[k];
+    if (E_out) for (int64_t k = 0; k < d; ++k) E_out[k] = 0.0;
+    return;
+  }
+  double* u = (double*)malloc(sizeof(double) * (size_t)F);
+  double* E = (double*)malloc(sizeof(double) * (size_t)d);
+  expert_ffn(x, W_in_e, W_out_e, d, F, u, E);
+  for (int64_t k = 0; k < d; ++k) out[k] = (double)x[k] + gate * E[k];
+  if (E_out) memcpy(E_out, E, sizeof(double) * (size_t)d);
+  free(u);
+  free(E);
+}
+
+/*
+ * Combine stage for a whole call, given a routing (expert_idx, gate, drop):
+ * O-7 and O-8 for every token.  W_in is [N, F, d], W_out is [N, d, F].
+ * E_out [T, d] (may be NULL) receives the expert output of kept tokens and 0
+ * for dropped ones.
+ */
+void oracle_combine(const float* x, const int32_t* expert_idx, const double* gate,
+                    const uint8_t* drop, const float* W_in, const float* W_out, int64_t T,
+                    int64_t d, int64_t F, double* out, double* E_out, int nthreads) {
+#pragma omp parallel for schedule(dynamic, 4) num_threads(NT(nthreads))
+  for (int64_t t = 0; t < T; ++t) {
+    int64_t e = expert_idx[t];
+    oracle_token_output(x + t * d, drop[t], gate[t], W_in + e * F * d, W_out + e * d * F, d, F,
+                        out + t * d, E_out ? E_out + t * d : NULL);
+  }
+}
+
+/*
+ * The whole layer: O-1 logits, O-2..O-6 routing, O-7..O-8 combine.
+ * Returns the capacity C.  h [T, N] is written (caller storage).
+ */
+int64_t oracle_forward(const float* x, const float* W_r, const float* b_r, const float* W_in,
+                       const float* W_out, int64_t T, int64_t d, int64_t F, int64_t N, double c,
+                       int64_t capacity_override, double alpha, double* h, int32_t* expert_idx,
+                       double* gate, int32_t* position, uint8_t* drop, int32_t* load, double* P,
+                       double* aux, double* out, double* E_out, int nthreads) {
+  oracle_logits(x, W_r, b_r, T, d, N, h, nthreads);
+  int64_t C = oracle_route(h, T, N, c, capacity_override, alpha, expert_idx, gate, position, drop,
+                           load, P, aux, nthreads);
+  oracle_combine(x, expert_idx, gate, drop, W_in, W_out, T, d, F, out, E_out, nthreads);
+  return C;
+}
