@@ -1,0 +1,197 @@
+"""Benchmark of the Switch FFN layer forward pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+
+One step = one switch_forward call over the whole workload (router, softmax and
+top-1, capacity assignment, load-balancing loss, dispatch, both expert matmuls,
+combine) on seeded synthetic inputs already resident in HBM.  The default
+workload is the Switch-Base-shaped layer: T=4096 tokens, d_model=768,
+d_ff=3072, 8 experts, capacity factor 1.25.
+
+Prints one JSON line: routed tokens/s over K timed steps, the roofline of the
+dominant kernel (algorithmic work / its mean duration from HIP events recorded
+on the library's stream), and the CPU oracle's throughput on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synthetic as S  # noqa: E402
+
+METRIC = "Switch-FFN fwd routed tokens/s (bf16); % MFMA peak & dispatch % HBM BW"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def stage_work(stage: str, spec, kept: int, active_experts: int) -> dict:
+    """Algorithmic FLOPs and HBM bytes one launch of a stage must do."""
+    T, d, F, N = spec.T, spec.d, spec.F, spec.N
+    es = 2 if spec.act == "bf16" else 4
+    if stage == "router_logits":
+        return dict(flops=2.0 * T * d * N, bytes=T * d * es + N * d * 4 + T * N * 4,
+                    peak_tflops=PEAK_FP32_TFLOPS)
+    if stage in ("gemm1_relu", "gemm2"):
+        return dict(flops=2.0 * kept * d * F,
+                    bytes=active_experts * d * F * es + kept * (d + F) * es,
+                    peak_tflops=PEAK_BF16_TFLOPS if spec.expert == "bf16" else PEAK_FP32_TFLOPS)
+    if stage == "dispatch":
+        return dict(flops=0.0, bytes=2 * kept * d * es, peak_tflops=None)
+    if stage == "combine":
+        return dict(flops=0.0, bytes=(kept + 2 * T) * d * es + 13 * T, peak_tflops=None)
+    if stage == "route_rows":
+        return dict(flops=0.0, bytes=T * N * 4 + 8 * T, peak_tflops=None)
+    return dict(flops=0.0, bytes=0, peak_tflops=None)
+
+
+def roofline_entry(stage: str, work: dict, ms: float) -> dict:
+    sec = ms * 1e-3
+    t_mfma = work["flops"] / (work["peak_tflops"] * 1e12) if work["peak_tflops"] else 0.0
+    t_hbm = work["bytes"] / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm and work["flops"] > 0:
+        bound = "mfma" if work["peak_tflops"] == PEAK_BF16_TFLOPS else "alu"
+        achieved = work["flops"] / sec / 1e12
+        peak = work["peak_tflops"]
+        unit = "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", work["bytes"] / sec / 1e9, PEAK_HBM_GBS, "GB/s"
+    return {"kernel": stage, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+            "roofline_frac": round(max(t_mfma, t_hbm) / sec, 4)}
+
+
+def cpu_baseline(spec, host, budget_s: float = 10.0) -> dict:
+    import oracle
+    xf = S.to_f32(host["x"], spec.act)
+    W_in = S.to_f32(host["W_in"], spec.expert)
+    W_out = S.to_f32(host["W_out"], spec.expert)
+    nt = oracle.threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(xf, host["W_r"], host["b_r"], W_in, W_out, spec.c, spec.capacity_override,
+                       spec.alpha, nthreads=nt)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(spec.T * reps / el, 1), "unit": "tokens/s", "cores": nt,
+            "kind": "oracle",
+            "sample": f"full {spec.name} workload (T={spec.T}) x {reps} run(s), {el:.1f} s, fp64 C"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--profile-iters", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs the Switch layer on a single "
+              "MI355X and has no multi-GPU path (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from switch_transformer_top_amd import binding as B
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    spec = S.CONFIGS[args.config]
+    host = S.host_inputs(spec)
+    layer = B.SwitchLayer.from_host(spec, host, device=dev)
+    x = B.to_device(host["x"], dev)
+    bufs = layer.alloc(spec.T)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    for _ in range(args.warmup):
+        layer.forward(x, spec.T, bufs, stream=sp, with_logits=False)
+    torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        layer.forward(x, spec.T, bufs, stream=sp, with_logits=False)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    drop = B.from_device(bufs["drop_mask"])
+    load = B.from_device(bufs["load"])
+    kept = int((drop == 0).sum())
+    C = B.switch_capacity(layer.handle, spec.T)
+    active = int((np.minimum(load, C) > 0).sum())
+
+    # per-kernel durations: HIP events recorded by the library around each launch
+    B.switch_profile_enable(layer.handle, True)
+    acc = {}
+    order = []
+    for _ in range(args.profile_iters):
+        layer.forward(x, spec.T, bufs, stream=sp, with_logits=False)
+        for name, ms in B.switch_profile_read(layer.handle):
+            if name not in acc:
+                acc[name] = []
+                order.append(name)
+            acc[name].append(ms)
+    B.switch_profile_enable(layer.handle, False)
+    stage_ms = {k: float(np.mean(acc[k])) for k in order}
+
+    rooflines = {k: roofline_entry(k, stage_work(k, spec, kept, active), v)
+                 for k, v in stage_ms.items()
+                 if k in ("router_logits", "gemm1_relu", "gemm2", "dispatch", "combine")}
+    dominant = max(rooflines, key=lambda k: stage_ms[k])
+    gemm_ms = stage_ms.get("gemm1_relu", 0) + stage_ms.get("gemm2", 0)
+    expert_tflops = 4.0 * kept * spec.d * spec.F / (gemm_ms * 1e-3) / 1e12 if gemm_ms else 0.0
+
+    result = {
+        "metric": METRIC,
+        "value": round(spec.T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.act,
+        "data": "synthetic (seeded counter-based generator; random-init weights)",
+        "config": {"workload": spec.name, "T": spec.T, "d_model": spec.d, "d_ff": spec.F,
+                   "n_experts": spec.N, "capacity_factor": spec.c, "capacity": C,
+                   "router": "fp32", "experts": spec.expert, "parallelism": "single-gpu"},
+        "roofline": rooflines[dominant],
+        "cpu_baseline": None,
+        "kept_tokens": kept,
+        "dropped_tokens": spec.T - kept,
+        "expert_tflops": round(expert_tflops, 2),
+        "expert_mfma_frac": round(expert_tflops / PEAK_BF16_TFLOPS, 4),
+        "dispatch_hbm_frac": rooflines.get("dispatch", {}).get("frac"),
+        "combine_hbm_frac": rooflines.get("combine", {}).get("frac"),
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "stage_rooflines": rooflines,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(spec, host, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

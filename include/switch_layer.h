@@ -1,0 +1,180 @@
+/*
+ * switch_layer.h -- C ABI of the Switch FFN layer forward pass on MI355X (gfx950).
+ *
+ * One call computes, for T tokens x[T, d] (flattened batch x sequence, row-major):
+ *   h[t, i]     = sum_k x[t, k] W_r[i, k] + b_r[i]              router logits, fp32
+ *   p_i(t)      = softmax_i(h[t, :]);  e_t = argmax_i h[t, i] (lowest i on ties)
+ *   gate[t]     = p_{e_t}(t)
+ *   C           = ceil(c * T / N)   (or the configured override)
+ *   position[t] = #{ t' < t : e_t' = e_t }                      token-order rank
+ *   drop[t]     = position[t] >= C
+ *   out[t]      = x[t] + gate[t] * W_out[e_t] relu(W_in[e_t] x[t])   if !drop[t]
+ *               = x[t] (bit for bit)                                  if  drop[t]
+ *   aux_loss    = alpha N sum_i f_i P_i,  f_i = load_i / T,  P_i = mean_t p_i(t)
+ *
+ * Sources (the Switch Transformers paper as described on these pages):
+ *   router logits and softmax -- "精读 06 | Switch Transformers" (llm-papers-study
+ *     close reading), section 3.1; top-1 choice and the gate-scaled output --
+ *     same page, section 3.2, and kasblo "Switch Transformerとは？", section
+ *     "Top-1 Routingを数式で追う";
+ *   capacity and overflow -- llm-papers-study section 3.4; kasblo sections
+ *     "Expert Capacityはtokenの受付上限" and "16 token、4 Expertで考える";
+ *     "Switch Transformer by Hand" (byhand.ai) steps 7 and 13;
+ *   token-order truncation -- Incredible.AI blog "Switch Transformer - Scaling to
+ *     Trillion Parameter Models...", section "MoE Layer";
+ *   load-balancing loss -- llm-papers-study section 3.3; kasblo section
+ *     "補助負荷分散lossは何を均等にするのか";
+ *   fp32 router, bf16 dispatch/combine -- kasblo section "Routerだけfloat32で
+ *     計算するSelective Precision";
+ *   dispatch / expert matmul / combine -- kasblo section
+ *     "tokenをExpertへ送って戻すforward pass".
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers (the caller owns them), contiguous,
+ *     row-major, 16-byte aligned.  Scalars are host values.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on it and return; SWITCH_OK means "enqueued".
+ *     Results are valid once the stream has reached that point.
+ *   - Nothing is launched when a call returns an error status.  No call
+ *     aborts the process, and no call allocates device memory: all scratch
+ *     lives in the caller's workspace.
+ *   - Calls do not synchronise the stream; one handle may be used on several
+ *     streams concurrently only with distinct workspaces and outputs.
+ *   - Inputs must be finite.
+ */
+#ifndef SWITCH_LAYER_H
+#define SWITCH_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SWITCH_OK = 0,
+  SWITCH_E_INVALID = 1,      /* bad size, NULL required pointer, misalignment, T > t_max,
+                                workspace too small */
+  SWITCH_E_UNSUPPORTED = 2,  /* dtype combination or shape the kernels do not handle */
+  SWITCH_E_HIP = 3           /* a HIP runtime call or kernel launch failed */
+} switch_status;
+
+typedef enum { SWITCH_F32 = 0, SWITCH_BF16 = 1 } switch_dtype;
+
+typedef struct {
+  int64_t t_max;            /* largest T any call on this handle may pass (>= 0) */
+  int32_t d_model;          /* d; a multiple of 8 (of 128 for bf16 layers) */
+  int32_t d_ff;             /* F; a multiple of 8 (of 128 for bf16 layers) */
+  int32_t n_experts;        /* 1 <= N <= 8192 */
+  double capacity_factor;   /* c >= 0; C = ceil(c * T / N) evaluated in double */
+  int32_t capacity_override;/* > 0: use this C instead of the formula */
+  float alpha;              /* load-balancing loss coefficient (the paper uses 0.01) */
+  int32_t act_dtype;        /* switch_dtype of x, out and the expert activations */
+  int32_t expert_dtype;     /* switch_dtype of W_in / W_out; must equal act_dtype */
+} switch_config;
+
+typedef struct switch_layer switch_layer;
+
+/*
+ * Create a layer handle over caller-owned device weights.  Nothing is copied:
+ * the weights are BORROWED and must stay valid and unchanged for the life of
+ * the handle.
+ *   W_r   [N, d] fp32 router weights (one row per expert)
+ *   b_r   [N] fp32 router bias, or NULL for none
+ *   W_in  [N, F, d] expert first-layer weights, expert_dtype
+ *   W_out [N, d, F] expert second-layer weights, expert_dtype
+ * On success *out receives the handle (host memory owned by the library;
+ * release with switch_layer_destroy).  Returns SWITCH_E_INVALID for bad sizes
+ * or NULL weights, SWITCH_E_UNSUPPORTED for other dtype mixes, SWITCH_E_HIP if
+ * the current device cannot be queried.
+ */
+switch_status switch_layer_create(const switch_config* cfg, const float* W_r, const float* b_r,
+                                  const void* W_in, const void* W_out, switch_layer** out);
+
+/* Release a handle (NULL is allowed).  Does not touch the borrowed weights. */
+void switch_layer_destroy(switch_layer* layer);
+
+/* Capacity C used for a call with T tokens (-1 on a NULL handle or T < 0). */
+int64_t switch_capacity(const switch_layer* layer, int64_t T);
+
+/* Bytes of device workspace a switch_forward / switch_route call with T tokens needs
+ * (0 on a NULL handle or T outside [0, t_max]). */
+size_t switch_workspace_bytes(const switch_layer* layer, int64_t T);
+
+/*
+ * Routing stage only: router logits, softmax, top-1, capacity positions,
+ * drops, per-expert loads and the load-balancing loss.
+ *   x          [T, d]  act_dtype input tokens
+ *   logits     [T, N]  fp32 router logits, or NULL if not wanted
+ *   expert_idx [T]     int32 chosen expert
+ *   gate       [T]     fp32 softmax probability of the chosen expert (also for
+ *                      dropped tokens)
+ *   position   [T]     int32 token-order rank within the chosen expert (may be >= C)
+ *   drop_mask  [T]     uint8 1 if position >= C
+ *   aux_loss   [1]     fp32 load-balancing loss (device scalar)
+ *   load       [N]     int32 tokens per expert before the capacity cut, or NULL
+ *   ws, ws_bytes       device workspace of at least switch_workspace_bytes(T)
+ * T = 0 is allowed (aux_loss = 0).
+ */
+switch_status switch_route(switch_layer* layer, const void* x, int64_t T, float* logits,
+                           int32_t* expert_idx, float* gate, int32_t* position,
+                           uint8_t* drop_mask, float* aux_loss, int32_t* load, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * The whole layer: everything switch_route returns, plus
+ *   out [T, d] act_dtype layer output x + gate * E(x) (dropped tokens: x
+ *   unchanged).  `out` must not overlap `x`.
+ * Expert activations are rounded to bf16 between the two expert matmuls and
+ * after the second (bf16 layers); accumulation is fp32 throughout.
+ */
+switch_status switch_forward(switch_layer* layer, const void* x, int64_t T, void* out,
+                             int32_t* expert_idx, float* gate, int32_t* position,
+                             uint8_t* drop_mask, float* aux_loss, float* logits, int32_t* load,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Test hook: the routing stage from given fp32 logits [T, N] (device), with the
+ * same outputs as switch_route minus the logits.  -inf logits are allowed
+ * (probability 0); NaN is not.
+ */
+switch_status switch_route_from_logits(switch_layer* layer, const float* logits, int64_t T,
+                                       int32_t* expert_idx, float* gate, int32_t* position,
+                                       uint8_t* drop_mask, float* aux_loss, int32_t* load,
+                                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Test hook: switch_forward that also copies the expert outputs E(x) of the
+ * kept tokens into expert_out [N, Cb, d], Cb = min(C, T) (act_dtype, row p of
+ * expert e holds the token with position p; rows p >= n_e are left untouched).
+ * expert_out may be NULL only when Cb = 0.
+ */
+switch_status switch_forward_debug(switch_layer* layer, const void* x, int64_t T, void* out,
+                                   int32_t* expert_idx, float* gate, int32_t* position,
+                                   uint8_t* drop_mask, float* aux_loss, float* logits,
+                                   int32_t* load, void* ws, size_t ws_bytes, void* expert_out,
+                                   void* stream);
+
+/*
+ * Per-kernel timing for measurement.  When enabled, later switch_forward /
+ * switch_route calls record a HIP event before and after every kernel they
+ * launch, on the call's stream.  switch_profile_read waits for the last such
+ * call to finish and writes up to `cap` stage times in milliseconds, in launch
+ * order, with their names (static strings).  Returns the number of stages, or
+ * -1 on error.  Enabling creates the events once (SWITCH_E_HIP on failure).
+ */
+switch_status switch_profile_enable(switch_layer* layer, int enable);
+int switch_profile_read(switch_layer* layer, float* ms, const char** names, int cap);
+
+/* Human-readable name of a status code (static string). */
+const char* switch_status_string(switch_status s);
+
+/* Status of the most recent asynchronous HIP error seen on this thread
+ * (hipGetLastError, which also clears it): SWITCH_OK or SWITCH_E_HIP. */
+switch_status switch_last_async_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SWITCH_LAYER_H */

@@ -1,0 +1,129 @@
+// Capacity assignment and the load-balancing loss.
+//
+// position[t] = number of earlier tokens (in flattened token order) routed to
+// the same expert; a token whose position reaches the capacity C overflows and
+// is dropped.  The token-order rule follows the Incredible.AI blog's "MoE Layer"
+// section (an expert keeps the first `capacity` tokens routed to it) and the
+// kasblo explainer's "16 token、4 Expertで考える"; the overflow token of
+// "Switch Transformer by Hand" (step 7) is the third token routed to a full
+// expert.  All of it is integer work on per-chunk counts and is deterministic:
+// the router leaves hist[c, e] and in-chunk ranks; this kernel turns hist into
+// exclusive prefixes over chunks; the dispatch pass adds the two.
+//
+// Load-balancing loss (llm-papers-study close reading, section 3.3):
+// aux = alpha N sum_i f_i P_i, f_i = load_i / T, P_i = (1/T) sum_t p_i(t), with
+// load_i counted before the capacity cut.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace swl {
+
+// One block of 1024 threads.  Experts are taken EG at a time (EG = N rounded
+// up to a power of two, at most 1024); the G = 1024 / EG threads of an expert
+// split the chunk range into contiguous pieces.  Each piece is summed (counts
+// and probability sums), the pieces are scanned in order, and each thread then
+// rewrites its piece of hist[:, e] as exclusive prefixes.  Probability sums
+// are added in fp64 in piece order, so every result is independent of timing.
+__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ hist,
+                                                          const float* __restrict__ P_part,
+                                                          int64_t nc, int N, int64_t T, int64_t C,
+                                                          float alpha, int32_t* __restrict__ load,
+                                                          int32_t* __restrict__ n_kept,
+                                                          float* __restrict__ aux) {
+  __shared__ int32_t s_cnt[1024];
+  __shared__ double s_p[1024];
+  const int tid = threadIdx.x;
+  int EG = 1;
+  while (EG < N && EG < 1024) EG <<= 1;
+  const int G = 1024 / EG;
+  const int el = tid % EG, g = tid / EG;
+  const int64_t per = (nc + G - 1) / G;
+  const int64_t c0 = (int64_t)g * per;
+  const int64_t c1 = (c0 + per < nc) ? c0 + per : nc;
+  double aux_acc = 0.0;
+
+  for (int e_base = 0; e_base < N; e_base += EG) {
+    const int e = e_base + el;
+    const bool valid = e < N;
+    int32_t cnt = 0;
+    double p = 0.0;
+    if (valid) {
+#pragma unroll 8
+      for (int64_t c = c0; c < c1; ++c) {
+        cnt += hist[c * N + e];
+        p += (double)P_part[c * N + e];
+      }
+    }
+    s_cnt[tid] = cnt;
+    s_p[tid] = p;
+    __syncthreads();
+    if (g == 0 && valid) {
+      int32_t run = 0;
+      double ps = 0.0;
+      for (int gg = 0; gg < G; ++gg) {
+        const int32_t v = s_cnt[gg * EG + el];
+        s_cnt[gg * EG + el] = run;
+        run += v;
+        ps += s_p[gg * EG + el];
+      }
+      load[e] = run;
+      n_kept[e] = (int32_t)((int64_t)run < C ? (int64_t)run : C);
+      aux_acc += (double)run * ps;
+    }
+    __syncthreads();
+    if (valid) {
+      int32_t run = s_cnt[tid];
+#pragma unroll 8
+      for (int64_t c = c0; c < c1; ++c) {
+        const int32_t v = hist[c * N + e];
+        hist[c * N + e] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+  }
+
+  s_p[tid] = aux_acc;
+  __syncthreads();
+  for (int s = 512; s >= 1; s >>= 1) {
+    if (tid < s) s_p[tid] += s_p[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    double v = 0.0;
+    if (T > 0) v = (double)alpha * (double)N * (s_p[0] / ((double)T * (double)T));
+    *aux = (float)v;
+  }
+}
+
+// position = chunk offset + in-chunk rank; drop when it reaches C (route only:
+// no data moves).  One thread per token.
+__global__ __launch_bounds__(256) void finalize_positions_kernel(
+    int64_t T, const int32_t* __restrict__ expert_idx, const int32_t* __restrict__ rank_local,
+    const int32_t* __restrict__ offsets, int N, int64_t chunk, int64_t C,
+    int32_t* __restrict__ position, uint8_t* __restrict__ drop_mask) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const int32_t pos = offsets[(t / chunk) * N + expert_idx[t]] + rank_local[t];
+  position[t] = pos;
+  drop_mask[t] = (int64_t)pos >= C ? 1 : 0;
+}
+
+// ------------------------------------------------------------------ launchers
+
+void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T,
+                       int64_t C, float alpha, int32_t* load, int32_t* n_kept, float* aux,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, P_part, nc, N, T, C,
+                     alpha, load, n_kept, aux);
+}
+
+void launch_finalize_positions(int64_t T, const int32_t* expert_idx, const int32_t* rank_local,
+                               const int32_t* offsets, int N, int64_t chunk, int64_t C,
+                               int32_t* position, uint8_t* drop_mask, hipStream_t s) {
+  if (T == 0) return;
+  hipLaunchKernelGGL(finalize_positions_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0,
+                     s, T, expert_idx, rank_local, offsets, N, chunk, C, position, drop_mask);
+}
+
+}  // namespace swl

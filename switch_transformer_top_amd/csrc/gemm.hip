@@ -1,0 +1,307 @@
+// Grouped expert FFN matmuls.
+//
+// Each expert is the dense FFN it replaces (kasblo explainer, section
+// "TransformerのどこへSwitch layerが入るのか"), here relu(x W_in^T) W_out^T with
+// no biases; every expert multiplies the block of tokens gathered for it
+// (section "tokenをExpertへ送って戻すforward pass").  Both matmuls have the
+// same shape class, C[m, n] = sum_k A[m, k] B[n, k] with A and B K-contiguous:
+//   GEMM1: A = Xbuf[e] [rows, d],  B = W_in[e]  [F, d] -> Hbuf[e] [rows, F], relu
+//   GEMM2: A = Hbuf[e] [rows, F],  B = W_out[e] [d, F] -> Ybuf[e] [rows, d]
+// The number of rows of expert e, n_kept[e], is read on the device: tiles past
+// it return at once, so the host never waits for the routing result.
+//
+// bf16 path: CDNA4 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation, the
+// result rounded to bf16 (after the ReLU for GEMM1).  fp32 path: plain FMA.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace swl {
+
+constexpr int GB_BK = 64, GB_PAD = 8;
+constexpr int GB_LDK = GB_BK + GB_PAD;  // LDS row stride in bf16 elements (144 bytes)
+
+// Block: 256 threads = 4 waves in a 2 x 2 grid; each wave owns a
+// (BM/2) x (BN/2) sub-tile made of 32 x 32 MFMA tiles.  K advances 64 at a
+// time through one padded LDS buffer per operand; the next K tile is fetched
+// into registers (unconditionally: the last iteration re-reads its own tile)
+// while the current one is multiplied.
+//
+// MFMA 32x32x16 operand layout (per lane l): A row (l % 32) with 8 consecutive
+// k, B column (l % 32) with the same 8 k; the k group is (l / 32).  Result: lane
+// l holds column (l % 32) and rows 8 (v / 4) + 4 (l / 32) + (v % 4), v < 16.
+// Tile order: the grid is 1-D.  Workgroups are handed to the 8 XCDs round
+// robin (block b runs on XCD b % 8), so block b takes tile
+// (b % 8) * ceil(tiles / 8) + b / 8: each XCD walks a contiguous stretch of the
+// tile list, whose order is expert, then N tile, then M tile.  The tiles of one
+// expert (its gathered rows and its weights) therefore share one XCD's L2, and
+// consecutive M tiles reuse the same weight tile.
+//
+// Pipeline: K tiles k+1 and k+2 are in flight in two register sets while tile
+// k is multiplied out of LDS (LDS_BUFS = 1: one buffer, two barriers per step;
+// LDS_BUFS = 2: double buffer, one barrier per step).  The prefetch of a tile
+// past the end re-reads the last tile, so every load is unconditional.
+template <int BM, int BN, int LDS_BUFS, int PF, bool RELU>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
+                                                        int64_t strideA,
+                                                        const uint16_t* __restrict__ B,
+                                                        int64_t strideB,
+                                                        uint16_t* __restrict__ Cout,
+                                                        int64_t strideC,
+                                                        const int32_t* __restrict__ rows, int K,
+                                                        int Nout, int m_tiles, int n_tiles,
+                                                        int tiles) {
+  constexpr int LA = BM / 32, LB = BN / 32;   // 16-byte loads per thread per operand
+  constexpr int TI = BM / 64, TJ = BN / 64;   // MFMA tiles per wave
+  __shared__ __attribute__((aligned(16))) uint16_t As[LDS_BUFS][BM * GB_LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[LDS_BUFS][BN * GB_LDK];
+
+  const int per_xcd = (tiles + 7) >> 3;
+  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (tile >= tiles) return;
+  const int mt = tile % m_tiles;
+  const int nt = (tile / m_tiles) % n_tiles;
+  const int e = tile / (m_tiles * n_tiles);
+  const int rows_e = rows[e];
+  const int m0 = mt * BM;
+  if (m0 >= rows_e) return;
+  const int n0 = nt * BN;
+
+  const uint16_t* Ae = A + (int64_t)e * strideA;
+  const uint16_t* Be = B + (int64_t)e * strideB + (int64_t)n0 * K;
+  uint16_t* Ce = Cout + (int64_t)e * strideC;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lrow = tid >> 3, lcol = (tid & 7) * 8;
+
+  int64_t a_off[LA], b_off[LB];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    int r = m0 + lrow + 32 * j;
+    r = r < rows_e ? r : rows_e - 1;  // rows past n_kept: any valid row, never stored
+    a_off[j] = (int64_t)r * K + lcol;
+  }
+#pragma unroll
+  for (int j = 0; j < LB; ++j) b_off[j] = (int64_t)(lrow + 32 * j) * K + lcol;
+
+  floatx16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int nk = K / GB_BK;
+  const int last = (nk - 1) * GB_BK;
+  u32x4 ra0[LA], rb0[LB], ra1[LA], rb1[LB];
+  // The scheduling barrier keeps the prefetch loads ahead of the MFMAs that
+  // follow; without it the compiler sinks them to the end of the loop body,
+  // where nothing is left to hide their latency.
+  auto fetch = [&](u32x4* ra, u32x4* rb, int k) {
+    k = k < last ? k : last;
+#pragma unroll
+    for (int j = 0; j < LA; ++j) ra[j] = *reinterpret_cast<const u32x4*>(Ae + a_off[j] + k);
+#pragma unroll
+    for (int j = 0; j < LB; ++j) rb[j] = *reinterpret_cast<const u32x4*>(Be + b_off[j] + k);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto stash = [&](const u32x4* ra, const u32x4* rb, int buf) {
+#pragma unroll
+    for (int j = 0; j < LA; ++j)
+      *reinterpret_cast<u32x4*>(&As[buf][(lrow + 32 * j) * GB_LDK + lcol]) = ra[j];
+#pragma unroll
+    for (int j = 0; j < LB; ++j)
+      *reinterpret_cast<u32x4*>(&Bs[buf][(lrow + 32 * j) * GB_LDK + lcol]) = rb[j];
+  };
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < GB_BK; ks += 16) {
+      bf16x8 a[TI], b[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(
+            &As[buf][(wm * (BM / 2) + i * 32 + fr) * GB_LDK + ks + fk]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(
+            &Bs[buf][(wn * (BN / 2) + j * 32 + fr) * GB_LDK + ks + fk]);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  if (PF == 1) {
+    // one register set: tile k + 1 is in flight while tile k is multiplied
+    fetch(ra0, rb0, 0);
+    if (LDS_BUFS == 1) {
+      for (int kt = 0; kt < nk; ++kt) {
+        __syncthreads();
+        stash(ra0, rb0, 0);
+        __syncthreads();
+        fetch(ra0, rb0, (kt + 1) * GB_BK);
+        compute(0);
+      }
+    } else {
+      stash(ra0, rb0, 0);
+      fetch(ra0, rb0, GB_BK);
+      __syncthreads();
+      for (int kt = 0; kt < nk; kt += 2) {
+        compute(0);
+        stash(ra0, rb0, LDS_BUFS - 1);
+        fetch(ra0, rb0, (kt + 2) * GB_BK);
+        __syncthreads();
+        if (kt + 1 >= nk) break;
+        compute(LDS_BUFS - 1);
+        stash(ra0, rb0, 0);
+        fetch(ra0, rb0, (kt + 3) * GB_BK);
+        __syncthreads();
+      }
+    }
+  } else {
+    fetch(ra0, rb0, 0);
+    fetch(ra1, rb1, GB_BK);
+    if (LDS_BUFS == 1) {
+      // step k: stash tile k (register set k % 2), refill that set with tile k + 2
+      for (int kt = 0; kt < nk; kt += 2) {
+        __syncthreads();
+        stash(ra0, rb0, 0);
+        __syncthreads();
+        fetch(ra0, rb0, (kt + 2) * GB_BK);
+        compute(0);
+        if (kt + 1 >= nk) break;
+        __syncthreads();
+        stash(ra1, rb1, 0);
+        __syncthreads();
+        fetch(ra1, rb1, (kt + 3) * GB_BK);
+        compute(0);
+      }
+    } else {
+      // LDS buffer kt % 2 holds tile kt; after computing it, tile kt + 1 goes to
+      // the other buffer and its register set is refilled with tile kt + 3.
+      stash(ra0, rb0, 0);
+      fetch(ra0, rb0, 2 * GB_BK);
+      __syncthreads();
+      for (int kt = 0; kt < nk; kt += 2) {
+        compute(0);
+        stash(ra1, rb1, LDS_BUFS - 1);
+        fetch(ra1, rb1, (kt + 3) * GB_BK);
+        __syncthreads();
+        if (kt + 1 >= nk) break;
+        compute(LDS_BUFS - 1);
+        stash(ra0, rb0, 0);
+        fetch(ra0, rb0, (kt + 4) * GB_BK);
+        __syncthreads();
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (r >= rows_e) continue;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int c = n0 + wn * (BN / 2) + j * 32 + fr;
+        float val = acc[i][j][v];
+        if (RELU) val = val > 0.f ? val : 0.f;
+        Ce[(int64_t)r * Nout + c] = f32_to_bf16_bits(val);
+      }
+    }
+  }
+}
+
+// fp32 path (parity-sized fp32 layers): 32 x 32 tile, K in steps of 32, each
+// of 256 threads owns 4 rows of one column.  Any sizes (bounds-checked).
+template <bool RELU>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int64_t strideA,
+                                                       const float* __restrict__ B, int64_t strideB,
+                                                       float* __restrict__ Cout, int64_t strideC,
+                                                       const int32_t* __restrict__ rows, int K,
+                                                       int Nout) {
+  __shared__ float As[32][33];
+  __shared__ float Bs[32][33];
+  const int e = blockIdx.z;
+  const int rows_e = rows[e];
+  const int m0 = blockIdx.y * 32;
+  if (m0 >= rows_e) return;
+  const int n0 = blockIdx.x * 32;
+  const float* Ae = A + (int64_t)e * strideA;
+  const float* Be = B + (int64_t)e * strideB;
+  float* Ce = Cout + (int64_t)e * strideC;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < K; k0 += 32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = threadIdx.x + 256 * j;
+      const int r = idx >> 5, k = idx & 31;
+      const int gk = k0 + k;
+      As[r][k] = (m0 + r < rows_e && gk < K) ? Ae[(int64_t)(m0 + r) * K + gk] : 0.f;
+      Bs[r][k] = (n0 + r < Nout && gk < K) ? Be[(int64_t)(n0 + r) * K + gk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      const float b = Bs[tx][k];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(As[ty + 8 * i][k], b, acc[i]);
+    }
+    __syncthreads();
+  }
+  const int c = n0 + tx;
+  if (c >= Nout) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = m0 + ty + 8 * i;
+    if (r < rows_e) {
+      float v = acc[i];
+      if (RELU) v = v > 0.f ? v : 0.f;
+      Ce[(int64_t)r * Nout + c] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+void launch_expert_gemm(bool bf16, bool relu, const void* A, int64_t strideA, const void* B,
+                        int64_t strideB, void* Cout, int64_t strideC, const int32_t* rows,
+                        int n_experts, int64_t C, int K, int Nout, hipStream_t s) {
+  if (C == 0 || n_experts == 0) return;
+  if (bf16) {
+    constexpr int BM = 128, BN = 128;
+    const int mt = (int)((C + BM - 1) / BM), nt = Nout / BN;
+    const int tiles = mt * nt * n_experts;
+    const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
+    if (relu)
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1, 1, true>), dim3(grid), dim3(256), 0, s,
+                         (const uint16_t*)A, strideA, (const uint16_t*)B, strideB,
+                         (uint16_t*)Cout, strideC, rows, K, Nout, mt, nt, tiles);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1, 1, false>), dim3(grid), dim3(256), 0, s,
+                         (const uint16_t*)A, strideA, (const uint16_t*)B, strideB,
+                         (uint16_t*)Cout, strideC, rows, K, Nout, mt, nt, tiles);
+  } else {
+    dim3 grid((unsigned)((Nout + 31) / 32), (unsigned)((C + 31) / 32), (unsigned)n_experts);
+    if (relu)
+      hipLaunchKernelGGL(gemm_f32_kernel<true>, grid, dim3(256), 0, s, (const float*)A, strideA,
+                         (const float*)B, strideB, (float*)Cout, strideC, rows, K, Nout);
+    else
+      hipLaunchKernelGGL(gemm_f32_kernel<false>, grid, dim3(256), 0, s, (const float*)A, strideA,
+                         (const float*)B, strideB, (float*)Cout, strideC, rows, K, Nout);
+  }
+}
+
+bool expert_gemm_shape_ok(bool bf16, int d, int F) {
+  if (!bf16) return true;
+  return d % 128 == 0 && F % 128 == 0;
+}
+
+}  // namespace swl

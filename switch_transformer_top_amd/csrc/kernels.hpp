@@ -1,0 +1,69 @@
+// Launchers of the Switch-layer kernels (host side) and the per-stage event
+// profiler used for measurement.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swl {
+
+// Records a HIP event on the launch stream before each stage; the next mark
+// (or the end mark) closes the stage.
+struct Profiler {
+  static constexpr int kMax = 24;
+  bool on = false;
+  bool created = false;
+  hipEvent_t ev[kMax + 1];
+  const char* names[kMax];
+  int n = 0;
+};
+
+inline void prof_begin(Profiler* p) {
+  if (p && p->on) p->n = 0;
+}
+inline void prof_mark(Profiler* p, hipStream_t s, const char* name) {
+  if (!p || !p->on || p->n >= Profiler::kMax) return;
+  p->names[p->n] = name;
+  (void)hipEventRecord(p->ev[p->n], s);
+  p->n += 1;
+}
+inline void prof_end(Profiler* p, hipStream_t s) {
+  if (!p || !p->on || p->n == 0) return;
+  (void)hipEventRecord(p->ev[p->n], s);
+}
+
+// router.hip
+bool router_fused_ok(bool x_bf16, int N);
+int64_t route_chunk_tokens(bool x_bf16, int N);
+void launch_router_logits(const void* x, bool x_bf16, const float* W_r, const float* b_r,
+                          float* h, int64_t T, int d, int N, hipStream_t s);
+void launch_router_fused(const uint16_t* x, const float* W_r, const float* b_r, int64_t T, int d,
+                         int N, float* logits, int32_t* expert_idx, float* gate, float* P_part,
+                         int32_t* hist, int32_t* rank_local, hipStream_t s);
+void launch_route_rows(const float* h, int64_t T, int N, int32_t* expert_idx, float* gate,
+                       float* P_part, int32_t* hist, int32_t* rank_local, hipStream_t s);
+
+// assign.hip
+void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T,
+                       int64_t C, float alpha, int32_t* load, int32_t* n_kept, float* aux,
+                       hipStream_t s);
+void launch_finalize_positions(int64_t T, const int32_t* expert_idx, const int32_t* rank_local,
+                               const int32_t* offsets, int N, int64_t chunk, int64_t C,
+                               int32_t* position, uint8_t* drop_mask, hipStream_t s);
+
+// move.hip
+void launch_dispatch(const void* x, int64_t T, int row_bytes, const int32_t* expert_idx,
+                     const int32_t* rank_local, const int32_t* offsets, int N, int64_t chunk,
+                     int64_t C, int32_t* position, uint8_t* drop_mask, void* Xbuf, hipStream_t s);
+void launch_combine(const void* x, bool bf16, int64_t T, int row_bytes, const int32_t* expert_idx,
+                    const int32_t* position, const uint8_t* drop_mask, const float* gate,
+                    int64_t C, const void* Ybuf, void* out, hipStream_t s);
+void launch_copy_expert_rows(const void* Ybuf, const int32_t* n_kept, int N, int64_t C,
+                             int row_bytes, void* dst, hipStream_t s);
+
+// gemm.hip
+void launch_expert_gemm(bool bf16, bool relu, const void* A, int64_t strideA, const void* B,
+                        int64_t strideB, void* Cout, int64_t strideC, const int32_t* rows,
+                        int n_experts, int64_t C, int K, int Nout, hipStream_t s);
+bool expert_gemm_shape_ok(bool bf16, int d, int F);
+
+}  // namespace swl

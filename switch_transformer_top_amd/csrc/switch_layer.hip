@@ -1,0 +1,374 @@
+// Host side of the C ABI declared in include/switch_layer.h: argument
+// validation, workspace layout and the launch sequence of one Switch FFN
+// forward pass.  Every step runs in the kernels of this directory; the host
+// only enqueues them on the caller's stream and never waits for them.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+
+#include "kernels.hpp"
+#include "switch_layer.h"
+
+struct switch_layer {
+  switch_config cfg;
+  const float* W_r;
+  const float* b_r;
+  const void* W_in;
+  const void* W_out;
+  int device;
+  swl::Profiler prof;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t dtype_size(int32_t dt) { return dt == SWITCH_BF16 ? 2 : 4; }
+
+// Capacity C = ceil(c * T / N) in double, or the override.  Buffers hold
+// min(C, T) rows per expert: a position is always below T, so a capacity above
+// T drops nothing and a capacity of min(C, T) keeps exactly the same tokens.
+int64_t capacity_of(const switch_config& c, int64_t T) {
+  if (c.capacity_override > 0) return c.capacity_override;
+  double v = ceil((c.capacity_factor * (double)T) / (double)c.n_experts);
+  if (!(v >= 0.0)) return 0;
+  if (v > 9.0e18) v = 9.0e18;
+  return (int64_t)v;
+}
+
+int64_t buffer_rows(const switch_config& c, int64_t T) {
+  int64_t C = capacity_of(c, T);
+  return C < T ? C : T;
+}
+
+struct Layout {
+  size_t logits, ppart, hist, rank, load, nkept, xbuf, hbuf, ybuf, total;
+};
+
+// Chunks of the routing statistics: the fused router uses small chunks, the
+// logits-based path 64 tokens; the workspace is sized for the smaller one.
+int64_t chunk_tokens(const switch_config& c) {
+  return swl::route_chunk_tokens(c.act_dtype == SWITCH_BF16, c.n_experts);
+}
+constexpr int64_t kRowsChunk = 64;  // chunk of the logits-based path
+
+Layout layout_of(const switch_layer* L, int64_t T) {
+  const switch_config& c = L->cfg;
+  const int64_t N = c.n_experts, Cb = buffer_rows(c, T);
+  const int64_t nc = (T + chunk_tokens(c) - 1) / chunk_tokens(c);
+  const size_t es = dtype_size(c.act_dtype);
+  Layout lo;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes); return at; };
+  lo.logits = take(sizeof(float) * (size_t)T * (size_t)N);
+  lo.ppart = take(sizeof(float) * (size_t)nc * (size_t)N);
+  lo.hist = take(sizeof(int32_t) * (size_t)nc * (size_t)N);
+  lo.rank = take(sizeof(int32_t) * (size_t)T);
+  lo.load = take(sizeof(int32_t) * (size_t)N);
+  lo.nkept = take(sizeof(int32_t) * (size_t)N);
+  lo.xbuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_model);
+  lo.hbuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_ff);
+  lo.ybuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_model);
+  lo.total = off;
+  return lo;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+switch_status check_device(const switch_layer* L) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SWITCH_E_HIP;
+  return dev == L->device ? SWITCH_OK : SWITCH_E_INVALID;
+}
+
+// Common validation of the routing outputs and the workspace.
+switch_status check_route_args(const switch_layer* L, int64_t T, const int32_t* expert_idx,
+                               const float* gate, const int32_t* position,
+                               const uint8_t* drop_mask, const float* aux_loss, void* ws,
+                               size_t ws_bytes) {
+  if (!L) return SWITCH_E_INVALID;
+  if (T < 0 || T > L->cfg.t_max) return SWITCH_E_INVALID;
+  if (!aux_loss || !aligned(aux_loss, 4)) return SWITCH_E_INVALID;
+  if (T > 0 && (!expert_idx || !gate || !position || !drop_mask)) return SWITCH_E_INVALID;
+  if (!aligned(expert_idx, 4) || !aligned(gate, 4) || !aligned(position, 4))
+    return SWITCH_E_INVALID;
+  if (!ws || !aligned(ws, 16)) return SWITCH_E_INVALID;
+  if (ws_bytes < layout_of(L, T).total) return SWITCH_E_INVALID;
+  return SWITCH_OK;
+}
+
+struct Routed {
+  int32_t* load;
+  int32_t* nkept;
+  int32_t* offsets;
+  int32_t* rank;
+  int64_t chunk;
+  int64_t Cb;
+};
+
+// Routing stage (logits, softmax / top-1 / gate, chunk statistics, scan and
+// the load-balancing loss).  `x` may be NULL when `given_logits` holds the
+// logits.  Positions and drops are finalised later: by dispatch in a forward
+// call, by finalize_positions otherwise.
+Routed enqueue_routing(switch_layer* L, const void* x, const float* given_logits, int64_t T,
+                       float* logits_out, int32_t* expert_idx, float* gate, float* aux_loss,
+                       int32_t* load, char* ws, const Layout& lo, hipStream_t s) {
+  const switch_config& c = L->cfg;
+  const int N = c.n_experts;
+  const bool bf16 = c.act_dtype == SWITCH_BF16;
+  swl::Profiler* P = &L->prof;
+  Routed r;
+  r.Cb = buffer_rows(c, T);
+  r.load = load ? load : (int32_t*)(ws + lo.load);
+  r.nkept = (int32_t*)(ws + lo.nkept);
+  r.offsets = (int32_t*)(ws + lo.hist);
+  r.rank = (int32_t*)(ws + lo.rank);
+  float* ppart = (float*)(ws + lo.ppart);
+  const bool fused = !given_logits && swl::router_fused_ok(bf16, N);
+  r.chunk = fused ? chunk_tokens(c) : kRowsChunk;
+  if (T > 0) {
+    if (fused) {
+      swl::prof_mark(P, s, "router");
+      swl::launch_router_fused((const uint16_t*)x, L->W_r, L->b_r, T, c.d_model, N, logits_out,
+                               expert_idx, gate, ppart, r.offsets, r.rank, s);
+    } else {
+      const float* h = given_logits;
+      if (!h) {
+        float* hw = logits_out ? logits_out : (float*)(ws + lo.logits);
+        swl::prof_mark(P, s, "router_logits");
+        swl::launch_router_logits(x, bf16, L->W_r, L->b_r, hw, T, c.d_model, N, s);
+        h = hw;
+      }
+      swl::prof_mark(P, s, "route_rows");
+      swl::launch_route_rows(h, T, N, expert_idx, gate, ppart, r.offsets, r.rank, s);
+    }
+  }
+  const int64_t nc = (T + r.chunk - 1) / r.chunk;
+  swl::prof_mark(P, s, "route_scan");
+  swl::launch_route_scan(r.offsets, ppart, nc, N, T, r.Cb, c.alpha, r.load, r.nkept, aux_loss, s);
+  return r;
+}
+
+switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
+                           int32_t* expert_idx, float* gate, int32_t* position,
+                           uint8_t* drop_mask, float* aux_loss, float* logits, int32_t* load,
+                           void* ws, size_t ws_bytes, void* expert_out, hipStream_t s) {
+  switch_status st = check_route_args(L, T, expert_idx, gate, position, drop_mask, aux_loss, ws,
+                                      ws_bytes);
+  if (st != SWITCH_OK) return st;
+  const switch_config& c = L->cfg;
+  const size_t es = dtype_size(c.act_dtype);
+  const size_t xbytes = es * (size_t)T * (size_t)c.d_model;
+  if (T > 0 && (!x || !out)) return SWITCH_E_INVALID;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(logits, 4) || !aligned(load, 4) ||
+      !aligned(expert_out, 16))
+    return SWITCH_E_INVALID;
+  if (overlaps(x, xbytes, out, xbytes)) return SWITCH_E_INVALID;
+  if ((st = check_device(L)) != SWITCH_OK) return st;
+
+  const Layout lo = layout_of(L, T);
+  char* w = (char*)ws;
+  const int N = c.n_experts, d = c.d_model, F = c.d_ff;
+  const bool bf16 = c.act_dtype == SWITCH_BF16;
+  swl::Profiler* P = &L->prof;
+  swl::prof_begin(P);
+
+  Routed r = enqueue_routing(L, x, nullptr, T, logits, expert_idx, gate, aux_loss, load, w, lo, s);
+  const int64_t Cb = r.Cb;
+  void* xbuf = w + lo.xbuf;
+  void* hbuf = w + lo.hbuf;
+  void* ybuf = w + lo.ybuf;
+  if (T > 0) {
+    swl::prof_mark(P, s, "dispatch");
+    swl::launch_dispatch(x, T, (int)(es * d), expert_idx, r.rank, r.offsets, N, r.chunk, Cb,
+                         position, drop_mask, xbuf, s);
+    swl::prof_mark(P, s, "gemm1_relu");
+    swl::launch_expert_gemm(bf16, true, xbuf, Cb * d, L->W_in, (int64_t)F * d, hbuf, Cb * F,
+                            r.nkept, N, Cb, d, F, s);
+    swl::prof_mark(P, s, "gemm2");
+    swl::launch_expert_gemm(bf16, false, hbuf, Cb * F, L->W_out, (int64_t)d * F, ybuf, Cb * d,
+                            r.nkept, N, Cb, F, d, s);
+    swl::prof_mark(P, s, "combine");
+    swl::launch_combine(x, bf16, T, (int)(es * d), expert_idx, position, drop_mask, gate, Cb,
+                        ybuf, out, s);
+    if (expert_out) {
+      swl::prof_mark(P, s, "copy_expert_rows");
+      swl::launch_copy_expert_rows(ybuf, r.nkept, N, Cb, (int)(es * d), expert_out, s);
+    }
+  }
+  swl::prof_end(P, s);
+  return hipGetLastError() == hipSuccess ? SWITCH_OK : SWITCH_E_HIP;
+}
+
+switch_status route_impl(switch_layer* L, const void* x, const float* given_logits, int64_t T,
+                         float* logits_out, int32_t* expert_idx, float* gate, int32_t* position,
+                         uint8_t* drop_mask, float* aux_loss, int32_t* load, void* ws,
+                         hipStream_t s) {
+  const Layout lo = layout_of(L, T);
+  swl::prof_begin(&L->prof);
+  Routed r = enqueue_routing(L, x, given_logits, T, logits_out, expert_idx, gate, aux_loss, load,
+                             (char*)ws, lo, s);
+  if (T > 0) {
+    swl::prof_mark(&L->prof, s, "finalize");
+    swl::launch_finalize_positions(T, expert_idx, r.rank, r.offsets, L->cfg.n_experts, r.chunk,
+                                   r.Cb, position, drop_mask, s);
+  }
+  swl::prof_end(&L->prof, s);
+  return hipGetLastError() == hipSuccess ? SWITCH_OK : SWITCH_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+switch_status switch_layer_create(const switch_config* cfg, const float* W_r, const float* b_r,
+                                  const void* W_in, const void* W_out, switch_layer** out) {
+  if (!cfg || !out) return SWITCH_E_INVALID;
+  *out = nullptr;
+  const switch_config& c = *cfg;
+  if (c.n_experts < 1 || c.n_experts > 8192) return SWITCH_E_INVALID;
+  if (c.d_model < 8 || c.d_model % 8 != 0 || c.d_ff < 8 || c.d_ff % 8 != 0)
+    return SWITCH_E_INVALID;
+  if (c.t_max < 0 || c.t_max > 0x7fffffff) return SWITCH_E_INVALID;
+  if (!(c.capacity_factor >= 0.0) || !isfinite(c.capacity_factor)) return SWITCH_E_INVALID;
+  if (c.capacity_override < 0 || !isfinite(c.alpha)) return SWITCH_E_INVALID;
+  if ((c.act_dtype != SWITCH_F32 && c.act_dtype != SWITCH_BF16) ||
+      (c.expert_dtype != SWITCH_F32 && c.expert_dtype != SWITCH_BF16))
+    return SWITCH_E_INVALID;
+  if (!W_r || !W_in || !W_out) return SWITCH_E_INVALID;
+  if (!aligned(W_r, 16) || !aligned(W_in, 16) || !aligned(W_out, 16) || !aligned(b_r, 4))
+    return SWITCH_E_INVALID;
+  if (c.act_dtype != c.expert_dtype) return SWITCH_E_UNSUPPORTED;
+  if (!swl::expert_gemm_shape_ok(c.act_dtype == SWITCH_BF16, c.d_model, c.d_ff))
+    return SWITCH_E_UNSUPPORTED;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SWITCH_E_HIP;
+  switch_layer* L = new (std::nothrow) switch_layer();
+  if (!L) return SWITCH_E_INVALID;
+  L->cfg = c;
+  L->W_r = W_r;
+  L->b_r = b_r;
+  L->W_in = W_in;
+  L->W_out = W_out;
+  L->device = dev;
+  *out = L;
+  return SWITCH_OK;
+}
+
+void switch_layer_destroy(switch_layer* L) {
+  if (!L) return;
+  if (L->prof.created)
+    for (int i = 0; i <= swl::Profiler::kMax; ++i) (void)hipEventDestroy(L->prof.ev[i]);
+  delete L;
+}
+
+int64_t switch_capacity(const switch_layer* L, int64_t T) {
+  if (!L || T < 0) return -1;
+  return capacity_of(L->cfg, T);
+}
+
+size_t switch_workspace_bytes(const switch_layer* L, int64_t T) {
+  if (!L || T < 0 || T > L->cfg.t_max) return 0;
+  return layout_of(L, T).total;
+}
+
+switch_status switch_route(switch_layer* L, const void* x, int64_t T, float* logits,
+                           int32_t* expert_idx, float* gate, int32_t* position,
+                           uint8_t* drop_mask, float* aux_loss, int32_t* load, void* ws,
+                           size_t ws_bytes, void* stream) {
+  switch_status st = check_route_args(L, T, expert_idx, gate, position, drop_mask, aux_loss, ws,
+                                      ws_bytes);
+  if (st != SWITCH_OK) return st;
+  if (T > 0 && !x) return SWITCH_E_INVALID;
+  if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(load, 4)) return SWITCH_E_INVALID;
+  if ((st = check_device(L)) != SWITCH_OK) return st;
+  return route_impl(L, x, nullptr, T, logits, expert_idx, gate, position, drop_mask, aux_loss,
+                    load, ws, (hipStream_t)stream);
+}
+
+switch_status switch_route_from_logits(switch_layer* L, const float* logits, int64_t T,
+                                       int32_t* expert_idx, float* gate, int32_t* position,
+                                       uint8_t* drop_mask, float* aux_loss, int32_t* load,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  switch_status st = check_route_args(L, T, expert_idx, gate, position, drop_mask, aux_loss, ws,
+                                      ws_bytes);
+  if (st != SWITCH_OK) return st;
+  if ((T > 0 && !logits) || !aligned(logits, 4) || !aligned(load, 4)) return SWITCH_E_INVALID;
+  if ((st = check_device(L)) != SWITCH_OK) return st;
+  return route_impl(L, nullptr, logits, T, nullptr, expert_idx, gate, position, drop_mask,
+                    aux_loss, load, ws, (hipStream_t)stream);
+}
+
+switch_status switch_forward(switch_layer* L, const void* x, int64_t T, void* out,
+                             int32_t* expert_idx, float* gate, int32_t* position,
+                             uint8_t* drop_mask, float* aux_loss, float* logits, int32_t* load,
+                             void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(L, x, T, out, expert_idx, gate, position, drop_mask, aux_loss, logits, load,
+                      ws, ws_bytes, nullptr, (hipStream_t)stream);
+}
+
+switch_status switch_forward_debug(switch_layer* L, const void* x, int64_t T, void* out,
+                                   int32_t* expert_idx, float* gate, int32_t* position,
+                                   uint8_t* drop_mask, float* aux_loss, float* logits,
+                                   int32_t* load, void* ws, size_t ws_bytes, void* expert_out,
+                                   void* stream) {
+  // an empty expert buffer (capacity 0 or T = 0) may come as NULL
+  if (!L || (!expert_out && T >= 0 && T <= L->cfg.t_max && buffer_rows(L->cfg, T) > 0))
+    return SWITCH_E_INVALID;
+  return forward_impl(L, x, T, out, expert_idx, gate, position, drop_mask, aux_loss, logits, load,
+                      ws, ws_bytes, expert_out, (hipStream_t)stream);
+}
+
+switch_status switch_profile_enable(switch_layer* L, int enable) {
+  if (!L) return SWITCH_E_INVALID;
+  if (enable && !L->prof.created) {
+    for (int i = 0; i <= swl::Profiler::kMax; ++i) {
+      if (hipEventCreate(&L->prof.ev[i]) != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(L->prof.ev[j]);
+        return SWITCH_E_HIP;
+      }
+    }
+    L->prof.created = true;
+  }
+  L->prof.on = enable != 0;
+  L->prof.n = 0;
+  return SWITCH_OK;
+}
+
+int switch_profile_read(switch_layer* L, float* ms, const char** names, int cap) {
+  if (!L || !L->prof.created || cap < 0) return -1;
+  const int n = L->prof.n;
+  if (n == 0) return 0;
+  if (hipEventSynchronize(L->prof.ev[n]) != hipSuccess) return -1;
+  for (int i = 0; i < n && i < cap; ++i) {
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, L->prof.ev[i], L->prof.ev[i + 1]) != hipSuccess) return -1;
+    if (ms) ms[i] = t;
+    if (names) names[i] = L->prof.names[i];
+  }
+  return n;
+}
+
+const char* switch_status_string(switch_status s) {
+  switch (s) {
+    case SWITCH_OK: return "SWITCH_OK";
+    case SWITCH_E_INVALID: return "SWITCH_E_INVALID: invalid argument";
+    case SWITCH_E_UNSUPPORTED: return "SWITCH_E_UNSUPPORTED: unsupported dtype or shape";
+    case SWITCH_E_HIP: return "SWITCH_E_HIP: HIP runtime error";
+  }
+  return "unknown switch_status";
+}
+
+switch_status switch_last_async_error(void) {
+  return hipGetLastError() == hipSuccess ? SWITCH_OK : SWITCH_E_HIP;
+}
+
+}  // extern "C"

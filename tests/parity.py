@@ -1,0 +1,150 @@
+"""Parity checks of the HIP layer against the CPU oracle (test infrastructure).
+
+The bars (from the layer's contract):
+  routing stage   expert_idx, position, drop_mask, load: bit-exact against the
+                  oracle's routing fed the GPU's own fp32 logits; gate within
+                  1e-6 relative; aux_loss within 1e-5 relative.
+  logits          within the standard error bound of an fp32-accumulated dot
+                  product, |h - h*| <= gamma_n sum_k |x_k w_k| + |b| u,
+                  gamma_n = n u / (1 - n u), u = 2^-24, with n = 3d: the bf16
+                  router splits every fp32 weight exactly into three bf16
+                  pieces, so it sums 3d exact products (doubled to cover the
+                  bias add and the order of the sum).
+  end to end      expert_idx and gate on every token whose oracle top-1/top-2
+                  logit margin exceeds 1e-4; position/drop end to end when no
+                  low-margin token flipped.
+  output          |out - ref| <= 1e-2 (1 + |ref|) against the oracle's combine
+                  evaluated with the GPU's (verified) routing; dropped tokens
+                  equal x bit for bit.
+  expert output   (stricter, not part of the contract) kept rows of the expert
+                  output within 2^-6 (|E| + rms(E)) of the oracle's E.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import synthetic as S
+
+U32 = 2.0 ** -24
+
+
+def margins(h: np.ndarray) -> np.ndarray:
+    """top-1 minus top-2 logit per row (inf for N = 1)."""
+    if h.shape[1] == 1:
+        return np.full(h.shape[0], np.inf)
+    part = np.partition(h, -2, axis=1)
+    return part[:, -1] - part[:, -2]
+
+
+def logits_bound(xf: np.ndarray, W_r: np.ndarray, b_r) -> np.ndarray:
+    n = 3 * xf.shape[1]
+    gamma = n * U32 / (1 - n * U32)
+    mag = np.abs(xf.astype(np.float64)) @ np.abs(W_r.astype(np.float64)).T
+    bound = 2.0 * gamma * mag
+    if b_r is not None:
+        bound += 2.0 * np.abs(b_r.astype(np.float64)) * U32
+    return bound + 1e-30
+
+
+def check_routing_stage(res: dict, spec, tag: str = "") -> dict:
+    """Oracle routing fed the GPU's logits must match bit for bit."""
+    ref = oracle.route(res["logits"].astype(np.float64), spec.c, spec.capacity_override, spec.alpha)
+    assert np.array_equal(res["expert_idx"], ref["expert_idx"]), f"{tag} expert_idx"
+    assert np.array_equal(res["position"], ref["position"]), f"{tag} position"
+    assert np.array_equal(res["drop_mask"], ref["drop"]), f"{tag} drop_mask"
+    assert np.array_equal(res["load"], ref["load"]), f"{tag} load"
+    rel = np.abs(res["gate"].astype(np.float64) - ref["gate"]) / ref["gate"]
+    assert rel.max(initial=0) <= 1e-6, f"{tag} gate rel err {rel.max()}"
+    if ref["aux"] != 0:
+        arel = abs(res["aux_loss"] - ref["aux"]) / abs(ref["aux"])
+        assert arel <= 1e-5, f"{tag} aux rel err {arel}"
+    else:
+        assert res["aux_loss"] == 0.0
+    return ref
+
+
+def check_logits(h_gpu: np.ndarray, xf: np.ndarray, W_r, b_r, rows=None, tag=""):
+    """Logit error bound on all rows, or on `rows` (indices) of a large call."""
+    if rows is None:
+        rows = np.arange(xf.shape[0])
+    h_ref = oracle.logits(xf[rows], W_r, b_r)
+    err = np.abs(h_gpu[rows].astype(np.float64) - h_ref)
+    bound = logits_bound(xf[rows], W_r, b_r)
+    worst = (err / bound).max(initial=0)
+    assert worst <= 1.0, f"{tag} logits exceed the dot-product bound (ratio {worst})"
+    return h_ref
+
+
+def check_end_to_end(res: dict, h_ref: np.ndarray, spec, rows=None, tag=""):
+    """Independent oracle routing on tokens with a clear top-1 (margin > 1e-4)."""
+    ref = oracle.route(h_ref, spec.c, spec.capacity_override, spec.alpha) if rows is None else None
+    h_rows = h_ref
+    idx = np.arange(h_ref.shape[0]) if rows is None else rows
+    mg = margins(h_rows)
+    clear = mg > 1e-4
+    top = np.argmax(h_rows, axis=1)
+    assert np.array_equal(res["expert_idx"][idx][clear], top[clear]), f"{tag} e2e expert_idx"
+    dh = np.abs(res["logits"][idx].astype(np.float64) - h_rows).max(initial=0)
+    m = h_rows.max(axis=1, keepdims=True)
+    g_ref = 1.0 / np.exp(h_rows - m).sum(axis=1)
+    rel = np.abs(res["gate"][idx].astype(np.float64) - g_ref) / g_ref
+    assert (rel[clear] <= 2 * dh + 1e-6).all(), f"{tag} e2e gate"
+    flips = int((res["expert_idx"][idx] != top).sum())
+    if ref is not None and flips == 0:
+        assert np.array_equal(res["position"], ref["position"]), f"{tag} e2e position"
+        assert np.array_equal(res["drop_mask"], ref["drop"]), f"{tag} e2e drop"
+        assert abs(res["aux_loss"] - ref["aux"]) <= 1e-5 * abs(ref["aux"]) + 1e-6
+    return flips
+
+
+def check_output_full(res: dict, spec, host: dict, tag=""):
+    """Output of every token against the oracle combine with the GPU routing."""
+    xf = S.to_f32(host["x"], spec.act)
+    W_in = S.to_f32(host["W_in"], spec.expert)
+    W_out = S.to_f32(host["W_out"], spec.expert)
+    out_ref, E_ref = oracle.combine(xf, res["expert_idx"], res["gate"].astype(np.float64),
+                                    res["drop_mask"], W_in, W_out)
+    _check_out_rows(res, spec, host["x"], out_ref, E_ref, np.arange(spec.T), tag)
+
+
+def check_output_rows(res: dict, spec, x_host: np.ndarray, rows: np.ndarray, expert_weights,
+                      tag=""):
+    """Output of sampled tokens; expert_weights(e) -> (W_in_e f32, W_out_e f32)."""
+    xf = S.to_f32(x_host, spec.act)
+    d = spec.d
+    out_ref = np.empty((len(rows), d))
+    E_ref = np.empty((len(rows), d))
+    cache = {}
+    for j, t in enumerate(rows):
+        e = int(res["expert_idx"][t])
+        if e not in cache:
+            cache[e] = expert_weights(e)
+        o, E = oracle.token_output(xf[t], res["drop_mask"][t], float(res["gate"][t]), *cache[e])
+        out_ref[j], E_ref[j] = o, E
+    full_out = np.zeros((spec.T, d))
+    full_E = np.zeros((spec.T, d))
+    full_out[rows], full_E[rows] = out_ref, E_ref
+    _check_out_rows(res, spec, x_host, full_out, full_E, rows, tag)
+
+
+def _check_out_rows(res, spec, x_host, out_ref, E_ref, rows, tag):
+    out = S.to_f32(res["out"], spec.act).astype(np.float64)
+    drop = res["drop_mask"][rows].astype(bool)
+    # dropped tokens pass through bit for bit
+    assert np.array_equal(res["out"][rows][drop], x_host[rows][drop]), f"{tag} dropped rows changed"
+    err = np.abs(out[rows] - out_ref[rows])
+    tol = 1e-2 * (1 + np.abs(out_ref[rows]))
+    assert (err <= tol).all(), f"{tag} out err {(err - tol).max()}"
+    if "expert_out" in res:
+        kept = rows[~drop]
+        if len(kept):
+            eo = S.to_f32(res["expert_out"], spec.act).astype(np.float64)
+            Cb = res["expert_out"].shape[1]
+            e = res["expert_idx"][kept].astype(np.int64)
+            p = res["position"][kept].astype(np.int64)
+            got = eo.reshape(-1, spec.d)[e * Cb + p]
+            want = E_ref[kept]
+            rms = np.sqrt(np.mean(want ** 2)) + 1e-30
+            bad = np.abs(got - want) > 2.0 ** -6 * (np.abs(want) + rms)
+            assert not bad.any(), f"{tag} expert output: {bad.sum()} elements off"

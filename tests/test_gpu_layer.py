@@ -1,0 +1,191 @@
+"""GPU parity of the HIP Switch layer against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as S
+from golden_util import keyed, rows
+import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from switch_transformer_top_amd import binding
+    return binding
+
+
+def _run(B, spec, host=None, debug=True):
+    host = host or S.host_inputs(spec)
+    layer = B.SwitchLayer.from_host(spec, host)
+    print(f"[case] {spec.name} T={spec.T} d={spec.d} F={spec.F} N={spec.N} c={spec.c}", flush=True)
+    res = layer.forward_host(host["x"], debug=debug)
+    return host, layer, res
+
+
+def _full_check(spec, host, res, tag):
+    parity.check_routing_stage(res, spec, tag)
+    xf = S.to_f32(host["x"], spec.act)
+    h_ref = parity.check_logits(res["logits"], xf, host["W_r"], host["b_r"], tag=tag)
+    parity.check_end_to_end(res, h_ref, spec, tag=tag)
+    parity.check_output_full(res, spec, host, tag)
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_tiny_fp32_config(B):
+    spec = S.CONFIGS[1]
+    host, _, res = _run(B, spec)
+    assert int(res["drop_mask"].sum()) >= 0
+    _full_check(spec, host, res, "tiny-fp32")
+
+
+@pytest.mark.parametrize("T,N,d,F,c,seed", [
+    (1000, 8, 256, 512, 1.0, 21),      # ragged T, several M tiles, drops
+    (777, 5, 128, 384, 1.25, 22),      # odd expert count
+    (130, 16, 128, 256, 0.5, 23),      # heavy overflow
+    (64, 1, 128, 128, 1.0, 24),        # one expert: gate 1, aux alpha
+    (9, 32, 128, 128, 2.0, 25),        # T < N
+])
+def test_bf16_ragged_shapes(B, T, N, d, F, c, seed):
+    spec = S.Spec(f"bf16-{T}-{N}", T=T, d=d, F=F, N=N, c=c, seed=seed)
+    host, _, res = _run(B, spec)
+    _full_check(spec, host, res, spec.name)
+    if N == 1:
+        assert np.all(res["gate"] == 1.0)
+        assert res["aux_loss"] == pytest.approx(spec.alpha, rel=1e-6)
+
+
+def test_switch_base_config_full(B):
+    spec = S.CONFIGS[2]
+    host, _, res = _run(B, spec)
+    _full_check(spec, host, res, "switch-base")
+
+
+def test_zipf_overflow_config_full(B):
+    spec = S.CONFIGS[3]
+    host, _, res = _run(B, spec)
+    _full_check(spec, host, res, "zipf")
+    assert res["drop_mask"].mean() > 0.3        # the Zipf bias overflows popular experts
+    assert (res["load"] < 0.25 * 128).sum() > 20  # and leaves many experts nearly empty
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_zero_tokens(B):
+    spec = S.Spec("empty", T=0, d=128, F=128, N=4, c=1.0, seed=30)
+    host = S.host_inputs(spec.with_(T=1))
+    layer = B.SwitchLayer.from_host(spec, host, t_max=8)
+    bufs = layer.alloc(0)
+    bufs["aux_loss"].fill_(123.0)
+    bufs["load"].fill_(-5)
+    x = torch.empty((0, 128), dtype=torch.int16, device="cuda")
+    layer.forward(x, 0, bufs)
+    torch.cuda.synchronize()
+    assert float(bufs["aux_loss"].item()) == 0.0
+    assert int(bufs["load"].abs().sum().item()) == 0
+
+
+def test_capacity_zero_passes_everything_through(B):
+    spec = S.Spec("c0", T=300, d=128, F=256, N=4, c=0.0, seed=31)
+    host, _, res = _run(B, spec)
+    assert np.all(res["drop_mask"] == 1)
+    assert np.array_equal(res["out"], host["x"])
+    parity.check_routing_stage(res, spec, "c0")
+
+
+def test_large_capacity_drops_nothing(B):
+    spec = S.Spec("cN", T=500, d=128, F=256, N=4, c=4.0, seed=32)
+    host, _, res = _run(B, spec)
+    assert not res["drop_mask"].any()
+    _full_check(spec, host, res, "cN")
+
+
+def test_deterministic_bitwise(B):
+    spec = S.Spec("det", T=2000, d=256, F=512, N=16, c=1.0, seed=33)
+    host = S.host_inputs(spec)
+    layer = B.SwitchLayer.from_host(spec, host)
+    a = layer.forward_host(host["x"])
+    b = layer.forward_host(host["x"])
+    for k in ("out", "expert_idx", "gate", "position", "drop_mask", "logits", "load"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["aux_loss"] == b["aux_loss"]
+
+
+# ---------------------------------------------------------------- pinned examples through the GPU
+
+def _route_logits(B, h: np.ndarray, c: float, capacity_override: int = 0):
+    """GPU routing stage (switch_route_from_logits) on given fp32 logits."""
+    T, N = h.shape
+    spec = S.Spec("pin", T=T, d=128, F=128, N=N, c=c, seed=40, capacity_override=capacity_override)
+    host = S.host_inputs(spec)
+    layer = B.SwitchLayer.from_host(spec, host)
+    bufs = layer.alloc(T)
+    hl = torch.from_numpy(np.ascontiguousarray(h, dtype=np.float32)).cuda()
+    layer.route_from_logits(hl, T, bufs)
+    torch.cuda.synchronize()
+    r = {k: B.from_device(bufs[k]) for k in ("expert_idx", "gate", "position", "drop_mask", "load")}
+    r["aux_loss"] = float(bufs["aux_loss"].item())
+    r["logits"] = h.astype(np.float32)
+    return r, spec
+
+
+def test_pin_softmax_table_on_gpu(B):
+    tab = np.array([[float(v) for v in r] for r in rows("ms_softmax_table.txt")])
+    p, sel = tab[:, :4], tab[:, 4].astype(np.int32)
+    h = np.log(np.where(p > 0, p, 1e-12)).astype(np.float32)
+    r, spec = _route_logits(B, h, c=1.0)
+    assert np.array_equal(r["expert_idx"], sel)
+    assert list(r["drop_mask"]) == [0, 0, 1, 1, 0]
+    assert r["aux_loss"] == pytest.approx(0.01 * 4 * 0.472, rel=1e-5)
+    parity.check_routing_stage(r, spec, "softmax-table")
+
+
+def test_pin_sixteen_tokens_on_gpu(B):
+    g = keyed("kb_capacity_16_4.txt")
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(np.repeat(np.arange(4), g["loads"]))
+    h = rng.uniform(-0.1, 0.1, size=(16, 4))
+    h[np.arange(16), perm] += 10.0
+    r, spec = _route_logits(B, h.astype(np.float32), c=g["c"])
+    assert list(r["load"]) == g["loads"]
+    assert int(r["drop_mask"].sum()) == g["overflow_count"]
+    assert set(perm[r["drop_mask"].astype(bool)]) == {g["overflow_expert"]}
+    parity.check_routing_stage(r, spec, "sixteen")
+
+
+def test_pin_ties_and_uniform_aux_on_gpu(B):
+    r, spec = _route_logits(B, np.zeros((50, 8), np.float32), c=1.0)
+    assert np.all(r["expert_idx"] == 0)
+    assert np.allclose(r["gate"], 1 / 8, rtol=1e-7)
+    assert r["aux_loss"] == pytest.approx(0.01, rel=1e-6)
+    h = np.full((3, 6), -1.0, np.float32)
+    h[:, 2] = h[:, 4] = 2.0
+    r, _ = _route_logits(B, h, c=1.0)
+    assert np.all(r["expert_idx"] == 2)
+
+
+def test_pin_hand_example_on_gpu(B):
+    """The overflowing token passes through unchanged (byhand.ai steps 7 and 13).
+    fp32 layer, d padded with zero features to the library's multiple of 8."""
+    g = keyed("bh_hand_example.txt")
+    d = F = 8
+    W_r = np.zeros((3, d), np.float32)
+    W_r[:, :3] = [[0, 0, 2], [0, 1, 0], g["switch_row_C"]]
+    x = np.zeros((5, d), np.float32)
+    x[:, :3] = [[0, 0, 3], [0, 2, 1], [0, 3, -1], [0, 3, 1], g["Z5"]]
+    rng = np.random.default_rng(0)
+    W_in = rng.normal(0, 0.5, size=(3, F, d)).astype(np.float32)
+    W_out = rng.normal(0, 0.5, size=(3, d, F)).astype(np.float32)
+    spec = S.Spec("hand", T=5, d=d, F=F, N=3, c=1.0, act="f32", expert="f32")
+    host = dict(x=x, W_r=W_r, b_r=None, W_in=W_in, W_out=W_out)
+    _, _, res = _run(B, spec, host)
+    assert list(res["expert_idx"]) == [0, 2, 1, 2, 2]
+    assert res["drop_mask"][4] == 1 and res["position"][4] == g["capacity"]
+    assert np.array_equal(res["out"][4], x[4])
+    _full_check(spec, host, res, "hand")
