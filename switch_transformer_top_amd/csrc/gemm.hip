@@ -218,6 +218,138 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
   }
 }
 
+// Deep-pipelined variant: PF register sets keep K tiles k+1 .. k+PF in flight
+// while tile k is multiplied out of a double-buffered LDS (one barrier per K
+// step).  Each step first stores tile k+1 (loaded PF-1 steps earlier) into the
+// other LDS buffer, refills that register set with tile k+1+PF, then runs the
+// MFMAs of tile k.
+template <int BM, int BN, int PF, bool RELU>
+__global__ __launch_bounds__(256) void gemm_bf16_deep_kernel(
+    const uint16_t* __restrict__ A, int64_t strideA, const uint16_t* __restrict__ B,
+    int64_t strideB, uint16_t* __restrict__ Cout, int64_t strideC,
+    const int32_t* __restrict__ rows, int K, int Nout, int m_tiles, int n_tiles, int tiles) {
+  constexpr int LA = BM / 32, LB = BN / 32;
+  constexpr int TI = BM / 64, TJ = BN / 64;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * GB_LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * GB_LDK];
+
+  const int per_xcd = (tiles + 7) >> 3;
+  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (tile >= tiles) return;
+  const int mt = tile % m_tiles;
+  const int nt = (tile / m_tiles) % n_tiles;
+  const int e = tile / (m_tiles * n_tiles);
+  const int rows_e = rows[e];
+  const int m0 = mt * BM;
+  if (m0 >= rows_e) return;
+  const int n0 = nt * BN;
+
+  const uint16_t* Ae = A + (int64_t)e * strideA;
+  const uint16_t* Be = B + (int64_t)e * strideB + (int64_t)n0 * K;
+  uint16_t* Ce = Cout + (int64_t)e * strideC;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lrow = tid >> 3, lcol = (tid & 7) * 8;
+
+  int64_t a_off[LA], b_off[LB];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    int r = m0 + lrow + 32 * j;
+    r = r < rows_e ? r : rows_e - 1;
+    a_off[j] = (int64_t)r * K + lcol;
+  }
+#pragma unroll
+  for (int j = 0; j < LB; ++j) b_off[j] = (int64_t)(lrow + 32 * j) * K + lcol;
+
+  floatx16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int nk = K / GB_BK;
+  const int last = (nk - 1) * GB_BK;
+  u32x4 ra[PF][LA], rb[PF][LB];
+  auto fetch = [&](int set, int kt) {
+    int k = kt * GB_BK;
+    k = k < last ? k : last;
+#pragma unroll
+    for (int j = 0; j < LA; ++j) ra[set][j] = *reinterpret_cast<const u32x4*>(Ae + a_off[j] + k);
+#pragma unroll
+    for (int j = 0; j < LB; ++j) rb[set][j] = *reinterpret_cast<const u32x4*>(Be + b_off[j] + k);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto stash = [&](int set, int buf) {
+#pragma unroll
+    for (int j = 0; j < LA; ++j)
+      *reinterpret_cast<u32x4*>(&As[buf][(lrow + 32 * j) * GB_LDK + lcol]) = ra[set][j];
+#pragma unroll
+    for (int j = 0; j < LB; ++j)
+      *reinterpret_cast<u32x4*>(&Bs[buf][(lrow + 32 * j) * GB_LDK + lcol]) = rb[set][j];
+  };
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < GB_BK; ks += 16) {
+      bf16x8 a[TI], b[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(
+            &As[buf][(wm * (BM / 2) + i * 32 + fr) * GB_LDK + ks + fk]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(
+            &Bs[buf][(wn * (BN / 2) + j * 32 + fr) * GB_LDK + ks + fk]);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // prologue: tiles 0 .. PF in flight, tile 0 in LDS buffer 0
+#pragma unroll
+  for (int p = 0; p < PF; ++p) fetch(p, p);
+  stash(0, 0);
+  fetch(0, PF);
+  __syncthreads();
+  // step kt uses register set (kt + 1) % PF for tile kt + 1
+  for (int kt = 0; kt < nk; kt += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int k = kt + u;
+      if (k < nk) {
+        const int set = (u + 1) % PF;
+        stash(set, (k + 1) & 1);
+        fetch(set, k + 1 + PF);
+        compute(k & 1);
+        __syncthreads();
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (r >= rows_e) continue;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int c = n0 + wn * (BN / 2) + j * 32 + fr;
+        float val = acc[i][j][v];
+        if (RELU) val = val > 0.f ? val : 0.f;
+        Ce[(int64_t)r * Nout + c] = f32_to_bf16_bits(val);
+      }
+    }
+  }
+}
+
 // fp32 path (parity-sized fp32 layers): 32 x 32 tile, K in steps of 32, each
 // of 256 threads owns 4 rows of one column.  Any sizes (bounds-checked).
 template <bool RELU>

@@ -111,7 +111,7 @@ def check_output_full(res: dict, spec, host: dict, tag=""):
 def check_output_rows(res: dict, spec, x_host: np.ndarray, rows: np.ndarray, expert_weights,
                       tag=""):
     """Output of sampled tokens; expert_weights(e) -> (W_in_e f32, W_out_e f32)."""
-    xf = S.to_f32(x_host, spec.act)
+    xf = S.to_f32(x_host[rows], spec.act)
     d = spec.d
     out_ref = np.empty((len(rows), d))
     E_ref = np.empty((len(rows), d))
@@ -120,31 +120,28 @@ def check_output_rows(res: dict, spec, x_host: np.ndarray, rows: np.ndarray, exp
         e = int(res["expert_idx"][t])
         if e not in cache:
             cache[e] = expert_weights(e)
-        o, E = oracle.token_output(xf[t], res["drop_mask"][t], float(res["gate"][t]), *cache[e])
+        o, E = oracle.token_output(xf[j], res["drop_mask"][t], float(res["gate"][t]), *cache[e])
         out_ref[j], E_ref[j] = o, E
-    full_out = np.zeros((spec.T, d))
-    full_E = np.zeros((spec.T, d))
-    full_out[rows], full_E[rows] = out_ref, E_ref
-    _check_out_rows(res, spec, x_host, full_out, full_E, rows, tag)
+    _check_out_rows(res, spec, x_host, out_ref, E_ref, rows, tag)
 
 
 def _check_out_rows(res, spec, x_host, out_ref, E_ref, rows, tag):
-    out = S.to_f32(res["out"], spec.act).astype(np.float64)
+    """out_ref / E_ref hold one row per entry of `rows`."""
+    out = S.to_f32(res["out"][rows], spec.act).astype(np.float64)
     drop = res["drop_mask"][rows].astype(bool)
     # dropped tokens pass through bit for bit
     assert np.array_equal(res["out"][rows][drop], x_host[rows][drop]), f"{tag} dropped rows changed"
-    err = np.abs(out[rows] - out_ref[rows])
-    tol = 1e-2 * (1 + np.abs(out_ref[rows]))
+    err = np.abs(out - out_ref)
+    tol = 1e-2 * (1 + np.abs(out_ref))
     assert (err <= tol).all(), f"{tag} out err {(err - tol).max()}"
     if "expert_out" in res:
-        kept = rows[~drop]
-        if len(kept):
-            eo = S.to_f32(res["expert_out"], spec.act).astype(np.float64)
+        kept = ~drop
+        if kept.any():
             Cb = res["expert_out"].shape[1]
-            e = res["expert_idx"][kept].astype(np.int64)
-            p = res["position"][kept].astype(np.int64)
-            got = eo.reshape(-1, spec.d)[e * Cb + p]
+            e = res["expert_idx"][rows][kept].astype(np.int64)
+            p = res["position"][rows][kept].astype(np.int64)
+            got = S.to_f32(res["expert_out"].reshape(-1, spec.d)[e * Cb + p], spec.act)
             want = E_ref[kept]
             rms = np.sqrt(np.mean(want ** 2)) + 1e-30
-            bad = np.abs(got - want) > 2.0 ** -6 * (np.abs(want) + rms)
+            bad = np.abs(got.astype(np.float64) - want) > 2.0 ** -6 * (np.abs(want) + rms)
             assert not bad.any(), f"{tag} expert output: {bad.sum()} elements off"

@@ -1,0 +1,117 @@
+"""Full-size parity for the two largest workloads, checked on samples.
+
+Switch-Large-shaped (T=32768, d=1024, F=4096, 128 experts) and one GPU's share
+of a 2048-expert layer (T=131072, d=2048, F=6144, ~103 GB of bf16 weights).
+The expert weight banks are written straight into HBM by the device twin of the
+input generator; the oracle regenerates the experts it needs on the host from
+the same counter-based definition (a test below checks the two agree).
+Routing is checked on every token (oracle routing stage fed the GPU logits);
+logits, expert outputs and layer outputs on sampled tokens.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import synthetic as S
+import parity
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from switch_transformer_top_amd import binding
+    return binding
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_device_generator_matches_host(B):
+    spec = S.CONFIGS[4]
+    for tid, count, start in ((S.TENSOR_WIN, 100_003, 7_777_777), (S.TENSOR_WOUT, 4096, 0),
+                              (S.TENSOR_X, 50_000, 123), (S.TENSOR_WR, 1000, 5)):
+        dt = S.tensor_dtype(spec, tid)
+        buf = torch.empty(count, dtype=torch.int16 if dt == "bf16" else torch.float32,
+                          device="cuda")
+        S.gpu_fill(spec, tid, buf.data_ptr(), start, count)
+        torch.cuda.synchronize()
+        got = B.from_device(buf)
+        want = S.tensor(spec, tid, start=start, count=count)
+        assert np.array_equal(got, want), f"tensor {tid}: {np.sum(got != want)} mismatches"
+
+
+def _device_layer(B, spec):
+    """Weights generated on the device; x and W_r on the host (the oracle needs them)."""
+    dev = torch.device("cuda:0")
+    host = S.host_inputs(spec, with_experts=False)
+    per = spec.N * spec.F * spec.d
+    W_in = torch.empty(per, dtype=torch.int16, device=dev)
+    W_out = torch.empty(per, dtype=torch.int16, device=dev)
+    S.gpu_fill(spec, S.TENSOR_WIN, W_in.data_ptr(), 0, per)
+    S.gpu_fill(spec, S.TENSOR_WOUT, W_out.data_ptr(), 0, per)
+    W_r = torch.from_numpy(host["W_r"]).to(dev)
+    b_r = None if host["b_r"] is None else torch.from_numpy(host["b_r"]).to(dev)
+    cfg = B.switch_config(t_max=spec.T, d_model=spec.d, d_ff=spec.F, n_experts=spec.N,
+                          capacity_factor=spec.c, capacity_override=0, alpha=spec.alpha,
+                          act_dtype=B.SWITCH_BF16, expert_dtype=B.SWITCH_BF16)
+    layer = B.SwitchLayer(cfg, W_r, b_r, W_in, W_out)
+    return host, layer
+
+
+def _sample_rows(res, rng, n_experts_sample=6, per_expert=6):
+    """Tokens of a few experts: kept ones and, where there are any, dropped ones."""
+    e_idx = res["expert_idx"]
+    experts = rng.choice(np.unique(e_idx), size=min(n_experts_sample, len(np.unique(e_idx))),
+                         replace=False)
+    rows = []
+    for e in experts:
+        toks = np.flatnonzero(e_idx == e)
+        kept = toks[res["drop_mask"][toks] == 0]
+        dropped = toks[res["drop_mask"][toks] == 1]
+        rows += list(rng.choice(kept, size=min(per_expert, len(kept)), replace=False))
+        rows += list(dropped[:2])
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _check_large(B, spec, tag):
+    print(f"[case] {tag} T={spec.T} d={spec.d} F={spec.F} N={spec.N}", flush=True)
+    host, layer = _device_layer(B, spec)
+    res = layer.forward_host(host["x"], debug=True)
+    print(f"[case] {tag}: forward done, kept={int((res['drop_mask'] == 0).sum())}", flush=True)
+    parity.check_routing_stage(res, spec, tag)
+    rng = np.random.default_rng(spec.seed)
+    xf = S.to_f32(host["x"], spec.act)
+    rows = np.unique(np.concatenate([rng.choice(spec.T, size=256, replace=False),
+                                     _sample_rows(res, rng)]))
+    h_ref = parity.check_logits(res["logits"], xf, host["W_r"], host["b_r"], rows=rows, tag=tag)
+    parity.check_end_to_end(res, h_ref, spec, rows=rows, tag=tag)
+    out_rows = _sample_rows(res, rng)
+
+    def weights(e):
+        return (S.to_f32(S.expert_slice(spec, S.TENSOR_WIN, int(e)), "bf16"),
+                S.to_f32(S.expert_slice(spec, S.TENSOR_WOUT, int(e)), "bf16"))
+
+    parity.check_output_rows(res, spec, host["x"], out_rows, weights, tag)
+    # every dropped token passes through bit for bit
+    drop = res["drop_mask"].astype(bool)
+    assert np.array_equal(res["out"][drop], host["x"][drop])
+    del layer, res
+    _free()
+
+
+def test_switch_large_config_sampled(B):
+    _check_large(B, S.CONFIGS[4], "switch-large")
+
+
+def test_switch_c_share_config_sampled(B):
+    props = torch.cuda.get_device_properties(0)
+    if props.total_memory < 150 * 2 ** 30:
+        pytest.skip("needs ~110 GB of device memory")
+    _check_large(B, S.CONFIGS[5], "switch-c-share")
