@@ -8,9 +8,10 @@ combine) on seeded synthetic inputs already resident in HBM.  The default
 workload is the Switch-Base-shaped layer: T=4096 tokens, d_model=768,
 d_ff=3072, 8 experts, capacity factor 1.25.
 
-Prints one JSON line: routed tokens/s over K timed steps, the roofline of the
-dominant kernel (algorithmic work / its mean duration from HIP events recorded
-on the library's stream), and the CPU oracle's throughput on the host cores.
+Prints one JSON line: routed tokens/s over K timed steps; the roofline of the
+dominant kernel (algorithmic work per launch / its mean duration from HIP
+events the library records on its own stream over a second pass of K steps);
+and the CPU oracle's throughput on the host cores.
 """
 from __future__ import annotations
 
@@ -31,21 +32,24 @@ METRIC = "Switch-FFN fwd routed tokens/s (bf16); % MFMA peak & dispatch % HBM BW
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+# workloads whose weight banks are written into HBM by the device generator
+DEVICE_WEIGHTS = {4, 5}
 
 
 def stage_work(stage: str, spec, kept: int, active_experts: int) -> dict:
     """Algorithmic FLOPs and HBM bytes one launch of a stage must do."""
     T, d, F, N = spec.T, spec.d, spec.F, spec.N
     es = 2 if spec.act == "bf16" else 4
-    if stage == "router_logits":
-        return dict(flops=2.0 * T * d * N, bytes=T * d * es + N * d * 4 + T * N * 4,
+    if stage in ("router", "router_logits"):
+        # the fused router reads x and W_r and writes the per-token routing results
+        return dict(flops=2.0 * T * d * N, bytes=T * d * es + N * d * 4 + 8 * T,
                     peak_tflops=PEAK_FP32_TFLOPS)
     if stage in ("gemm1_relu", "gemm2"):
         return dict(flops=2.0 * kept * d * F,
                     bytes=active_experts * d * F * es + kept * (d + F) * es,
                     peak_tflops=PEAK_BF16_TFLOPS if spec.expert == "bf16" else PEAK_FP32_TFLOPS)
     if stage == "dispatch":
-        return dict(flops=0.0, bytes=2 * kept * d * es, peak_tflops=None)
+        return dict(flops=0.0, bytes=2 * kept * d * es + 9 * T, peak_tflops=None)
     if stage == "combine":
         return dict(flops=0.0, bytes=(kept + 2 * T) * d * es + 13 * T, peak_tflops=None)
     if stage == "route_rows":
@@ -59,33 +63,91 @@ def roofline_entry(stage: str, work: dict, ms: float) -> dict:
     t_hbm = work["bytes"] / (PEAK_HBM_GBS * 1e9)
     if t_mfma >= t_hbm and work["flops"] > 0:
         bound = "mfma" if work["peak_tflops"] == PEAK_BF16_TFLOPS else "alu"
-        achieved = work["flops"] / sec / 1e12
-        peak = work["peak_tflops"]
-        unit = "TFLOP/s"
+        achieved, peak, unit = work["flops"] / sec / 1e12, work["peak_tflops"], "TFLOP/s"
     else:
         bound, achieved, peak, unit = "hbm", work["bytes"] / sec / 1e9, PEAK_HBM_GBS, "GB/s"
     return {"kernel": stage, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
             "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
-            "roofline_frac": round(max(t_mfma, t_hbm) / sec, 4)}
+            "algorithmic_flops": work["flops"], "algorithmic_bytes": work["bytes"],
+            "mean_ms": round(ms, 5),
+            "mfma_frac": round(work["flops"] / sec / 1e12 / PEAK_BF16_TFLOPS, 4)
+            if work["flops"] else None}
 
 
-def cpu_baseline(spec, host, budget_s: float = 10.0) -> dict:
+def cpu_baseline(spec, host, budget_s: float) -> dict:
+    """The oracle as it stands on the host cores, over a bounded sample."""
     import oracle
-    xf = S.to_f32(host["x"], spec.act)
-    W_in = S.to_f32(host["W_in"], spec.expert)
-    W_out = S.to_f32(host["W_out"], spec.expert)
     nt = oracle.threads()
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.forward(xf, host["W_r"], host["b_r"], W_in, W_out, spec.c, spec.capacity_override,
-                       spec.alpha, nthreads=nt)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": round(spec.T * reps / el, 1), "unit": "tokens/s", "cores": nt,
+    if spec.N * spec.F * spec.d <= 2e8:
+        # the whole workload fits in host memory: run it whole, as often as the budget allows
+        xf = S.to_f32(host["x"], spec.act)
+        W_in = S.to_f32(host["W_in"], spec.expert)
+        W_out = S.to_f32(host["W_out"], spec.expert)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.forward(xf, host["W_r"], host["b_r"], W_in, W_out, spec.c,
+                           spec.capacity_override, spec.alpha, nthreads=nt)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+        return {"value": round(spec.T * reps / el, 1), "unit": "tokens/s", "cores": nt,
+                "kind": "oracle",
+                "sample": f"full {spec.name} workload (T={spec.T}) x {reps} run(s), "
+                          f"{el:.1f} s, fp64 C oracle"}
+    # large banks: logits and routing of a token prefix, expert FFN of a shorter
+    # prefix (per-token costs do not depend on which tokens or experts they are)
+    n_r = int(min(spec.T, max(1024, 2e9 // (spec.d * spec.N))))
+    xf = S.to_f32(host["x"][:n_r], spec.act)
+    t0 = time.perf_counter()
+    h = oracle.logits(xf, host["W_r"], host["b_r"], nthreads=nt)
+    r = oracle.route(h, spec.c, spec.capacity_override, spec.alpha, nthreads=nt)
+    t_route = time.perf_counter() - t0
+    del h
+    n, t_ffn = 0, 0.0
+    cache = {}
+    t1 = time.perf_counter()
+    while t_ffn < budget_s and n < n_r:
+        e = int(r["expert_idx"][n])
+        if e not in cache:
+            tg = time.perf_counter()
+            cache = {e: (S.to_f32(S.expert_slice(spec, S.TENSOR_WIN, e), spec.expert),
+                         S.to_f32(S.expert_slice(spec, S.TENSOR_WOUT, e), spec.expert))}
+            t1 += time.perf_counter() - tg   # weight regeneration is not oracle work
+        oracle.token_output(xf[n], r["drop"][n], r["gate"][n], *cache[e])
+        n += 1
+        t_ffn = time.perf_counter() - t1
+    per_token = t_route / n_r + t_ffn / n
+    return {"value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": nt,
             "kind": "oracle",
-            "sample": f"full {spec.name} workload (T={spec.T}) x {reps} run(s), {el:.1f} s, fp64 C"}
+            "sample": f"{spec.name}: logits and routing of the first {n_r} tokens "
+                      f"({t_route:.1f} s, {nt} threads) plus the expert FFN of the first {n} "
+                      f"tokens ({t_ffn:.1f} s, 1 thread); rate = 1 / per-token time"}
+
+
+def build_layer(spec, B, torch, dev):
+    if spec_id_of(spec) in DEVICE_WEIGHTS:
+        host = S.host_inputs(spec, with_experts=False)
+        per = spec.N * spec.F * spec.d
+        W_in = torch.empty(per, dtype=torch.int16, device=dev)
+        W_out = torch.empty(per, dtype=torch.int16, device=dev)
+        S.gpu_fill(spec, S.TENSOR_WIN, W_in.data_ptr(), 0, per)
+        S.gpu_fill(spec, S.TENSOR_WOUT, W_out.data_ptr(), 0, per)
+        W_r = torch.from_numpy(host["W_r"]).to(dev)
+        b_r = None if host["b_r"] is None else torch.from_numpy(host["b_r"]).to(dev)
+        cfg = B.switch_config(t_max=spec.T, d_model=spec.d, d_ff=spec.F, n_experts=spec.N,
+                              capacity_factor=spec.c, capacity_override=0, alpha=spec.alpha,
+                              act_dtype=B.SWITCH_BF16, expert_dtype=B.SWITCH_BF16)
+        return host, B.SwitchLayer(cfg, W_r, b_r, W_in, W_out)
+    host = S.host_inputs(spec)
+    return host, B.SwitchLayer.from_host(spec, host, device=dev)
+
+
+def spec_id_of(spec) -> int:
+    for k, v in S.CONFIGS.items():
+        if v == spec:
+            return k
+    return 0
 
 
 def main():
@@ -93,10 +155,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--profile-iters", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=sorted(S.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed region, run one device-to-device copy of 1 GiB "
+                         "(reference for hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -110,8 +174,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     spec = S.CONFIGS[args.config]
-    host = S.host_inputs(spec)
-    layer = B.SwitchLayer.from_host(spec, host, device=dev)
+    host, layer = build_layer(spec, B, torch, dev)
     x = B.to_device(host["x"], dev)
     bufs = layer.alloc(spec.T)
     stream = torch.cuda.current_stream(dev)
@@ -122,7 +185,6 @@ def main():
     torch.cuda.synchronize()
 
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
@@ -130,8 +192,24 @@ def main():
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
+    ms_per_step = start.elapsed_time(stop) / args.steps
+
+    # second pass of K steps: the library records HIP events around every kernel
+    B.switch_profile_enable(layer.handle, args.steps)
+    for _ in range(args.steps):
+        layer.forward(x, spec.T, bufs, stream=sp, with_logits=False)
+    stage_ms = dict(B.switch_profile_read(layer.handle))
+    B.switch_profile_enable(layer.handle, 0)
+    torch.cuda.synchronize()
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     drop = B.from_device(bufs["drop_mask"])
     load = B.from_device(bufs["load"])
@@ -139,23 +217,10 @@ def main():
     C = B.switch_capacity(layer.handle, spec.T)
     active = int((np.minimum(load, C) > 0).sum())
 
-    # per-kernel durations: HIP events recorded by the library around each launch
-    B.switch_profile_enable(layer.handle, True)
-    acc = {}
-    order = []
-    for _ in range(args.profile_iters):
-        layer.forward(x, spec.T, bufs, stream=sp, with_logits=False)
-        for name, ms in B.switch_profile_read(layer.handle):
-            if name not in acc:
-                acc[name] = []
-                order.append(name)
-            acc[name].append(ms)
-    B.switch_profile_enable(layer.handle, False)
-    stage_ms = {k: float(np.mean(acc[k])) for k in order}
-
     rooflines = {k: roofline_entry(k, stage_work(k, spec, kept, active), v)
                  for k, v in stage_ms.items()
-                 if k in ("router_logits", "gemm1_relu", "gemm2", "dispatch", "combine")}
+                 if k in ("router", "router_logits", "gemm1_relu", "gemm2", "dispatch",
+                          "combine")}
     dominant = max(rooflines, key=lambda k: stage_ms[k])
     gemm_ms = stage_ms.get("gemm1_relu", 0) + stage_ms.get("gemm2", 0)
     expert_tflops = 4.0 * kept * spec.d * spec.F / (gemm_ms * 1e-3) / 1e12 if gemm_ms else 0.0

@@ -157,14 +157,18 @@ switch_status switch_forward_debug(switch_layer* layer, const void* x, int64_t T
                                    void* stream);
 
 /*
- * Per-kernel timing for measurement.  When enabled, later switch_forward /
- * switch_route calls record a HIP event before and after every kernel they
- * launch, on the call's stream.  switch_profile_read waits for the last such
- * call to finish and writes up to `cap` stage times in milliseconds, in launch
- * order, with their names (static strings).  Returns the number of stages, or
- * -1 on error.  Enabling creates the events once (SWITCH_E_HIP on failure).
+ * Per-kernel timing for measurement.  switch_profile_enable(layer, n) makes the
+ * next n switch_forward / switch_route calls record a HIP event before every
+ * kernel they launch and one after the last, on the call's stream, without
+ * synchronising (n = 0 turns recording off and frees the events; calls past
+ * the n-th are not recorded).  switch_profile_read waits for the last
+ * recorded call to finish and writes, for each stage in launch order, the mean
+ * time in milliseconds over the recorded calls and its name (a static string);
+ * all recorded calls must have launched the same stages.  Returns the number of
+ * stages (at most `cap` are written), 0 if nothing was recorded, -1 on error.
+ * Enabling allocates host memory and HIP events (SWITCH_E_HIP on failure).
  */
-switch_status switch_profile_enable(switch_layer* layer, int enable);
+switch_status switch_profile_enable(switch_layer* layer, int max_calls);
 int switch_profile_read(switch_layer* layer, float* ms, const char** names, int cap);
 
 /* Human-readable name of a status code (static string). */

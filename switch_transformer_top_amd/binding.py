@@ -141,8 +141,8 @@ def switch_forward_debug(handle, x, T, out, expert_idx, gate, position, drop_mas
                                     _ptr(expert_out), stream)
 
 
-def switch_profile_enable(handle: int, enable: bool) -> None:
-    _check(lib.switch_profile_enable(handle, int(bool(enable))), "switch_profile_enable")
+def switch_profile_enable(handle: int, max_calls: int) -> None:
+    _check(lib.switch_profile_enable(handle, int(max_calls)), "switch_profile_enable")
 
 
 def switch_profile_read(handle: int, cap: int = 24):

@@ -17,12 +17,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (inputs here are finite; NaN stays NaN).
+// fp32 -> bf16 with round-to-nearest-even: the conversion instruction of
+// gfx950 (v_cvt_pk_bf16_f32, IEEE rounding in the default mode), no branches.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two fp32 values to a packed pair of bf16 (first value in the low half).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float floatx2 __attribute__((ext_vector_type(2)));
+  const floatx2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Element access for the two activation types.

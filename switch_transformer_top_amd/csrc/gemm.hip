@@ -20,15 +20,35 @@ namespace swl {
 constexpr int GB_BK = 64, GB_PAD = 8;
 constexpr int GB_LDK = GB_BK + GB_PAD;  // LDS row stride in bf16 elements (144 bytes)
 
-// Block: 256 threads = 4 waves in a 2 x 2 grid; each wave owns a
-// (BM/2) x (BN/2) sub-tile made of 32 x 32 MFMA tiles.  K advances 64 at a
-// time through one padded LDS buffer per operand; the next K tile is fetched
-// into registers (unconditionally: the last iteration re-reads its own tile)
-// while the current one is multiplied.
-//
-// MFMA 32x32x16 operand layout (per lane l): A row (l % 32) with 8 consecutive
-// k, B column (l % 32) with the same 8 k; the k group is (l / 32).  Result: lane
-// l holds column (l % 32) and rows 8 (v / 4) + 4 (l / 32) + (v % 4), v < 16.
+// Epilogue shared by the bf16 kernels: a wave's TI x TJ grid of 32 x 32 fp32
+// accumulators goes through LDS (rows of TJ * 32 + 8 bf16, after the optional
+// ReLU and round-to-nearest-even) and then out in 16-byte row pieces, instead
+// of one 2-byte store per accumulator.  Rows at or past rows_e are not stored.
+template <int TI, int TJ, bool RELU>
+__device__ __forceinline__ void store_tile_bf16(const floatx16 (&acc)[TI][TJ], uint16_t* stage,
+                                                uint16_t* __restrict__ Ce, int r0, int c0,
+                                                int rows_e, int Nout, int lane) {
+  constexpr int W = TJ * 32, LD = W + 8, CPR = W / 8;
+  const int fr = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float val = acc[i][j][v];
+        if (RELU) val = val > 0.f ? val : 0.f;
+        stage[(i * 32 + 8 * (v >> 2) + 4 * g + (v & 3)) * LD + j * 32 + fr] = f32_to_bf16_bits(val);
+      }
+#pragma unroll 4
+  for (int idx = lane; idx < TI * 32 * CPR; idx += kWave) {
+    const int row = idx / CPR, ch = idx - row * CPR;
+    if (r0 + row < rows_e)
+      *reinterpret_cast<u32x4*>(Ce + (int64_t)(r0 + row) * Nout + c0 + ch * 8) =
+          *reinterpret_cast<const u32x4*>(stage + row * LD + ch * 8);
+  }
+}
+
 // Tile order: the grid is 1-D.  Workgroups are handed to the 8 XCDs round
 // robin (block b runs on XCD b % 8), so block b takes tile
 // (b % 8) * ceil(tiles / 8) + b / 8: each XCD walks a contiguous stretch of the
@@ -36,12 +56,18 @@ constexpr int GB_LDK = GB_BK + GB_PAD;  // LDS row stride in bf16 elements (144 
 // expert (its gathered rows and its weights) therefore share one XCD's L2, and
 // consecutive M tiles reuse the same weight tile.
 //
-// Pipeline: K tiles k+1 and k+2 are in flight in two register sets while tile
-// k is multiplied out of LDS (LDS_BUFS = 1: one buffer, two barriers per step;
-// LDS_BUFS = 2: double buffer, one barrier per step).  The prefetch of a tile
-// past the end re-reads the last tile, so every load is unconditional.
-template <int BM, int BN, int LDS_BUFS, int PF, bool RELU>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
+// Block: 256 threads = 4 waves in a 2 x 2 grid; each wave owns a
+// (BM/2) x (BN/2) sub-tile made of 32 x 32 MFMA tiles.  The launch bound asks
+// for three waves per SIMD (three blocks per CU share the LDS and MFMA pipes).  K advances 64 at a
+// time through one padded LDS buffer per operand; the next K tile is fetched
+// into registers (unconditionally: the last step re-reads its own tile) while
+// the current one is multiplied.
+//
+// MFMA 32x32x16 operand layout (per lane l): A row (l % 32) with 8 consecutive
+// k, B column (l % 32) with the same 8 k; the k group is (l / 32).  Result: lane
+// l holds column (l % 32) and rows 8 (v / 4) + 4 (l / 32) + (v % 4), v < 16.
+template <int BM, int BN, bool RELU>
+__global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                         int64_t strideA,
                                                         const uint16_t* __restrict__ B,
                                                         int64_t strideB,
@@ -52,8 +78,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
                                                         int tiles) {
   constexpr int LA = BM / 32, LB = BN / 32;   // 16-byte loads per thread per operand
   constexpr int TI = BM / 64, TJ = BN / 64;   // MFMA tiles per wave
-  __shared__ __attribute__((aligned(16))) uint16_t As[LDS_BUFS][BM * GB_LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[LDS_BUFS][BN * GB_LDK];
+  // one buffer holding the A rows then the B rows; reused by the epilogue
+  __shared__ __attribute__((aligned(16))) uint16_t lds[(BM + BN) * GB_LDK];
+  static_assert(4 * (BM / 2) * (BN / 2 + 8) <= (BM + BN) * GB_LDK, "epilogue staging fits");
+  uint16_t* As = lds;
+  uint16_t* Bs = lds + BM * GB_LDK;
 
   const int per_xcd = (tiles + 7) >> 3;
   const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -93,13 +122,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = K / GB_BK;
-  const int last = (nk - 1) * GB_BK;
-  u32x4 ra0[LA], rb0[LB], ra1[LA], rb1[LB];
+  const int last = K - GB_BK;
+  u32x4 ra[LA], rb[LB];
   // The scheduling barrier keeps the prefetch loads ahead of the MFMAs that
   // follow; without it the compiler sinks them to the end of the loop body,
   // where nothing is left to hide their latency.
-  auto fetch = [&](u32x4* ra, u32x4* rb, int k) {
+  auto fetch = [&](int k) {
     k = k < last ? k : last;
 #pragma unroll
     for (int j = 0; j < LA; ++j) ra[j] = *reinterpret_cast<const u32x4*>(Ae + a_off[j] + k);
@@ -107,247 +135,41 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
     for (int j = 0; j < LB; ++j) rb[j] = *reinterpret_cast<const u32x4*>(Be + b_off[j] + k);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto stash = [&](const u32x4* ra, const u32x4* rb, int buf) {
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+
+  fetch(0);
+  for (int k0 = 0; k0 < K; k0 += GB_BK) {
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < LA; ++j)
-      *reinterpret_cast<u32x4*>(&As[buf][(lrow + 32 * j) * GB_LDK + lcol]) = ra[j];
+      *reinterpret_cast<u32x4*>(&As[(lrow + 32 * j) * GB_LDK + lcol]) = ra[j];
 #pragma unroll
     for (int j = 0; j < LB; ++j)
-      *reinterpret_cast<u32x4*>(&Bs[buf][(lrow + 32 * j) * GB_LDK + lcol]) = rb[j];
-  };
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
-  auto compute = [&](int buf) {
+      *reinterpret_cast<u32x4*>(&Bs[(lrow + 32 * j) * GB_LDK + lcol]) = rb[j];
+    __syncthreads();
+    fetch(k0 + GB_BK);
 #pragma unroll
     for (int ks = 0; ks < GB_BK; ks += 16) {
       bf16x8 a[TI], b[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i)
         a[i] = *reinterpret_cast<const bf16x8*>(
-            &As[buf][(wm * (BM / 2) + i * 32 + fr) * GB_LDK + ks + fk]);
+            &As[(wm * (BM / 2) + i * 32 + fr) * GB_LDK + ks + fk]);
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
         b[j] = *reinterpret_cast<const bf16x8*>(
-            &Bs[buf][(wn * (BN / 2) + j * 32 + fr) * GB_LDK + ks + fk]);
+            &Bs[(wn * (BN / 2) + j * 32 + fr) * GB_LDK + ks + fk]);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-  };
-
-  if (PF == 1) {
-    // one register set: tile k + 1 is in flight while tile k is multiplied
-    fetch(ra0, rb0, 0);
-    if (LDS_BUFS == 1) {
-      for (int kt = 0; kt < nk; ++kt) {
-        __syncthreads();
-        stash(ra0, rb0, 0);
-        __syncthreads();
-        fetch(ra0, rb0, (kt + 1) * GB_BK);
-        compute(0);
-      }
-    } else {
-      stash(ra0, rb0, 0);
-      fetch(ra0, rb0, GB_BK);
-      __syncthreads();
-      for (int kt = 0; kt < nk; kt += 2) {
-        compute(0);
-        stash(ra0, rb0, LDS_BUFS - 1);
-        fetch(ra0, rb0, (kt + 2) * GB_BK);
-        __syncthreads();
-        if (kt + 1 >= nk) break;
-        compute(LDS_BUFS - 1);
-        stash(ra0, rb0, 0);
-        fetch(ra0, rb0, (kt + 3) * GB_BK);
-        __syncthreads();
-      }
-    }
-  } else {
-    fetch(ra0, rb0, 0);
-    fetch(ra1, rb1, GB_BK);
-    if (LDS_BUFS == 1) {
-      // step k: stash tile k (register set k % 2), refill that set with tile k + 2
-      for (int kt = 0; kt < nk; kt += 2) {
-        __syncthreads();
-        stash(ra0, rb0, 0);
-        __syncthreads();
-        fetch(ra0, rb0, (kt + 2) * GB_BK);
-        compute(0);
-        if (kt + 1 >= nk) break;
-        __syncthreads();
-        stash(ra1, rb1, 0);
-        __syncthreads();
-        fetch(ra1, rb1, (kt + 3) * GB_BK);
-        compute(0);
-      }
-    } else {
-      // LDS buffer kt % 2 holds tile kt; after computing it, tile kt + 1 goes to
-      // the other buffer and its register set is refilled with tile kt + 3.
-      stash(ra0, rb0, 0);
-      fetch(ra0, rb0, 2 * GB_BK);
-      __syncthreads();
-      for (int kt = 0; kt < nk; kt += 2) {
-        compute(0);
-        stash(ra1, rb1, LDS_BUFS - 1);
-        fetch(ra1, rb1, (kt + 3) * GB_BK);
-        __syncthreads();
-        if (kt + 1 >= nk) break;
-        compute(LDS_BUFS - 1);
-        stash(ra0, rb0, 0);
-        fetch(ra0, rb0, (kt + 4) * GB_BK);
-        __syncthreads();
-      }
-    }
   }
 
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (r >= rows_e) continue;
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int c = n0 + wn * (BN / 2) + j * 32 + fr;
-        float val = acc[i][j][v];
-        if (RELU) val = val > 0.f ? val : 0.f;
-        Ce[(int64_t)r * Nout + c] = f32_to_bf16_bits(val);
-      }
-    }
-  }
-}
-
-// Deep-pipelined variant: PF register sets keep K tiles k+1 .. k+PF in flight
-// while tile k is multiplied out of a double-buffered LDS (one barrier per K
-// step).  Each step first stores tile k+1 (loaded PF-1 steps earlier) into the
-// other LDS buffer, refills that register set with tile k+1+PF, then runs the
-// MFMAs of tile k.
-template <int BM, int BN, int PF, bool RELU>
-__global__ __launch_bounds__(256) void gemm_bf16_deep_kernel(
-    const uint16_t* __restrict__ A, int64_t strideA, const uint16_t* __restrict__ B,
-    int64_t strideB, uint16_t* __restrict__ Cout, int64_t strideC,
-    const int32_t* __restrict__ rows, int K, int Nout, int m_tiles, int n_tiles, int tiles) {
-  constexpr int LA = BM / 32, LB = BN / 32;
-  constexpr int TI = BM / 64, TJ = BN / 64;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * GB_LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * GB_LDK];
-
-  const int per_xcd = (tiles + 7) >> 3;
-  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (tile >= tiles) return;
-  const int mt = tile % m_tiles;
-  const int nt = (tile / m_tiles) % n_tiles;
-  const int e = tile / (m_tiles * n_tiles);
-  const int rows_e = rows[e];
-  const int m0 = mt * BM;
-  if (m0 >= rows_e) return;
-  const int n0 = nt * BN;
-
-  const uint16_t* Ae = A + (int64_t)e * strideA;
-  const uint16_t* Be = B + (int64_t)e * strideB + (int64_t)n0 * K;
-  uint16_t* Ce = Cout + (int64_t)e * strideC;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid >> 3, lcol = (tid & 7) * 8;
-
-  int64_t a_off[LA], b_off[LB];
-#pragma unroll
-  for (int j = 0; j < LA; ++j) {
-    int r = m0 + lrow + 32 * j;
-    r = r < rows_e ? r : rows_e - 1;
-    a_off[j] = (int64_t)r * K + lcol;
-  }
-#pragma unroll
-  for (int j = 0; j < LB; ++j) b_off[j] = (int64_t)(lrow + 32 * j) * K + lcol;
-
-  floatx16 acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  const int nk = K / GB_BK;
-  const int last = (nk - 1) * GB_BK;
-  u32x4 ra[PF][LA], rb[PF][LB];
-  auto fetch = [&](int set, int kt) {
-    int k = kt * GB_BK;
-    k = k < last ? k : last;
-#pragma unroll
-    for (int j = 0; j < LA; ++j) ra[set][j] = *reinterpret_cast<const u32x4*>(Ae + a_off[j] + k);
-#pragma unroll
-    for (int j = 0; j < LB; ++j) rb[set][j] = *reinterpret_cast<const u32x4*>(Be + b_off[j] + k);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto stash = [&](int set, int buf) {
-#pragma unroll
-    for (int j = 0; j < LA; ++j)
-      *reinterpret_cast<u32x4*>(&As[buf][(lrow + 32 * j) * GB_LDK + lcol]) = ra[set][j];
-#pragma unroll
-    for (int j = 0; j < LB; ++j)
-      *reinterpret_cast<u32x4*>(&Bs[buf][(lrow + 32 * j) * GB_LDK + lcol]) = rb[set][j];
-  };
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int ks = 0; ks < GB_BK; ks += 16) {
-      bf16x8 a[TI], b[TJ];
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(
-            &As[buf][(wm * (BM / 2) + i * 32 + fr) * GB_LDK + ks + fk]);
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(
-            &Bs[buf][(wn * (BN / 2) + j * 32 + fr) * GB_LDK + ks + fk]);
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // prologue: tiles 0 .. PF in flight, tile 0 in LDS buffer 0
-#pragma unroll
-  for (int p = 0; p < PF; ++p) fetch(p, p);
-  stash(0, 0);
-  fetch(0, PF);
-  __syncthreads();
-  // step kt uses register set (kt + 1) % PF for tile kt + 1
-  for (int kt = 0; kt < nk; kt += PF) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int k = kt + u;
-      if (k < nk) {
-        const int set = (u + 1) % PF;
-        stash(set, (k + 1) & 1);
-        fetch(set, k + 1 + PF);
-        compute(k & 1);
-        __syncthreads();
-      }
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (r >= rows_e) continue;
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int c = n0 + wn * (BN / 2) + j * 32 + fr;
-        float val = acc[i][j][v];
-        if (RELU) val = val > 0.f ? val : 0.f;
-        Ce[(int64_t)r * Nout + c] = f32_to_bf16_bits(val);
-      }
-    }
-  }
+  __syncthreads();  // every wave is done with the LDS operand tiles
+  store_tile_bf16<TI, TJ, RELU>(acc, lds + wave * (BM / 2) * (BN / 2 + 8), Ce,
+                                m0 + wm * (BM / 2), n0 + wn * (BN / 2), rows_e, Nout, lane);
 }
 
 // fp32 path (parity-sized fp32 layers): 32 x 32 tile, K in steps of 32, each
@@ -413,11 +235,11 @@ void launch_expert_gemm(bool bf16, bool relu, const void* A, int64_t strideA, co
     const int tiles = mt * nt * n_experts;
     const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
     if (relu)
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1, 1, true>), dim3(grid), dim3(256), 0, s,
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true>), dim3(grid), dim3(256), 0, s,
                          (const uint16_t*)A, strideA, (const uint16_t*)B, strideB,
                          (uint16_t*)Cout, strideC, rows, K, Nout, mt, nt, tiles);
     else
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 1, 1, false>), dim3(grid), dim3(256), 0, s,
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false>), dim3(grid), dim3(256), 0, s,
                          (const uint16_t*)A, strideA, (const uint16_t*)B, strideB,
                          (uint16_t*)Cout, strideC, rows, K, Nout, mt, nt, tiles);
   } else {

@@ -6,29 +6,35 @@
 
 namespace swl {
 
-// Records a HIP event on the launch stream before each stage; the next mark
-// (or the end mark) closes the stage.
+// Records a HIP event on the launch stream before each stage of a call and
+// one after its last stage, for up to max_calls calls (no synchronisation).
 struct Profiler {
-  static constexpr int kMax = 24;
+  static constexpr int kMax = 24;   // stages per call
   bool on = false;
-  bool created = false;
-  hipEvent_t ev[kMax + 1];
+  int max_calls = 0;
+  int calls = 0;                    // calls recorded so far
+  int n = 0;                        // stages recorded in the current call
+  bool active = false;              // the current call is being recorded
+  hipEvent_t* ev = nullptr;         // max_calls * (kMax + 1)
   const char* names[kMax];
-  int n = 0;
 };
 
 inline void prof_begin(Profiler* p) {
-  if (p && p->on) p->n = 0;
+  if (!p || !p->on) return;
+  p->active = p->calls < p->max_calls;
+  p->n = 0;
 }
 inline void prof_mark(Profiler* p, hipStream_t s, const char* name) {
-  if (!p || !p->on || p->n >= Profiler::kMax) return;
+  if (!p || !p->on || !p->active || p->n >= Profiler::kMax) return;
   p->names[p->n] = name;
-  (void)hipEventRecord(p->ev[p->n], s);
+  (void)hipEventRecord(p->ev[p->calls * (Profiler::kMax + 1) + p->n], s);
   p->n += 1;
 }
 inline void prof_end(Profiler* p, hipStream_t s) {
-  if (!p || !p->on || p->n == 0) return;
-  (void)hipEventRecord(p->ev[p->n], s);
+  if (!p || !p->on || !p->active || p->n == 0) return;
+  (void)hipEventRecord(p->ev[p->calls * (Profiler::kMax + 1) + p->n], s);
+  p->calls += 1;
+  p->active = false;
 }
 
 // router.hip

@@ -52,9 +52,7 @@ __device__ __forceinline__ uint4 combine_vec_bf16(uint4 xv, uint4 yv, float g) {
   for (int i = 0; i < 4; ++i) {
     float x0 = __uint_as_float(xs[i] << 16), x1 = __uint_as_float(xs[i] & 0xFFFF0000u);
     float y0 = __uint_as_float(ys[i] << 16), y1 = __uint_as_float(ys[i] & 0xFFFF0000u);
-    uint32_t lo = f32_to_bf16_bits(fmaf(g, y0, x0));
-    uint32_t hi = f32_to_bf16_bits(fmaf(g, y1, x1));
-    o[i] = lo | (hi << 16);
+    o[i] = f32x2_to_bf16x2_bits(fmaf(g, y0, x0), fmaf(g, y1, x1));
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Routing statistics shared by both router variants.  Tokens are grouped in
+// Routing statistics shared by the router variants.  Tokens are grouped in
 // chunks (consecutive tokens, one chunk per routing block); for every chunk c
 //   hist[c, e]      tokens of the chunk routed to expert e
 //   P_part[c, e]    sum over the chunk's tokens of p_e(t)
@@ -136,22 +136,28 @@ __device__ __forceinline__ void wave_rank(int32_t e, int& rank, bool& last) {
   last = after == 0;
 }
 
-// Writes rank_local and the chunk's histogram row from the chunk's experts
-// held one per lane (lanes >= n are inactive).  cnt: LDS scratch of N ints;
-// the whole block must call this (it synchronises).
-__device__ __forceinline__ void chunk_hist_rank(int32_t e, int n, int64_t t, int N, int32_t* cnt,
-                                                int32_t* __restrict__ hist_row,
+// Ranks and histogram of one chunk from its experts s_idx[0..n) (LDS).  Wave 0
+// walks the chunk 64 tokens at a time; cnt (LDS, N ints) holds the running
+// count per expert, which ends as the chunk's histogram.  The whole block must
+// call this (it synchronises).
+__device__ __forceinline__ void chunk_hist_rank(const int32_t* s_idx, int n, int64_t t0, int N,
+                                                int32_t* cnt, int32_t* __restrict__ hist_row,
                                                 int32_t* __restrict__ rank_local) {
   for (int i = threadIdx.x; i < N; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
   if (threadIdx.x < kWave) {
-    const bool active = (int)threadIdx.x < n;
-    int rank;
-    bool last;
-    wave_rank(active ? e : -1, rank, last);
-    if (active) {
-      rank_local[t] = rank;
-      if (last) cnt[e] = rank + 1;
+    for (int base = 0; base < n; base += kWave) {
+      const int i = base + (int)threadIdx.x;
+      const bool active = i < n;
+      const int32_t e = active ? s_idx[i] : -1;
+      int rank;
+      bool last;
+      wave_rank(e, rank, last);
+      if (active) {
+        const int32_t r = cnt[e] + rank;  // every lane reads before any lane writes
+        rank_local[t0 + i] = r;
+        if (last) cnt[e] = r + 1;
+      }
     }
   }
   __syncthreads();
@@ -159,73 +165,122 @@ __device__ __forceinline__ void chunk_hist_rank(int32_t e, int n, int64_t t, int
 }
 
 // ---------------------------------------------------------------------------
-// Fused router for bf16 tokens and up to 256 experts, one wave per block.
+// bf16 routers on MFMA with fp32 semantics.  x is bf16 (exact), and each fp32
+// router weight is split exactly into three bf16 pieces w = hi + mid + lo
+// (8 + 8 + 8 significant bits; each piece is the round-to-nearest bf16 of what
+// the earlier ones leave).  Every product x * piece is exact in fp32 and the
+// MFMA accumulates in fp32, so h is an fp32 dot product of the exact values
+// over 3d terms (smallest pieces first).  v_mfma_f32_16x16x32_bf16 layout per
+// lane l: A row (token) l % 16 and B column (expert) l % 16 with k = 8 (l / 16)
+// .. +8; result rows 4 (l / 16) + i, i < 4, column l % 16.
 //
-// Logits on MFMA with fp32 semantics: x is bf16 (exact), and each fp32 router
-// weight is split exactly into three bf16 pieces w = hi + mid + lo (8 + 8 + 8
-// significant bits; each piece is the round-to-nearest bf16 of what the
-// earlier ones leave).  Every product x * piece is exact in fp32 and the MFMA
-// accumulates in fp32, so h is an fp32 dot product of the exact values over 3d
-// terms (smallest pieces first).  v_mfma_f32_16x16x32_bf16 layout per lane l:
-// A row (token) l % 16 and B column (expert) l % 16 with k = 8 (l / 16) .. +8;
-// result rows 4 (l / 16) + i, i < 4, column l % 16.
-//
-// A block owns 16 * ROWT consecutive tokens (one chunk) and all NPAD >= N
-// experts (padded columns get -inf).  After the K loop the wave has whole
-// logit rows spread over the 16 lanes of each lane group, so softmax, top-1
-// (lowest index on ties), gate = 1 / sum_i exp(h_i - max) and the chunk sums
-// of p_i are shuffle reductions; then the chunk histogram and ranks.
+// After the K loop a wave holds whole logit rows spread over the 16 lanes of
+// each lane group, so softmax, top-1 (lowest index on ties), gate = 1 / sum_i
+// exp(h_i - max) and the sums of p_i over the wave's tokens are shuffle
+// reductions (row_stats below).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint16_t bf16_rne_bits(float f) { return f32_to_bf16_bits(f); }
-
 __device__ __forceinline__ void split3(const float* w, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint16_t h = bf16_rne_bits(w[i]);
+    const uint16_t h = f32_to_bf16_bits(w[i]);
     const float r1 = w[i] - bf16_bits_to_f32(h);
-    const uint16_t m = bf16_rne_bits(r1);
+    const uint16_t m = f32_to_bf16_bits(r1);
     const float r2 = r1 - bf16_bits_to_f32(m);
-    const uint16_t l = bf16_rne_bits(r2);
+    const uint16_t l = f32_to_bf16_bits(r2);
     hi[i] = __builtin_bit_cast(__bf16, h);
     mid[i] = __builtin_bit_cast(__bf16, m);
     lo[i] = __builtin_bit_cast(__bf16, l);
   }
 }
 
-template <int NPAD, int ROWT>
-__global__ __launch_bounds__(256) void router_mfma_kernel(
+// Routing statistics of a block's logit tile st[BT][LD] (LDS, fp32, bias
+// added, padded experts at -inf), tokens t0 .. t0 + n_tok.  A few consecutive
+// threads share a token row (TPR = blockDim / BT): max with the lowest index,
+// S = sum_i exp(h_i - max) (fp64), gate = 1 / S; then thread e owns expert e and
+// sums p_e over the chunk's tokens in token order (fp64) for P_part; the
+// logits leave in full coalesced rows when requested.  Synchronises the block.
+template <int BT, int NPAD, int LD>
+__device__ __forceinline__ void block_stats(const float* st, int N, int64_t t0, int n_tok,
+                                            float* __restrict__ logits,
+                                            int32_t* __restrict__ expert_idx,
+                                            float* __restrict__ gate,
+                                            float* __restrict__ P_row, int32_t* s_idx,
+                                            float* s_m, double* s_inv) {
+  constexpr int TPR = 256 / BT;          // threads per token row
+  constexpr int SPAN = NPAD / TPR;       // experts per thread
+  static_assert(TPR >= 1 && TPR <= 16 && SPAN >= 1, "row split");
+  const int tid = threadIdx.x;
+  const int row = tid / TPR, part = tid % TPR;
+  const float* rp = st + row * LD + part * SPAN;
+  float m = rp[0];
+  int mi = part * SPAN;
+#pragma unroll 8
+  for (int i = 1; i < SPAN; ++i)
+    if (rp[i] > m) { m = rp[i]; mi = part * SPAN + i; }
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) {
+    const float om = __shfl_xor(m, o, TPR);
+    const int oi = __shfl_xor(mi, o, TPR);
+    if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
+  }
+  double ssum = 0.0;
+#pragma unroll 8
+  for (int i = 0; i < SPAN; ++i) ssum += (double)expf(rp[i] - m);
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) ssum += shfl_xor_f64_w(ssum, o, TPR);
+  if (part == 0 && row < n_tok) {
+    const double inv = 1.0 / ssum;
+    s_m[row] = m;
+    s_inv[row] = inv;
+    s_idx[row] = mi;
+    expert_idx[t0 + row] = mi;
+    gate[t0 + row] = (float)inv;
+  }
+  if (logits) {
+    for (int idx = tid; idx < n_tok * N; idx += 256) {
+      const int r = idx / N, e = idx - r * N;
+      logits[(t0 + r) * N + e] = st[r * LD + e];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < N; e += 256) {
+    double acc = 0.0;
+    for (int r = 0; r < n_tok; ++r) acc += (double)expf(st[r * LD + e] - s_m[r]) * s_inv[r];
+    P_row[e] = (float)acc;
+  }
+}
+
+// Few experts (N <= 32): a block owns 16 tokens (one chunk) and its four waves
+// take consecutive quarters of K, with every K step of the quarter loaded up
+// front (8 at a time) so the loads' latency is paid once.  The partial sums of
+// the quarters meet in wave 0, added in wave order.
+template <int NPAD>
+__global__ __launch_bounds__(256) void router_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ W_r, const float* __restrict__ b_r,
     int64_t T, int d, int N, float* __restrict__ logits, int32_t* __restrict__ expert_idx,
     float* __restrict__ gate, float* __restrict__ P_part, int32_t* __restrict__ hist,
     int32_t* __restrict__ rank_local) {
-  constexpr int NJ = NPAD / 16;
-  constexpr int BT = 16 * ROWT;
-  constexpr int NACC = ROWT * NJ * 4;  // accumulator floats per lane
+  constexpr int NJ = NPAD / 16, BT = 16, NACC = NJ * 4, GRP = 8, LD = NPAD + 4;
   __shared__ int32_t s_idx[BT];
   __shared__ int32_t cnt[NPAD];
   __shared__ float red[3][NACC][kWave];
+  __shared__ float st[BT * LD];
+  __shared__ float s_m[BT];
+  __shared__ double s_inv[BT];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * BT;
   const int n_tok = (int)((T - t0) < BT ? (T - t0) : BT);
   const int fr = lane & 15, fk = (lane >> 4) * 8;
 
-  floatx4 acc[ROWT][NJ];
+  floatx4 acc[1][NJ];
 #pragma unroll
-  for (int r = 0; r < ROWT; ++r)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[r][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NJ; ++j) acc[0][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // the four waves take consecutive quarters of K (d is a multiple of 128)
-  const int kq = d / 4;
-  const int kbeg = wave * kq;
-  const uint16_t* xrow[ROWT];
-#pragma unroll
-  for (int r = 0; r < ROWT; ++r) {
-    int64_t t = t0 + 16 * r + fr;
-    t = t < T ? t : T - 1;  // rows past T: any valid row, never stored
-    xrow[r] = x + t * d + kbeg + fk;
-  }
+  const int kq = d / 4, kbeg = wave * kq;
+  int64_t t = t0 + fr;
+  t = t < T ? t : T - 1;  // rows past T: any valid row, never stored
+  const uint16_t* xrow = x + t * d + kbeg + fk;
   const float* wrow[NJ];
   bool wvalid[NJ];
 #pragma unroll
@@ -235,134 +290,230 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     wrow[j] = W_r + (int64_t)(e < N ? e : 0) * d + kbeg + fk;
   }
 
-  // register double buffer: operands of step k + 32 load while step k runs
-  bf16x8 a_nx[ROWT];
-  float4 w_nx[NJ][2];
-  auto load_step = [&](int k) {
+  for (int kg = 0; kg < kq; kg += GRP * 32) {
+    bf16x8 a[GRP];
+    float4 wv[GRP][NJ][2];
 #pragma unroll
-    for (int r = 0; r < ROWT; ++r) a_nx[r] = *reinterpret_cast<const bf16x8*>(xrow[r] + k);
+    for (int s = 0; s < GRP; ++s) {
+      int k = kg + 32 * s;
+      k = k < kq ? k : kq - 32;  // past the quarter: reload its last step, never used
+      a[s] = *reinterpret_cast<const bf16x8*>(xrow + k);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      w_nx[j][0] = *reinterpret_cast<const float4*>(wrow[j] + k);
-      w_nx[j][1] = *reinterpret_cast<const float4*>(wrow[j] + k + 4);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  load_step(0);
-  for (int k0 = 0; k0 < kq; k0 += 32) {
-    bf16x8 a[ROWT];
-    float4 wv[NJ][2];
-#pragma unroll
-    for (int r = 0; r < ROWT; ++r) a[r] = a_nx[r];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) { wv[j][0] = w_nx[j][0]; wv[j][1] = w_nx[j][1]; }
-    load_step(k0 + 32 < kq ? k0 + 32 : k0);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      float w[8] = {wv[j][0].x, wv[j][0].y, wv[j][0].z, wv[j][0].w,
-                    wv[j][1].x, wv[j][1].y, wv[j][1].z, wv[j][1].w};
-      if (!wvalid[j]) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = 0.f;
+      for (int j = 0; j < NJ; ++j) {
+        wv[s][j][0] = *reinterpret_cast<const float4*>(wrow[j] + k);
+        wv[s][j][1] = *reinterpret_cast<const float4*>(wrow[j] + k + 4);
       }
-      bf16x8 hi, mid, lo;
-      split3(w, hi, mid, lo);
+    }
 #pragma unroll
-      for (int r = 0; r < ROWT; ++r) {
-        acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], lo, acc[r][j], 0, 0, 0);
-        acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], mid, acc[r][j], 0, 0, 0);
-        acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], hi, acc[r][j], 0, 0, 0);
+    for (int s = 0; s < GRP; ++s) {
+      if (kg + 32 * s >= kq) break;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float w[8] = {wv[s][j][0].x, wv[s][j][0].y, wv[s][j][0].z, wv[s][j][0].w,
+                      wv[s][j][1].x, wv[s][j][1].y, wv[s][j][1].z, wv[s][j][1].w};
+        if (!wvalid[j]) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i] = 0.f;
+        }
+        bf16x8 hi, mid, lo;
+        split3(w, hi, mid, lo);
+        acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], lo, acc[0][j], 0, 0, 0);
+        acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], mid, acc[0][j], 0, 0, 0);
+        acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], hi, acc[0][j], 0, 0, 0);
       }
     }
   }
 
-  // partial sums of the K quarters meet in wave 0, added in wave order
   if (wave > 0) {
 #pragma unroll
-    for (int r = 0; r < ROWT; ++r)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave - 1][(r * NJ + j) * 4 + i][lane] = acc[r][j][i];
+      for (int i = 0; i < 4; ++i) red[wave - 1][j * 4 + i][lane] = acc[0][j][i];
   }
   __syncthreads();
   if (wave == 0) {
-#pragma unroll
-    for (int w = 0; w < 3; ++w)
-#pragma unroll
-      for (int r = 0; r < ROWT; ++r)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[r][j][i] += red[w][(r * NJ + j) * 4 + i][lane];
-
-    // logits (+ bias), padded experts at -inf
     const int g = lane >> 4;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int e = 16 * j + fr;
       const float bias = (e < N && b_r) ? b_r[e] : 0.f;
 #pragma unroll
-      for (int r = 0; r < ROWT; ++r)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = acc[r][j][i] + bias;
-          acc[r][j][i] = e < N ? v : -__builtin_huge_valf();
-          const int64_t t = t0 + 16 * r + 4 * g + i;
-          if (logits && e < N && t < T) logits[t * N + e] = v;
-        }
-    }
-
-    // per token: max with lowest index, sum of exp, gate; chunk sums of p
-    float psum[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) psum[j] = 0.f;
-#pragma unroll
-    for (int r = 0; r < ROWT; ++r) {
-#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float m = acc[r][0][i];
-        int mi = fr;
+        float v = acc[0][j][i];
 #pragma unroll
-        for (int j = 1; j < NJ; ++j)
-          if (acc[r][j][i] > m) { m = acc[r][j][i]; mi = 16 * j + fr; }
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) {
-          const float om = __shfl_xor(m, o, 16);
-          const int oi = __shfl_xor(mi, o, 16);
-          if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
-        }
-        double ssum = 0.0;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) ssum += (double)expf(acc[r][j][i] - m);
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) ssum += shfl_xor_f64_w(ssum, o, 16);
-        const double inv = 1.0 / ssum;
-        const int tl = 16 * r + 4 * g + i;
-        const int64_t t = t0 + tl;
-        if (t < T) {
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) psum[j] += (float)((double)expf(acc[r][j][i] - m) * inv);
-          if (fr == 0) {
-            expert_idx[t] = mi;
-            gate[t] = (float)inv;
-            s_idx[tl] = mi;
-          }
-        }
+        for (int w = 0; w < 3; ++w) v += red[w][j * 4 + i][lane];
+        st[(4 * g + i) * LD + e] = e < N ? v + bias : -__builtin_huge_valf();
       }
-    }
-    // column sums over the 4 lane groups, then one lane per expert writes
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      psum[j] += __shfl_xor(psum[j], 16, 64);
-      psum[j] += __shfl_xor(psum[j], 32, 64);
-      const int e = 16 * j + fr;
-      if (g == 0 && e < N) P_part[(int64_t)blockIdx.x * N + e] = psum[j];
     }
   }
   __syncthreads();
-  const int32_t my_e = (wave == 0 && lane < n_tok) ? s_idx[lane] : -1;
-  chunk_hist_rank(my_e, n_tok, t0 + lane, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
+  block_stats<BT, NPAD, LD>(&st[0], N, t0, n_tok, logits, expert_idx, gate,
+                            P_part + (int64_t)blockIdx.x * N, s_idx, s_m, s_inv);
+  chunk_hist_rank(s_idx, n_tok, t0, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
+}
+
+// More experts (32 < N): a block owns 64 * ROWT tokens and NPAD experts
+// starting at e0 = blockIdx.y * NPAD; each wave takes 16 * ROWT of the tokens
+// and the whole K.  Every 32-wide K chunk of W_r is loaded once per block,
+// split into its three bf16 planes and stored in LDS (double buffered, rows of
+// 40 bf16), where all four waves read their B fragments; the next chunk is
+// loaded into registers while the current one is multiplied.
+// FUSED (N <= NPAD, one expert tile): routing statistics and the chunk
+// histogram / ranks follow; otherwise only the logits are written.
+template <int NPAD, int ROWT, bool FUSED>
+__global__ __launch_bounds__(256) void router_tok_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ W_r, const float* __restrict__ b_r,
+    int64_t T, int d, int N, float* __restrict__ logits, int32_t* __restrict__ expert_idx,
+    float* __restrict__ gate, float* __restrict__ P_part, int32_t* __restrict__ hist,
+    int32_t* __restrict__ rank_local) {
+  constexpr int NJ = NPAD / 16, BT = 64 * ROWT, WLD = 40, LD = NPAD + 4;
+  constexpr int WL = NPAD * 8 / 256;  // float4 loads per thread per K chunk
+  static_assert(WL >= 1, "at least one expert row per 32 threads");
+  // the weight planes during the K loop, then the block's logit tile
+  constexpr int PLANES = 2 * 3 * NPAD * WLD * 2, TILE = BT * LD * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char raw[PLANES > TILE ? PLANES : TILE];
+  typedef uint16_t PlaneArr[3][NPAD * WLD];
+  PlaneArr* wpl = reinterpret_cast<PlaneArr*>(raw);
+  float* st = reinterpret_cast<float*>(raw);
+  __shared__ int32_t s_idx[BT];
+  __shared__ int32_t cnt[FUSED ? NPAD : 1];
+  __shared__ float s_m[BT];
+  __shared__ double s_inv[BT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * BT;
+  const int e0 = blockIdx.y * NPAD;
+  const int n_tok = (int)((T - t0) < BT ? (T - t0) : BT);
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  const int64_t tw0 = t0 + wave * 16 * ROWT;
+
+  floatx4 acc[ROWT][NJ];
+#pragma unroll
+  for (int r = 0; r < ROWT; ++r)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[r][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* xrow[ROWT];
+#pragma unroll
+  for (int r = 0; r < ROWT; ++r) {
+    int64_t t = tw0 + 16 * r + fr;
+    t = t < T ? t : T - 1;  // rows past T: any valid row, never stored
+    xrow[r] = x + t * d + fk;
+  }
+  // W loader: thread covers expert row (tid / 8) + 32 q and k offset 4 (tid % 8)
+  const int wr = tid >> 3, wk = (tid & 7) * 4;
+  const float* wsrc[WL];
+  bool wok[WL];
+#pragma unroll
+  for (int q = 0; q < WL; ++q) {
+    const int e = e0 + wr + 32 * q;
+    wok[q] = e < N;
+    wsrc[q] = W_r + (int64_t)(e < N ? e : 0) * d + wk;
+  }
+  // PF register stages: K chunks kc+1 .. kc+PF are in flight while kc runs
+  constexpr int PF = 3;
+  float4 wreg[PF][WL];
+  bf16x8 xa[PF][ROWT];
+  const int nk = d / 32;
+  auto load_chunk = [&](int st, int kc) {
+    const int k = (kc < nk ? kc : nk - 1) * 32;
+#pragma unroll
+    for (int q = 0; q < WL; ++q) wreg[st][q] = *reinterpret_cast<const float4*>(wsrc[q] + k);
+#pragma unroll
+    for (int r = 0; r < ROWT; ++r) xa[st][r] = *reinterpret_cast<const bf16x8*>(xrow[r] + k);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto store_planes = [&](int st, int buf) {
+#pragma unroll
+    for (int q = 0; q < WL; ++q) {
+      const float4 wq = wreg[st][q];
+      const float w4[4] = {wok[q] ? wq.x : 0.f, wok[q] ? wq.y : 0.f, wok[q] ? wq.z : 0.f,
+                           wok[q] ? wq.w : 0.f};
+      uint32_t hv[2], mv[2], lv[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint16_t hb[2], mb[2], lb[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float w = w4[2 * h + u];
+          hb[u] = f32_to_bf16_bits(w);
+          const float r1 = w - bf16_bits_to_f32(hb[u]);
+          mb[u] = f32_to_bf16_bits(r1);
+          lb[u] = f32_to_bf16_bits(r1 - bf16_bits_to_f32(mb[u]));
+        }
+        hv[h] = hb[0] | ((uint32_t)hb[1] << 16);
+        mv[h] = mb[0] | ((uint32_t)mb[1] << 16);
+        lv[h] = lb[0] | ((uint32_t)lb[1] << 16);
+      }
+      const int off = (wr + 32 * q) * WLD + wk;
+      *reinterpret_cast<uint2*>(&wpl[buf][0][off]) = make_uint2(hv[0], hv[1]);
+      *reinterpret_cast<uint2*>(&wpl[buf][1][off]) = make_uint2(mv[0], mv[1]);
+      *reinterpret_cast<uint2*>(&wpl[buf][2][off]) = make_uint2(lv[0], lv[1]);
+    }
+  };
+  auto compute = [&](int st, int buf) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int off = (16 * j + fr) * WLD + fk;
+      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(&wpl[buf][2][off]);
+      const bf16x8 mid = *reinterpret_cast<const bf16x8*>(&wpl[buf][1][off]);
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&wpl[buf][0][off]);
+#pragma unroll
+      for (int r = 0; r < ROWT; ++r) {
+        acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[st][r], lo, acc[r][j], 0, 0, 0);
+        acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[st][r], mid, acc[r][j], 0, 0, 0);
+        acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[st][r], hi, acc[r][j], 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int st = 0; st < PF; ++st) load_chunk(st, st);
+  // chunk kc lives in register stage kc % PF and LDS buffer kc % 2; after its
+  // planes are stored and multiplied, the stage is refilled with chunk kc + PF
+  for (int kc0 = 0; kc0 < nk; kc0 += PF) {
+#pragma unroll
+    for (int st = 0; st < PF; ++st) {
+      const int kc = kc0 + st;
+      if (kc < nk) {
+        const int buf = kc & 1;
+        store_planes(st, buf);
+        __syncthreads();
+        compute(st, buf);
+        load_chunk(st, kc + PF);
+      }
+    }
+  }
+
+  // logit tile (+ bias, padded experts at -inf) into LDS over the weight planes
+  __syncthreads();
+  {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = e0 + 16 * j + fr;
+      const float bias = (e < N && b_r) ? b_r[e] : 0.f;
+#pragma unroll
+      for (int r = 0; r < ROWT; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          st[(wave * 16 * ROWT + 16 * r + 4 * g + i) * LD + 16 * j + fr] =
+              e < N ? acc[r][j][i] + bias : -__builtin_huge_valf();
+    }
+  }
+  __syncthreads();
+  if (!FUSED) {
+    // logits only, in full rows of the tile; statistics come from route_rows_kernel
+    const int ne = (N - e0) < NPAD ? (N - e0) : NPAD;
+    for (int idx = tid; idx < n_tok * ne; idx += 256) {
+      const int r = idx / ne, e = idx - r * ne;
+      logits[(t0 + r) * N + e0 + e] = st[r * LD + e];
+    }
+    return;
+  }
+  block_stats<BT, NPAD, LD>(st, N, t0, n_tok, logits, expert_idx, gate,
+                            P_part + (int64_t)blockIdx.x * N, s_idx, s_m, s_inv);
+  chunk_hist_rank(s_idx, n_tok, t0, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
 }
 
 // ---------------------------------------------------------------------------
@@ -417,29 +568,35 @@ __global__ __launch_bounds__(256) void route_rows_kernel(const float* __restrict
     for (int r = 0; r < rows; ++r) acc += (double)expf(h[(t0 + r) * N + i] - s_m[r]) * s_inv[r];
     P_part[(int64_t)blockIdx.x * N + i] = (float)acc;
   }
-  const int32_t my_e = (wave == 0 && lane < rows) ? s_idx[lane] : -1;
-  chunk_hist_rank(my_e, rows, t0 + lane, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
+  chunk_hist_rank(s_idx, rows, t0, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
 }
 
 // ------------------------------------------------------------------ launchers
+
+constexpr int kTokRowt = 2;                 // router_tok_kernel: 128 tokens per block
 
 bool router_fused_ok(bool x_bf16, int N) { return x_bf16 && N <= 256; }
 
 int64_t route_chunk_tokens(bool x_bf16, int N) {
   if (!router_fused_ok(x_bf16, N)) return RR_ROWS;
-  return 16;
+  return N <= 32 ? 16 : 64 * kTokRowt;
 }
 
 void launch_router_logits(const void* x, bool x_bf16, const float* W_r, const float* b_r,
                           float* h, int64_t T, int d, int N, hipStream_t s) {
   if (T == 0) return;
+  if (x_bf16) {
+    // MFMA logits in expert tiles of 256, statistics by route_rows_kernel
+    constexpr int BT = 64 * kTokRowt;
+    const dim3 grid((unsigned)((T + BT - 1) / BT), (unsigned)((N + 255) / 256));
+    hipLaunchKernelGGL((router_tok_kernel<256, kTokRowt, false>), grid, dim3(256), 0, s,
+                       (const uint16_t*)x, W_r, b_r, T, d, N, h, nullptr, nullptr, nullptr,
+                       nullptr, nullptr);
+    return;
+  }
   dim3 grid((unsigned)((T + RT_BT - 1) / RT_BT), (unsigned)((N + RT_BE - 1) / RT_BE));
-  if (x_bf16)
-    hipLaunchKernelGGL(router_logits_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       (const uint16_t*)x, W_r, b_r, h, T, d, N);
-  else
-    hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, s, (const float*)x, W_r,
-                       b_r, h, T, d, N);
+  hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, s, (const float*)x, W_r,
+                     b_r, h, T, d, N);
 }
 
 void launch_router_fused(const uint16_t* x, const float* W_r, const float* b_r, int64_t T, int d,
@@ -448,15 +605,19 @@ void launch_router_fused(const uint16_t* x, const float* W_r, const float* b_r, 
   if (T == 0) return;
   const int64_t ch = route_chunk_tokens(true, N);
   const dim3 grid((unsigned)((T + ch - 1) / ch));
-#define SWL_ROUTER(NP, RT)                                                                       \
-  hipLaunchKernelGGL((router_mfma_kernel<NP, RT>), grid, dim3(256), 0, s, x, W_r, b_r, T, d, N,  \
+#define SWL_SMALL(NP)                                                                           \
+  hipLaunchKernelGGL((router_small_kernel<NP>), grid, dim3(256), 0, s, x, W_r, b_r, T, d, N,    \
                      logits, expert_idx, gate, P_part, hist, rank_local)
-  if (N <= 16) SWL_ROUTER(16, 1);
-  else if (N <= 32) SWL_ROUTER(32, 1);
-  else if (N <= 64) SWL_ROUTER(64, 1);
-  else if (N <= 128) SWL_ROUTER(128, 1);
-  else SWL_ROUTER(256, 1);
-#undef SWL_ROUTER
+#define SWL_TOK(NP)                                                                             \
+  hipLaunchKernelGGL((router_tok_kernel<NP, kTokRowt, true>), grid, dim3(256), 0, s, x, W_r,    \
+                     b_r, T, d, N, logits, expert_idx, gate, P_part, hist, rank_local)
+  if (N <= 16) SWL_SMALL(16);
+  else if (N <= 32) SWL_SMALL(32);
+  else if (N <= 64) SWL_TOK(64);
+  else if (N <= 128) SWL_TOK(128);
+  else SWL_TOK(256);
+#undef SWL_SMALL
+#undef SWL_TOK
 }
 
 void launch_route_rows(const float* h, int64_t T, int N, int32_t* expert_idx, float* gate,

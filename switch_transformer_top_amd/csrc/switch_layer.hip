@@ -58,7 +58,9 @@ constexpr int64_t kRowsChunk = 64;  // chunk of the logits-based path
 Layout layout_of(const switch_layer* L, int64_t T) {
   const switch_config& c = L->cfg;
   const int64_t N = c.n_experts, Cb = buffer_rows(c, T);
-  const int64_t nc = (T + chunk_tokens(c) - 1) / chunk_tokens(c);
+  // the smallest chunk any entry point may use sets the number of chunk rows
+  const int64_t ch = chunk_tokens(c) < kRowsChunk ? chunk_tokens(c) : kRowsChunk;
+  const int64_t nc = (T + ch - 1) / ch;
   const size_t es = dtype_size(c.act_dtype);
   Layout lo;
   size_t off = 0;
@@ -265,8 +267,7 @@ switch_status switch_layer_create(const switch_config* cfg, const float* W_r, co
 
 void switch_layer_destroy(switch_layer* L) {
   if (!L) return;
-  if (L->prof.created)
-    for (int i = 0; i <= swl::Profiler::kMax; ++i) (void)hipEventDestroy(L->prof.ev[i]);
+  (void)switch_profile_enable(L, 0);
   delete L;
 }
 
@@ -327,32 +328,53 @@ switch_status switch_forward_debug(switch_layer* L, const void* x, int64_t T, vo
                       ws, ws_bytes, expert_out, (hipStream_t)stream);
 }
 
-switch_status switch_profile_enable(switch_layer* L, int enable) {
-  if (!L) return SWITCH_E_INVALID;
-  if (enable && !L->prof.created) {
-    for (int i = 0; i <= swl::Profiler::kMax; ++i) {
-      if (hipEventCreate(&L->prof.ev[i]) != hipSuccess) {
-        for (int j = 0; j < i; ++j) (void)hipEventDestroy(L->prof.ev[j]);
-        return SWITCH_E_HIP;
-      }
-    }
-    L->prof.created = true;
+switch_status switch_profile_enable(switch_layer* L, int max_calls) {
+  if (!L || max_calls < 0) return SWITCH_E_INVALID;
+  swl::Profiler& P = L->prof;
+  if (P.ev) {
+    for (int i = 0; i < P.max_calls * (swl::Profiler::kMax + 1); ++i) (void)hipEventDestroy(P.ev[i]);
+    delete[] P.ev;
+    P.ev = nullptr;
   }
-  L->prof.on = enable != 0;
-  L->prof.n = 0;
+  P.on = false;
+  P.max_calls = 0;
+  P.calls = 0;
+  P.n = 0;
+  if (max_calls == 0) return SWITCH_OK;
+  const int count = max_calls * (swl::Profiler::kMax + 1);
+  P.ev = new (std::nothrow) hipEvent_t[count];
+  if (!P.ev) return SWITCH_E_INVALID;
+  for (int i = 0; i < count; ++i) {
+    if (hipEventCreate(&P.ev[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(P.ev[j]);
+      delete[] P.ev;
+      P.ev = nullptr;
+      return SWITCH_E_HIP;
+    }
+  }
+  P.max_calls = max_calls;
+  P.on = true;
   return SWITCH_OK;
 }
 
 int switch_profile_read(switch_layer* L, float* ms, const char** names, int cap) {
-  if (!L || !L->prof.created || cap < 0) return -1;
-  const int n = L->prof.n;
-  if (n == 0) return 0;
-  if (hipEventSynchronize(L->prof.ev[n]) != hipSuccess) return -1;
+  if (!L || !L->prof.ev || cap < 0) return -1;
+  swl::Profiler& P = L->prof;
+  if (P.calls == 0) return 0;
+  const int stride = swl::Profiler::kMax + 1;
+  // every recorded call of this session has the same stages (the last one's)
+  const int n = P.n;
+  if (hipEventSynchronize(P.ev[(P.calls - 1) * stride + n]) != hipSuccess) return -1;
   for (int i = 0; i < n && i < cap; ++i) {
-    float t = 0.f;
-    if (hipEventElapsedTime(&t, L->prof.ev[i], L->prof.ev[i + 1]) != hipSuccess) return -1;
-    if (ms) ms[i] = t;
-    if (names) names[i] = L->prof.names[i];
+    double sum = 0.0;
+    for (int c = 0; c < P.calls; ++c) {
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, P.ev[c * stride + i], P.ev[c * stride + i + 1]) != hipSuccess)
+        return -1;
+      sum += t;
+    }
+    if (ms) ms[i] = (float)(sum / P.calls);
+    if (names) names[i] = P.names[i];
   }
   return n;
 }
