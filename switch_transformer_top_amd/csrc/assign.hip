@@ -18,72 +18,79 @@
 
 namespace swl {
 
-// One block of 1024 threads.  Experts are taken EG at a time (EG = N rounded
-// up to a power of two, at most 1024); the G = 1024 / EG threads of an expert
-// split the chunk range into contiguous pieces.  Each piece is summed (counts
-// and probability sums), the pieces are scanned in order, and each thread then
-// rewrites its piece of hist[:, e] as exclusive prefixes.  Probability sums
-// are added in fp64 in piece order, so every result is independent of timing.
+// Chunk scan.  A block of 1024 threads takes EG consecutive experts (EG a power
+// of two: N rounded up when one block covers all experts, 64 otherwise); the
+// G = 1024 / EG threads of an expert split the chunk range into contiguous
+// pieces.  Each thread sums its piece (counts and
+// probability sums); a log-step scan over the pieces (in LDS) gives each
+// piece's start, and the thread rewrites its piece of hist[:, e] as exclusive
+// prefixes.  Probability sums of the pieces add in a fixed pairwise tree
+// (fp64).  Every result is independent of timing.  With more than one block
+// the loss terms load_e * Psum_e go to `terms` for aux_kernel; with one block
+// the loss is finished here.
 __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ hist,
                                                           const float* __restrict__ P_part,
-                                                          int64_t nc, int N, int64_t T, int64_t C,
-                                                          float alpha, int32_t* __restrict__ load,
+                                                          int64_t nc, int N, int EG, int64_t T,
+                                                          int64_t C, float alpha,
+                                                          int32_t* __restrict__ load,
                                                           int32_t* __restrict__ n_kept,
+                                                          double* __restrict__ terms,
                                                           float* __restrict__ aux) {
   __shared__ int32_t s_cnt[1024];
   __shared__ double s_p[1024];
   const int tid = threadIdx.x;
-  int EG = 1;
-  while (EG < N && EG < 1024) EG <<= 1;
   const int G = 1024 / EG;
   const int el = tid % EG, g = tid / EG;
   const int64_t per = (nc + G - 1) / G;
   const int64_t c0 = (int64_t)g * per;
   const int64_t c1 = (c0 + per < nc) ? c0 + per : nc;
-  double aux_acc = 0.0;
+  const int e = blockIdx.x * EG + el;
+  const bool valid = e < N;
 
-  for (int e_base = 0; e_base < N; e_base += EG) {
-    const int e = e_base + el;
-    const bool valid = e < N;
-    int32_t cnt = 0;
-    double p = 0.0;
-    if (valid) {
+  int32_t cnt = 0;
+  double p = 0.0;
+  if (valid) {
 #pragma unroll 8
-      for (int64_t c = c0; c < c1; ++c) {
-        cnt += hist[c * N + e];
-        p += (double)P_part[c * N + e];
-      }
+    for (int64_t c = c0; c < c1; ++c) {
+      cnt += hist[c * N + e];
+      p += (double)P_part[c * N + e];
     }
-    s_cnt[tid] = cnt;
-    s_p[tid] = p;
+  }
+  s_cnt[tid] = cnt;
+  s_p[tid] = p;
+  __syncthreads();
+  // inclusive scan of the pieces' counts along g (Hillis-Steele)
+  for (int off = 1; off < G; off <<= 1) {
+    const int32_t v = g >= off ? s_cnt[tid - off * EG] : 0;
     __syncthreads();
-    if (g == 0 && valid) {
-      int32_t run = 0;
-      double ps = 0.0;
-      for (int gg = 0; gg < G; ++gg) {
-        const int32_t v = s_cnt[gg * EG + el];
-        s_cnt[gg * EG + el] = run;
-        run += v;
-        ps += s_p[gg * EG + el];
-      }
-      load[e] = run;
-      n_kept[e] = (int32_t)((int64_t)run < C ? (int64_t)run : C);
-      aux_acc += (double)run * ps;
-    }
-    __syncthreads();
-    if (valid) {
-      int32_t run = s_cnt[tid];
-#pragma unroll 8
-      for (int64_t c = c0; c < c1; ++c) {
-        const int32_t v = hist[c * N + e];
-        hist[c * N + e] = run;
-        run += v;
-      }
-    }
+    s_cnt[tid] += v;
     __syncthreads();
   }
-
-  s_p[tid] = aux_acc;
+  // pairwise sum of the pieces' probability sums along g
+  for (int half = G >> 1; half >= 1; half >>= 1) {
+    if (g < half) s_p[tid] += s_p[tid + half * EG];
+    __syncthreads();
+  }
+  if (valid) {
+    int32_t run = s_cnt[tid] - cnt;  // exclusive start of this piece
+#pragma unroll 8
+    for (int64_t c = c0; c < c1; ++c) {
+      const int32_t v = hist[c * N + e];
+      hist[c * N + e] = run;
+      run += v;
+    }
+  }
+  double term = 0.0;
+  if (g == G - 1 && valid) {
+    const int32_t total = s_cnt[tid];
+    load[e] = total;
+    n_kept[e] = (int32_t)((int64_t)total < C ? (int64_t)total : C);
+    term = (double)total * s_p[el];
+    if (terms) terms[e] = term;
+  }
+  if (terms) return;
+  __syncthreads();
+  s_p[tid] = term;
   __syncthreads();
   for (int s = 512; s >= 1; s >>= 1) {
     if (tid < s) s_p[tid] += s_p[tid + s];
@@ -92,6 +99,25 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
   if (tid == 0) {
     double v = 0.0;
     if (T > 0) v = (double)alpha * (double)N * (s_p[0] / ((double)T * (double)T));
+    *aux = (float)v;
+  }
+}
+
+// aux = alpha N sum_e terms[e] / T^2, summed in a fixed tree (fp64).
+__global__ __launch_bounds__(1024) void aux_kernel(const double* __restrict__ terms, int N,
+                                                   int64_t T, float alpha, float* __restrict__ aux) {
+  __shared__ double red[1024];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < N; i += 1024) acc += terms[i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 512; s >= 1; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double v = 0.0;
+    if (T > 0) v = (double)alpha * (double)N * (red[0] / ((double)T * (double)T));
     *aux = (float)v;
   }
 }
@@ -112,10 +138,19 @@ __global__ __launch_bounds__(256) void finalize_positions_kernel(
 // ------------------------------------------------------------------ launchers
 
 void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T,
-                       int64_t C, float alpha, int32_t* load, int32_t* n_kept, float* aux,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, P_part, nc, N, T, C,
-                     alpha, load, n_kept, aux);
+                       int64_t C, float alpha, int32_t* load, int32_t* n_kept, double* terms,
+                       float* aux, hipStream_t s) {
+  if (N <= 1024) {
+    int EG = 1;
+    while (EG < N) EG <<= 1;
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, P_part, nc, N, EG, T,
+                       C, alpha, load, n_kept, nullptr, aux);
+    return;
+  }
+  constexpr int EG = 64;
+  hipLaunchKernelGGL(route_scan_kernel, dim3((unsigned)((N + EG - 1) / EG)), dim3(1024), 0, s,
+                     hist, P_part, nc, N, EG, T, C, alpha, load, n_kept, terms, aux);
+  hipLaunchKernelGGL(aux_kernel, dim3(1), dim3(1024), 0, s, terms, N, T, alpha, aux);
 }
 
 void launch_finalize_positions(int64_t T, const int32_t* expert_idx, const int32_t* rank_local,

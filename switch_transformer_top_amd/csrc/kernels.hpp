@@ -50,8 +50,8 @@ void launch_route_rows(const float* h, int64_t T, int N, int32_t* expert_idx, fl
 
 // assign.hip
 void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T,
-                       int64_t C, float alpha, int32_t* load, int32_t* n_kept, float* aux,
-                       hipStream_t s);
+                       int64_t C, float alpha, int32_t* load, int32_t* n_kept, double* terms,
+                       float* aux, hipStream_t s);
 void launch_finalize_positions(int64_t T, const int32_t* expert_idx, const int32_t* rank_local,
                                const int32_t* offsets, int N, int64_t chunk, int64_t C,
                                int32_t* position, uint8_t* drop_mask, hipStream_t s);

@@ -45,7 +45,7 @@ int64_t buffer_rows(const switch_config& c, int64_t T) {
 }
 
 struct Layout {
-  size_t logits, ppart, hist, rank, load, nkept, xbuf, hbuf, ybuf, total;
+  size_t logits, ppart, hist, rank, load, nkept, terms, xbuf, hbuf, ybuf, total;
 };
 
 // Chunks of the routing statistics: the fused router uses small chunks, the
@@ -71,6 +71,7 @@ Layout layout_of(const switch_layer* L, int64_t T) {
   lo.rank = take(sizeof(int32_t) * (size_t)T);
   lo.load = take(sizeof(int32_t) * (size_t)N);
   lo.nkept = take(sizeof(int32_t) * (size_t)N);
+  lo.terms = take(sizeof(double) * (size_t)N);
   lo.xbuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_model);
   lo.hbuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_ff);
   lo.ybuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_model);
@@ -155,7 +156,8 @@ Routed enqueue_routing(switch_layer* L, const void* x, const float* given_logits
   }
   const int64_t nc = (T + r.chunk - 1) / r.chunk;
   swl::prof_mark(P, s, "route_scan");
-  swl::launch_route_scan(r.offsets, ppart, nc, N, T, r.Cb, c.alpha, r.load, r.nkept, aux_loss, s);
+  swl::launch_route_scan(r.offsets, ppart, nc, N, T, r.Cb, c.alpha, r.load, r.nkept,
+                         (double*)(ws + lo.terms), aux_loss, s);
   return r;
 }
 
