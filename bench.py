@@ -16,6 +16,8 @@ and the CPU oracle's throughput on the host cores.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -41,9 +43,13 @@ def stage_work(stage: str, spec, kept: int, active_experts: int) -> dict:
     T, d, F, N = spec.T, spec.d, spec.F, spec.N
     es = 2 if spec.act == "bf16" else 4
     if stage in ("router", "router_logits"):
-        # the fused router reads x and W_r and writes the per-token routing results
-        return dict(flops=2.0 * T * d * N, bytes=T * d * es + N * d * 4 + 8 * T,
-                    peak_tflops=PEAK_FP32_TFLOPS)
+        # fp32 logits of bf16 tokens run as three exact bf16 MFMA passes (one per
+        # piece of the split fp32 weight); fp32 tokens run on the fp32 FMA units.
+        # The router reads x and W_r and writes the per-token routing results.
+        nbytes = T * d * es + N * d * 4 + 8 * T + (T * N * 4 if stage == "router_logits" else 0)
+        if spec.act == "bf16":
+            return dict(flops=3 * 2.0 * T * d * N, bytes=nbytes, peak_tflops=PEAK_BF16_TFLOPS)
+        return dict(flops=2.0 * T * d * N, bytes=nbytes, peak_tflops=PEAK_FP32_TFLOPS)
     if stage in ("gemm1_relu", "gemm2"):
         return dict(flops=2.0 * kept * d * F,
                     bytes=active_experts * d * F * es + kept * (d + F) * es,
@@ -72,6 +78,45 @@ def roofline_entry(stage: str, work: dict, ms: float) -> dict:
             "mean_ms": round(ms, 5),
             "mfma_frac": round(work["flops"] / sec / 1e12 / PEAK_BF16_TFLOPS, 4)
             if work["flops"] else None}
+
+
+# stage of the forward call -> (kernel name in the hardware-counter profiles, source file)
+STAGE_KERNEL = {"gemm1_relu": ("gemm_bf16_kernel<", "true>", "gemm.hip"),
+                "gemm2": ("gemm_bf16_kernel<", "false>", "gemm.hip"),
+                "router": ("router_", "", "router.hip"),
+                "dispatch": ("dispatch_kernel", "", "move.hip"),
+                "combine": ("combine_kernel<", "", "move.hip")}
+
+
+def measured_traffic(stage: str, workload: str):
+    """HBM bytes per launch from the committed counter profiles (FETCH_SIZE and
+    WRITE_SIZE, scaled by a 1 GiB copy), or None when there is no figure for this
+    kernel and workload or its source has changed since the counters were taken."""
+    if stage not in STAGE_KERNEL:
+        return None
+    prefix, suffix, src = STAGE_KERNEL[stage]
+    h = hashlib.sha256()
+    for f in (src, "common.hpp"):
+        with open(os.path.join(ROOT, "switch_transformer_top_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_bytes.md")):
+        with open(path, encoding="utf-8") as fh:
+            for line in fh:
+                if not line.startswith("traffic:"):
+                    continue
+                kv = dict(part.split("=", 1) for part in
+                          line[len("traffic:"):].strip().replace("kernel=", "\x00kernel=")
+                          .replace(" bytes_per_launch=", "\x00bytes_per_launch=")
+                          .replace(" source=", "\x00source=")
+                          .replace(" source_sha256=", "\x00source_sha256=").split("\x00")
+                          if "=" in part)
+                kv = {k.strip(): v.strip() for k, v in kv.items()}
+                k = kv.get("kernel", "")
+                if (kv.get("workload") == workload and k.startswith(prefix) and k.endswith(suffix)
+                        and kv.get("source_sha256") == digest):
+                    return float(kv["bytes_per_launch"])
+    return None
 
 
 def cpu_baseline(spec, host, budget_s: float) -> dict:
@@ -222,6 +267,8 @@ def main():
                  if k in ("router", "router_logits", "gemm1_relu", "gemm2", "dispatch",
                           "combine")}
     dominant = max(rooflines, key=lambda k: stage_ms[k])
+    for k, r in rooflines.items():
+        r["traffic"] = measured_traffic(k, spec.name)
     gemm_ms = stage_ms.get("gemm1_relu", 0) + stage_ms.get("gemm2", 0)
     expert_tflops = 4.0 * kept * spec.d * spec.F / (gemm_ms * 1e-3) / 1e12 if gemm_ms else 0.0
 
