@@ -20,6 +20,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -88,6 +89,11 @@ STAGE_KERNEL = {"gemm1_relu": ("gemm_bf16_kernel<", "true>", "gemm.hip"),
                 "combine": ("combine_kernel<", "", "move.hip")}
 
 
+_TRAFFIC_LINE = re.compile(
+    r"traffic: workload=(?P<workload>\S+) kernel=(?P<kernel>.+?) bytes_per_launch=(?P<bytes_per_launch>\d+)"
+    r" source=(?P<source>\S+) source_sha256=(?P<source_sha256>[0-9a-f]+)\s*$")
+
+
 def measured_traffic(stage: str, workload: str):
     """HBM bytes per launch from the committed counter profiles (FETCH_SIZE and
     WRITE_SIZE, scaled by a 1 GiB copy), or None when there is no figure for this
@@ -103,15 +109,10 @@ def measured_traffic(stage: str, workload: str):
     for path in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_bytes.md")):
         with open(path, encoding="utf-8") as fh:
             for line in fh:
-                if not line.startswith("traffic:"):
+                m = _TRAFFIC_LINE.match(line)
+                if not m:
                     continue
-                kv = dict(part.split("=", 1) for part in
-                          line[len("traffic:"):].strip().replace("kernel=", "\x00kernel=")
-                          .replace(" bytes_per_launch=", "\x00bytes_per_launch=")
-                          .replace(" source=", "\x00source=")
-                          .replace(" source_sha256=", "\x00source_sha256=").split("\x00")
-                          if "=" in part)
-                kv = {k.strip(): v.strip() for k, v in kv.items()}
+                kv = m.groupdict()
                 k = kv.get("kernel", "")
                 if (kv.get("workload") == workload and k.startswith(prefix) and k.endswith(suffix)
                         and kv.get("source_sha256") == digest):
