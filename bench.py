@@ -51,11 +51,21 @@ def stage_work(stage: str, spec, kept: int, active_experts: int) -> dict:
         if spec.act == "bf16":
             return dict(flops=3 * 2.0 * T * d * N, bytes=nbytes, peak_tflops=PEAK_BF16_TFLOPS)
         return dict(flops=2.0 * T * d * N, bytes=nbytes, peak_tflops=PEAK_FP32_TFLOPS)
+    peak = PEAK_BF16_TFLOPS if spec.expert == "bf16" else PEAK_FP32_TFLOPS
     if stage in ("gemm1_relu", "gemm2"):
+        # weights of the experts in use, the kept rows in and the outputs out
         return dict(flops=2.0 * kept * d * F,
-                    bytes=active_experts * d * F * es + kept * (d + F) * es,
-                    peak_tflops=PEAK_BF16_TFLOPS if spec.expert == "bf16" else PEAK_FP32_TFLOPS)
+                    bytes=active_experts * d * F * es + kept * (d + F) * es, peak_tflops=peak)
+    if stage == "gemm2_combine":
+        # as gemm2, plus the residual rows read and the layer output written in
+        # place of the expert output (gate and slot table: 8 bytes per row)
+        return dict(flops=2.0 * kept * d * F,
+                    bytes=active_experts * d * F * es + kept * (F + 2 * d) * es + 8 * kept,
+                    peak_tflops=peak)
     if stage == "dispatch":
+        if spec.act == "bf16":
+            # slot table only (the rows stay in place); dropped rows copied to out
+            return dict(flops=0.0, bytes=2 * (T - kept) * d * es + 21 * T, peak_tflops=None)
         return dict(flops=0.0, bytes=2 * kept * d * es + 9 * T, peak_tflops=None)
     if stage == "combine":
         return dict(flops=0.0, bytes=(kept + 2 * T) * d * es + 13 * T, peak_tflops=None)
@@ -82,10 +92,11 @@ def roofline_entry(stage: str, work: dict, ms: float) -> dict:
 
 
 # stage of the forward call -> (kernel name in the hardware-counter profiles, source file)
-STAGE_KERNEL = {"gemm1_relu": ("gemm_bf16_kernel<", "true>", "gemm.hip"),
-                "gemm2": ("gemm_bf16_kernel<", "false>", "gemm.hip"),
+STAGE_KERNEL = {"gemm1_relu": ("gemm_bf16_kernel<", "true, 1>", "gemm.hip"),
+                "gemm2": ("gemm_bf16_kernel<", "false, 0>", "gemm.hip"),
+                "gemm2_combine": ("gemm_bf16_kernel<", "false, 2>", "gemm.hip"),
                 "router": ("router_", "", "router.hip"),
-                "dispatch": ("dispatch_kernel", "", "move.hip"),
+                "dispatch": ("dispatch_index_kernel", "", "move.hip"),
                 "combine": ("combine_kernel<", "", "move.hip")}
 
 
@@ -265,12 +276,13 @@ def main():
 
     rooflines = {k: roofline_entry(k, stage_work(k, spec, kept, active), v)
                  for k, v in stage_ms.items()
-                 if k in ("router", "router_logits", "gemm1_relu", "gemm2", "dispatch",
-                          "combine")}
+                 if k in ("router", "router_logits", "gemm1_relu", "gemm2", "gemm2_combine",
+                          "dispatch", "combine")}
     dominant = max(rooflines, key=lambda k: stage_ms[k])
     for k, r in rooflines.items():
         r["traffic"] = measured_traffic(k, spec.name)
-    gemm_ms = stage_ms.get("gemm1_relu", 0) + stage_ms.get("gemm2", 0)
+    gemm_ms = (stage_ms.get("gemm1_relu", 0) + stage_ms.get("gemm2", 0)
+               + stage_ms.get("gemm2_combine", 0))
     expert_tflops = 4.0 * kept * spec.d * spec.F / (gemm_ms * 1e-3) / 1e12 if gemm_ms else 0.0
 
     result = {

@@ -31,6 +31,19 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// out = x + g * y on eight bf16 values (16 bytes): fp32 fused multiply-add,
+// rounded to nearest even.  y is the expert output already rounded to bf16.
+__device__ __forceinline__ u32x4 combine_vec_bf16(u32x4 xv, u32x4 yv, float g) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x0 = __uint_as_float(xv[i] << 16), x1 = __uint_as_float(xv[i] & 0xFFFF0000u);
+    const float y0 = __uint_as_float(yv[i] << 16), y1 = __uint_as_float(yv[i] & 0xFFFF0000u);
+    o[i] = f32x2_to_bf16x2_bits(fmaf(g, y0, x0), fmaf(g, y1, x1));
+  }
+  return o;
+}
+
 // Element access for the two activation types.
 template <typename T> struct Elem;
 template <> struct Elem<float> {

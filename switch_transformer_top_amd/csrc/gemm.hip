@@ -10,6 +10,13 @@
 // The number of rows of expert e, n_kept[e], is read on the device: tiles past
 // it return at once, so the host never waits for the routing result.
 //
+// On the bf16 path the token rows never move: GEMM1 reads the A rows of
+// expert e straight from x through the slot table tok[e * C + m] (the dispatch
+// of the kasblo explainer's forward pass becomes an indexed load), and GEMM2
+// combines its output rows into out[t] = x[t] + gate[t] * y (the combine, with
+// the gate multiply of llm-papers-study section 3.2 and the residual of its
+// part 六 diagram) in its epilogue.
+//
 // bf16 path: CDNA4 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation, the
 // result rounded to bf16 (after the ReLU for GEMM1).  fp32 path: plain FMA.
 #include "common.hpp"
@@ -49,6 +56,40 @@ __device__ __forceinline__ void store_tile_bf16(const floatx16 (&acc)[TI][TJ], u
   }
 }
 
+// Combine epilogue: like store_tile_bf16 (no ReLU), but each 16-byte piece of
+// output row m goes to token t = tok_e[m]: out[t] = x[t] + gate[t] * y, with y
+// the expert output rounded to bf16 first (the same arithmetic as a separate
+// combine pass over a stored expert output).
+template <int TI, int TJ>
+__device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ], uint16_t* stage,
+                                                   const int32_t* __restrict__ tok_e,
+                                                   const uint16_t* __restrict__ x,
+                                                   const float* __restrict__ gate,
+                                                   uint16_t* __restrict__ out, int r0, int c0,
+                                                   int rows_e, int d, int lane) {
+  constexpr int W = TJ * 32, LD = W + 8, CPR = W / 8;
+  const int fr = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        stage[(i * 32 + 8 * (v >> 2) + 4 * g + (v & 3)) * LD + j * 32 + fr] =
+            f32_to_bf16_bits(acc[i][j][v]);
+#pragma unroll 4
+  for (int idx = lane; idx < TI * 32 * CPR; idx += kWave) {
+    const int row = idx / CPR, ch = idx - row * CPR;
+    if (r0 + row < rows_e) {
+      const int64_t t = tok_e[r0 + row];
+      const int64_t at = t * d + c0 + ch * 8;
+      const u32x4 yv = *reinterpret_cast<const u32x4*>(stage + row * LD + ch * 8);
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(x + at);
+      *reinterpret_cast<u32x4*>(out + at) = combine_vec_bf16(xv, yv, gate[t]);
+    }
+  }
+}
+
 // Tile order: the grid is 1-D.  Workgroups are handed to the 8 XCDs round
 // robin (block b runs on XCD b % 8), so block b takes tile
 // (b % 8) * ceil(tiles / 8) + b / 8: each XCD walks a contiguous stretch of the
@@ -66,7 +107,7 @@ __device__ __forceinline__ void store_tile_bf16(const floatx16 (&acc)[TI][TJ], u
 // MFMA 32x32x16 operand layout (per lane l): A row (l % 32) with 8 consecutive
 // k, B column (l % 32) with the same 8 k; the k group is (l / 32).  Result: lane
 // l holds column (l % 32) and rows 8 (v / 4) + 4 (l / 32) + (v % 4), v < 16.
-template <int BM, int BN, bool RELU>
+template <int BM, int BN, bool RELU, int MODE>
 __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                         int64_t strideA,
                                                         const uint16_t* __restrict__ B,
@@ -75,7 +116,7 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
                                                         int64_t strideC,
                                                         const int32_t* __restrict__ rows, int K,
                                                         int Nout, int m_tiles, int n_tiles,
-                                                        int tiles) {
+                                                        int tiles, GemmIO io, int64_t C) {
   constexpr int LA = BM / 32, LB = BN / 32;   // 16-byte loads per thread per operand
   constexpr int TI = BM / 64, TJ = BN / 64;   // MFMA tiles per wave
   // one buffer holding the A rows then the B rows; reused by the epilogue
@@ -95,9 +136,11 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
   if (m0 >= rows_e) return;
   const int n0 = nt * BN;
 
-  const uint16_t* Ae = A + (int64_t)e * strideA;
+  // GATHER: A is x itself and the rows come from the slot table
+  const uint16_t* Ae = MODE == kRowsGather ? io.x : A + (int64_t)e * strideA;
   const uint16_t* Be = B + (int64_t)e * strideB + (int64_t)n0 * K;
   uint16_t* Ce = Cout + (int64_t)e * strideC;
+  const int32_t* tok_e = MODE == kRowsDense ? nullptr : io.tok + (int64_t)e * C;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -109,7 +152,8 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
   for (int j = 0; j < LA; ++j) {
     int r = m0 + lrow + 32 * j;
     r = r < rows_e ? r : rows_e - 1;  // rows past n_kept: any valid row, never stored
-    a_off[j] = (int64_t)r * K + lcol;
+    const int64_t src = MODE == kRowsGather ? (int64_t)tok_e[r] : (int64_t)r;
+    a_off[j] = src * K + lcol;
   }
 #pragma unroll
   for (int j = 0; j < LB; ++j) b_off[j] = (int64_t)(lrow + 32 * j) * K + lcol;
@@ -168,8 +212,12 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
   }
 
   __syncthreads();  // every wave is done with the LDS operand tiles
-  store_tile_bf16<TI, TJ, RELU>(acc, lds + wave * (BM / 2) * (BN / 2 + 8), Ce,
-                                m0 + wm * (BM / 2), n0 + wn * (BN / 2), rows_e, Nout, lane);
+  if (MODE == kRowsCombine)
+    store_tile_combine<TI, TJ>(acc, lds + wave * (BM / 2) * (BN / 2 + 8), tok_e, io.x, io.gate,
+                               io.out, m0 + wm * (BM / 2), n0 + wn * (BN / 2), rows_e, Nout, lane);
+  else
+    store_tile_bf16<TI, TJ, RELU>(acc, lds + wave * (BM / 2) * (BN / 2 + 8), Ce,
+                                  m0 + wm * (BM / 2), n0 + wn * (BN / 2), rows_e, Nout, lane);
 }
 
 // fp32 path (parity-sized fp32 layers): 32 x 32 tile, K in steps of 32, each
@@ -225,23 +273,39 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 // ------------------------------------------------------------------ launchers
 
+void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t strideA,
+                             const void* B, int64_t strideB, void* Cout, int64_t strideC,
+                             const int32_t* rows, int n_experts, int64_t C, int K, int Nout,
+                             const GemmIO& io, hipStream_t s) {
+  if (C == 0 || n_experts == 0) return;
+  constexpr int BM = 128, BN = 128;
+  const int mt = (int)((C + BM - 1) / BM), nt = Nout / BN;
+  const int tiles = mt * nt * n_experts;
+  const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
+  const uint16_t* a = (const uint16_t*)A;
+  const uint16_t* b = (const uint16_t*)B;
+  uint16_t* c = (uint16_t*)Cout;
+  if (mode == kRowsGather && relu)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true, kRowsGather>), dim3(grid), dim3(256), 0, s,
+                       a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
+  else if (mode == kRowsCombine)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false, kRowsCombine>), dim3(grid), dim3(256), 0,
+                       s, a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
+  else if (relu)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true, kRowsDense>), dim3(grid), dim3(256), 0, s,
+                       a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false, kRowsDense>), dim3(grid), dim3(256), 0, s,
+                       a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
+}
+
 void launch_expert_gemm(bool bf16, bool relu, const void* A, int64_t strideA, const void* B,
                         int64_t strideB, void* Cout, int64_t strideC, const int32_t* rows,
                         int n_experts, int64_t C, int K, int Nout, hipStream_t s) {
   if (C == 0 || n_experts == 0) return;
   if (bf16) {
-    constexpr int BM = 128, BN = 128;
-    const int mt = (int)((C + BM - 1) / BM), nt = Nout / BN;
-    const int tiles = mt * nt * n_experts;
-    const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
-    if (relu)
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true>), dim3(grid), dim3(256), 0, s,
-                         (const uint16_t*)A, strideA, (const uint16_t*)B, strideB,
-                         (uint16_t*)Cout, strideC, rows, K, Nout, mt, nt, tiles);
-    else
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false>), dim3(grid), dim3(256), 0, s,
-                         (const uint16_t*)A, strideA, (const uint16_t*)B, strideB,
-                         (uint16_t*)Cout, strideC, rows, K, Nout, mt, nt, tiles);
+    launch_expert_gemm_bf16(kRowsDense, relu, A, strideA, B, strideB, Cout, strideC, rows,
+                            n_experts, C, K, Nout, GemmIO{}, s);
   } else {
     dim3 grid((unsigned)((Nout + 31) / 32), (unsigned)((C + 31) / 32), (unsigned)n_experts);
     if (relu)

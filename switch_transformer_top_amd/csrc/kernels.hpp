@@ -60,6 +60,10 @@ void launch_finalize_positions(int64_t T, const int32_t* expert_idx, const int32
 void launch_dispatch(const void* x, int64_t T, int row_bytes, const int32_t* expert_idx,
                      const int32_t* rank_local, const int32_t* offsets, int N, int64_t chunk,
                      int64_t C, int32_t* position, uint8_t* drop_mask, void* Xbuf, hipStream_t s);
+void launch_dispatch_index(const void* x, int64_t T, int row_bytes, const int32_t* expert_idx,
+                           const int32_t* rank_local, const int32_t* offsets, int N, int64_t chunk,
+                           int64_t C, int32_t* position, uint8_t* drop_mask, int32_t* tok,
+                           void* out, hipStream_t s);
 void launch_combine(const void* x, bool bf16, int64_t T, int row_bytes, const int32_t* expert_idx,
                     const int32_t* position, const uint8_t* drop_mask, const float* gate,
                     int64_t C, const void* Ybuf, void* out, hipStream_t s);
@@ -67,6 +71,20 @@ void launch_copy_expert_rows(const void* Ybuf, const int32_t* n_kept, int N, int
                              int row_bytes, void* dst, hipStream_t s);
 
 // gemm.hip
+// Row routing of the bf16 expert matmuls.  GATHER: the A rows of expert e are
+// rows tok[e * C + m] of x (K = d_model).  COMBINE: output row m of expert e is
+// combined into out[tok[e * C + m]] = x + gate * y instead of being stored.
+enum GemmRows { kRowsDense = 0, kRowsGather = 1, kRowsCombine = 2 };
+struct GemmIO {
+  const int32_t* tok = nullptr;
+  const uint16_t* x = nullptr;
+  const float* gate = nullptr;
+  uint16_t* out = nullptr;
+};
+void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t strideA,
+                             const void* B, int64_t strideB, void* Cout, int64_t strideC,
+                             const int32_t* rows, int n_experts, int64_t C, int K, int Nout,
+                             const GemmIO& io, hipStream_t s);
 void launch_expert_gemm(bool bf16, bool relu, const void* A, int64_t strideA, const void* B,
                         int64_t strideB, void* Cout, int64_t strideC, const int32_t* rows,
                         int n_experts, int64_t C, int K, int Nout, hipStream_t s);

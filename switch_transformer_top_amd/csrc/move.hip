@@ -44,19 +44,6 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const uint4* __restrict__
   if (!dropped) Xbuf[((int64_t)e * C + pos) * row_vec16 + c] = x[t * row_vec16 + c];
 }
 
-__device__ __forceinline__ uint4 combine_vec_bf16(uint4 xv, uint4 yv, float g) {
-  uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-  uint32_t ys[4] = {yv.x, yv.y, yv.z, yv.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float x0 = __uint_as_float(xs[i] << 16), x1 = __uint_as_float(xs[i] & 0xFFFF0000u);
-    float y0 = __uint_as_float(ys[i] << 16), y1 = __uint_as_float(ys[i] & 0xFFFF0000u);
-    o[i] = f32x2_to_bf16x2_bits(fmaf(g, y0, x0), fmaf(g, y1, x1));
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
 __device__ __forceinline__ uint4 combine_vec_f32(uint4 xv, uint4 yv, float g) {
   float4 a = *reinterpret_cast<float4*>(&xv), b = *reinterpret_cast<float4*>(&yv);
   float4 o = make_float4(fmaf(g, b.x, a.x), fmaf(g, b.y, a.y), fmaf(g, b.z, a.z), fmaf(g, b.w, a.w));
@@ -83,7 +70,42 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   }
   const float g = gate[t];
   const uint4 yv = Ybuf[((int64_t)expert_idx[t] * C + position[t]) * row_vec16 + c];
-  out[t * row_vec16 + c] = BF16 ? combine_vec_bf16(xv, yv, g) : combine_vec_f32(xv, yv, g);
+  if (BF16) {
+    const u32x4 o = combine_vec_bf16(u32x4{xv.x, xv.y, xv.z, xv.w}, u32x4{yv.x, yv.y, yv.z, yv.w}, g);
+    out[t * row_vec16 + c] = make_uint4(o.x, o.y, o.z, o.w);
+  } else {
+    out[t * row_vec16 + c] = combine_vec_f32(xv, yv, g);
+  }
+}
+
+// Dispatch by index (bf16 path): the expert matmuls read the rows of x in
+// place, so dispatch only finalises the routing and records, for every kept
+// token, which token sits in slot (e, position): tok[e * C + position] = t.
+// A dropped token leaves the layer unchanged: its row of x is copied to out
+// here, and the fused combine never touches it.
+__global__ __launch_bounds__(256) void dispatch_index_kernel(const uint4* __restrict__ x, int64_t T,
+                                                             int row_vec16,
+                                                             const int32_t* __restrict__ expert_idx,
+                                                             const int32_t* __restrict__ rank_local,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int N, int64_t chunk, int64_t C,
+                                                             int32_t* __restrict__ position,
+                                                             uint8_t* __restrict__ drop_mask,
+                                                             int32_t* __restrict__ tok,
+                                                             uint4* __restrict__ out) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t = gid / row_vec16;
+  const int c = (int)(gid - t * row_vec16);
+  if (t >= T) return;
+  const int32_t e = expert_idx[t];
+  const int32_t pos = offsets[(t / chunk) * N + e] + rank_local[t];
+  const bool dropped = (int64_t)pos >= C;
+  if (c == 0) {
+    position[t] = pos;
+    drop_mask[t] = dropped ? 1 : 0;
+    if (!dropped) tok[(int64_t)e * C + pos] = (int32_t)t;
+  }
+  if (dropped) out[t * row_vec16 + c] = x[t * row_vec16 + c];
 }
 
 // Copy of the expert outputs for the debug entry point: rows p < n_kept[e].
@@ -113,6 +135,16 @@ void launch_dispatch(const void* x, int64_t T, int row_bytes, const int32_t* exp
   hipLaunchKernelGGL(dispatch_kernel, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s, (const uint4*)x, T,
                      row_bytes / 16, expert_idx, rank_local, offsets, N, chunk, C, position,
                      drop_mask, (uint4*)Xbuf);
+}
+
+void launch_dispatch_index(const void* x, int64_t T, int row_bytes, const int32_t* expert_idx,
+                           const int32_t* rank_local, const int32_t* offsets, int N, int64_t chunk,
+                           int64_t C, int32_t* position, uint8_t* drop_mask, int32_t* tok,
+                           void* out, hipStream_t s) {
+  if (T == 0) return;
+  hipLaunchKernelGGL(dispatch_index_kernel, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
+                     (const uint4*)x, T, row_bytes / 16, expert_idx, rank_local, offsets, N, chunk,
+                     C, position, drop_mask, tok, (uint4*)out);
 }
 
 void launch_combine(const void* x, bool bf16, int64_t T, int row_bytes, const int32_t* expert_idx,

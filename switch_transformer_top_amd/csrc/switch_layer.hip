@@ -45,7 +45,7 @@ int64_t buffer_rows(const switch_config& c, int64_t T) {
 }
 
 struct Layout {
-  size_t logits, ppart, hist, rank, load, nkept, terms, xbuf, hbuf, ybuf, total;
+  size_t logits, ppart, hist, rank, load, nkept, terms, tok, xbuf, hbuf, ybuf, total;
 };
 
 // Chunks of the routing statistics: the fused router uses small chunks, the
@@ -72,7 +72,10 @@ Layout layout_of(const switch_layer* L, int64_t T) {
   lo.load = take(sizeof(int32_t) * (size_t)N);
   lo.nkept = take(sizeof(int32_t) * (size_t)N);
   lo.terms = take(sizeof(double) * (size_t)N);
-  lo.xbuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_model);
+  lo.tok = take(sizeof(int32_t) * (size_t)N * (size_t)Cb);
+  // the bf16 path reads token rows in place; only the fp32 path gathers them
+  const bool gather_copy = c.act_dtype != SWITCH_BF16;
+  lo.xbuf = take(gather_copy ? es * (size_t)N * (size_t)Cb * (size_t)c.d_model : 0);
   lo.hbuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_ff);
   lo.ybuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_model);
   lo.total = off;
@@ -190,7 +193,37 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
   void* xbuf = w + lo.xbuf;
   void* hbuf = w + lo.hbuf;
   void* ybuf = w + lo.ybuf;
-  if (T > 0) {
+  if (T > 0 && bf16) {
+    // rows stay in place: dispatch records the slot table, GEMM1 gathers
+    // through it, GEMM2 combines into out (or stores the expert output when
+    // the caller asks for it, and the combine pass follows)
+    int32_t* tok = (int32_t*)(w + lo.tok);
+    swl::GemmIO io;
+    io.tok = tok;
+    io.x = (const uint16_t*)x;
+    io.gate = gate;
+    io.out = (uint16_t*)out;
+    swl::prof_mark(P, s, "dispatch");
+    swl::launch_dispatch_index(x, T, (int)(es * d), expert_idx, r.rank, r.offsets, N, r.chunk, Cb,
+                               position, drop_mask, tok, out, s);
+    swl::prof_mark(P, s, "gemm1_relu");
+    swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
+                                 hbuf, Cb * F, r.nkept, N, Cb, d, F, io, s);
+    if (!expert_out) {
+      swl::prof_mark(P, s, "gemm2_combine");
+      swl::launch_expert_gemm_bf16(swl::kRowsCombine, false, hbuf, Cb * F, L->W_out,
+                                   (int64_t)d * F, nullptr, 0, r.nkept, N, Cb, F, d, io, s);
+    } else {
+      swl::prof_mark(P, s, "gemm2");
+      swl::launch_expert_gemm_bf16(swl::kRowsDense, false, hbuf, Cb * F, L->W_out, (int64_t)d * F,
+                                   ybuf, Cb * d, r.nkept, N, Cb, F, d, io, s);
+      swl::prof_mark(P, s, "combine");
+      swl::launch_combine(x, bf16, T, (int)(es * d), expert_idx, position, drop_mask, gate, Cb,
+                          ybuf, out, s);
+      swl::prof_mark(P, s, "copy_expert_rows");
+      swl::launch_copy_expert_rows(ybuf, r.nkept, N, Cb, (int)(es * d), expert_out, s);
+    }
+  } else if (T > 0) {
     swl::prof_mark(P, s, "dispatch");
     swl::launch_dispatch(x, T, (int)(es * d), expert_idx, r.rank, r.offsets, N, r.chunk, Cb,
                          position, drop_mask, xbuf, s);
