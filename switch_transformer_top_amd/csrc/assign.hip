@@ -18,6 +18,33 @@
 
 namespace swl {
 
+// tile_start[e] = sum over e' < e of ceil(n_kept[e'] / tile_rows), and
+// tile_start[N] the total: the compact tile list of the grouped matmuls.  One
+// block of 1024 threads; each thread takes a contiguous run of experts.
+__device__ void tile_prefix_block(const int32_t* __restrict__ n_kept, int N, int tile_rows,
+                                  int32_t* __restrict__ tile_start, int32_t* s_run) {
+  const int tid = threadIdx.x;
+  const int per = (N + 1023) / 1024;
+  const int used = (N + per - 1) / per;             // threads that own experts
+  const int e0 = tid * per, e1 = (e0 + per < N) ? e0 + per : N;
+  int32_t sum = 0;
+  for (int e = e0; e < e1; ++e) sum += (n_kept[e] + tile_rows - 1) / tile_rows;
+  s_run[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < used; off <<= 1) {
+    const int32_t v = tid >= off ? s_run[tid - off] : 0;
+    __syncthreads();
+    s_run[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = s_run[tid] - sum;
+  for (int e = e0; e < e1; ++e) {
+    tile_start[e] = run;
+    run += (n_kept[e] + tile_rows - 1) / tile_rows;
+  }
+  if (tid == used - 1) tile_start[N] = s_run[tid];
+}
+
 // Chunk scan.  A block of 1024 threads takes EG consecutive experts (EG a power
 // of two: N rounded up when one block covers all experts, 64 otherwise); the
 // G = 1024 / EG threads of an expert split the chunk range into contiguous
@@ -35,7 +62,9 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
                                                           int32_t* __restrict__ load,
                                                           int32_t* __restrict__ n_kept,
                                                           double* __restrict__ terms,
-                                                          float* __restrict__ aux) {
+                                                          float* __restrict__ aux,
+                                                          int32_t* __restrict__ tile_start,
+                                                          int tile_rows) {
   __shared__ int32_t s_cnt[1024];
   __shared__ double s_p[1024];
   const int tid = threadIdx.x;
@@ -89,10 +118,11 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
     if (terms) terms[e] = term;
   }
   if (terms) return;
+  // the EG loss terms sit in the last EG threads: a fixed pairwise tree over them
   __syncthreads();
-  s_p[tid] = term;
+  if (g == G - 1) s_p[el] = term;
   __syncthreads();
-  for (int s = 512; s >= 1; s >>= 1) {
+  for (int s = EG >> 1; s >= 1; s >>= 1) {
     if (tid < s) s_p[tid] += s_p[tid + s];
     __syncthreads();
   }
@@ -101,12 +131,18 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
     if (T > 0) v = (double)alpha * (double)N * (s_p[0] / ((double)T * (double)T));
     *aux = (float)v;
   }
+  // n_kept of every expert was written by this block above
+  if (tile_start) tile_prefix_block(n_kept, N, tile_rows, tile_start, s_cnt);
 }
 
 // aux = alpha N sum_e terms[e] / T^2, summed in a fixed tree (fp64).
 __global__ __launch_bounds__(1024) void aux_kernel(const double* __restrict__ terms, int N,
-                                                   int64_t T, float alpha, float* __restrict__ aux) {
+                                                   int64_t T, float alpha, float* __restrict__ aux,
+                                                   const int32_t* __restrict__ n_kept,
+                                                   int32_t* __restrict__ tile_start,
+                                                   int tile_rows) {
   __shared__ double red[1024];
+  __shared__ int32_t s_run[1024];
   double acc = 0.0;
   for (int i = threadIdx.x; i < N; i += 1024) acc += terms[i];
   red[threadIdx.x] = acc;
@@ -120,6 +156,7 @@ __global__ __launch_bounds__(1024) void aux_kernel(const double* __restrict__ te
     if (T > 0) v = (double)alpha * (double)N * (red[0] / ((double)T * (double)T));
     *aux = (float)v;
   }
+  if (tile_start) tile_prefix_block(n_kept, N, tile_rows, tile_start, s_run);
 }
 
 // position = chunk offset + in-chunk rank; drop when it reaches C (route only:
@@ -139,18 +176,20 @@ __global__ __launch_bounds__(256) void finalize_positions_kernel(
 
 void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T,
                        int64_t C, float alpha, int32_t* load, int32_t* n_kept, double* terms,
-                       float* aux, hipStream_t s) {
+                       float* aux, int32_t* tile_start, int tile_rows, hipStream_t s) {
   if (N <= 1024) {
     int EG = 1;
     while (EG < N) EG <<= 1;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, P_part, nc, N, EG, T,
-                       C, alpha, load, n_kept, nullptr, aux);
+                       C, alpha, load, n_kept, nullptr, aux, tile_start, tile_rows);
     return;
   }
   constexpr int EG = 64;
   hipLaunchKernelGGL(route_scan_kernel, dim3((unsigned)((N + EG - 1) / EG)), dim3(1024), 0, s,
-                     hist, P_part, nc, N, EG, T, C, alpha, load, n_kept, terms, aux);
-  hipLaunchKernelGGL(aux_kernel, dim3(1), dim3(1024), 0, s, terms, N, T, alpha, aux);
+                     hist, P_part, nc, N, EG, T, C, alpha, load, n_kept, terms, aux, nullptr,
+                     tile_rows);
+  hipLaunchKernelGGL(aux_kernel, dim3(1), dim3(1024), 0, s, terms, N, T, alpha, aux, n_kept,
+                     tile_start, tile_rows);
 }
 
 void launch_finalize_positions(int64_t T, const int32_t* expert_idx, const int32_t* rank_local,

@@ -67,8 +67,19 @@ __device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ]
                                                    const float* __restrict__ gate,
                                                    uint16_t* __restrict__ out, int r0, int c0,
                                                    int rows_e, int d, int lane) {
-  constexpr int W = TJ * 32, LD = W + 8, CPR = W / 8;
+  constexpr int W = TJ * 32, LD = W + 8, CPR = W / 8, NR = TI * 32 / kWave;
+  static_assert(TI * 32 % kWave == 0, "whole waves of rows");
   const int fr = lane & 31, g = lane >> 5;
+  // lane l fetches the token and gate of rows l, l + 64, ... up front; the
+  // store loop below takes them with a lane shuffle
+  int tl[NR];
+  float gl[NR];
+#pragma unroll
+  for (int q = 0; q < NR; ++q) {
+    const int r = r0 + q * kWave + lane;
+    tl[q] = r < rows_e ? tok_e[r] : 0;
+    gl[q] = r < rows_e ? gate[tl[q]] : 0.f;
+  }
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -77,15 +88,19 @@ __device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ]
       for (int v = 0; v < 16; ++v)
         stage[(i * 32 + 8 * (v >> 2) + 4 * g + (v & 3)) * LD + j * 32 + fr] =
             f32_to_bf16_bits(acc[i][j][v]);
-#pragma unroll 4
-  for (int idx = lane; idx < TI * 32 * CPR; idx += kWave) {
+#pragma unroll
+  for (int it = 0; it < TI * 32 * CPR / kWave; ++it) {
+    const int idx = it * kWave + lane;
     const int row = idx / CPR, ch = idx - row * CPR;
+    constexpr int RPI = kWave / CPR;                 // rows per iteration
+    const int q = it * RPI / kWave;                  // register holding this row
+    const int64_t t = __shfl(tl[q], row & (kWave - 1), kWave);
+    const float gt = __shfl(gl[q], row & (kWave - 1), kWave);
     if (r0 + row < rows_e) {
-      const int64_t t = tok_e[r0 + row];
       const int64_t at = t * d + c0 + ch * 8;
       const u32x4 yv = *reinterpret_cast<const u32x4*>(stage + row * LD + ch * 8);
       const u32x4 xv = *reinterpret_cast<const u32x4*>(x + at);
-      *reinterpret_cast<u32x4*>(out + at) = combine_vec_bf16(xv, yv, gate[t]);
+      *reinterpret_cast<u32x4*>(out + at) = combine_vec_bf16(xv, yv, gt);
     }
   }
 }
@@ -220,6 +235,155 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
                                   m0 + wm * (BM / 2), n0 + wn * (BN / 2), rows_e, Nout, lane);
 }
 
+// Wide variant for experts with many rows (the Switch-Base shape, about 512
+// rows per expert): a 256 x 256 tile, 8 waves in a 2 x 4 grid, each wave
+// 128 x 64 (4 x 2 MFMA tiles).  Against 128 x 128 it halves the operand bytes
+// each CU must load per MFMA, which is what bounds these grouped matmuls.
+// Two padded LDS buffers (one barrier per K step of 64); the loads of step
+// k + 2 and the LDS stores of step k + 1 are spread over the MFMAs of step k.
+// Tiles come from the compact list io.tile_start (prefix over experts of their
+// 256-row M tiles, from the routing scan): block b takes list entry
+// (b % 8) * ceil(total / 8) + b / 8, so each XCD walks one stretch of the list
+// (order expert, N tile, M tile), and a grid sized for full capacity leaves
+// its extra blocks idle.  No XCD gets more tiles than its share.
+constexpr int GW_BM = 256, GW_BN = 256;
+constexpr size_t kWideLds = (size_t)2 * (GW_BM + GW_BN) * GB_LDK * sizeof(uint16_t);
+
+template <bool RELU, int MODE>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
+    const uint16_t* __restrict__ A, int64_t strideA, const uint16_t* __restrict__ B,
+    int64_t strideB, uint16_t* __restrict__ Cout, int64_t strideC,
+    const int32_t* __restrict__ rows, int K, int Nout, int m_tiles, int n_tiles, int tiles,
+    GemmIO io, int64_t C, int n_exp) {
+  constexpr int BM = GW_BM, BN = GW_BN, BK = GB_BK, LDK = GB_LDK;
+  constexpr int TI = 4, TJ = 2;
+  constexpr int STAGE = (BM + BN) * LDK;
+  constexpr int NL = 8;  // 16-byte loads per thread per K step: 4 of A, 4 of B
+  static_assert(8 * 128 * (64 + 8) * sizeof(uint16_t) <= kWideLds, "epilogue staging fits");
+  extern __shared__ __attribute__((aligned(16))) uint16_t wlds[];
+  (void)m_tiles;
+  (void)tiles;
+
+  const int32_t* ts = io.tile_start;
+  const int total = ts[n_exp] * n_tiles;
+  const int per_xcd = (total + 7) >> 3;
+  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || tile >= total) return;
+  // expert: the last e with ts[e] * n_tiles <= tile (it has M tiles)
+  int lo = 0, hi = n_exp - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ts[mid] * n_tiles <= tile) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int me = ts[e + 1] - ts[e];
+  const int local = tile - ts[e] * n_tiles;
+  const int nt = local / me;
+  const int mt = local - nt * me;
+  const int rows_e = rows[e];
+  const int m0 = mt * BM;
+  const int n0 = nt * BN;
+
+  const uint16_t* Ae = MODE == kRowsGather ? io.x : A + (int64_t)e * strideA;
+  const uint16_t* Be = B + (int64_t)e * strideB + (int64_t)n0 * K;
+  uint16_t* Ce = Cout + (int64_t)e * strideC;
+  const int32_t* tok_e = MODE == kRowsDense ? nullptr : io.tok + (int64_t)e * C;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lrow = tid >> 3, lcol = (tid & 7) * 8;  // 64 rows per pass of 512 threads
+
+  int64_t go[NL];  // element offsets: A rows (j < 4) from Ae, B rows (j >= 4) from Be
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int r = m0 + lrow + 64 * j;
+    r = r < rows_e ? r : rows_e - 1;  // rows past n_kept: any valid row, never stored
+    const int64_t src = MODE == kRowsGather ? (int64_t)tok_e[r] : (int64_t)r;
+    go[j] = src * K + lcol;
+    go[4 + j] = (int64_t)(lrow + 64 * j) * K + lcol;
+  }
+  const int lbase = lrow * LDK + lcol;
+  const int nk = K / BK;
+  u32x4 g[NL];
+  auto gload = [&](int j0, int j1, int t) {
+    t = t < nk ? t : nk - 1;
+    const int k = t * BK;
+#pragma unroll
+    for (int j = j0; j < j1; ++j)
+      g[j] = *reinterpret_cast<const u32x4*>((j < 4 ? Ae : Be) + go[j] + k);
+  };
+  auto gstore = [&](int j0, int j1, int buf) {
+#pragma unroll
+    for (int j = j0; j < j1; ++j)
+      *reinterpret_cast<u32x4*>(
+          &wlds[buf * STAGE + lbase + ((j & 3) * 64 + (j < 4 ? 0 : BM)) * LDK]) = g[j];
+  };
+  floatx16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  bf16x8 fa[2][TI], fb[2][TJ];
+  auto frags = [&](int f, int buf, int ks) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+      fa[f][i] = *reinterpret_cast<const bf16x8*>(
+          &wlds[buf * STAGE + (wm * 128 + i * 32 + fr) * LDK + ks * 16 + fk]);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+      fb[f][j] = *reinterpret_cast<const bf16x8*>(
+          &wlds[buf * STAGE + (BM + wn * 64 + j * 32 + fr) * LDK + ks * 16 + fk]);
+  };
+  auto mfmas = [&](int f) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
+  };
+
+  gload(0, NL, 0);
+  gstore(0, NL, 0);
+  gload(0, NL, 1);
+  __syncthreads();
+  frags(0, 0, 0);
+  for (int t = 0; t < nk; ++t) {
+    const int cur = t & 1, nxt = cur ^ 1;
+    // buffer nxt was last read in step t - 1, before the barrier that ended it
+    frags(1, cur, 1);
+    gstore(0, 3, nxt);
+    gload(0, 3, t + 2);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    frags(0, cur, 2);
+    gstore(3, 6, nxt);
+    gload(3, 6, t + 2);
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
+    frags(1, cur, 3);
+    gstore(6, 8, nxt);
+    gload(6, 8, t + 2);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    __syncthreads();
+    frags(0, nxt, 0);
+  }
+
+  __syncthreads();  // every wave is done with the LDS operand buffers
+  uint16_t* stage = wlds + wave * 128 * (64 + 8);
+  if (MODE == kRowsCombine)
+    store_tile_combine<TI, TJ>(acc, stage, tok_e, io.x, io.gate, io.out, m0 + wm * 128,
+                               n0 + wn * 64, rows_e, Nout, lane);
+  else
+    store_tile_bf16<TI, TJ, RELU>(acc, stage, Ce, m0 + wm * 128, n0 + wn * 64, rows_e, Nout,
+                                  lane);
+}
+
 // fp32 path (parity-sized fp32 layers): 32 x 32 tile, K in steps of 32, each
 // of 256 threads owns 4 rows of one column.  Any sizes (bounds-checked).
 template <bool RELU>
@@ -273,18 +437,55 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 // ------------------------------------------------------------------ launchers
 
+namespace {
+
+// The wide tile pays off when experts hold at least two of its M tiles and N
+// splits into 256-column tiles.
+bool use_wide(int64_t C, int Nout, const GemmIO& io) {
+  static_assert(GW_BM == kWideTileRows, "tile list and kernel agree");
+  return io.tile_start && C >= 2 * GW_BM && Nout % GW_BN == 0;
+}
+
+template <bool RELU, int MODE>
+void launch_wide(const uint16_t* a, int64_t strideA, const uint16_t* b, int64_t strideB,
+                 uint16_t* c, int64_t strideC, const int32_t* rows, int n_experts, int64_t C,
+                 int K, int Nout, const GemmIO& io, hipStream_t s) {
+  // kernels above 64 KiB of LDS must say so once per device
+  static uint64_t set_on = 0;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev < 64 && !(set_on >> dev & 1)) {
+    (void)hipFuncSetAttribute((const void*)gemm_bf16_wide_kernel<RELU, MODE>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWideLds);
+    set_on |= 1ull << dev;
+  }
+  const int mt = (int)((C + GW_BM - 1) / GW_BM), nt = Nout / GW_BN;
+  const int tiles = mt * nt * n_experts;
+  const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
+  hipLaunchKernelGGL((gemm_bf16_wide_kernel<RELU, MODE>), dim3(grid), dim3(512), kWideLds, s, a,
+                     strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C,
+                     n_experts);
+}
+
+}  // namespace
+
 void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t strideA,
                              const void* B, int64_t strideB, void* Cout, int64_t strideC,
                              const int32_t* rows, int n_experts, int64_t C, int K, int Nout,
                              const GemmIO& io, hipStream_t s) {
   if (C == 0 || n_experts == 0) return;
+  const uint16_t* a = (const uint16_t*)A;
+  const uint16_t* b = (const uint16_t*)B;
+  uint16_t* c = (uint16_t*)Cout;
+  if (mode == kRowsGather && relu && use_wide(C, Nout, io)) {
+    launch_wide<true, kRowsGather>(a, strideA, b, strideB, c, strideC, rows, n_experts, C, K,
+                                   Nout, io, s);
+    return;
+  }
   constexpr int BM = 128, BN = 128;
   const int mt = (int)((C + BM - 1) / BM), nt = Nout / BN;
   const int tiles = mt * nt * n_experts;
   const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
-  const uint16_t* a = (const uint16_t*)A;
-  const uint16_t* b = (const uint16_t*)B;
-  uint16_t* c = (uint16_t*)Cout;
   if (mode == kRowsGather && relu)
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true, kRowsGather>), dim3(grid), dim3(256), 0, s,
                        a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);

@@ -49,9 +49,11 @@ void launch_route_rows(const float* h, int64_t T, int N, int32_t* expert_idx, fl
                        float* P_part, int32_t* hist, int32_t* rank_local, hipStream_t s);
 
 // assign.hip
+// tile_start (optional, N + 1 entries): exclusive prefix over experts of
+// ceil(n_kept / tile_rows), with the total last.
 void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T,
                        int64_t C, float alpha, int32_t* load, int32_t* n_kept, double* terms,
-                       float* aux, hipStream_t s);
+                       float* aux, int32_t* tile_start, int tile_rows, hipStream_t s);
 void launch_finalize_positions(int64_t T, const int32_t* expert_idx, const int32_t* rank_local,
                                const int32_t* offsets, int N, int64_t chunk, int64_t C,
                                int32_t* position, uint8_t* drop_mask, hipStream_t s);
@@ -76,6 +78,7 @@ void launch_copy_expert_rows(const void* Ybuf, const int32_t* n_kept, int N, int
 // combined into out[tok[e * C + m]] = x + gate * y instead of being stored.
 enum GemmRows { kRowsDense = 0, kRowsGather = 1, kRowsCombine = 2 };
 struct GemmIO {
+  const int32_t* tile_start = nullptr;  // compact tile list of the wide kernel
   const int32_t* tok = nullptr;
   const uint16_t* x = nullptr;
   const float* gate = nullptr;
@@ -89,5 +92,6 @@ void launch_expert_gemm(bool bf16, bool relu, const void* A, int64_t strideA, co
                         int64_t strideB, void* Cout, int64_t strideC, const int32_t* rows,
                         int n_experts, int64_t C, int K, int Nout, hipStream_t s);
 bool expert_gemm_shape_ok(bool bf16, int d, int F);
+constexpr int kWideTileRows = 256;   // M tile of the wide bf16 kernel
 
 }  // namespace swl

@@ -45,7 +45,7 @@ int64_t buffer_rows(const switch_config& c, int64_t T) {
 }
 
 struct Layout {
-  size_t logits, ppart, hist, rank, load, nkept, terms, tok, xbuf, hbuf, ybuf, total;
+  size_t logits, ppart, hist, rank, load, nkept, terms, tiles, tok, xbuf, hbuf, ybuf, total;
 };
 
 // Chunks of the routing statistics: the fused router uses small chunks, the
@@ -72,6 +72,7 @@ Layout layout_of(const switch_layer* L, int64_t T) {
   lo.load = take(sizeof(int32_t) * (size_t)N);
   lo.nkept = take(sizeof(int32_t) * (size_t)N);
   lo.terms = take(sizeof(double) * (size_t)N);
+  lo.tiles = take(sizeof(int32_t) * (size_t)(N + 1));
   lo.tok = take(sizeof(int32_t) * (size_t)N * (size_t)Cb);
   // the bf16 path reads token rows in place; only the fp32 path gathers them
   const bool gather_copy = c.act_dtype != SWITCH_BF16;
@@ -114,6 +115,7 @@ switch_status check_route_args(const switch_layer* L, int64_t T, const int32_t* 
 struct Routed {
   int32_t* load;
   int32_t* nkept;
+  int32_t* tile_start;
   int32_t* offsets;
   int32_t* rank;
   int64_t chunk;
@@ -135,6 +137,7 @@ Routed enqueue_routing(switch_layer* L, const void* x, const float* given_logits
   r.Cb = buffer_rows(c, T);
   r.load = load ? load : (int32_t*)(ws + lo.load);
   r.nkept = (int32_t*)(ws + lo.nkept);
+  r.tile_start = (int32_t*)(ws + lo.tiles);
   r.offsets = (int32_t*)(ws + lo.hist);
   r.rank = (int32_t*)(ws + lo.rank);
   float* ppart = (float*)(ws + lo.ppart);
@@ -160,7 +163,7 @@ Routed enqueue_routing(switch_layer* L, const void* x, const float* given_logits
   const int64_t nc = (T + r.chunk - 1) / r.chunk;
   swl::prof_mark(P, s, "route_scan");
   swl::launch_route_scan(r.offsets, ppart, nc, N, T, r.Cb, c.alpha, r.load, r.nkept,
-                         (double*)(ws + lo.terms), aux_loss, s);
+                         (double*)(ws + lo.terms), aux_loss, r.tile_start, swl::kWideTileRows, s);
   return r;
 }
 
@@ -199,6 +202,7 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
     // the caller asks for it, and the combine pass follows)
     int32_t* tok = (int32_t*)(w + lo.tok);
     swl::GemmIO io;
+    io.tile_start = r.tile_start;
     io.tok = tok;
     io.x = (const uint16_t*)x;
     io.gate = gate;
