@@ -85,6 +85,12 @@ def _check_large(B, spec, tag):
     host, layer = _device_layer(B, spec)
     res = layer.forward_host(host["x"], debug=True)
     print(f"[case] {tag}: forward done, kept={int((res['drop_mask'] == 0).sum())}", flush=True)
+    # the default entry point (combine fused into the second matmul) gives the same bits
+    plain = layer.forward_host(host["x"])
+    for k in ("out", "expert_idx", "gate", "position", "drop_mask", "logits", "load"):
+        assert np.array_equal(plain[k], res[k]), f"default path differs in {k}"
+    assert plain["aux_loss"] == res["aux_loss"]
+    del plain
     parity.check_routing_stage(res, spec, tag)
     rng = np.random.default_rng(spec.seed)
     xf = S.to_f32(host["x"], spec.act)

@@ -20,11 +20,25 @@ def B():
     return binding
 
 
+ROUTE_KEYS = ("expert_idx", "gate", "position", "drop_mask", "logits", "load")
+
+
+def same_as_default_path(layer, x, res):
+    """switch_forward (combine fused into the second matmul) must give the same
+    bits as switch_forward_debug (expert output stored, separate combine pass)."""
+    plain = layer.forward_host(x)
+    for k in ("out",) + ROUTE_KEYS:
+        assert np.array_equal(plain[k], res[k]), f"default path differs in {k}"
+    assert plain["aux_loss"] == res["aux_loss"]
+
+
 def _run(B, spec, host=None, debug=True):
     host = host or S.host_inputs(spec)
     layer = B.SwitchLayer.from_host(spec, host)
     print(f"[case] {spec.name} T={spec.T} d={spec.d} F={spec.F} N={spec.N} c={spec.c}", flush=True)
     res = layer.forward_host(host["x"], debug=debug)
+    if debug:
+        same_as_default_path(layer, host["x"], res)
     return host, layer, res
 
 
@@ -51,6 +65,8 @@ def test_tiny_fp32_config(B):
     (130, 16, 128, 256, 0.5, 23),      # heavy overflow
     (64, 1, 128, 128, 1.0, 24),        # one expert: gate 1, aux alpha
     (9, 32, 128, 128, 2.0, 25),        # T < N
+    (3000, 4, 128, 512, 1.0, 26),      # capacity >= 512: 256-row tiles, three M tiles
+    (2100, 4, 256, 768, 1.0, 27),      # 256-row tiles with a ragged last tile and drops
 ])
 def test_bf16_ragged_shapes(B, T, N, d, F, c, seed):
     spec = S.Spec(f"bf16-{T}-{N}", T=T, d=d, F=F, N=N, c=c, seed=seed)
@@ -112,7 +128,7 @@ def test_deterministic_bitwise(B):
     layer = B.SwitchLayer.from_host(spec, host)
     a = layer.forward_host(host["x"])
     b = layer.forward_host(host["x"])
-    for k in ("out", "expert_idx", "gate", "position", "drop_mask", "logits", "load"):
+    for k in ("out",) + ROUTE_KEYS:
         assert np.array_equal(a[k], b[k]), k
     assert a["aux_loss"] == b["aux_loss"]
 
