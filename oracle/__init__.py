@@ -52,6 +52,15 @@ def lib():
         L.oracle_combine.argtypes = [_f32p, _i32p, _f64p, _u8p, _f32p, _f32p, _i64, _i64, _i64,
                                      _f64p, _f64p, ctypes.c_int]
         L.oracle_combine.restype = None
+        L.oracle_capacity_topk.argtypes = [_i64, _i64, _i64, ctypes.c_double, _i64]
+        L.oracle_capacity_topk.restype = _i64
+        L.oracle_route_topk.argtypes = [_f64p, _i64, _i64, _i64, ctypes.c_double, _i64,
+                                        ctypes.c_double, _i32p, _f64p, _i32p, _u8p, _i32p, _f64p,
+                                        _f64p, ctypes.c_int]
+        L.oracle_route_topk.restype = _i64
+        L.oracle_combine_topk.argtypes = [_f32p, _i32p, _f64p, _u8p, _f32p, _f32p, _i64, _i64,
+                                          _i64, _i64, _f64p, _f64p, ctypes.c_int]
+        L.oracle_combine_topk.restype = None
         _lib = L
     return _lib
 
@@ -113,6 +122,44 @@ def combine(x, expert_idx, gate, drop, W_in, W_out, nthreads: int = 0):
     E = np.empty((T, d), np.float64)
     lib().oracle_combine(x, _c(expert_idx, np.int32), _c(gate, np.float64), _c(drop, np.uint8),
                          W_in, W_out, T, d, F, out, E, nthreads or threads())
+    return out, E
+
+
+def capacity_topk(T: int, N: int, k: int, c: float, capacity_override: int = 0) -> int:
+    return int(lib().oracle_capacity_topk(T, N, k, c, capacity_override))
+
+
+def route_topk(h, k: int, c: float, capacity_override: int = 0, alpha: float = 0.01,
+               nthreads: int = 0) -> dict:
+    """Top-k routing stage on given logits [T, N]; per-choice outputs are [T, k]."""
+    h = _c(h, np.float64)
+    T, N = h.shape
+    assert 1 <= k <= N
+    r = dict(expert_idx=np.empty((T, k), np.int32), gate=np.empty((T, k), np.float64),
+             position=np.empty((T, k), np.int32), drop=np.empty((T, k), np.uint8),
+             load=np.empty(N, np.int32), P=np.empty(N, np.float64))
+    aux = np.zeros(1, np.float64)
+    C = lib().oracle_route_topk(h, T, N, k, c, capacity_override, alpha, r["expert_idx"],
+                                r["gate"], r["position"], r["drop"], r["load"], r["P"], aux,
+                                nthreads or threads())
+    r["aux"] = float(aux[0])
+    r["C"] = int(C)
+    return r
+
+
+def combine_topk(x, expert_idx, gate, drop, W_in, W_out, nthreads: int = 0):
+    """(out [T, d], per-choice expert outputs [T, k, d])."""
+    x = _c(x, np.float32)
+    W_in = _c(W_in, np.float32)
+    W_out = _c(W_out, np.float32)
+    T, d = x.shape
+    F = W_in.shape[1]
+    expert_idx = _c(expert_idx, np.int32)
+    k = expert_idx.shape[1]
+    out = np.empty((T, d), np.float64)
+    E = np.empty((T, k, d), np.float64)
+    lib().oracle_combine_topk(x, expert_idx, _c(gate, np.float64), _c(drop, np.uint8), W_in,
+                              W_out, T, k, d, F, out, E, nthreads or threads())
     return out, E
 
 

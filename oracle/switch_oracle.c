@@ -36,6 +36,10 @@
  *   - the expert FFN is relu(x W_in^T) W_out^T without biases;
  *   - out = x + gate * E(x) inside the layer; a dropped token leaves unchanged.
  *
+ * Top-k routing (the MoE routing the Switch layer simplifies; [LP 3.1] and
+ * [MS] "Mixture of Experts Routing") follows further down, with its own
+ * readings.
+ *
  * Parity pins: every function here is pinned by the -m "not gpu" tests
  * (worked examples of the pages, closed forms, brute force, a library matmul
  * for the dense special case).
@@ -243,4 +247,145 @@ int64_t oracle_forward(const float* x, const float* W_r, const float* b_r, const
                            load, P, aux, nthreads);
   oracle_combine(x, expert_idx, gate, drop, W_in, W_out, T, d, F, out, E_out, nthreads);
   return C;
+}
+
+/* ------------------------------------------------------------------------
+ * Top-k routing, the MoE routing that the Switch layer reduces to k = 1.
+ * [LP 3.1]: the router scores all N experts, p = softmax(h), and the output
+ * is the sum over the selected set T of p_i(x) E_i(x), where T holds the K
+ * experts with the highest scores (classic MoE: usually K = 2); its hospital
+ * illustration weights the two chosen departments by 0.6 and 0.3.  [MS]
+ * "Mixture of Experts Routing" (MoELayer code): torch.topk over the softmax
+ * probabilities, each chosen expert's output weighted by its probability.
+ * [LP 3.2], point (2): with one expert per token the capacity can at least be
+ * halved, i.e. k choices per token need k times the top-1 capacity.
+ *
+ * Readings (the pages do not give these steps):
+ *   - the k experts are the k largest logits, ties to the lower index, chosen
+ *     one after another (the best, then the best of the rest, ...);
+ *   - gates are the full-softmax probabilities of the chosen experts, not
+ *     renormalised over the chosen set;
+ *   - capacity C = ceil(k c T / N), or the override;
+ *   - assignments take positions in the order (t, j): token order, and within
+ *     a token its choices in rank order; each assignment is dropped on its own
+ *     when its position reaches C;
+ *   - out = x + sum over kept choices of gate_j E_{e_j}(x); a token with all
+ *     choices dropped leaves unchanged;
+ *   - the loss keeps its form with f_e = load_e / (k T), load_e counting all
+ *     assignments before the capacity cut (so f sums to 1 and a uniform load
+ *     still gives alpha).
+ * With k = 1 every one of these is the top-1 definition above.
+ * ------------------------------------------------------------------------ */
+
+int64_t oracle_capacity_topk(int64_t T, int64_t N, int64_t k, double c,
+                             int64_t capacity_override) {
+  if (capacity_override > 0) return capacity_override;
+  if (N <= 0) return 0;
+  double v = ceil(((double)k * c * (double)T) / (double)N);
+  return v < 0.0 ? 0 : (int64_t)v;
+}
+
+/* The k best experts of one token by logit (ties: lower index first), their
+ * softmax probabilities, and the row's max and sum for P. */
+static void route_token_topk(const double* h, int64_t N, int64_t k, int32_t* idx, double* gate,
+                             double* m_out, double* S_out) {
+  double m = h[0];
+  for (int64_t i = 1; i < N; ++i)
+    if (h[i] > m) m = h[i];
+  double S = 0.0;
+  for (int64_t i = 0; i < N; ++i) S += exp(h[i] - m);
+  for (int64_t j = 0; j < k; ++j) {
+    int32_t best = -1;
+    for (int64_t i = 0; i < N; ++i) {
+      int taken = 0;
+      for (int64_t q = 0; q < j; ++q) taken |= (idx[q] == (int32_t)i);
+      if (taken) continue;
+      if (best < 0 || h[i] > h[best]) best = (int32_t)i;
+    }
+    idx[j] = best;
+    gate[j] = exp(h[best] - m) / S;
+  }
+  *m_out = m;
+  *S_out = S;
+}
+
+/*
+ * Top-k routing stage on given logits h [T, N].  Outputs are [T, k] row-major
+ * (expert_idx, gate, position, drop) and load [N]; P_out [N] may be NULL.
+ * Returns C.  Requires 1 <= k <= N.
+ */
+int64_t oracle_route_topk(const double* h, int64_t T, int64_t N, int64_t k, double c,
+                          int64_t capacity_override, double alpha, int32_t* expert_idx,
+                          double* gate, int32_t* position, uint8_t* drop, int32_t* load,
+                          double* P_out, double* aux, int nthreads) {
+  int64_t C = oracle_capacity_topk(T, N, k, c, capacity_override);
+  double* m = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+  double* S = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+  double* P = (double*)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+
+#pragma omp parallel for schedule(static) num_threads(NT(nthreads))
+  for (int64_t t = 0; t < T; ++t)
+    route_token_topk(h + t * N, N, k, expert_idx + t * k, gate + t * k, &m[t], &S[t]);
+
+  /* one sequential pass over the assignments in (token, choice) order */
+  for (int64_t e = 0; e < N; ++e) load[e] = 0;
+  for (int64_t a = 0; a < T * k; ++a) {
+    int32_t e = expert_idx[a];
+    position[a] = load[e];
+    load[e] += 1;
+    drop[a] = (uint8_t)((int64_t)position[a] >= C);
+  }
+
+#pragma omp parallel for schedule(static) num_threads(NT(nthreads))
+  for (int64_t e = 0; e < N; ++e) {
+    double acc = 0.0;
+    for (int64_t t = 0; t < T; ++t) acc += exp(h[t * N + e] - m[t]) / S[t];
+    P[e] = T > 0 ? acc / (double)T : 0.0;
+  }
+
+  double sum = 0.0;
+  for (int64_t e = 0; e < N; ++e) {
+    double f = T > 0 ? (double)load[e] / ((double)k * (double)T) : 0.0;
+    sum += f * P[e];
+  }
+  *aux = alpha * (double)N * sum;
+  if (P_out) memcpy(P_out, P, sizeof(double) * (size_t)N);
+  free(m);
+  free(S);
+  free(P);
+  return C;
+}
+
+/*
+ * Top-k combine: out[t] = x[t] + sum over kept j of gate[t,j] E_{e[t,j]}(x[t])
+ * ([LP 3.1] weighted sum of the selected experts, plus the residual of part
+ * 六).  E_out [T, k, d] (may be NULL) receives each choice's expert output, 0
+ * for a dropped choice.
+ */
+void oracle_combine_topk(const float* x, const int32_t* expert_idx, const double* gate,
+                         const uint8_t* drop, const float* W_in, const float* W_out, int64_t T,
+                         int64_t k, int64_t d, int64_t F, double* out, double* E_out,
+                         int nthreads) {
+#pragma omp parallel for schedule(dynamic, 4) num_threads(NT(nthreads))
+  for (int64_t t = 0; t < T; ++t) {
+    double* u = (double*)malloc(sizeof(double) * (size_t)F);
+    double* E = (double*)malloc(sizeof(double) * (size_t)d);
+    const float* xt = x + t * d;
+    double* o = out + t * d;
+    for (int64_t q = 0; q < d; ++q) o[q] = (double)xt[q];
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t a = t * k + j;
+      double* Ea = E_out ? E_out + a * d : NULL;
+      if (drop[a]) {
+        if (Ea) for (int64_t q = 0; q < d; ++q) Ea[q] = 0.0;
+        continue;
+      }
+      const int64_t e = expert_idx[a];
+      expert_ffn(xt, W_in + e * F * d, W_out + e * d * F, d, F, u, E);
+      for (int64_t q = 0; q < d; ++q) o[q] += gate[a] * E[q];
+      if (Ea) memcpy(Ea, E, sizeof(double) * (size_t)d);
+    }
+    free(u);
+    free(E);
+  }
 }

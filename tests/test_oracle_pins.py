@@ -302,3 +302,128 @@ def test_relabelling_experts_permutes_routing_only():
     np.testing.assert_allclose(a["gate"], b["gate"], rtol=1e-14)
     np.testing.assert_allclose(a["out"], b["out"], rtol=1e-13, atol=1e-13)
     assert a["aux"] == pytest.approx(b["aux"], rel=1e-13)
+
+
+# ---------------------------------------------------------------- top-k routing (next row)
+
+def test_topk_hospital_example():
+    """llm-papers-study 3.1: top-2 picks the two best experts, weighted by their
+    softmax probabilities (0.6 and 0.3); top-1 picks the best alone."""
+    g = keyed("lp_hospital_top2.txt")
+    p = np.array(g["p"], dtype=np.float64)
+    h = np.log(p)[None, :]
+    r2 = oracle.route_topk(h, 2, c=10.0)
+    assert list(r2["expert_idx"][0]) == [int(v) for v in g["top2_experts"]]
+    assert np.allclose(r2["gate"][0], g["top2_weights"], rtol=0, atol=1e-12)
+    r1 = oracle.route_topk(h, 1, c=10.0)
+    assert r1["expert_idx"][0, 0] == int(g["top1_expert"])
+    # output = x + 0.6 E_0(x) + 0.3 E_1(x), with the experts evaluated by a library matmul
+    rng = np.random.default_rng(7)
+    d, F, N = 4, 6, 3
+    x = rng.standard_normal((1, d)).astype(np.float32)
+    W_in = rng.standard_normal((N, F, d)).astype(np.float32)
+    W_out = rng.standard_normal((N, d, F)).astype(np.float32)
+    out, E = oracle.combine_topk(x, r2["expert_idx"], r2["gate"], r2["drop"], W_in, W_out)
+    ex = [np.maximum(W_in[e].astype(np.float64) @ x[0], 0) @ W_out[e].T.astype(np.float64)
+          for e in range(N)]
+    want = x[0] + 0.6 * ex[0] + 0.3 * ex[1]
+    assert np.allclose(out[0], want, rtol=1e-12, atol=1e-12)
+    assert np.allclose(E[0, 0], ex[0]) and np.allclose(E[0, 1], ex[1])
+
+
+def test_topk_capacity_doubles_for_two_choices():
+    """llm-papers-study 3.2 point (2): one expert per token at least halves the
+    capacity; read as: k choices take k times the top-1 capacity.  With section
+    3.4's 512 tokens / 8 experts / factor 1.5 (capacity 96), top-2 gives 192."""
+    g = keyed("lp_capacity_512_8.txt")
+    assert oracle.capacity_topk(g["T"], g["N"], 1, g["c"]) == g["capacity"]
+    assert oracle.capacity_topk(g["T"], g["N"], 2, g["c"]) == 2 * g["capacity"]
+
+
+def test_topk_two_of_two_experts():
+    """Closed form, N = 2 and k = 2: every token uses both experts, the gates sum
+    to 1 and each expert's assignments arrive one per token, so the position of
+    token t is t in both choices; capacity ceil(2 c T / 2) cuts the tail."""
+    rng = np.random.default_rng(11)
+    T = 37
+    h = rng.standard_normal((T, 2))
+    r = oracle.route_topk(h, 2, c=0.75)
+    assert r["C"] == int(np.ceil(0.75 * T))
+    assert np.all(np.sort(r["expert_idx"], axis=1) == [0, 1])
+    assert np.allclose(r["gate"].sum(axis=1), 1.0, atol=1e-15)
+    assert np.all(r["gate"][:, 0] >= r["gate"][:, 1])
+    assert np.array_equal(r["position"], np.repeat(np.arange(T)[:, None], 2, axis=1))
+    assert np.array_equal(r["drop"], (r["position"] >= r["C"]).astype(np.uint8))
+    assert np.array_equal(r["load"], [T, T])
+
+
+def test_topk_all_experts_identical_is_dense_mlp():
+    """k = N with identical experts and no drops: the gates are all of softmax and
+    sum to 1, so the layer is x + FFN(x), a dense two-matmul MLP (library matmul)."""
+    rng = np.random.default_rng(12)
+    T, d, F, N = 20, 8, 12, 3
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    w1 = rng.standard_normal((F, d)).astype(np.float32)
+    w2 = rng.standard_normal((d, F)).astype(np.float32)
+    W_in = np.repeat(w1[None], N, axis=0)
+    W_out = np.repeat(w2[None], N, axis=0)
+    h = rng.standard_normal((T, N))
+    r = oracle.route_topk(h, N, c=2.0)
+    assert not r["drop"].any()
+    out, _ = oracle.combine_topk(x, r["expert_idx"], r["gate"], r["drop"], W_in, W_out)
+    dense = x.astype(np.float64) + np.maximum(x.astype(np.float64) @ w1.T.astype(np.float64), 0) \
+        @ w2.T.astype(np.float64)
+    assert np.allclose(out, dense, rtol=1e-12, atol=1e-11)
+
+
+def test_topk_uniform_load_gives_alpha():
+    """The loss keeps aux = alpha when f is uniform: token t prefers expert t mod N
+    then t + 1 mod N, so every expert receives the same number of assignments."""
+    rng = np.random.default_rng(13)
+    N, T = 4, 40
+    h = rng.uniform(-0.1, 0.1, size=(T, N))
+    h[np.arange(T), np.arange(T) % N] += 10.0
+    h[np.arange(T), (np.arange(T) + 1) % N] += 5.0
+    r = oracle.route_topk(h, 2, c=1.0)
+    assert np.all(r["load"] == 2 * T // N)
+    assert r["aux"] == pytest.approx(ALPHA, rel=1e-12)
+
+
+def test_topk_ties_go_low_and_k1_is_top1():
+    """Equal logits: the choices are experts 0, 1, ... in order; with k = 1 the
+    top-k routing is the top-1 routing."""
+    r = oracle.route_topk(np.zeros((3, 5)), 3, c=5.0)
+    assert np.array_equal(r["expert_idx"], [[0, 1, 2]] * 3)
+    assert np.allclose(r["gate"], 0.2)
+    rng = np.random.default_rng(14)
+    h = rng.standard_normal((300, 7))
+    a = oracle.route(h, 1.1)
+    b = oracle.route_topk(h, 1, 1.1)
+    for k in ("expert_idx", "position", "drop"):
+        assert np.array_equal(a[k], b[k][:, 0]), k
+    assert np.array_equal(a["gate"], b["gate"][:, 0])
+    assert np.array_equal(a["load"], b["load"])
+    assert a["aux"] == b["aux"]
+
+
+@pytest.mark.parametrize("T,N,c", [(4, 3, 0.5), (5, 3, 0.8), (4, 4, 0.5)])
+def test_topk_brute_force_positions(T, N, c):
+    """Every ordering of N experts per token (tiny T): positions by the quadratic
+    rule over the (token, choice) order, drops by the capacity, loads by count."""
+    rng = np.random.default_rng(15)
+    perms = list(itertools.permutations(range(N)))
+    for combo in itertools.product(range(len(perms)), repeat=T):
+        if rng.random() > 0.2:
+            continue
+        h = np.zeros((T, N))
+        for t, pi in enumerate(combo):
+            h[t, list(perms[pi])] = [10.0 - q for q in range(N)]  # rank order = the permutation
+        r = oracle.route_topk(h, 2, c)
+        seq = [perms[pi][j] for pi in combo for j in range(2)]
+        assert np.array_equal(r["expert_idx"].ravel(), seq)
+        C = int(np.ceil(2 * c * T / N))
+        for a, e in enumerate(seq):
+            pos = sum(1 for b in range(a) if seq[b] == e)
+            assert r["position"].ravel()[a] == pos
+            assert r["drop"].ravel()[a] == (pos >= C)
+        assert np.array_equal(r["load"], np.bincount(seq, minlength=N))
