@@ -12,6 +12,16 @@
  *               = x[t] (bit for bit)                                  if  drop[t]
  *   aux_loss    = alpha N sum_i f_i P_i,  f_i = load_i / T,  P_i = mean_t p_i(t)
  *
+ * With top_k = 2 (classic top-2 MoE routing, the routing the Switch layer
+ * simplifies: llm-papers-study section 3.1, where the output is the sum over
+ * the K best experts of p_i(x) E_i(x), and the MoELayer code of the Incredible.AI
+ * blog, section "Mixture of Experts Routing") every per-token output is [T, 2],
+ * choice 0 the best expert and choice 1 the best of the rest (lowest index on
+ * ties), gate[t, j] = p_{e_tj}(t) (not renormalised); assignments (t, j) take
+ * positions in (token, choice) order against C = ceil(2 c T / N), each dropped
+ * on its own; out[t] = x[t] + sum over kept j of gate[t, j] E_{e_tj}(x[t]); and
+ * f_i = load_i / (2 T) with load_i counting assignments.
+ *
  * Sources (the Switch Transformers paper as described on these pages):
  *   router logits and softmax -- "精读 06 | Switch Transformers" (llm-papers-study
  *     close reading), section 3.1; top-1 choice and the gate-scaled output --
@@ -72,6 +82,10 @@ typedef struct {
   float alpha;              /* load-balancing loss coefficient (the paper uses 0.01) */
   int32_t act_dtype;        /* switch_dtype of x, out and the expert activations */
   int32_t expert_dtype;     /* switch_dtype of W_in / W_out; must equal act_dtype */
+  int32_t top_k;            /* experts per token: 1 (the Switch layer; 0 also means 1)
+                               or 2 (top-2 routing); k <= n_experts.  Per-token
+                               outputs (expert_idx, gate, position, drop_mask) are
+                               [T, k] row-major, and C = ceil(k c T / N) */
 } switch_config;
 
 typedef struct switch_layer switch_layer;

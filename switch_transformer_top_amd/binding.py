@@ -29,7 +29,8 @@ class switch_config(ctypes.Structure):
     _fields_ = [("t_max", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("capacity_factor", ctypes.c_double),
                 ("capacity_override", ctypes.c_int32), ("alpha", ctypes.c_float),
-                ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32)]
+                ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
+                ("top_k", ctypes.c_int32)]
 
 
 class SwitchError(RuntimeError):
@@ -183,7 +184,8 @@ class SwitchLayer:
 
     # -- construction from the synthetic generator's host arrays
     @classmethod
-    def from_host(cls, spec, host: dict, device=None, t_max: Optional[int] = None):
+    def from_host(cls, spec, host: dict, device=None, t_max: Optional[int] = None,
+                  top_k: int = 1):
         import torch
         dev = device or torch.device("cuda:0")
         act = SWITCH_BF16 if spec.act == "bf16" else SWITCH_F32
@@ -191,7 +193,7 @@ class SwitchLayer:
         cfg = switch_config(t_max=t_max if t_max is not None else spec.T, d_model=spec.d,
                             d_ff=spec.F, n_experts=spec.N, capacity_factor=spec.c,
                             capacity_override=spec.capacity_override, alpha=spec.alpha,
-                            act_dtype=act, expert_dtype=exp)
+                            act_dtype=act, expert_dtype=exp, top_k=top_k)
         W_r = torch.from_numpy(np.ascontiguousarray(host["W_r"])).to(dev)
         b_r = None if host.get("b_r") is None else torch.from_numpy(host["b_r"]).to(dev)
         W_in = to_device(host["W_in"], dev)
@@ -207,12 +209,14 @@ class SwitchLayer:
         if self._ws is None or self._ws.numel() < nbytes:
             self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         xdt = torch.int16 if es == 2 else torch.float32
+        k = max(1, int(self.cfg.top_k))
+        per = (T,) if k == 1 else (T, k)   # per-token outputs: [T] for top-1, [T, k] otherwise
         return dict(
             out=torch.empty((T, d), dtype=xdt, device=dev),
-            expert_idx=torch.empty(T, dtype=torch.int32, device=dev),
-            gate=torch.empty(T, dtype=torch.float32, device=dev),
-            position=torch.empty(T, dtype=torch.int32, device=dev),
-            drop_mask=torch.empty(T, dtype=torch.uint8, device=dev),
+            expert_idx=torch.empty(per, dtype=torch.int32, device=dev),
+            gate=torch.empty(per, dtype=torch.float32, device=dev),
+            position=torch.empty(per, dtype=torch.int32, device=dev),
+            drop_mask=torch.empty(per, dtype=torch.uint8, device=dev),
             aux_loss=torch.empty(1, dtype=torch.float32, device=dev),
             logits=torch.empty((T, N), dtype=torch.float32, device=dev),
             load=torch.empty(N, dtype=torch.int32, device=dev),

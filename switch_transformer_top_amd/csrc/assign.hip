@@ -12,7 +12,8 @@
 //
 // Load-balancing loss (llm-papers-study close reading, section 3.3):
 // aux = alpha N sum_i f_i P_i, f_i = load_i / T, P_i = (1/T) sum_t p_i(t), with
-// load_i counted before the capacity cut.
+// load_i counted before the capacity cut.  With k choices per token load_i
+// counts assignments and f_i = load_i / (k T).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -58,7 +59,7 @@ __device__ void tile_prefix_block(const int32_t* __restrict__ n_kept, int N, int
 __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ hist,
                                                           const float* __restrict__ P_part,
                                                           int64_t nc, int N, int EG, int64_t T,
-                                                          int64_t C, float alpha,
+                                                          int k, int64_t C, float alpha,
                                                           int32_t* __restrict__ load,
                                                           int32_t* __restrict__ n_kept,
                                                           double* __restrict__ terms,
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
   }
   if (tid == 0) {
     double v = 0.0;
-    if (T > 0) v = (double)alpha * (double)N * (s_p[0] / ((double)T * (double)T));
+    if (T > 0) v = (double)alpha * (double)N * (s_p[0] / ((double)k * (double)T * (double)T));
     *aux = (float)v;
   }
   // n_kept of every expert was written by this block above
@@ -137,7 +138,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
 
 // aux = alpha N sum_e terms[e] / T^2, summed in a fixed tree (fp64).
 __global__ __launch_bounds__(1024) void aux_kernel(const double* __restrict__ terms, int N,
-                                                   int64_t T, float alpha, float* __restrict__ aux,
+                                                   int64_t T, int k, float alpha,
+                                                   float* __restrict__ aux,
                                                    const int32_t* __restrict__ n_kept,
                                                    int32_t* __restrict__ tile_start,
                                                    int tile_rows) {
@@ -153,51 +155,54 @@ __global__ __launch_bounds__(1024) void aux_kernel(const double* __restrict__ te
   }
   if (threadIdx.x == 0) {
     double v = 0.0;
-    if (T > 0) v = (double)alpha * (double)N * (red[0] / ((double)T * (double)T));
+    if (T > 0) v = (double)alpha * (double)N * (red[0] / ((double)k * (double)T * (double)T));
     *aux = (float)v;
   }
   if (tile_start) tile_prefix_block(n_kept, N, tile_rows, tile_start, s_run);
 }
 
 // position = chunk offset + in-chunk rank; drop when it reaches C (route only:
-// no data moves).  One thread per token.
+// no data moves).  One thread per assignment a = t * k + j.
 __global__ __launch_bounds__(256) void finalize_positions_kernel(
-    int64_t T, const int32_t* __restrict__ expert_idx, const int32_t* __restrict__ rank_local,
-    const int32_t* __restrict__ offsets, int N, int64_t chunk, int64_t C,
-    int32_t* __restrict__ position, uint8_t* __restrict__ drop_mask) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  const int32_t pos = offsets[(t / chunk) * N + expert_idx[t]] + rank_local[t];
-  position[t] = pos;
-  drop_mask[t] = (int64_t)pos >= C ? 1 : 0;
+    int64_t T, int k, const int32_t* __restrict__ expert_idx,
+    const int32_t* __restrict__ rank_local, const int32_t* __restrict__ offsets, int N,
+    int64_t chunk, int64_t C, int32_t* __restrict__ position, uint8_t* __restrict__ drop_mask) {
+  const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (a >= T * k) return;
+  const int64_t t = a / k;
+  const int32_t pos = offsets[(t / chunk) * N + expert_idx[a]] + rank_local[a];
+  position[a] = pos;
+  drop_mask[a] = (int64_t)pos >= C ? 1 : 0;
 }
 
 // ------------------------------------------------------------------ launchers
 
-void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T,
+void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T, int k,
                        int64_t C, float alpha, int32_t* load, int32_t* n_kept, double* terms,
                        float* aux, int32_t* tile_start, int tile_rows, hipStream_t s) {
   if (N <= 1024) {
     int EG = 1;
     while (EG < N) EG <<= 1;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, P_part, nc, N, EG, T,
-                       C, alpha, load, n_kept, nullptr, aux, tile_start, tile_rows);
+                       k, C, alpha, load, n_kept, nullptr, aux, tile_start, tile_rows);
     return;
   }
   constexpr int EG = 64;
   hipLaunchKernelGGL(route_scan_kernel, dim3((unsigned)((N + EG - 1) / EG)), dim3(1024), 0, s,
-                     hist, P_part, nc, N, EG, T, C, alpha, load, n_kept, terms, aux, nullptr,
+                     hist, P_part, nc, N, EG, T, k, C, alpha, load, n_kept, terms, aux, nullptr,
                      tile_rows);
-  hipLaunchKernelGGL(aux_kernel, dim3(1), dim3(1024), 0, s, terms, N, T, alpha, aux, n_kept,
+  hipLaunchKernelGGL(aux_kernel, dim3(1), dim3(1024), 0, s, terms, N, T, k, alpha, aux, n_kept,
                      tile_start, tile_rows);
 }
 
-void launch_finalize_positions(int64_t T, const int32_t* expert_idx, const int32_t* rank_local,
-                               const int32_t* offsets, int N, int64_t chunk, int64_t C,
-                               int32_t* position, uint8_t* drop_mask, hipStream_t s) {
+void launch_finalize_positions(int64_t T, int k, const int32_t* expert_idx,
+                               const int32_t* rank_local, const int32_t* offsets, int N,
+                               int64_t chunk, int64_t C, int32_t* position, uint8_t* drop_mask,
+                               hipStream_t s) {
   if (T == 0) return;
-  hipLaunchKernelGGL(finalize_positions_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0,
-                     s, T, expert_idx, rank_local, offsets, N, chunk, C, position, drop_mask);
+  const int64_t n = T * k;
+  hipLaunchKernelGGL(finalize_positions_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     s, T, k, expert_idx, rank_local, offsets, N, chunk, C, position, drop_mask);
 }
 
 }  // namespace swl

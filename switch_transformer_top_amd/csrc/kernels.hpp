@@ -37,38 +37,46 @@ inline void prof_end(Profiler* p, hipStream_t s) {
   p->active = false;
 }
 
+// Experts per token: 1 (the Switch layer) or 2 (classic top-2 MoE routing).
+// Per-token outputs are laid out [T, k]; assignment a = t * k + j.
+constexpr int kMaxTopK = 2;
+
 // router.hip
 bool router_fused_ok(bool x_bf16, int N);
 int64_t route_chunk_tokens(bool x_bf16, int N);
 void launch_router_logits(const void* x, bool x_bf16, const float* W_r, const float* b_r,
                           float* h, int64_t T, int d, int N, hipStream_t s);
 void launch_router_fused(const uint16_t* x, const float* W_r, const float* b_r, int64_t T, int d,
-                         int N, float* logits, int32_t* expert_idx, float* gate, float* P_part,
-                         int32_t* hist, int32_t* rank_local, hipStream_t s);
-void launch_route_rows(const float* h, int64_t T, int N, int32_t* expert_idx, float* gate,
+                         int N, int k, float* logits, int32_t* expert_idx, float* gate,
+                         float* P_part, int32_t* hist, int32_t* rank_local, hipStream_t s);
+void launch_route_rows(const float* h, int64_t T, int N, int k, int32_t* expert_idx, float* gate,
                        float* P_part, int32_t* hist, int32_t* rank_local, hipStream_t s);
 
 // assign.hip
 // tile_start (optional, N + 1 entries): exclusive prefix over experts of
 // ceil(n_kept / tile_rows), with the total last.
-void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T,
+// k: assignments per token (the loss divides load by k T).
+void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T, int k,
                        int64_t C, float alpha, int32_t* load, int32_t* n_kept, double* terms,
                        float* aux, int32_t* tile_start, int tile_rows, hipStream_t s);
-void launch_finalize_positions(int64_t T, const int32_t* expert_idx, const int32_t* rank_local,
-                               const int32_t* offsets, int N, int64_t chunk, int64_t C,
-                               int32_t* position, uint8_t* drop_mask, hipStream_t s);
+void launch_finalize_positions(int64_t T, int k, const int32_t* expert_idx,
+                               const int32_t* rank_local, const int32_t* offsets, int N,
+                               int64_t chunk, int64_t C, int32_t* position, uint8_t* drop_mask,
+                               hipStream_t s);
 
 // move.hip
-void launch_dispatch(const void* x, int64_t T, int row_bytes, const int32_t* expert_idx,
+void launch_dispatch(const void* x, int64_t T, int k, int row_bytes, const int32_t* expert_idx,
                      const int32_t* rank_local, const int32_t* offsets, int N, int64_t chunk,
                      int64_t C, int32_t* position, uint8_t* drop_mask, void* Xbuf, hipStream_t s);
-void launch_dispatch_index(const void* x, int64_t T, int row_bytes, const int32_t* expert_idx,
-                           const int32_t* rank_local, const int32_t* offsets, int N, int64_t chunk,
-                           int64_t C, int32_t* position, uint8_t* drop_mask, int32_t* tok,
+// copy_dropped: copy the rows of dropped tokens to out (k = 1 with the fused combine)
+void launch_dispatch_index(const void* x, int64_t T, int k, int row_bytes,
+                           const int32_t* expert_idx, const int32_t* rank_local,
+                           const int32_t* offsets, int N, int64_t chunk, int64_t C,
+                           int32_t* position, uint8_t* drop_mask, int32_t* tok, bool copy_dropped,
                            void* out, hipStream_t s);
-void launch_combine(const void* x, bool bf16, int64_t T, int row_bytes, const int32_t* expert_idx,
-                    const int32_t* position, const uint8_t* drop_mask, const float* gate,
-                    int64_t C, const void* Ybuf, void* out, hipStream_t s);
+void launch_combine(const void* x, bool bf16, int64_t T, int k, int row_bytes,
+                    const int32_t* expert_idx, const int32_t* position, const uint8_t* drop_mask,
+                    const float* gate, int64_t C, const void* Ybuf, void* out, hipStream_t s);
 void launch_copy_expert_rows(const void* Ybuf, const int32_t* n_kept, int N, int64_t C,
                              int row_bytes, void* dst, hipStream_t s);
 

@@ -20,9 +20,12 @@ namespace swl {
 // row_vec16 = bytes of one row / 16 (rows are a multiple of 16 bytes).
 
 // Dispatch also finalises the routing: position = chunk offset + in-chunk
-// rank, drop = position >= C; kept rows are copied to their expert slot.
+// rank, drop = position >= C; kept rows are copied to their expert slot.  With
+// k choices per token, assignment a = t * k + j goes to expert_idx[a]; thread
+// c < k of a token finalises choice c, and every thread copies its piece of the
+// row for each kept choice.
 __global__ __launch_bounds__(256) void dispatch_kernel(const uint4* __restrict__ x, int64_t T,
-                                                       int row_vec16,
+                                                       int k, int row_vec16,
                                                        const int32_t* __restrict__ expert_idx,
                                                        const int32_t* __restrict__ rank_local,
                                                        const int32_t* __restrict__ offsets, int N,
@@ -34,25 +37,25 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const uint4* __restrict__
   const int64_t t = gid / row_vec16;
   const int c = (int)(gid - t * row_vec16);
   if (t >= T) return;
-  const int32_t e = expert_idx[t];
-  const int32_t pos = offsets[(t / chunk) * N + e] + rank_local[t];
-  const bool dropped = (int64_t)pos >= C;
-  if (c == 0) {
-    position[t] = pos;
-    drop_mask[t] = dropped ? 1 : 0;
+  for (int j = 0; j < k; ++j) {
+    const int64_t a = t * k + j;
+    const int32_t e = expert_idx[a];
+    const int32_t pos = offsets[(t / chunk) * N + e] + rank_local[a];
+    const bool dropped = (int64_t)pos >= C;
+    if (c == j) {
+      position[a] = pos;
+      drop_mask[a] = dropped ? 1 : 0;
+    }
+    if (!dropped) Xbuf[((int64_t)e * C + pos) * row_vec16 + c] = x[t * row_vec16 + c];
   }
-  if (!dropped) Xbuf[((int64_t)e * C + pos) * row_vec16 + c] = x[t * row_vec16 + c];
 }
 
-__device__ __forceinline__ uint4 combine_vec_f32(uint4 xv, uint4 yv, float g) {
-  float4 a = *reinterpret_cast<float4*>(&xv), b = *reinterpret_cast<float4*>(&yv);
-  float4 o = make_float4(fmaf(g, b.x, a.x), fmaf(g, b.y, a.y), fmaf(g, b.z, a.z), fmaf(g, b.w, a.w));
-  return *reinterpret_cast<uint4*>(&o);
-}
-
+// out[t] = x[t] + sum over kept choices j of gate[t, j] * Y[e_tj, position_tj]:
+// fp32 fused multiply-adds in choice order, then one rounding (bf16 layers).
+// A token with no kept choice leaves bit for bit.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ x, int64_t T,
-                                                      int row_vec16,
+                                                      int k, int row_vec16,
                                                       const int32_t* __restrict__ expert_idx,
                                                       const int32_t* __restrict__ position,
                                                       const uint8_t* __restrict__ drop_mask,
@@ -64,27 +67,55 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   const int c = (int)(gid - t * row_vec16);
   if (t >= T) return;
   const uint4 xv = x[t * row_vec16 + c];
-  if (drop_mask[t]) {
+  constexpr int NV = BF16 ? 8 : 4;   // values per 16-byte piece
+  float acc[NV];
+  const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (BF16) {
+      acc[2 * i] = __uint_as_float(xs[i] << 16);
+      acc[2 * i + 1] = __uint_as_float(xs[i] & 0xFFFF0000u);
+    } else {
+      acc[i] = __uint_as_float(xs[i]);
+    }
+  }
+  bool any = false;
+  for (int j = 0; j < k; ++j) {
+    const int64_t a = t * k + j;
+    if (drop_mask[a]) continue;
+    any = true;
+    const float g = gate[a];
+    const uint4 yv = Ybuf[((int64_t)expert_idx[a] * C + position[a]) * row_vec16 + c];
+    const uint32_t ys[4] = {yv.x, yv.y, yv.z, yv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (BF16) {
+        acc[2 * i] = fmaf(g, __uint_as_float(ys[i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(g, __uint_as_float(ys[i] & 0xFFFF0000u), acc[2 * i + 1]);
+      } else {
+        acc[i] = fmaf(g, __uint_as_float(ys[i]), acc[i]);
+      }
+    }
+  }
+  if (!any) {
     out[t * row_vec16 + c] = xv;
     return;
   }
-  const float g = gate[t];
-  const uint4 yv = Ybuf[((int64_t)expert_idx[t] * C + position[t]) * row_vec16 + c];
-  if (BF16) {
-    const u32x4 o = combine_vec_bf16(u32x4{xv.x, xv.y, xv.z, xv.w}, u32x4{yv.x, yv.y, yv.z, yv.w}, g);
-    out[t * row_vec16 + c] = make_uint4(o.x, o.y, o.z, o.w);
-  } else {
-    out[t * row_vec16 + c] = combine_vec_f32(xv, yv, g);
-  }
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = BF16 ? f32x2_to_bf16x2_bits(acc[2 * i], acc[2 * i + 1]) : __float_as_uint(acc[i]);
+  out[t * row_vec16 + c] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // Dispatch by index (bf16 path): the expert matmuls read the rows of x in
 // place, so dispatch only finalises the routing and records, for every kept
-// token, which token sits in slot (e, position): tok[e * C + position] = t.
-// A dropped token leaves the layer unchanged: its row of x is copied to out
-// here, and the fused combine never touches it.
+// assignment, which token sits in slot (e, position): tok[e * C + position] = t.
+// With the fused combine (k = 1) a dropped token leaves the layer unchanged:
+// its row of x is copied to out here, and the combine never touches it.
+// Thread c < k of a token handles choice c.
 __global__ __launch_bounds__(256) void dispatch_index_kernel(const uint4* __restrict__ x, int64_t T,
-                                                             int row_vec16,
+                                                             int k, int row_vec16,
                                                              const int32_t* __restrict__ expert_idx,
                                                              const int32_t* __restrict__ rank_local,
                                                              const int32_t* __restrict__ offsets,
@@ -92,20 +123,26 @@ __global__ __launch_bounds__(256) void dispatch_index_kernel(const uint4* __rest
                                                              int32_t* __restrict__ position,
                                                              uint8_t* __restrict__ drop_mask,
                                                              int32_t* __restrict__ tok,
+                                                             bool copy_dropped,
                                                              uint4* __restrict__ out) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t t = gid / row_vec16;
   const int c = (int)(gid - t * row_vec16);
   if (t >= T) return;
-  const int32_t e = expert_idx[t];
-  const int32_t pos = offsets[(t / chunk) * N + e] + rank_local[t];
-  const bool dropped = (int64_t)pos >= C;
-  if (c == 0) {
-    position[t] = pos;
-    drop_mask[t] = dropped ? 1 : 0;
+  if (c < k) {
+    const int64_t a = t * k + c;
+    const int32_t e = expert_idx[a];
+    const int32_t pos = offsets[(t / chunk) * N + e] + rank_local[a];
+    const bool dropped = (int64_t)pos >= C;
+    position[a] = pos;
+    drop_mask[a] = dropped ? 1 : 0;
     if (!dropped) tok[(int64_t)e * C + pos] = (int32_t)t;
   }
-  if (dropped) out[t * row_vec16 + c] = x[t * row_vec16 + c];
+  if (copy_dropped) {
+    const int32_t e = expert_idx[t];
+    const int32_t pos = offsets[(t / chunk) * N + e] + rank_local[t];
+    if ((int64_t)pos >= C) out[t * row_vec16 + c] = x[t * row_vec16 + c];
+  }
 }
 
 // Copy of the expert outputs for the debug entry point: rows p < n_kept[e].
@@ -128,37 +165,38 @@ static unsigned move_blocks(int64_t T, int row_bytes) {
   return (unsigned)((threads + 255) / 256);
 }
 
-void launch_dispatch(const void* x, int64_t T, int row_bytes, const int32_t* expert_idx,
+void launch_dispatch(const void* x, int64_t T, int k, int row_bytes, const int32_t* expert_idx,
                      const int32_t* rank_local, const int32_t* offsets, int N, int64_t chunk,
                      int64_t C, int32_t* position, uint8_t* drop_mask, void* Xbuf, hipStream_t s) {
   if (T == 0) return;
-  hipLaunchKernelGGL(dispatch_kernel, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s, (const uint4*)x, T,
-                     row_bytes / 16, expert_idx, rank_local, offsets, N, chunk, C, position,
-                     drop_mask, (uint4*)Xbuf);
+  hipLaunchKernelGGL(dispatch_kernel, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
+                     (const uint4*)x, T, k, row_bytes / 16, expert_idx, rank_local, offsets, N,
+                     chunk, C, position, drop_mask, (uint4*)Xbuf);
 }
 
-void launch_dispatch_index(const void* x, int64_t T, int row_bytes, const int32_t* expert_idx,
-                           const int32_t* rank_local, const int32_t* offsets, int N, int64_t chunk,
-                           int64_t C, int32_t* position, uint8_t* drop_mask, int32_t* tok,
+void launch_dispatch_index(const void* x, int64_t T, int k, int row_bytes,
+                           const int32_t* expert_idx, const int32_t* rank_local,
+                           const int32_t* offsets, int N, int64_t chunk, int64_t C,
+                           int32_t* position, uint8_t* drop_mask, int32_t* tok, bool copy_dropped,
                            void* out, hipStream_t s) {
   if (T == 0) return;
   hipLaunchKernelGGL(dispatch_index_kernel, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
-                     (const uint4*)x, T, row_bytes / 16, expert_idx, rank_local, offsets, N, chunk,
-                     C, position, drop_mask, tok, (uint4*)out);
+                     (const uint4*)x, T, k, row_bytes / 16, expert_idx, rank_local, offsets, N,
+                     chunk, C, position, drop_mask, tok, copy_dropped && k == 1, (uint4*)out);
 }
 
-void launch_combine(const void* x, bool bf16, int64_t T, int row_bytes, const int32_t* expert_idx,
-                    const int32_t* position, const uint8_t* drop_mask, const float* gate,
-                    int64_t C, const void* Ybuf, void* out, hipStream_t s) {
+void launch_combine(const void* x, bool bf16, int64_t T, int k, int row_bytes,
+                    const int32_t* expert_idx, const int32_t* position, const uint8_t* drop_mask,
+                    const float* gate, int64_t C, const void* Ybuf, void* out, hipStream_t s) {
   if (T == 0) return;
   if (bf16)
     hipLaunchKernelGGL(combine_kernel<true>, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
-                       (const uint4*)x, T, row_bytes / 16, expert_idx, position, drop_mask, gate,
-                       C, (const uint4*)Ybuf, (uint4*)out);
+                       (const uint4*)x, T, k, row_bytes / 16, expert_idx, position, drop_mask,
+                       gate, C, (const uint4*)Ybuf, (uint4*)out);
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
-                       (const uint4*)x, T, row_bytes / 16, expert_idx, position, drop_mask, gate,
-                       C, (const uint4*)Ybuf, (uint4*)out);
+                       (const uint4*)x, T, k, row_bytes / 16, expert_idx, position, drop_mask,
+                       gate, C, (const uint4*)Ybuf, (uint4*)out);
 }
 
 void launch_copy_expert_rows(const void* Ybuf, const int32_t* n_kept, int N, int64_t C,

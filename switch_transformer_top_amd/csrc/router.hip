@@ -136,11 +136,12 @@ __device__ __forceinline__ void wave_rank(int32_t e, int& rank, bool& last) {
   last = after == 0;
 }
 
-// Ranks and histogram of one chunk from its experts s_idx[0..n) (LDS).  Wave 0
-// walks the chunk 64 tokens at a time; cnt (LDS, N ints) holds the running
+// Ranks and histogram of one chunk from its experts s_idx[0..n) (LDS), one
+// entry per assignment in (token, choice) order starting at assignment a0 of
+// the call (a0 = t0 * k).  Wave 0 walks the chunk 64 assignments at a time; cnt (LDS, N ints) holds the running
 // count per expert, which ends as the chunk's histogram.  The whole block must
 // call this (it synchronises).
-__device__ __forceinline__ void chunk_hist_rank(const int32_t* s_idx, int n, int64_t t0, int N,
+__device__ __forceinline__ void chunk_hist_rank(const int32_t* s_idx, int n, int64_t a0, int N,
                                                 int32_t* cnt, int32_t* __restrict__ hist_row,
                                                 int32_t* __restrict__ rank_local) {
   for (int i = threadIdx.x; i < N; i += blockDim.x) cnt[i] = 0;
@@ -155,7 +156,7 @@ __device__ __forceinline__ void chunk_hist_rank(const int32_t* s_idx, int n, int
       wave_rank(e, rank, last);
       if (active) {
         const int32_t r = cnt[e] + rank;  // every lane reads before any lane writes
-        rank_local[t0 + i] = r;
+        rank_local[a0 + i] = r;
         if (last) cnt[e] = r + 1;
       }
     }
@@ -196,11 +197,14 @@ __device__ __forceinline__ void split3(const float* w, bf16x8& hi, bf16x8& mid, 
 // Routing statistics of a block's logit tile st[BT][LD] (LDS, fp32, bias
 // added, padded experts at -inf), tokens t0 .. t0 + n_tok.  A few consecutive
 // threads share a token row (TPR = blockDim / BT): max with the lowest index,
-// S = sum_i exp(h_i - max) (fp64), gate = 1 / S; then thread e owns expert e and
-// sums p_e over the chunk's tokens in token order (fp64) for P_part; the
-// logits leave in full coalesced rows when requested.  Synchronises the block.
+// S = sum_i exp(h_i - max) (fp64), gate = 1 / S; with k = 2 also the best of
+// the other experts (lowest index on ties) and its probability
+// exp(h - max) / S.  Choices go to expert_idx / gate [t * k + j] and s_idx
+// [row * k + j].  Then thread e owns expert e and sums p_e over the chunk's
+// tokens in token order (fp64) for P_part; the logits leave in full coalesced
+// rows when requested.  Synchronises the block.
 template <int BT, int NPAD, int LD>
-__device__ __forceinline__ void block_stats(const float* st, int N, int64_t t0, int n_tok,
+__device__ __forceinline__ void block_stats(const float* st, int N, int k, int64_t t0, int n_tok,
                                             float* __restrict__ logits,
                                             int32_t* __restrict__ expert_idx,
                                             float* __restrict__ gate,
@@ -228,13 +232,37 @@ __device__ __forceinline__ void block_stats(const float* st, int N, int64_t t0, 
   for (int i = 0; i < SPAN; ++i) ssum += (double)expf(rp[i] - m);
 #pragma unroll
   for (int o = TPR / 2; o >= 1; o >>= 1) ssum += shfl_xor_f64_w(ssum, o, TPR);
+  // second choice: the largest logit among the other experts (real ones only)
+  float m2 = -__builtin_huge_valf();
+  int mi2 = 0x7fffffff;
+  if (k > 1) {
+#pragma unroll 8
+    for (int i = 0; i < SPAN; ++i) {
+      const int e = part * SPAN + i;
+      if (e != mi && e < N && (rp[i] > m2 || mi2 == 0x7fffffff)) { m2 = rp[i]; mi2 = e; }
+    }
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o >>= 1) {
+      const float om = __shfl_xor(m2, o, TPR);
+      const int oi = __shfl_xor(mi2, o, TPR);
+      if (oi != 0x7fffffff && (mi2 == 0x7fffffff || om > m2 || (om == m2 && oi < mi2))) {
+        m2 = om;
+        mi2 = oi;
+      }
+    }
+  }
   if (part == 0 && row < n_tok) {
     const double inv = 1.0 / ssum;
     s_m[row] = m;
     s_inv[row] = inv;
-    s_idx[row] = mi;
-    expert_idx[t0 + row] = mi;
-    gate[t0 + row] = (float)inv;
+    s_idx[row * k] = mi;
+    expert_idx[(t0 + row) * k] = mi;
+    gate[(t0 + row) * k] = (float)inv;
+    if (k > 1) {
+      s_idx[row * k + 1] = mi2;
+      expert_idx[(t0 + row) * k + 1] = mi2;
+      gate[(t0 + row) * k + 1] = (float)((double)expf(m2 - m) * inv);
+    }
   }
   if (logits) {
     for (int idx = tid; idx < n_tok * N; idx += 256) {
@@ -257,11 +285,11 @@ __device__ __forceinline__ void block_stats(const float* st, int N, int64_t t0, 
 template <int NPAD>
 __global__ __launch_bounds__(256) void router_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ W_r, const float* __restrict__ b_r,
-    int64_t T, int d, int N, float* __restrict__ logits, int32_t* __restrict__ expert_idx,
+    int64_t T, int d, int N, int k, float* __restrict__ logits, int32_t* __restrict__ expert_idx,
     float* __restrict__ gate, float* __restrict__ P_part, int32_t* __restrict__ hist,
     int32_t* __restrict__ rank_local) {
   constexpr int NJ = NPAD / 16, BT = 16, NACC = NJ * 4, GRP = 8, LD = NPAD + 4;
-  __shared__ int32_t s_idx[BT];
+  __shared__ int32_t s_idx[BT * kMaxTopK];
   __shared__ int32_t cnt[NPAD];
   __shared__ float red[3][NACC][kWave];
   __shared__ float st[BT * LD];
@@ -347,9 +375,9 @@ __global__ __launch_bounds__(256) void router_small_kernel(
     }
   }
   __syncthreads();
-  block_stats<BT, NPAD, LD>(&st[0], N, t0, n_tok, logits, expert_idx, gate,
+  block_stats<BT, NPAD, LD>(&st[0], N, k, t0, n_tok, logits, expert_idx, gate,
                             P_part + (int64_t)blockIdx.x * N, s_idx, s_m, s_inv);
-  chunk_hist_rank(s_idx, n_tok, t0, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
+  chunk_hist_rank(s_idx, n_tok * k, t0 * k, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
 }
 
 // More experts (32 < N): a block owns 64 * ROWT tokens and NPAD experts
@@ -363,7 +391,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(
 template <int NPAD, int ROWT, bool FUSED>
 __global__ __launch_bounds__(256) void router_tok_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ W_r, const float* __restrict__ b_r,
-    int64_t T, int d, int N, float* __restrict__ logits, int32_t* __restrict__ expert_idx,
+    int64_t T, int d, int N, int k, float* __restrict__ logits, int32_t* __restrict__ expert_idx,
     float* __restrict__ gate, float* __restrict__ P_part, int32_t* __restrict__ hist,
     int32_t* __restrict__ rank_local) {
   constexpr int NJ = NPAD / 16, BT = 64 * ROWT, WLD = 40, LD = NPAD + 4;
@@ -375,7 +403,7 @@ __global__ __launch_bounds__(256) void router_tok_kernel(
   typedef uint16_t PlaneArr[3][NPAD * WLD];
   PlaneArr* wpl = reinterpret_cast<PlaneArr*>(raw);
   float* st = reinterpret_cast<float*>(raw);
-  __shared__ int32_t s_idx[BT];
+  __shared__ int32_t s_idx[FUSED ? BT * kMaxTopK : 1];
   __shared__ int32_t cnt[FUSED ? NPAD : 1];
   __shared__ float s_m[BT];
   __shared__ double s_inv[BT];
@@ -511,9 +539,9 @@ __global__ __launch_bounds__(256) void router_tok_kernel(
     }
     return;
   }
-  block_stats<BT, NPAD, LD>(st, N, t0, n_tok, logits, expert_idx, gate,
+  block_stats<BT, NPAD, LD>(st, N, k, t0, n_tok, logits, expert_idx, gate,
                             P_part + (int64_t)blockIdx.x * N, s_idx, s_m, s_inv);
-  chunk_hist_rank(s_idx, n_tok, t0, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
+  chunk_hist_rank(s_idx, n_tok * k, t0 * k, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
 }
 
 // ---------------------------------------------------------------------------
@@ -528,7 +556,8 @@ __global__ __launch_bounds__(256) void router_tok_kernel(
 constexpr int RR_ROWS = 64;
 
 __global__ __launch_bounds__(256) void route_rows_kernel(const float* __restrict__ h, int64_t T,
-                                                         int N, int32_t* __restrict__ expert_idx,
+                                                         int N, int k,
+                                                         int32_t* __restrict__ expert_idx,
                                                          float* __restrict__ gate,
                                                          float* __restrict__ P_part,
                                                          int32_t* __restrict__ hist,
@@ -536,7 +565,7 @@ __global__ __launch_bounds__(256) void route_rows_kernel(const float* __restrict
   extern __shared__ int32_t cnt[];
   __shared__ float s_m[RR_ROWS];
   __shared__ double s_inv[RR_ROWS];
-  __shared__ int32_t s_idx[RR_ROWS];
+  __shared__ int32_t s_idx[RR_ROWS * kMaxTopK];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * RR_ROWS;
   const int rows = (int)((T - t0) < RR_ROWS ? (T - t0) : RR_ROWS);
@@ -554,12 +583,35 @@ __global__ __launch_bounds__(256) void route_rows_kernel(const float* __restrict
     double s = 0.0;
     for (int i = lane; i < N; i += kWave) s += (double)expf(row[i] - m);
     s = wave_sum_f64(s);
+    // second choice (k = 2): the best of the other experts, lowest index on ties
+    float m2 = -__builtin_huge_valf();
+    int mi2 = 0x7fffffff;
+    if (k > 1) {
+      for (int i = lane; i < N; i += kWave) {
+        const float v = row[i];
+        if (i != mi && (v > m2 || mi2 == 0x7fffffff)) { m2 = v; mi2 = i; }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float om = __shfl_xor(m2, o, kWave);
+        const int oi = __shfl_xor(mi2, o, kWave);
+        if (oi != 0x7fffffff && (mi2 == 0x7fffffff || om > m2 || (om == m2 && oi < mi2))) {
+          m2 = om;
+          mi2 = oi;
+        }
+      }
+    }
     if (lane == 0) {
-      expert_idx[t0 + r] = mi;
-      gate[t0 + r] = (float)(1.0 / s);
+      expert_idx[(t0 + r) * k] = mi;
+      gate[(t0 + r) * k] = (float)(1.0 / s);
       s_m[r] = m;
       s_inv[r] = 1.0 / s;
-      s_idx[r] = mi;
+      s_idx[r * k] = mi;
+      if (k > 1) {
+        expert_idx[(t0 + r) * k + 1] = mi2;
+        gate[(t0 + r) * k + 1] = (float)((double)expf(m2 - m) * (1.0 / s));
+        s_idx[r * k + 1] = mi2;
+      }
     }
   }
   __syncthreads();
@@ -568,7 +620,7 @@ __global__ __launch_bounds__(256) void route_rows_kernel(const float* __restrict
     for (int r = 0; r < rows; ++r) acc += (double)expf(h[(t0 + r) * N + i] - s_m[r]) * s_inv[r];
     P_part[(int64_t)blockIdx.x * N + i] = (float)acc;
   }
-  chunk_hist_rank(s_idx, rows, t0, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
+  chunk_hist_rank(s_idx, rows * k, t0 * k, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -590,7 +642,7 @@ void launch_router_logits(const void* x, bool x_bf16, const float* W_r, const fl
     constexpr int BT = 64 * kTokRowt;
     const dim3 grid((unsigned)((T + BT - 1) / BT), (unsigned)((N + 255) / 256));
     hipLaunchKernelGGL((router_tok_kernel<256, kTokRowt, false>), grid, dim3(256), 0, s,
-                       (const uint16_t*)x, W_r, b_r, T, d, N, h, nullptr, nullptr, nullptr,
+                       (const uint16_t*)x, W_r, b_r, T, d, N, 1, h, nullptr, nullptr, nullptr,
                        nullptr, nullptr);
     return;
   }
@@ -600,17 +652,17 @@ void launch_router_logits(const void* x, bool x_bf16, const float* W_r, const fl
 }
 
 void launch_router_fused(const uint16_t* x, const float* W_r, const float* b_r, int64_t T, int d,
-                         int N, float* logits, int32_t* expert_idx, float* gate, float* P_part,
-                         int32_t* hist, int32_t* rank_local, hipStream_t s) {
+                         int N, int k, float* logits, int32_t* expert_idx, float* gate,
+                         float* P_part, int32_t* hist, int32_t* rank_local, hipStream_t s) {
   if (T == 0) return;
   const int64_t ch = route_chunk_tokens(true, N);
   const dim3 grid((unsigned)((T + ch - 1) / ch));
 #define SWL_SMALL(NP)                                                                           \
-  hipLaunchKernelGGL((router_small_kernel<NP>), grid, dim3(256), 0, s, x, W_r, b_r, T, d, N,    \
+  hipLaunchKernelGGL((router_small_kernel<NP>), grid, dim3(256), 0, s, x, W_r, b_r, T, d, N, k, \
                      logits, expert_idx, gate, P_part, hist, rank_local)
 #define SWL_TOK(NP)                                                                             \
   hipLaunchKernelGGL((router_tok_kernel<NP, kTokRowt, true>), grid, dim3(256), 0, s, x, W_r,    \
-                     b_r, T, d, N, logits, expert_idx, gate, P_part, hist, rank_local)
+                     b_r, T, d, N, k, logits, expert_idx, gate, P_part, hist, rank_local)
   if (N <= 16) SWL_SMALL(16);
   else if (N <= 32) SWL_SMALL(32);
   else if (N <= 64) SWL_TOK(64);
@@ -620,11 +672,11 @@ void launch_router_fused(const uint16_t* x, const float* W_r, const float* b_r, 
 #undef SWL_TOK
 }
 
-void launch_route_rows(const float* h, int64_t T, int N, int32_t* expert_idx, float* gate,
+void launch_route_rows(const float* h, int64_t T, int N, int k, int32_t* expert_idx, float* gate,
                        float* P_part, int32_t* hist, int32_t* rank_local, hipStream_t s) {
   if (T == 0) return;
   hipLaunchKernelGGL(route_rows_kernel, dim3((unsigned)((T + RR_ROWS - 1) / RR_ROWS)), dim3(256),
-                     sizeof(int32_t) * (size_t)N, s, h, T, N, expert_idx, gate, P_part, hist,
+                     sizeof(int32_t) * (size_t)N, s, h, T, N, k, expert_idx, gate, P_part, hist,
                      rank_local);
 }
 

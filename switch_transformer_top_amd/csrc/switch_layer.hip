@@ -28,12 +28,16 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 size_t dtype_size(int32_t dt) { return dt == SWITCH_BF16 ? 2 : 4; }
 
-// Capacity C = ceil(c * T / N) in double, or the override.  Buffers hold
-// min(C, T) rows per expert: a position is always below T, so a capacity above
-// T drops nothing and a capacity of min(C, T) keeps exactly the same tokens.
+// Experts per token (the stored config has 0 replaced by 1).
+int top_k(const switch_config& c) { return c.top_k; }
+
+// Capacity C = ceil(k * c * T / N) in double, or the override.  Buffers hold
+// min(C, T) rows per expert: the k choices of a token are distinct experts, so
+// a position is always below T; a capacity above T drops nothing and a
+// capacity of min(C, T) keeps exactly the same assignments.
 int64_t capacity_of(const switch_config& c, int64_t T) {
   if (c.capacity_override > 0) return c.capacity_override;
-  double v = ceil((c.capacity_factor * (double)T) / (double)c.n_experts);
+  double v = ceil(((double)top_k(c) * c.capacity_factor * (double)T) / (double)c.n_experts);
   if (!(v >= 0.0)) return 0;
   if (v > 9.0e18) v = 9.0e18;
   return (int64_t)v;
@@ -68,7 +72,7 @@ Layout layout_of(const switch_layer* L, int64_t T) {
   lo.logits = take(sizeof(float) * (size_t)T * (size_t)N);
   lo.ppart = take(sizeof(float) * (size_t)nc * (size_t)N);
   lo.hist = take(sizeof(int32_t) * (size_t)nc * (size_t)N);
-  lo.rank = take(sizeof(int32_t) * (size_t)T);
+  lo.rank = take(sizeof(int32_t) * (size_t)T * (size_t)top_k(c));
   lo.load = take(sizeof(int32_t) * (size_t)N);
   lo.nkept = take(sizeof(int32_t) * (size_t)N);
   lo.terms = take(sizeof(double) * (size_t)N);
@@ -146,8 +150,8 @@ Routed enqueue_routing(switch_layer* L, const void* x, const float* given_logits
   if (T > 0) {
     if (fused) {
       swl::prof_mark(P, s, "router");
-      swl::launch_router_fused((const uint16_t*)x, L->W_r, L->b_r, T, c.d_model, N, logits_out,
-                               expert_idx, gate, ppart, r.offsets, r.rank, s);
+      swl::launch_router_fused((const uint16_t*)x, L->W_r, L->b_r, T, c.d_model, N, top_k(c),
+                               logits_out, expert_idx, gate, ppart, r.offsets, r.rank, s);
     } else {
       const float* h = given_logits;
       if (!h) {
@@ -157,12 +161,12 @@ Routed enqueue_routing(switch_layer* L, const void* x, const float* given_logits
         h = hw;
       }
       swl::prof_mark(P, s, "route_rows");
-      swl::launch_route_rows(h, T, N, expert_idx, gate, ppart, r.offsets, r.rank, s);
+      swl::launch_route_rows(h, T, N, top_k(c), expert_idx, gate, ppart, r.offsets, r.rank, s);
     }
   }
   const int64_t nc = (T + r.chunk - 1) / r.chunk;
   swl::prof_mark(P, s, "route_scan");
-  swl::launch_route_scan(r.offsets, ppart, nc, N, T, r.Cb, c.alpha, r.load, r.nkept,
+  swl::launch_route_scan(r.offsets, ppart, nc, N, T, top_k(c), r.Cb, c.alpha, r.load, r.nkept,
                          (double*)(ws + lo.terms), aux_loss, r.tile_start, swl::kWideTileRows, s);
   return r;
 }
@@ -196,10 +200,12 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
   void* xbuf = w + lo.xbuf;
   void* hbuf = w + lo.hbuf;
   void* ybuf = w + lo.ybuf;
+  const int k = top_k(c);
   if (T > 0 && bf16) {
     // rows stay in place: dispatch records the slot table, GEMM1 gathers
-    // through it, GEMM2 combines into out (or stores the expert output when
-    // the caller asks for it, and the combine pass follows)
+    // through it, GEMM2 combines into out (top-1 without a copy of the expert
+    // output), or stores the expert output for the combine pass (top-2, where
+    // two experts add into one row, or when the caller asks for it)
     int32_t* tok = (int32_t*)(w + lo.tok);
     swl::GemmIO io;
     io.tile_start = r.tile_start;
@@ -207,13 +213,14 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
     io.x = (const uint16_t*)x;
     io.gate = gate;
     io.out = (uint16_t*)out;
+    const bool fused = !expert_out && k == 1;
     swl::prof_mark(P, s, "dispatch");
-    swl::launch_dispatch_index(x, T, (int)(es * d), expert_idx, r.rank, r.offsets, N, r.chunk, Cb,
-                               position, drop_mask, tok, out, s);
+    swl::launch_dispatch_index(x, T, k, (int)(es * d), expert_idx, r.rank, r.offsets, N, r.chunk,
+                               Cb, position, drop_mask, tok, fused, out, s);
     swl::prof_mark(P, s, "gemm1_relu");
     swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
                                  hbuf, Cb * F, r.nkept, N, Cb, d, F, io, s);
-    if (!expert_out) {
+    if (fused) {
       swl::prof_mark(P, s, "gemm2_combine");
       swl::launch_expert_gemm_bf16(swl::kRowsCombine, false, hbuf, Cb * F, L->W_out,
                                    (int64_t)d * F, nullptr, 0, r.nkept, N, Cb, F, d, io, s);
@@ -222,14 +229,16 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
       swl::launch_expert_gemm_bf16(swl::kRowsDense, false, hbuf, Cb * F, L->W_out, (int64_t)d * F,
                                    ybuf, Cb * d, r.nkept, N, Cb, F, d, io, s);
       swl::prof_mark(P, s, "combine");
-      swl::launch_combine(x, bf16, T, (int)(es * d), expert_idx, position, drop_mask, gate, Cb,
+      swl::launch_combine(x, bf16, T, k, (int)(es * d), expert_idx, position, drop_mask, gate, Cb,
                           ybuf, out, s);
-      swl::prof_mark(P, s, "copy_expert_rows");
-      swl::launch_copy_expert_rows(ybuf, r.nkept, N, Cb, (int)(es * d), expert_out, s);
+      if (expert_out) {
+        swl::prof_mark(P, s, "copy_expert_rows");
+        swl::launch_copy_expert_rows(ybuf, r.nkept, N, Cb, (int)(es * d), expert_out, s);
+      }
     }
   } else if (T > 0) {
     swl::prof_mark(P, s, "dispatch");
-    swl::launch_dispatch(x, T, (int)(es * d), expert_idx, r.rank, r.offsets, N, r.chunk, Cb,
+    swl::launch_dispatch(x, T, k, (int)(es * d), expert_idx, r.rank, r.offsets, N, r.chunk, Cb,
                          position, drop_mask, xbuf, s);
     swl::prof_mark(P, s, "gemm1_relu");
     swl::launch_expert_gemm(bf16, true, xbuf, Cb * d, L->W_in, (int64_t)F * d, hbuf, Cb * F,
@@ -238,7 +247,7 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
     swl::launch_expert_gemm(bf16, false, hbuf, Cb * F, L->W_out, (int64_t)d * F, ybuf, Cb * d,
                             r.nkept, N, Cb, F, d, s);
     swl::prof_mark(P, s, "combine");
-    swl::launch_combine(x, bf16, T, (int)(es * d), expert_idx, position, drop_mask, gate, Cb,
+    swl::launch_combine(x, bf16, T, k, (int)(es * d), expert_idx, position, drop_mask, gate, Cb,
                         ybuf, out, s);
     if (expert_out) {
       swl::prof_mark(P, s, "copy_expert_rows");
@@ -259,8 +268,8 @@ switch_status route_impl(switch_layer* L, const void* x, const float* given_logi
                              (char*)ws, lo, s);
   if (T > 0) {
     swl::prof_mark(&L->prof, s, "finalize");
-    swl::launch_finalize_positions(T, expert_idx, r.rank, r.offsets, L->cfg.n_experts, r.chunk,
-                                   r.Cb, position, drop_mask, s);
+    swl::launch_finalize_positions(T, top_k(L->cfg), expert_idx, r.rank, r.offsets,
+                                   L->cfg.n_experts, r.chunk, r.Cb, position, drop_mask, s);
   }
   swl::prof_end(&L->prof, s);
   return hipGetLastError() == hipSuccess ? SWITCH_OK : SWITCH_E_HIP;
@@ -281,6 +290,8 @@ switch_status switch_layer_create(const switch_config* cfg, const float* W_r, co
   if (c.t_max < 0 || c.t_max > 0x7fffffff) return SWITCH_E_INVALID;
   if (!(c.capacity_factor >= 0.0) || !isfinite(c.capacity_factor)) return SWITCH_E_INVALID;
   if (c.capacity_override < 0 || !isfinite(c.alpha)) return SWITCH_E_INVALID;
+  const int k = c.top_k == 0 ? 1 : c.top_k;
+  if (k < 1 || k > swl::kMaxTopK || k > c.n_experts) return SWITCH_E_INVALID;
   if ((c.act_dtype != SWITCH_F32 && c.act_dtype != SWITCH_BF16) ||
       (c.expert_dtype != SWITCH_F32 && c.expert_dtype != SWITCH_BF16))
     return SWITCH_E_INVALID;
@@ -295,6 +306,7 @@ switch_status switch_layer_create(const switch_config* cfg, const float* W_r, co
   switch_layer* L = new (std::nothrow) switch_layer();
   if (!L) return SWITCH_E_INVALID;
   L->cfg = c;
+  L->cfg.top_k = k;
   L->W_r = W_r;
   L->b_r = b_r;
   L->W_in = W_in;

@@ -55,6 +55,9 @@ def test_null_and_invalid_arguments_are_rejected_without_a_gpu():
     assert create(act_dtype=7) == B.SWITCH_E_INVALID
     assert create(expert_dtype=B.SWITCH_F32) == B.SWITCH_E_UNSUPPORTED
     assert create(d_model=136) == B.SWITCH_E_UNSUPPORTED        # bf16 tiles need multiples of 128
+    assert create(top_k=3) == B.SWITCH_E_INVALID                 # one or two experts per token
+    assert create(top_k=-1) == B.SWITCH_E_INVALID
+    assert create(top_k=2, n_experts=1) == B.SWITCH_E_INVALID    # k <= N
     cfg = B.switch_config(**ok)
     assert B.lib.switch_layer_create(ctypes.byref(cfg), None, None, fake, fake,
                                      ctypes.byref(h)) == B.SWITCH_E_INVALID
