@@ -39,8 +39,9 @@ PEAK_HBM_GBS = 8000.0
 DEVICE_WEIGHTS = {4, 5}
 
 
-def stage_work(stage: str, spec, kept: int, active_experts: int) -> dict:
-    """Algorithmic FLOPs and HBM bytes one launch of a stage must do."""
+def stage_work(stage: str, spec, kept: int, active_experts: int, k: int = 1) -> dict:
+    """Algorithmic FLOPs and HBM bytes one launch of a stage must do (kept counts
+    assignments: tokens at top-1, token-expert pairs at top-2)."""
     T, d, F, N = spec.T, spec.d, spec.F, spec.N
     es = 2 if spec.act == "bf16" else 4
     if stage in ("router", "router_logits"):
@@ -64,11 +65,12 @@ def stage_work(stage: str, spec, kept: int, active_experts: int) -> dict:
                     peak_tflops=peak)
     if stage == "dispatch":
         if spec.act == "bf16":
-            # slot table only (the rows stay in place); dropped rows copied to out
-            return dict(flops=0.0, bytes=2 * (T - kept) * d * es + 21 * T, peak_tflops=None)
-        return dict(flops=0.0, bytes=2 * kept * d * es + 9 * T, peak_tflops=None)
+            # slot table only (the rows stay in place); at top-1 dropped rows copied to out
+            rows = 2 * (T - kept) * d * es if k == 1 else 0
+            return dict(flops=0.0, bytes=rows + (13 * k + 8) * T, peak_tflops=None)
+        return dict(flops=0.0, bytes=2 * kept * d * es + (13 * k + 8) * T, peak_tflops=None)
     if stage == "combine":
-        return dict(flops=0.0, bytes=(kept + 2 * T) * d * es + 13 * T, peak_tflops=None)
+        return dict(flops=0.0, bytes=(kept + 2 * T) * d * es + 13 * k * T, peak_tflops=None)
     if stage == "route_rows":
         return dict(flops=0.0, bytes=T * N * 4 + 8 * T, peak_tflops=None)
     return dict(flops=0.0, bytes=0, peak_tflops=None)
@@ -131,7 +133,7 @@ def measured_traffic(stage: str, workload: str):
     return None
 
 
-def cpu_baseline(spec, host, budget_s: float) -> dict:
+def cpu_baseline(spec, host, budget_s: float, top_k: int = 1) -> dict:
     """The oracle as it stands on the host cores, over a bounded sample."""
     import oracle
     nt = oracle.threads()
@@ -142,8 +144,15 @@ def cpu_baseline(spec, host, budget_s: float) -> dict:
         W_out = S.to_f32(host["W_out"], spec.expert)
         reps, t0 = 0, time.perf_counter()
         while True:
-            oracle.forward(xf, host["W_r"], host["b_r"], W_in, W_out, spec.c,
-                           spec.capacity_override, spec.alpha, nthreads=nt)
+            if top_k == 1:
+                oracle.forward(xf, host["W_r"], host["b_r"], W_in, W_out, spec.c,
+                               spec.capacity_override, spec.alpha, nthreads=nt)
+            else:
+                h = oracle.logits(xf, host["W_r"], host["b_r"], nthreads=nt)
+                r = oracle.route_topk(h, top_k, spec.c, spec.capacity_override, spec.alpha,
+                                      nthreads=nt)
+                oracle.combine_topk(xf, r["expert_idx"], r["gate"], r["drop"], W_in, W_out,
+                                    nthreads=nt)
             reps += 1
             el = time.perf_counter() - t0
             if el >= budget_s:
@@ -158,20 +167,21 @@ def cpu_baseline(spec, host, budget_s: float) -> dict:
     xf = S.to_f32(host["x"][:n_r], spec.act)
     t0 = time.perf_counter()
     h = oracle.logits(xf, host["W_r"], host["b_r"], nthreads=nt)
-    r = oracle.route(h, spec.c, spec.capacity_override, spec.alpha, nthreads=nt)
+    r = oracle.route_topk(h, top_k, spec.c, spec.capacity_override, spec.alpha, nthreads=nt)
     t_route = time.perf_counter() - t0
     del h
     n, t_ffn = 0, 0.0
     cache = {}
     t1 = time.perf_counter()
     while t_ffn < budget_s and n < n_r:
-        e = int(r["expert_idx"][n])
-        if e not in cache:
-            tg = time.perf_counter()
-            cache = {e: (S.to_f32(S.expert_slice(spec, S.TENSOR_WIN, e), spec.expert),
-                         S.to_f32(S.expert_slice(spec, S.TENSOR_WOUT, e), spec.expert))}
-            t1 += time.perf_counter() - tg   # weight regeneration is not oracle work
-        oracle.token_output(xf[n], r["drop"][n], r["gate"][n], *cache[e])
+        for j in range(top_k):   # one expert FFN per choice of the token
+            e = int(r["expert_idx"][n, j])
+            if e not in cache:
+                tg = time.perf_counter()
+                cache = {e: (S.to_f32(S.expert_slice(spec, S.TENSOR_WIN, e), spec.expert),
+                             S.to_f32(S.expert_slice(spec, S.TENSOR_WOUT, e), spec.expert))}
+                t1 += time.perf_counter() - tg   # weight regeneration is not oracle work
+            oracle.token_output(xf[n], r["drop"][n, j], r["gate"][n, j], *cache[e])
         n += 1
         t_ffn = time.perf_counter() - t1
     per_token = t_route / n_r + t_ffn / n
@@ -182,7 +192,7 @@ def cpu_baseline(spec, host, budget_s: float) -> dict:
                       f"tokens ({t_ffn:.1f} s, 1 thread); rate = 1 / per-token time"}
 
 
-def build_layer(spec, B, torch, dev):
+def build_layer(spec, B, torch, dev, top_k: int = 1):
     if spec_id_of(spec) in DEVICE_WEIGHTS:
         host = S.host_inputs(spec, with_experts=False)
         per = spec.N * spec.F * spec.d
@@ -194,10 +204,10 @@ def build_layer(spec, B, torch, dev):
         b_r = None if host["b_r"] is None else torch.from_numpy(host["b_r"]).to(dev)
         cfg = B.switch_config(t_max=spec.T, d_model=spec.d, d_ff=spec.F, n_experts=spec.N,
                               capacity_factor=spec.c, capacity_override=0, alpha=spec.alpha,
-                              act_dtype=B.SWITCH_BF16, expert_dtype=B.SWITCH_BF16)
+                              act_dtype=B.SWITCH_BF16, expert_dtype=B.SWITCH_BF16, top_k=top_k)
         return host, B.SwitchLayer(cfg, W_r, b_r, W_in, W_out)
     host = S.host_inputs(spec)
-    return host, B.SwitchLayer.from_host(spec, host, device=dev)
+    return host, B.SwitchLayer.from_host(spec, host, device=dev, top_k=top_k)
 
 
 def spec_id_of(spec) -> int:
@@ -215,6 +225,9 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=sorted(S.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--top-k", type=int, default=1, choices=(1, 2),
+                    help="experts per token: 1 is the Switch layer (the headline); 2 times the "
+                         "top-2 routing variant on the same workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, run one device-to-device copy of 1 GiB "
                          "(reference for hardware byte counters)")
@@ -231,7 +244,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     spec = S.CONFIGS[args.config]
-    host, layer = build_layer(spec, B, torch, dev)
+    host, layer = build_layer(spec, B, torch, dev, args.top_k)
+    workload = spec.name if args.top_k == 1 else f"{spec.name}-top{args.top_k}"
     x = B.to_device(host["x"], dev)
     bufs = layer.alloc(spec.T)
     stream = torch.cuda.current_stream(dev)
@@ -270,17 +284,17 @@ def main():
 
     drop = B.from_device(bufs["drop_mask"])
     load = B.from_device(bufs["load"])
-    kept = int((drop == 0).sum())
+    kept = int((drop == 0).sum())          # kept assignments (tokens at top-1)
     C = B.switch_capacity(layer.handle, spec.T)
     active = int((np.minimum(load, C) > 0).sum())
 
-    rooflines = {k: roofline_entry(k, stage_work(k, spec, kept, active), v)
+    rooflines = {k: roofline_entry(k, stage_work(k, spec, kept, active, args.top_k), v)
                  for k, v in stage_ms.items()
                  if k in ("router", "router_logits", "gemm1_relu", "gemm2", "gemm2_combine",
                           "dispatch", "combine")}
     dominant = max(rooflines, key=lambda k: stage_ms[k])
     for k, r in rooflines.items():
-        r["traffic"] = measured_traffic(k, spec.name)
+        r["traffic"] = measured_traffic(k, workload)
     gemm_ms = (stage_ms.get("gemm1_relu", 0) + stage_ms.get("gemm2", 0)
                + stage_ms.get("gemm2_combine", 0))
     expert_tflops = 4.0 * kept * spec.d * spec.F / (gemm_ms * 1e-3) / 1e12 if gemm_ms else 0.0
@@ -298,13 +312,14 @@ def main():
         "vs_baseline": None,
         "dtype": spec.act,
         "data": "synthetic (seeded counter-based generator; random-init weights)",
-        "config": {"workload": spec.name, "T": spec.T, "d_model": spec.d, "d_ff": spec.F,
+        "config": {"workload": workload, "T": spec.T, "d_model": spec.d, "d_ff": spec.F,
                    "n_experts": spec.N, "capacity_factor": spec.c, "capacity": C,
                    "router": "fp32", "experts": spec.expert, "parallelism": "single-gpu"},
         "roofline": rooflines[dominant],
         "cpu_baseline": None,
-        "kept_tokens": kept,
-        "dropped_tokens": spec.T - kept,
+        "top_k": args.top_k,
+        "kept_assignments": kept,
+        "dropped_assignments": spec.T * args.top_k - kept,
         "expert_tflops": round(expert_tflops, 2),
         "expert_mfma_frac": round(expert_tflops / PEAK_BF16_TFLOPS, 4),
         "dispatch_hbm_frac": rooflines.get("dispatch", {}).get("frac"),
@@ -314,7 +329,7 @@ def main():
         "wall_s_timed_region": round(wall, 4),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(spec, host, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(spec, host, args.cpu_budget, args.top_k)
     print(json.dumps(result), flush=True)
 
 
