@@ -61,6 +61,10 @@ def lib():
         L.oracle_combine_topk.argtypes = [_f32p, _i32p, _f64p, _u8p, _f32p, _f32p, _i64, _i64,
                                           _i64, _i64, _f64p, _f64p, ctypes.c_int]
         L.oracle_combine_topk.restype = None
+        L.oracle_backward.argtypes = [_f32p, _f32p, _f32p, _f32p, _f64p, _i32p, _f64p, _u8p,
+                                      _i32p, _f64p, ctypes.c_double, ctypes.c_double, _i64, _i64,
+                                      _i64, _i64, _f64p, _f64p, _f64p, _f64p, _f64p, ctypes.c_int]
+        L.oracle_backward.restype = None
         _lib = L
     return _lib
 
@@ -170,4 +174,23 @@ def forward(x, W_r, b_r, W_in, W_out, c: float, capacity_override: int = 0, alph
     r = route(h, c, capacity_override, alpha, nthreads)
     out, E = combine(x, r["expert_idx"], r["gate"], r["drop"], W_in, W_out, nthreads)
     r.update(h=h, out=out, E=E)
+    return r
+
+
+def backward(x, W_r, W_in, W_out, h, expert_idx, gate, drop, load, G, g_aux: float = 0.0,
+             alpha: float = 0.01, nthreads: int = 0) -> dict:
+    """Gradients of the top-1 layer for dL/dout = G and dL/daux = g_aux, at the
+    forward's routing (expert_idx, gate, drop), logits h and loads."""
+    x = _c(x, np.float32)
+    T, d = x.shape
+    W_in = _c(W_in, np.float32)
+    W_out = _c(W_out, np.float32)
+    N, F = W_in.shape[0], W_in.shape[1]
+    r = dict(dx=np.empty((T, d)), dW_r=np.empty((N, d)), db=np.empty(N),
+             dW_in=np.empty((N, F, d)), dW_out=np.empty((N, d, F)))
+    lib().oracle_backward(x, _c(W_r, np.float32), W_in, W_out, _c(h, np.float64),
+                          _c(expert_idx, np.int32), _c(gate, np.float64), _c(drop, np.uint8),
+                          _c(load, np.int32), _c(G, np.float64), g_aux, alpha, T, d, F, N,
+                          r["dx"], r["dW_r"], r["db"], r["dW_in"], r["dW_out"],
+                          nthreads or threads())
     return r

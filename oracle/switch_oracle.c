@@ -389,3 +389,151 @@ void oracle_combine_topk(const float* x, const int32_t* expert_idx, const double
     free(E);
   }
 }
+
+/* ------------------------------------------------------------------------
+ * Backward pass of the top-1 layer: gradients of L with respect to x, W_r,
+ * b_r, W_in and W_out, given G = dL/dout [T, d] and g_aux = dL/daux.
+ *
+ * [KB "argmaxは離散なのに、Routerはなぜ学習できるのか"]: the chosen expert id
+ * is discrete and gives no gradient; the output keeps the continuous gate
+ * p_{i*}(x), through which the gradient reaches the softmax and W_r.  The
+ * capacity cut is piecewise constant as well.  [LP 3.3]: f_i is discrete and
+ * P_i continuous, so the loss reaches the router through P_i only.  The rest
+ * is the chain rule on the forward's definition:
+ *   kept t (expert e, gate g):  u = W_in[e] x, a = relu(u), E = W_out[e] a,
+ *     dE = g G_t, dg_t = G_t . E, du = (W_out[e]^T dE) * [u > 0],
+ *     dW_out[e] += dE a^T,  dW_in[e] += du x_t^T,  dx_t += W_in[e]^T du;
+ *   every t:  p = softmax(h_t),
+ *     dp_i = [i = e_t and kept] dg_t + g_aux alpha N f_i / T   (f_i = load_i / T),
+ *     dh = p * (dp - p . dp),  dW_r += dh x_t^T,  db += dh,  dx_t += W_r^T dh,
+ *     dx_t += G_t (the residual).
+ * The routing (expert_idx, gate, drop), the logits h and load are the
+ * forward's.  Sums over tokens run in token order; OpenMP splits tokens or
+ * experts.  db may be NULL.
+ * ------------------------------------------------------------------------ */
+void oracle_backward(const float* x, const float* W_r, const float* W_in, const float* W_out,
+                     const double* h, const int32_t* expert_idx, const double* gate,
+                     const uint8_t* drop, const int32_t* load, const double* G, double g_aux,
+                     double alpha, int64_t T, int64_t d, int64_t F, int64_t N, double* dx,
+                     double* dW_r, double* db, double* dW_in, double* dW_out, int nthreads) {
+  double* dg = (double*)calloc((size_t)(T > 0 ? T : 1), sizeof(double));
+  double* dh = (double*)calloc((size_t)(T > 0 ? T : 1) * (size_t)N, sizeof(double));
+
+  /* expert path of dx and dg, per token */
+#pragma omp parallel for schedule(dynamic, 4) num_threads(NT(nthreads))
+  for (int64_t t = 0; t < T; ++t) {
+    const float* xt = x + t * d;
+    const double* Gt = G + t * d;
+    for (int64_t k = 0; k < d; ++k) dx[t * d + k] = Gt[k];
+    if (drop[t]) continue;
+    const int64_t e = expert_idx[t];
+    const float* Wi = W_in + e * F * d;
+    const float* Wo = W_out + e * d * F;
+    double* u = (double*)malloc(sizeof(double) * (size_t)F);
+    double* du = (double*)malloc(sizeof(double) * (size_t)F);
+    for (int64_t j = 0; j < F; ++j) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < d; ++k) acc += (double)Wi[j * d + k] * (double)xt[k];
+      u[j] = acc;
+    }
+    double s = 0.0;  /* dg = G . E, E_i = sum_j Wo[i, j] relu(u_j) */
+    for (int64_t i = 0; i < d; ++i) {
+      double E = 0.0;
+      for (int64_t j = 0; j < F; ++j) E += (double)Wo[i * F + j] * (u[j] > 0.0 ? u[j] : 0.0);
+      s += Gt[i] * E;
+    }
+    dg[t] = s;
+    for (int64_t j = 0; j < F; ++j) {
+      double acc = 0.0;
+      if (u[j] > 0.0)
+        for (int64_t i = 0; i < d; ++i) acc += (double)Wo[i * F + j] * gate[t] * Gt[i];
+      du[j] = acc;
+    }
+    for (int64_t k = 0; k < d; ++k) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < F; ++j) acc += (double)Wi[j * d + k] * du[j];
+      dx[t * d + k] += acc;
+    }
+    free(u);
+    free(du);
+  }
+
+  /* router path: softmax Jacobian on each token's logits */
+#pragma omp parallel for schedule(static) num_threads(NT(nthreads))
+  for (int64_t t = 0; t < T; ++t) {
+    const double* ht = h + t * N;
+    double m = ht[0];
+    for (int64_t i = 1; i < N; ++i) m = ht[i] > m ? ht[i] : m;
+    double S = 0.0;
+    for (int64_t i = 0; i < N; ++i) S += exp(ht[i] - m);
+    double pdp = 0.0;
+    for (int64_t i = 0; i < N; ++i) {
+      const double p = exp(ht[i] - m) / S;
+      double dp = g_aux * alpha * (double)N * ((double)load[i] / (double)T) / (double)T;
+      if (i == expert_idx[t] && !drop[t]) dp += dg[t];
+      dh[t * N + i] = dp;       /* dp for now */
+      pdp += p * dp;
+    }
+    for (int64_t i = 0; i < N; ++i) {
+      const double p = exp(ht[i] - m) / S;
+      dh[t * N + i] = p * (dh[t * N + i] - pdp);
+    }
+    for (int64_t k = 0; k < d; ++k) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < N; ++i) acc += (double)W_r[i * d + k] * dh[t * N + i];
+      dx[t * d + k] += acc;
+    }
+  }
+
+  /* router weight and bias gradients: sums over tokens, per expert row */
+#pragma omp parallel for schedule(static) num_threads(NT(nthreads))
+  for (int64_t i = 0; i < N; ++i) {
+    double bsum = 0.0;
+    for (int64_t k = 0; k < d; ++k) dW_r[i * d + k] = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      const double v = dh[t * N + i];
+      bsum += v;
+      for (int64_t k = 0; k < d; ++k) dW_r[i * d + k] += v * (double)x[t * d + k];
+    }
+    if (db) db[i] = bsum;
+  }
+
+  /* expert weight gradients: per expert, its kept tokens in token order */
+#pragma omp parallel for schedule(dynamic, 1) num_threads(NT(nthreads))
+  for (int64_t e = 0; e < N; ++e) {
+    const float* Wi = W_in + e * F * d;
+    const float* Wo = W_out + e * d * F;
+    double* gWi = dW_in + e * F * d;
+    double* gWo = dW_out + e * d * F;
+    for (int64_t q = 0; q < F * d; ++q) gWi[q] = 0.0;
+    for (int64_t q = 0; q < d * F; ++q) gWo[q] = 0.0;
+    double* u = (double*)malloc(sizeof(double) * (size_t)F);
+    double* du = (double*)malloc(sizeof(double) * (size_t)F);
+    for (int64_t t = 0; t < T; ++t) {
+      if (drop[t] || expert_idx[t] != e) continue;
+      const float* xt = x + t * d;
+      const double* Gt = G + t * d;
+      for (int64_t j = 0; j < F; ++j) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < d; ++k) acc += (double)Wi[j * d + k] * (double)xt[k];
+        u[j] = acc;
+      }
+      for (int64_t j = 0; j < F; ++j) {
+        double acc = 0.0;
+        if (u[j] > 0.0)
+          for (int64_t i = 0; i < d; ++i) acc += (double)Wo[i * F + j] * gate[t] * Gt[i];
+        du[j] = acc;
+      }
+      for (int64_t i = 0; i < d; ++i) {
+        const double dE = gate[t] * Gt[i];
+        for (int64_t j = 0; j < F; ++j) gWo[i * F + j] += dE * (u[j] > 0.0 ? u[j] : 0.0);
+      }
+      for (int64_t j = 0; j < F; ++j)
+        for (int64_t k = 0; k < d; ++k) gWi[j * d + k] += du[j] * (double)xt[k];
+    }
+    free(u);
+    free(du);
+  }
+  free(dg);
+  free(dh);
+}
