@@ -149,6 +149,45 @@ switch_status switch_forward(switch_layer* layer, const void* x, int64_t T, void
                              void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Backward pass of the top-1 layer (bf16 layers): gradients of a loss L given
+ * grad_out = dL/dout and grad_aux = dL/daux_loss, at the routing of a forward
+ * call on the same x.  The expert choice and the capacity cut carry no
+ * gradient; the router learns through the gate p_{i*}(x) that scales the
+ * chosen expert's output (kasblo "Switch Transformerとは？", section
+ * "argmaxは離散なのに、Routerはなぜ学習できるのか") and through P_i of the
+ * load-balancing loss (llm-papers-study section 3.3: f_i is a count, P_i is
+ * differentiable):
+ *   kept t:  dE = gate_t grad_out_t,  dgate_t = grad_out_t . E_t,
+ *            dW_out[e] += dE relu(u)^T,  du = (W_out[e]^T dE) * [u > 0],
+ *            dW_in[e] += du x_t^T,  dx_t += W_in[e]^T du;
+ *   all t:   dp_i = [i = e_t, kept] dgate_t + grad_aux alpha N load_i / T^2,
+ *            dh = p * (dp - p . dp),  dW_r += dh x_t^T,  db += dh,
+ *            dx_t += grad_out_t + W_r^T dh.
+ *   x, grad_out   [T, d] bf16 (grad_x must overlap neither)
+ *   logits [T, N] fp32, expert_idx, gate, position, drop_mask [T], load [N]:
+ *                 the outputs of switch_forward / switch_route for this x
+ *   grad_x        [T, d] bf16 out
+ *   grad_W_r      [N, d] fp32 out;  grad_b_r [N] fp32 out, or NULL
+ *   grad_W_in     [N, F, d] bf16 out;  grad_W_out [N, d, F] bf16 out
+ *   ws, ws_bytes  device workspace of at least switch_backward_workspace_bytes(T)
+ * Weight gradients are fp32 sums over the expert's tokens rounded once to bf16;
+ * grad_x is summed in fp32 and rounded once.  Every output is written (zeros
+ * where nothing contributes).  SWITCH_E_UNSUPPORTED for fp32 layers or
+ * top_k = 2.  The expert activations are recomputed (nothing is kept from the
+ * forward call besides its listed outputs).
+ */
+switch_status switch_backward(switch_layer* layer, const void* x, int64_t T, const void* grad_out,
+                              float grad_aux, const float* logits, const int32_t* expert_idx,
+                              const float* gate, const int32_t* position,
+                              const uint8_t* drop_mask, const int32_t* load, void* grad_x,
+                              float* grad_W_r, float* grad_b_r, void* grad_W_in,
+                              void* grad_W_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace a switch_backward call with T tokens needs (0 on a
+ * NULL handle or T outside [0, t_max]). */
+size_t switch_backward_workspace_bytes(const switch_layer* layer, int64_t T);
+
+/*
  * Test hook: the routing stage from given fp32 logits [T, N] (device), with the
  * same outputs as switch_route minus the logits.  -inf logits are allowed
  * (probability 0); NaN is not.

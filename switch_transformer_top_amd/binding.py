@@ -22,7 +22,8 @@ SWITCH_F32, SWITCH_BF16 = 0, 1
 EXPORTS = ("switch_layer_create", "switch_layer_destroy", "switch_capacity",
            "switch_workspace_bytes", "switch_route", "switch_forward",
            "switch_route_from_logits", "switch_forward_debug", "switch_profile_enable",
-           "switch_profile_read", "switch_status_string", "switch_last_async_error")
+           "switch_profile_read", "switch_status_string", "switch_last_async_error",
+           "switch_backward", "switch_backward_workspace_bytes")
 
 
 class switch_config(ctypes.Structure):
@@ -64,6 +65,11 @@ lib.switch_route_from_logits.restype = ctypes.c_int
 lib.switch_forward_debug.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _sz, _vp, _vp]
 lib.switch_forward_debug.restype = ctypes.c_int
+lib.switch_backward.argtypes = [_vp, _vp, _i64, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+lib.switch_backward.restype = ctypes.c_int
+lib.switch_backward_workspace_bytes.argtypes = [_vp, _i64]
+lib.switch_backward_workspace_bytes.restype = _sz
 lib.switch_profile_enable.argtypes = [_vp, ctypes.c_int]
 lib.switch_profile_enable.restype = ctypes.c_int
 lib.switch_profile_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_float),
@@ -142,6 +148,19 @@ def switch_forward_debug(handle, x, T, out, expert_idx, gate, position, drop_mas
                                     _ptr(expert_out), stream)
 
 
+def switch_backward(handle, x, T, grad_out, grad_aux, logits, expert_idx, gate, position,
+                    drop_mask, load, grad_x, grad_W_r, grad_b_r, grad_W_in, grad_W_out, ws,
+                    ws_bytes, stream=0) -> int:
+    return lib.switch_backward(handle, _ptr(x), T, _ptr(grad_out), float(grad_aux), _ptr(logits),
+                               _ptr(expert_idx), _ptr(gate), _ptr(position), _ptr(drop_mask),
+                               _ptr(load), _ptr(grad_x), _ptr(grad_W_r), _ptr(grad_b_r),
+                               _ptr(grad_W_in), _ptr(grad_W_out), _ptr(ws), ws_bytes, stream)
+
+
+def switch_backward_workspace_bytes(handle: int, T: int) -> int:
+    return lib.switch_backward_workspace_bytes(handle, T)
+
+
 def switch_profile_enable(handle: int, max_calls: int) -> None:
     _check(lib.switch_profile_enable(handle, int(max_calls)), "switch_profile_enable")
 
@@ -179,7 +198,10 @@ class SwitchLayer:
     def __del__(self):
         h = getattr(self, "handle", None)
         if h:
-            switch_layer_destroy(h)
+            try:
+                switch_layer_destroy(h)
+            except TypeError:   # interpreter shutdown: the module is already torn down
+                pass
             self.handle = None
 
     # -- construction from the synthetic generator's host arrays
@@ -245,6 +267,31 @@ class SwitchLayer:
         _check(switch_route_from_logits(self.handle, logits, T, b["expert_idx"], b["gate"],
                                         b["position"], b["drop_mask"], b["aux_loss"], b["load"],
                                         b["ws"], b["ws_bytes"], stream), "switch_route_from_logits")
+
+    def alloc_backward(self, T: int) -> dict:
+        """Gradient outputs and the backward workspace (device tensors)."""
+        torch = self.torch
+        dev = self.device
+        N, d, F = self.cfg.n_experts, self.cfg.d_model, self.cfg.d_ff
+        nbytes = switch_backward_workspace_bytes(self.handle, T)
+        return dict(
+            grad_x=torch.empty((T, d), dtype=torch.int16, device=dev),
+            grad_W_r=torch.empty((N, d), dtype=torch.float32, device=dev),
+            grad_b_r=torch.empty(N, dtype=torch.float32, device=dev),
+            grad_W_in=torch.empty((N, F, d), dtype=torch.int16, device=dev),
+            grad_W_out=torch.empty((N, d, F), dtype=torch.int16, device=dev),
+            ws=torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev), ws_bytes=nbytes)
+
+    def backward(self, x, T: int, grad_out, grad_aux: float, fwd: dict, grads: dict,
+                 stream: int = 0):
+        """Gradients at the routing of a forward call whose outputs are in fwd (logits
+        included)."""
+        g = grads
+        _check(switch_backward(self.handle, x, T, grad_out, grad_aux, fwd["logits"],
+                               fwd["expert_idx"], fwd["gate"], fwd["position"], fwd["drop_mask"],
+                               fwd["load"], g["grad_x"], g["grad_W_r"], g["grad_b_r"],
+                               g["grad_W_in"], g["grad_W_out"], g["ws"], g["ws_bytes"], stream),
+               "switch_backward")
 
     def forward_host(self, x_host: np.ndarray, debug: bool = False) -> dict:
         """Upload x, run the layer on the current stream, download every output."""

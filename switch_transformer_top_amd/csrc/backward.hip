@@ -1,0 +1,307 @@
+// Backward pass of the top-1 Switch layer: the kernels around the grouped
+// matmuls.
+//
+// The expert choice and the capacity cut are piecewise constant and carry no
+// gradient; the gradient reaches the router through the continuous gate
+// p_{i*}(x) that scales the chosen expert's output (kasblo explainer, section
+// "argmaxは離散なのに、Routerはなぜ学習できるのか"), and through P_i of the
+// load-balancing loss, f_i being a count (llm-papers-study close reading,
+// section 3.3).  With G = dL/dout and g_aux = dL/daux:
+//   kept t (expert e, slot p, gate g):  Gs[e, p] = g G_t,
+//     dU = (Gs W_out[e]) * [H > 0],  dX[e, p] = dU W_in[e],
+//     dW_out[e] = Gs^T H,  dW_in[e] = dU^T X  (sums over the expert's rows),
+//     dg_t = G_t . Y[e, p];
+//   every t:  dp_i = [i = e_t, kept] dg_t + g_aux alpha N load_i / T^2,
+//     dh = p * (dp - p . dp),  dW_r = dh^T x,  db = sum_t dh,
+//     dx_t = G_t + dX[e_t, p_t] + W_r^T dh_t.
+// The matmuls are the grouped bf16 kernels of gemm.hip (fp32 accumulation);
+// this file holds the slot/scale pass, the transposes that put their K
+// dimension innermost, the router backward and the assembly of dx.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace swl {
+
+// n_kept[e] = min(load[e], C) (the forward's per-expert loads).
+__global__ __launch_bounds__(256) void bwd_rows_kernel(const int32_t* __restrict__ load, int N,
+                                                       int64_t C, int32_t* __restrict__ n_kept) {
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < N; e += gridDim.x * blockDim.x)
+    n_kept[e] = (int32_t)((int64_t)load[e] < C ? (int64_t)load[e] : C);
+}
+
+// Slot table and scaled output gradient of every kept token:
+// tok[e * C + p] = t and Gs[e, p, :] = bf16(gate_t * G_t) (fp32 product,
+// rounded to nearest even).  One thread per 16-byte piece of a row.
+__global__ __launch_bounds__(256) void bwd_slots_kernel(const u32x4* __restrict__ G, int64_t T,
+                                                        int row_vec16,
+                                                        const int32_t* __restrict__ expert_idx,
+                                                        const int32_t* __restrict__ position,
+                                                        const uint8_t* __restrict__ drop_mask,
+                                                        const float* __restrict__ gate, int64_t C,
+                                                        int32_t* __restrict__ tok,
+                                                        u32x4* __restrict__ Gs) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t = gid / row_vec16;
+  const int c = (int)(gid - t * row_vec16);
+  if (t >= T || drop_mask[t]) return;
+  const int64_t slot = (int64_t)expert_idx[t] * C + position[t];
+  if (c == 0) tok[slot] = (int32_t)t;
+  const float g = gate[t];
+  const u32x4 v = G[t * row_vec16 + c];
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = f32x2_to_bf16x2_bits(g * __uint_as_float(v[i] << 16),
+                                g * __uint_as_float(v[i] & 0xFFFF0000u));
+  Gs[slot * row_vec16 + c] = o;
+}
+
+// Per-expert transpose of a bf16 matrix block src[e] [R, Ccols] (row stride
+// ld) into dst[e] [Ccols, Rpad]: dst[c][r] = src[r][c] for r < rows_e, 0 for
+// rows_e <= r < Rpad.  rows_e = valid[e], or R when valid is NULL.  With tok,
+// row r of expert e is row tok[e * R + r] of src (a gathered row of x).
+// 64 x 64 tiles through LDS (padded rows); grid (ceil(Ccols / 64), Rpad / 64, N).
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src,
+                                                        int64_t src_estride, int ld, int R,
+                                                        int Ccols,
+                                                        const int32_t* __restrict__ valid,
+                                                        const int32_t* __restrict__ tok,
+                                                        uint16_t* __restrict__ dst,
+                                                        int64_t dst_estride, int Rpad) {
+  __shared__ uint16_t tile[64][66];
+  const int e = blockIdx.z;
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int rows_e = valid ? valid[e] : R;
+  const uint16_t* se = src + (tok ? 0 : (int64_t)e * src_estride);
+  const int32_t* te = tok ? tok + (int64_t)e * R : nullptr;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    uint16_t v = 0;
+    if (r < rows_e && c < Ccols) {
+      const int64_t row = te ? (int64_t)te[r] : (int64_t)r;
+      v = se[row * ld + c];
+    }
+    tile[i][tx] = v;
+  }
+  __syncthreads();
+  uint16_t* de = dst + (int64_t)e * dst_estride;
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < Ccols && r < Rpad) de[(int64_t)c * Rpad + r] = tile[tx][i];
+  }
+}
+
+// Router backward, one wave per token: dg = G_t . Y[e, p] (kept tokens),
+// p = softmax(h_t) (fp32 exponentials, fp64 sums as in the forward), dp, and
+// dh_t = p * (dp - p . dp) written to dh [T, N] (fp32).
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ h, int64_t T,
+                                                         int N, int d,
+                                                         const uint16_t* __restrict__ G,
+                                                         const uint16_t* __restrict__ Ybuf,
+                                                         int64_t C,
+                                                         const int32_t* __restrict__ expert_idx,
+                                                         const int32_t* __restrict__ position,
+                                                         const uint8_t* __restrict__ drop_mask,
+                                                         const int32_t* __restrict__ load,
+                                                         float loss_scale,
+                                                         float* __restrict__ dh) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int e = expert_idx[t];
+  const bool kept = drop_mask[t] == 0;
+  double dg = 0.0;
+  if (kept) {
+    const uint16_t* gt = G + t * d;
+    const uint16_t* yt = Ybuf + ((int64_t)e * C + position[t]) * d;
+    for (int k = lane; k < d; k += kWave) dg += (double)bf16_bits_to_f32(gt[k]) * bf16_bits_to_f32(yt[k]);
+    dg = wave_sum_f64(dg);
+  }
+  const float* ht = h + t * N;
+  float m = -__builtin_huge_valf();
+  for (int i = lane; i < N; i += kWave) m = fmaxf(m, ht[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  double S = 0.0;
+  for (int i = lane; i < N; i += kWave) S += (double)expf(ht[i] - m);
+  S = wave_sum_f64(S);
+  const double inv = 1.0 / S;
+  // dp_i = [i = e, kept] dg + loss_scale * load_i, loss_scale = g_aux alpha N / T^2
+  double pdp = 0.0;
+  for (int i = lane; i < N; i += kWave) {
+    const double p = (double)expf(ht[i] - m) * inv;
+    double dp = (double)loss_scale * (double)load[i];
+    if (kept && i == e) dp += dg;
+    pdp += p * dp;
+  }
+  pdp = wave_sum_f64(pdp);
+  for (int i = lane; i < N; i += kWave) {
+    const double p = (double)expf(ht[i] - m) * inv;
+    double dp = (double)loss_scale * (double)load[i];
+    if (kept && i == e) dp += dg;
+    dh[t * N + i] = (float)(p * (dp - pdp));
+  }
+}
+
+// dW_r[i, k] = sum_t dh[t, i] x[t, k] and db[i] = sum_t dh[t, i] (fp32, token
+// order).  Block: 64 experts x 64 columns, 256 threads each 4 x 4 outputs; T
+// in chunks of 32 tokens through LDS.
+__global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restrict__ dh,
+                                                           const uint16_t* __restrict__ x,
+                                                           int64_t T, int N, int d,
+                                                           float* __restrict__ dW_r,
+                                                           float* __restrict__ db) {
+  __shared__ float Ds[32][68];
+  __shared__ float Xs[32][68];
+  const int i0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4] = {};
+  float bacc = 0.f;
+  for (int64_t t0 = 0; t0 < T; t0 += 32) {
+    for (int idx = threadIdx.x; idx < 32 * 64; idx += 256) {
+      const int r = idx >> 6, c = idx & 63;
+      const int64_t t = t0 + r;
+      Ds[r][c] = (t < T && i0 + c < N) ? dh[t * N + i0 + c] : 0.f;
+      Xs[r][c] = (t < T && k0 + c < d) ? bf16_bits_to_f32(x[t * d + k0 + c]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+      float a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { a[q] = Ds[r][ty + 16 * q]; b[q] = Xs[r][tx + 16 * q]; }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[q][w] = fmaf(a[q], b[w], acc[q][w]);
+      if (blockIdx.x == 0 && threadIdx.x < 64) bacc += Ds[r][threadIdx.x];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int i = i0 + ty + 16 * q, k = k0 + tx + 16 * w;
+      if (i < N && k < d) dW_r[(int64_t)i * d + k] = acc[q][w];
+    }
+  if (db && blockIdx.x == 0 && threadIdx.x < 64 && i0 + threadIdx.x < N) db[i0 + threadIdx.x] = bacc;
+}
+
+// dx_t = G_t + dX[e_t, p_t] (kept) + sum_i dh[t, i] W_r[i, :], fp32 then one
+// rounding to bf16.  One thread per 16-byte piece (8 columns) of a row.
+__global__ __launch_bounds__(256) void grad_x_kernel(const u32x4* __restrict__ G, int64_t T,
+                                                     int row_vec16,
+                                                     const int32_t* __restrict__ expert_idx,
+                                                     const int32_t* __restrict__ position,
+                                                     const uint8_t* __restrict__ drop_mask,
+                                                     int64_t C, const u32x4* __restrict__ dXe,
+                                                     const float* __restrict__ dh,
+                                                     const float* __restrict__ W_r, int N,
+                                                     u32x4* __restrict__ dx) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t = gid / row_vec16;
+  const int c = (int)(gid - t * row_vec16);
+  if (t >= T) return;
+  const int d = row_vec16 * 8;
+  float acc[8];
+  const u32x4 gv = G[t * row_vec16 + c];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] = __uint_as_float(gv[i] << 16);
+    acc[2 * i + 1] = __uint_as_float(gv[i] & 0xFFFF0000u);
+  }
+  if (!drop_mask[t]) {
+    const u32x4 v = dXe[((int64_t)expert_idx[t] * C + position[t]) * row_vec16 + c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += __uint_as_float(v[i] << 16);
+      acc[2 * i + 1] += __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+  }
+  const float* dht = dh + t * N;
+  for (int i = 0; i < N; ++i) {
+    const float g = dht[i];
+    const float4 w0 = *reinterpret_cast<const float4*>(W_r + (int64_t)i * d + c * 8);
+    const float4 w1 = *reinterpret_cast<const float4*>(W_r + (int64_t)i * d + c * 8 + 4);
+    acc[0] = fmaf(g, w0.x, acc[0]); acc[1] = fmaf(g, w0.y, acc[1]);
+    acc[2] = fmaf(g, w0.z, acc[2]); acc[3] = fmaf(g, w0.w, acc[3]);
+    acc[4] = fmaf(g, w1.x, acc[4]); acc[5] = fmaf(g, w1.y, acc[5]);
+    acc[6] = fmaf(g, w1.z, acc[6]); acc[7] = fmaf(g, w1.w, acc[7]);
+  }
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x2_to_bf16x2_bits(acc[2 * i], acc[2 * i + 1]);
+  dx[t * row_vec16 + c] = o;
+}
+
+// Zero fill (16-byte stores; bytes a multiple of 16).
+__global__ __launch_bounds__(256) void fill_zero_kernel(u32x4* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// ------------------------------------------------------------------ launchers
+
+void launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 16);
+  if (n == 0) return;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
+                     0, s, (u32x4*)p, n);
+}
+
+void launch_bwd_rows(const int32_t* load, int N, int64_t C, int32_t* n_kept, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, load, N,
+                     C, n_kept);
+}
+
+void launch_bwd_slots(const void* G, int64_t T, int d, const int32_t* expert_idx,
+                      const int32_t* position, const uint8_t* drop_mask, const float* gate,
+                      int64_t C, int32_t* tok, void* Gs, hipStream_t s) {
+  if (T == 0) return;
+  const int rv = d / 8;
+  hipLaunchKernelGGL(bwd_slots_kernel, dim3((unsigned)((T * rv + 255) / 256)), dim3(256), 0, s,
+                     (const u32x4*)G, T, rv, expert_idx, position, drop_mask, gate, C, tok,
+                     (u32x4*)Gs);
+}
+
+void launch_transpose(const void* src, int64_t src_estride, int ld, int R, int Ccols,
+                      const int32_t* valid, const int32_t* tok, void* dst, int64_t dst_estride,
+                      int Rpad, int n_experts, hipStream_t s) {
+  if (Ccols == 0 || Rpad == 0 || n_experts == 0) return;
+  const dim3 grid((unsigned)((Ccols + 63) / 64), (unsigned)(Rpad / 64), (unsigned)n_experts);
+  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, (const uint16_t*)src, src_estride,
+                     ld, R, Ccols, valid, tok, (uint16_t*)dst, dst_estride, Rpad);
+}
+
+void launch_router_bwd(const float* h, int64_t T, int N, int d, const void* G, const void* Ybuf,
+                       int64_t C, const int32_t* expert_idx, const int32_t* position,
+                       const uint8_t* drop_mask, const int32_t* load, float loss_scale, float* dh,
+                       hipStream_t s) {
+  if (T == 0) return;
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, h, T, N,
+                     d, (const uint16_t*)G, (const uint16_t*)Ybuf, C, expert_idx, position,
+                     drop_mask, load, loss_scale, dh);
+}
+
+void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d, float* dW_r,
+                         float* db, hipStream_t s) {
+  const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((N + 63) / 64));
+  hipLaunchKernelGGL(router_wgrad_kernel, grid, dim3(256), 0, s, dh, (const uint16_t*)x, T, N, d,
+                     dW_r, db);
+}
+
+void launch_grad_x(const void* G, int64_t T, int d, const int32_t* expert_idx,
+                   const int32_t* position, const uint8_t* drop_mask, int64_t C, const void* dXe,
+                   const float* dh, const float* W_r, int N, void* dx, hipStream_t s) {
+  if (T == 0) return;
+  const int rv = d / 8;
+  hipLaunchKernelGGL(grad_x_kernel, dim3((unsigned)((T * rv + 255) / 256)), dim3(256), 0, s,
+                     (const u32x4*)G, T, rv, expert_idx, position, drop_mask, C,
+                     (const u32x4*)dXe, dh, W_r, N, (u32x4*)dx);
+}
+
+}  // namespace swl

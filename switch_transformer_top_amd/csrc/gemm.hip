@@ -31,10 +31,11 @@ constexpr int GB_LDK = GB_BK + GB_PAD;  // LDS row stride in bf16 elements (144 
 // accumulators goes through LDS (rows of TJ * 32 + 8 bf16, after the optional
 // ReLU and round-to-nearest-even) and then out in 16-byte row pieces, instead
 // of one 2-byte store per accumulator.  Rows at or past rows_e are not stored.
-template <int TI, int TJ, bool RELU>
+template <int TI, int TJ, bool RELU, bool MASK = false>
 __device__ __forceinline__ void store_tile_bf16(const floatx16 (&acc)[TI][TJ], uint16_t* stage,
                                                 uint16_t* __restrict__ Ce, int r0, int c0,
-                                                int rows_e, int Nout, int lane) {
+                                                int rows_e, int Nout, int lane,
+                                                const uint16_t* __restrict__ Me = nullptr) {
   constexpr int W = TJ * 32, LD = W + 8, CPR = W / 8;
   const int fr = lane & 31, g = lane >> 5;
 #pragma unroll
@@ -50,9 +51,23 @@ __device__ __forceinline__ void store_tile_bf16(const floatx16 (&acc)[TI][TJ], u
 #pragma unroll 4
   for (int idx = lane; idx < TI * 32 * CPR; idx += kWave) {
     const int row = idx / CPR, ch = idx - row * CPR;
-    if (r0 + row < rows_e)
-      *reinterpret_cast<u32x4*>(Ce + (int64_t)(r0 + row) * Nout + c0 + ch * 8) =
-          *reinterpret_cast<const u32x4*>(stage + row * LD + ch * 8);
+    if (r0 + row < rows_e) {
+      const int64_t at = (int64_t)(r0 + row) * Nout + c0 + ch * 8;
+      u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * LD + ch * 8);
+      if (MASK) {
+        // keep a value where the matching activation is positive (bf16 sign bit
+        // clear and not zero), zero it elsewhere
+        const u32x4 m = *reinterpret_cast<const u32x4*>(Me + at);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = (m[i] & 0x8000u) == 0 && (m[i] & 0x7FFFu) != 0 ? 0xFFFFu : 0u;
+          const uint32_t hi = (m[i] & 0x80000000u) == 0 && (m[i] & 0x7FFF0000u) != 0
+                                  ? 0xFFFF0000u : 0u;
+          v[i] &= lo | hi;
+        }
+      }
+      *reinterpret_cast<u32x4*>(Ce + at) = v;
+    }
   }
 }
 
@@ -146,7 +161,7 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
   const int mt = tile % m_tiles;
   const int nt = (tile / m_tiles) % n_tiles;
   const int e = tile / (m_tiles * n_tiles);
-  const int rows_e = rows[e];
+  const int rows_e = rows ? rows[e] : (int)C;
   const int m0 = mt * BM;
   if (m0 >= rows_e) return;
   const int n0 = nt * BN;
@@ -230,6 +245,10 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
   if (MODE == kRowsCombine)
     store_tile_combine<TI, TJ>(acc, lds + wave * (BM / 2) * (BN / 2 + 8), tok_e, io.x, io.gate,
                                io.out, m0 + wm * (BM / 2), n0 + wn * (BN / 2), rows_e, Nout, lane);
+  else if (MODE == kRowsMask)
+    store_tile_bf16<TI, TJ, false, true>(acc, lds + wave * (BM / 2) * (BN / 2 + 8), Ce,
+                                         m0 + wm * (BM / 2), n0 + wn * (BN / 2), rows_e, Nout,
+                                         lane, io.mask + (int64_t)e * strideC);
   else
     store_tile_bf16<TI, TJ, RELU>(acc, lds + wave * (BM / 2) * (BN / 2 + 8), Ce,
                                   m0 + wm * (BM / 2), n0 + wn * (BN / 2), rows_e, Nout, lane);
@@ -492,6 +511,9 @@ void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t st
   else if (mode == kRowsCombine)
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false, kRowsCombine>), dim3(grid), dim3(256), 0,
                        s, a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
+  else if (mode == kRowsMask)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false, kRowsMask>), dim3(grid), dim3(256), 0, s,
+                       a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
   else if (relu)
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true, kRowsDense>), dim3(grid), dim3(256), 0, s,
                        a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);

@@ -84,9 +84,13 @@ void launch_copy_expert_rows(const void* Ybuf, const int32_t* n_kept, int N, int
 // Row routing of the bf16 expert matmuls.  GATHER: the A rows of expert e are
 // rows tok[e * C + m] of x (K = d_model).  COMBINE: output row m of expert e is
 // combined into out[tok[e * C + m]] = x + gate * y instead of being stored.
-enum GemmRows { kRowsDense = 0, kRowsGather = 1, kRowsCombine = 2 };
+// MASK: the stored result is zeroed where io.mask (same layout as the output,
+// bf16) is not positive -- the ReLU derivative of the backward pass.
+// rows == NULL: every expert has C valid rows (dense weight-gradient matmuls).
+enum GemmRows { kRowsDense = 0, kRowsGather = 1, kRowsCombine = 2, kRowsMask = 3 };
 struct GemmIO {
   const int32_t* tile_start = nullptr;  // compact tile list of the wide kernel
+  const uint16_t* mask = nullptr;       // kRowsMask: the forward activation H
   const int32_t* tok = nullptr;
   const uint16_t* x = nullptr;
   const float* gate = nullptr;
@@ -101,5 +105,24 @@ void launch_expert_gemm(bool bf16, bool relu, const void* A, int64_t strideA, co
                         int n_experts, int64_t C, int K, int Nout, hipStream_t s);
 bool expert_gemm_shape_ok(bool bf16, int d, int F);
 constexpr int kWideTileRows = 256;   // M tile of the wide bf16 kernel
+
+// backward.hip
+void launch_bwd_rows(const int32_t* load, int N, int64_t C, int32_t* n_kept, hipStream_t s);
+void launch_bwd_slots(const void* G, int64_t T, int d, const int32_t* expert_idx,
+                      const int32_t* position, const uint8_t* drop_mask, const float* gate,
+                      int64_t C, int32_t* tok, void* Gs, hipStream_t s);
+void launch_transpose(const void* src, int64_t src_estride, int ld, int R, int Ccols,
+                      const int32_t* valid, const int32_t* tok, void* dst, int64_t dst_estride,
+                      int Rpad, int n_experts, hipStream_t s);
+void launch_router_bwd(const float* h, int64_t T, int N, int d, const void* G, const void* Ybuf,
+                       int64_t C, const int32_t* expert_idx, const int32_t* position,
+                       const uint8_t* drop_mask, const int32_t* load, float loss_scale, float* dh,
+                       hipStream_t s);
+void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d, float* dW_r,
+                         float* db, hipStream_t s);
+void launch_grad_x(const void* G, int64_t T, int d, const int32_t* expert_idx,
+                   const int32_t* position, const uint8_t* drop_mask, int64_t C, const void* dXe,
+                   const float* dh, const float* W_r, int N, void* dx, hipStream_t s);
+void launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace swl

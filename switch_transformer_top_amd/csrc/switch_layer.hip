@@ -275,6 +275,141 @@ switch_status route_impl(switch_layer* L, const void* x, const float* given_logi
   return hipGetLastError() == hipSuccess ? SWITCH_OK : SWITCH_E_HIP;
 }
 
+// Workspace of the backward pass (bf16 layers, top-1).  Cbp = Cb rounded up
+// to 64: the weight-gradient matmuls run over the expert's rows as their K
+// dimension, zero-padded to whole K steps.
+struct BwdLayout {
+  size_t nkept, tok, gs, hbuf, ybuf, du, dxe, woutT, winT, gsT, hT, duT, xT, dh, total;
+  int64_t Cb, Cbp;
+};
+
+BwdLayout bwd_layout_of(const switch_layer* L, int64_t T) {
+  const switch_config& c = L->cfg;
+  const size_t N = (size_t)c.n_experts, d = (size_t)c.d_model, F = (size_t)c.d_ff;
+  BwdLayout lo;
+  lo.Cb = buffer_rows(c, T);
+  lo.Cbp = (lo.Cb + 63) / 64 * 64;
+  const size_t Cb = (size_t)lo.Cb, Cbp = (size_t)lo.Cbp;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes); return at; };
+  lo.nkept = take(4 * N);
+  lo.tok = take(4 * N * Cb);
+  lo.gs = take(2 * N * Cb * d);
+  lo.hbuf = take(2 * N * Cb * F);
+  lo.ybuf = take(2 * N * Cb * d);
+  lo.du = take(2 * N * Cb * F);
+  lo.dxe = take(2 * N * Cb * d);
+  lo.woutT = take(2 * N * F * d);
+  lo.winT = take(2 * N * d * F);
+  lo.gsT = take(2 * N * d * Cbp);
+  lo.hT = take(2 * N * F * Cbp);
+  lo.duT = take(2 * N * F * Cbp);
+  lo.xT = take(2 * N * d * Cbp);
+  lo.dh = take(4 * (size_t)T * N);
+  lo.total = off;
+  return lo;
+}
+
+switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const void* grad_out,
+                            float grad_aux, const float* logits, const int32_t* expert_idx,
+                            const float* gate, const int32_t* position, const uint8_t* drop_mask,
+                            const int32_t* load, void* grad_x, float* grad_W_r, float* grad_b_r,
+                            void* grad_W_in, void* grad_W_out, void* ws, hipStream_t s) {
+  const switch_config& c = L->cfg;
+  const int N = c.n_experts, d = c.d_model, F = c.d_ff;
+  const BwdLayout lo = bwd_layout_of(L, T);
+  const int64_t Cb = lo.Cb, Cbp = lo.Cbp;
+  char* w = (char*)ws;
+  int32_t* nkept = (int32_t*)(w + lo.nkept);
+  int32_t* tok = (int32_t*)(w + lo.tok);
+  void* gs = w + lo.gs;
+  void* hbuf = w + lo.hbuf;
+  void* ybuf = w + lo.ybuf;
+  void* du = w + lo.du;
+  void* dxe = w + lo.dxe;
+  float* dh = (float*)(w + lo.dh);
+  swl::Profiler* P = &L->prof;
+  swl::prof_begin(P);
+  if (T > 0) {
+    swl::prof_mark(P, s, "bwd_slots");
+    swl::launch_bwd_rows(load, N, Cb, nkept, s);
+    swl::launch_bwd_slots(grad_out, T, d, expert_idx, position, drop_mask, gate, Cb, tok, gs, s);
+    swl::GemmIO io;
+    io.tok = tok;
+    io.x = (const uint16_t*)x;
+    if (Cb > 0) {
+      // the forward's expert activations, recomputed
+      swl::prof_mark(P, s, "recompute_h");
+      swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
+                                   hbuf, Cb * F, nkept, N, Cb, d, F, io, s);
+      swl::prof_mark(P, s, "recompute_y");
+      swl::launch_expert_gemm_bf16(swl::kRowsDense, false, hbuf, Cb * F, L->W_out,
+                                   (int64_t)d * F, ybuf, Cb * d, nkept, N, Cb, F, d, io, s);
+    }
+    swl::prof_mark(P, s, "router_bwd");
+    const float loss_scale =
+        (float)((double)grad_aux * (double)c.alpha * (double)N / ((double)T * (double)T));
+    swl::launch_router_bwd(logits, T, N, d, grad_out, ybuf, Cb, expert_idx, position, drop_mask,
+                           load, loss_scale, dh, s);
+    swl::launch_router_wgrad(dh, x, T, N, d, grad_W_r, grad_b_r, s);
+    if (Cb > 0) {
+      swl::prof_mark(P, s, "weight_transpose");
+      void* woutT = w + lo.woutT;
+      void* winT = w + lo.winT;
+      swl::launch_transpose(L->W_out, (int64_t)d * F, F, d, F, nullptr, nullptr, woutT,
+                            (int64_t)F * d, d, N, s);
+      swl::launch_transpose(L->W_in, (int64_t)F * d, d, F, d, nullptr, nullptr, winT,
+                            (int64_t)d * F, F, N, s);
+      // dU = (Gs W_out[e]) * [H > 0]
+      swl::prof_mark(P, s, "grad_h");
+      io.mask = (const uint16_t*)hbuf;
+      swl::launch_expert_gemm_bf16(swl::kRowsMask, false, gs, Cb * d, woutT, (int64_t)F * d, du,
+                                   Cb * F, nkept, N, Cb, d, F, io, s);
+      // dX = dU W_in[e]
+      swl::prof_mark(P, s, "grad_x_expert");
+      swl::launch_expert_gemm_bf16(swl::kRowsDense, false, du, Cb * F, winT, (int64_t)d * F, dxe,
+                                   Cb * d, nkept, N, Cb, F, d, io, s);
+      // token-major operands of the weight gradients (K = the expert's rows)
+      swl::prof_mark(P, s, "act_transpose");
+      void* gsT = w + lo.gsT;
+      void* hT = w + lo.hT;
+      void* duT = w + lo.duT;
+      void* xT = w + lo.xT;
+      swl::launch_transpose(gs, Cb * d, d, (int)Cb, d, nkept, nullptr, gsT, (int64_t)d * Cbp,
+                            (int)Cbp, N, s);
+      swl::launch_transpose(hbuf, Cb * F, F, (int)Cb, F, nkept, nullptr, hT, (int64_t)F * Cbp,
+                            (int)Cbp, N, s);
+      swl::launch_transpose(du, Cb * F, F, (int)Cb, F, nkept, nullptr, duT, (int64_t)F * Cbp,
+                            (int)Cbp, N, s);
+      swl::launch_transpose(x, 0, d, (int)Cb, d, nkept, tok, xT, (int64_t)d * Cbp, (int)Cbp, N,
+                            s);
+      // dW_out[e] = Gs^T H: [d, Cbp] x [F, Cbp]^T;  dW_in[e] = dU^T X: [F, Cbp] x [d, Cbp]^T
+      swl::prof_mark(P, s, "grad_w_out");
+      swl::launch_expert_gemm_bf16(swl::kRowsDense, false, gsT, (int64_t)d * Cbp, hT,
+                                   (int64_t)F * Cbp, grad_W_out, (int64_t)d * F, nullptr, N, d,
+                                   (int)Cbp, F, io, s);
+      swl::prof_mark(P, s, "grad_w_in");
+      swl::launch_expert_gemm_bf16(swl::kRowsDense, false, duT, (int64_t)F * Cbp, xT,
+                                   (int64_t)d * Cbp, grad_W_in, (int64_t)F * d, nullptr, N, F,
+                                   (int)Cbp, d, io, s);
+    }
+    swl::prof_mark(P, s, "grad_x");
+    swl::launch_grad_x(grad_out, T, d, expert_idx, position, drop_mask, Cb, dxe, dh, L->W_r, N,
+                       grad_x, s);
+  }
+  if (T == 0 || Cb == 0) {
+    // no token reached an expert: the expert weights get no gradient
+    swl::launch_fill_zero(grad_W_in, (size_t)N * F * d * 2, s);
+    swl::launch_fill_zero(grad_W_out, (size_t)N * d * F * 2, s);
+  }
+  if (T == 0) {
+    // no tokens: the router gradient sums are empty (the kernel writes zeros)
+    swl::launch_router_wgrad(dh, x, 0, N, d, grad_W_r, grad_b_r, s);
+  }
+  swl::prof_end(P, s);
+  return hipGetLastError() == hipSuccess ? SWITCH_OK : SWITCH_E_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -377,6 +512,41 @@ switch_status switch_forward_debug(switch_layer* L, const void* x, int64_t T, vo
     return SWITCH_E_INVALID;
   return forward_impl(L, x, T, out, expert_idx, gate, position, drop_mask, aux_loss, logits, load,
                       ws, ws_bytes, expert_out, (hipStream_t)stream);
+}
+
+size_t switch_backward_workspace_bytes(const switch_layer* L, int64_t T) {
+  if (!L || T < 0 || T > L->cfg.t_max) return 0;
+  return bwd_layout_of(L, T).total;
+}
+
+switch_status switch_backward(switch_layer* L, const void* x, int64_t T, const void* grad_out,
+                              float grad_aux, const float* logits, const int32_t* expert_idx,
+                              const float* gate, const int32_t* position,
+                              const uint8_t* drop_mask, const int32_t* load, void* grad_x,
+                              float* grad_W_r, float* grad_b_r, void* grad_W_in,
+                              void* grad_W_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!L || T < 0 || T > L->cfg.t_max) return SWITCH_E_INVALID;
+  const switch_config& c = L->cfg;
+  if (c.act_dtype != SWITCH_BF16 || top_k(c) != 1) return SWITCH_E_UNSUPPORTED;
+  if (!isfinite(grad_aux)) return SWITCH_E_INVALID;
+  if (T > 0 && (!x || !grad_out || !logits || !expert_idx || !gate || !position || !drop_mask ||
+                !grad_x))
+    return SWITCH_E_INVALID;
+  if (!load || !grad_W_r || !grad_W_in || !grad_W_out || !ws) return SWITCH_E_INVALID;
+  if (!aligned(x, 16) || !aligned(grad_out, 16) || !aligned(grad_x, 16) || !aligned(logits, 4) ||
+      !aligned(expert_idx, 4) || !aligned(gate, 4) || !aligned(position, 4) ||
+      !aligned(load, 4) || !aligned(grad_W_r, 16) || !aligned(grad_b_r, 16) ||
+      !aligned(grad_W_in, 16) || !aligned(grad_W_out, 16) || !aligned(ws, 16))
+    return SWITCH_E_INVALID;
+  if (ws_bytes < bwd_layout_of(L, T).total) return SWITCH_E_INVALID;
+  const size_t xbytes = (size_t)T * (size_t)c.d_model * 2;
+  if (overlaps(grad_x, xbytes, x, xbytes) || overlaps(grad_x, xbytes, grad_out, xbytes))
+    return SWITCH_E_INVALID;
+  switch_status st = check_device(L);
+  if (st != SWITCH_OK) return st;
+  return backward_impl(L, x, T, grad_out, grad_aux, logits, expert_idx, gate, position, drop_mask,
+                       load, grad_x, grad_W_r, grad_b_r, grad_W_in, grad_W_out, ws,
+                       (hipStream_t)stream);
 }
 
 switch_status switch_profile_enable(switch_layer* L, int max_calls) {
