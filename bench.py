@@ -228,6 +228,9 @@ def main():
     ap.add_argument("--top-k", type=int, default=1, choices=(1, 2),
                     help="experts per token: 1 is the Switch layer (the headline); 2 times the "
                          "top-2 routing variant on the same workload")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward pass (gradients of every input and weight) "
+                         "after the forward, and report it beside the forward line's fields")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, run one device-to-device copy of 1 GiB "
                          "(reference for hardware byte counters)")
@@ -272,6 +275,42 @@ def main():
     stage_ms = dict(B.switch_profile_read(layer.handle))
     B.switch_profile_enable(layer.handle, 0)
     torch.cuda.synchronize()
+
+    backward = None
+    if args.backward:
+        if args.top_k != 1:
+            sys.exit("the backward pass is built for top-1 routing")
+        # forward outputs (logits included) for the routing the backward differentiates at
+        layer.forward(x, spec.T, bufs, stream=sp, with_logits=True)
+        gen = torch.Generator(device=dev).manual_seed(1000 + spec.seed)   # seeded dL/dout
+        g_out = torch.randn((spec.T, spec.d), device=dev, generator=gen).to(torch.bfloat16)
+        g_out = g_out.view(torch.int16)
+        grads = layer.alloc_backward(spec.T)
+        for _ in range(args.warmup):
+            layer.backward(x, spec.T, g_out, 1.0, bufs, grads, stream=sp)
+        torch.cuda.synchronize()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(args.steps):
+            layer.backward(x, spec.T, g_out, 1.0, bufs, grads, stream=sp)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = b0.elapsed_time(b1) / args.steps
+        B.switch_profile_enable(layer.handle, args.steps)
+        for _ in range(args.steps):
+            layer.backward(x, spec.T, g_out, 1.0, bufs, grads, stream=sp)
+        bwd_stages = dict(B.switch_profile_read(layer.handle))
+        B.switch_profile_enable(layer.handle, 0)
+        torch.cuda.synchronize()
+        bwd_kept = int((B.from_device(bufs["drop_mask"]) == 0).sum())
+        # matmul work of the backward: two recomputed forward matmuls and four gradient
+        # matmuls over the kept rows (the weight-gradient K runs over padded rows)
+        bwd_flops = 12.0 * bwd_kept * spec.d * spec.F
+        backward = {"ms_per_step": round(bwd_ms, 5),
+                    "tokens_per_s": round(spec.T / (bwd_ms * 1e-3), 1),
+                    "fwd_bwd_tokens_per_s": round(spec.T / ((bwd_ms + ms_per_step) * 1e-3), 1),
+                    "matmul_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+                    "stage_ms": {k: round(v, 5) for k, v in bwd_stages.items()}}
 
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -328,6 +367,8 @@ def main():
         "stage_rooflines": rooflines,
         "wall_s_timed_region": round(wall, 4),
     }
+    if backward is not None:
+        result["backward"] = backward
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(spec, host, args.cpu_budget, args.top_k)
     print(json.dumps(result), flush=True)

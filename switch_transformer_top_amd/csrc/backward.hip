@@ -60,7 +60,10 @@ __global__ __launch_bounds__(256) void bwd_slots_kernel(const u32x4* __restrict_
 // ld) into dst[e] [Ccols, Rpad]: dst[c][r] = src[r][c] for r < rows_e, 0 for
 // rows_e <= r < Rpad.  rows_e = valid[e], or R when valid is NULL.  With tok,
 // row r of expert e is row tok[e * R + r] of src (a gathered row of x).
-// 64 x 64 tiles through LDS (padded rows); grid (ceil(Ccols / 64), Rpad / 64, N).
+// 64 x 64 tiles through LDS (rows of 72 bf16); every global access moves 16
+// bytes: a thread loads 8 consecutive columns of a source row and stores 8
+// consecutive rows of a destination row.  Ccols, ld and Rpad are multiples of
+// 8 (Rpad of 64); grid (ceil(Ccols / 64), Rpad / 64, N).
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src,
                                                         int64_t src_estride, int ld, int R,
                                                         int Ccols,
@@ -68,27 +71,36 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
                                                         const int32_t* __restrict__ tok,
                                                         uint16_t* __restrict__ dst,
                                                         int64_t dst_estride, int Rpad) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
   const int e = blockIdx.z;
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
   const int rows_e = valid ? valid[e] : R;
   const uint16_t* se = src + (tok ? 0 : (int64_t)e * src_estride);
   const int32_t* te = tok ? tok + (int64_t)e * R : nullptr;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    uint16_t v = 0;
+  const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = lr + 32 * j;
+    const int r = r0 + i, c = c0 + lc;
+    u32x4 v = {0u, 0u, 0u, 0u};
     if (r < rows_e && c < Ccols) {
       const int64_t row = te ? (int64_t)te[r] : (int64_t)r;
-      v = se[row * ld + c];
+      v = *reinterpret_cast<const u32x4*>(se + row * ld + c);
     }
-    tile[i][tx] = v;
+    *reinterpret_cast<u32x4*>(&tile[i][lc]) = v;
   }
   __syncthreads();
   uint16_t* de = dst + (int64_t)e * dst_estride;
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < Ccols && r < Rpad) de[(int64_t)c * Rpad + r] = tile[tx][i];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int cc = lr + 32 * j;          // destination row (source column)
+    const int c = c0 + cc, r = r0 + lc;
+    if (c >= Ccols) continue;
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = (uint32_t)tile[lc + 2 * q][cc] | ((uint32_t)tile[lc + 2 * q + 1][cc] << 16);
+    *reinterpret_cast<u32x4*>(de + (int64_t)c * Rpad + r) = o;
   }
 }
 
@@ -144,26 +156,33 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   }
 }
 
-// dW_r[i, k] = sum_t dh[t, i] x[t, k] and db[i] = sum_t dh[t, i] (fp32, token
-// order).  Block: 64 experts x 64 columns, 256 threads each 4 x 4 outputs; T
-// in chunks of 32 tokens through LDS.
+// dW_r[i, k] = sum_t dh[t, i] x[t, k] and db[i] = sum_t dh[t, i] (fp32).
+// Block (k tile, i tile, s): 64 experts x 64 columns over the tokens of slice
+// s (RW_SLICE consecutive tokens), 256 threads each 4 x 4 outputs, the slice
+// in steps of 32 tokens through LDS.  Each slice writes its partial sums to
+// part[s] ([N, d], and part_b[s] [N] from the k-tile-0 blocks);
+// router_wgrad_reduce adds the slices in slice order.  Fixed order throughout.
+constexpr int RW_SLICE = 256;
+
 __global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restrict__ dh,
                                                            const uint16_t* __restrict__ x,
                                                            int64_t T, int N, int d,
-                                                           float* __restrict__ dW_r,
-                                                           float* __restrict__ db) {
+                                                           float* __restrict__ part,
+                                                           float* __restrict__ part_b) {
   __shared__ float Ds[32][68];
   __shared__ float Xs[32][68];
   const int i0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
+  const int64_t ts = (int64_t)blockIdx.z * RW_SLICE;
+  const int64_t te = ts + RW_SLICE < T ? ts + RW_SLICE : T;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   float acc[4][4] = {};
   float bacc = 0.f;
-  for (int64_t t0 = 0; t0 < T; t0 += 32) {
+  for (int64_t t0 = ts; t0 < te; t0 += 32) {
     for (int idx = threadIdx.x; idx < 32 * 64; idx += 256) {
       const int r = idx >> 6, c = idx & 63;
       const int64_t t = t0 + r;
-      Ds[r][c] = (t < T && i0 + c < N) ? dh[t * N + i0 + c] : 0.f;
-      Xs[r][c] = (t < T && k0 + c < d) ? bf16_bits_to_f32(x[t * d + k0 + c]) : 0.f;
+      Ds[r][c] = (t < te && i0 + c < N) ? dh[t * N + i0 + c] : 0.f;
+      Xs[r][c] = (t < te && k0 + c < d) ? bf16_bits_to_f32(x[t * d + k0 + c]) : 0.f;
     }
     __syncthreads();
 #pragma unroll 4
@@ -179,61 +198,103 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restri
     }
     __syncthreads();
   }
+  float* ps = part + (int64_t)blockIdx.z * N * d;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int i = i0 + ty + 16 * q, k = k0 + tx + 16 * w;
-      if (i < N && k < d) dW_r[(int64_t)i * d + k] = acc[q][w];
+      if (i < N && k < d) ps[(int64_t)i * d + k] = acc[q][w];
     }
-  if (db && blockIdx.x == 0 && threadIdx.x < 64 && i0 + threadIdx.x < N) db[i0 + threadIdx.x] = bacc;
+  if (blockIdx.x == 0 && threadIdx.x < 64 && i0 + threadIdx.x < N)
+    part_b[(int64_t)blockIdx.z * N + i0 + threadIdx.x] = bacc;
+}
+
+// dW_r = sum over slices of part[s] (slice order); db likewise (when db != NULL).
+__global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restrict__ part,
+                                                           const float* __restrict__ part_b,
+                                                           int slices, int N, int d,
+                                                           float* __restrict__ dW_r,
+                                                           float* __restrict__ db) {
+  const int64_t n = (int64_t)N * d;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n + N;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float acc = 0.f;
+    if (i < n) {
+      for (int s = 0; s < slices; ++s) acc += part[(int64_t)s * n + i];
+      dW_r[i] = acc;
+    } else if (db) {
+      const int64_t j = i - n;
+      for (int s = 0; s < slices; ++s) acc += part_b[(int64_t)s * N + j];
+      db[j] = acc;
+    }
+  }
 }
 
 // dx_t = G_t + dX[e_t, p_t] (kept) + sum_i dh[t, i] W_r[i, :], fp32 then one
-// rounding to bf16.  One thread per 16-byte piece (8 columns) of a row.
-__global__ __launch_bounds__(256) void grad_x_kernel(const u32x4* __restrict__ G, int64_t T,
-                                                     int row_vec16,
-                                                     const int32_t* __restrict__ expert_idx,
+// rounding to bf16.  Block: 64 tokens x 64 columns; the router part is a
+// small matmul with K = N, in steps of 32 experts through LDS; thread (ty, tx)
+// owns tokens ty + 16 q and the four columns 4 tx .. 4 tx + 3.
+__global__ __launch_bounds__(256) void grad_x_kernel(const uint16_t* __restrict__ G, int64_t T,
+                                                     int d, const int32_t* __restrict__ expert_idx,
                                                      const int32_t* __restrict__ position,
                                                      const uint8_t* __restrict__ drop_mask,
-                                                     int64_t C, const u32x4* __restrict__ dXe,
+                                                     int64_t C, const uint16_t* __restrict__ dXe,
                                                      const float* __restrict__ dh,
                                                      const float* __restrict__ W_r, int N,
-                                                     u32x4* __restrict__ dx) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t t = gid / row_vec16;
-  const int c = (int)(gid - t * row_vec16);
-  if (t >= T) return;
-  const int d = row_vec16 * 8;
-  float acc[8];
-  const u32x4 gv = G[t * row_vec16 + c];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc[2 * i] = __uint_as_float(gv[i] << 16);
-    acc[2 * i + 1] = __uint_as_float(gv[i] & 0xFFFF0000u);
-  }
-  if (!drop_mask[t]) {
-    const u32x4 v = dXe[((int64_t)expert_idx[t] * C + position[t]) * row_vec16 + c];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += __uint_as_float(v[i] << 16);
-      acc[2 * i + 1] += __uint_as_float(v[i] & 0xFFFF0000u);
+                                                     uint16_t* __restrict__ dx) {
+  __shared__ float Ds[64][33];
+  __shared__ float Ws[32][68];
+  const int64_t t0 = (int64_t)blockIdx.y * 64;
+  const int k0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4] = {};
+  for (int i0 = 0; i0 < N; i0 += 32) {
+    for (int idx = threadIdx.x; idx < 64 * 32; idx += 256) {
+      const int r = idx >> 5, c = idx & 31;
+      const int64_t t = t0 + r;
+      Ds[r][c] = (t < T && i0 + c < N) ? dh[t * N + i0 + c] : 0.f;
     }
-  }
-  const float* dht = dh + t * N;
-  for (int i = 0; i < N; ++i) {
-    const float g = dht[i];
-    const float4 w0 = *reinterpret_cast<const float4*>(W_r + (int64_t)i * d + c * 8);
-    const float4 w1 = *reinterpret_cast<const float4*>(W_r + (int64_t)i * d + c * 8 + 4);
-    acc[0] = fmaf(g, w0.x, acc[0]); acc[1] = fmaf(g, w0.y, acc[1]);
-    acc[2] = fmaf(g, w0.z, acc[2]); acc[3] = fmaf(g, w0.w, acc[3]);
-    acc[4] = fmaf(g, w1.x, acc[4]); acc[5] = fmaf(g, w1.y, acc[5]);
-    acc[6] = fmaf(g, w1.z, acc[6]); acc[7] = fmaf(g, w1.w, acc[7]);
-  }
-  u32x4 o;
+    for (int idx = threadIdx.x; idx < 32 * 64; idx += 256) {
+      const int r = idx >> 6, c = idx & 63;
+      Ws[r][c] = (i0 + r < N && k0 + c < d) ? W_r[(int64_t)(i0 + r) * d + k0 + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+      float w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x2_to_bf16x2_bits(acc[2 * i], acc[2 * i + 1]);
-  dx[t * row_vec16 + c] = o;
+      for (int c = 0; c < 4; ++c) w[c] = Ws[i][4 * tx + c];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a = Ds[ty + 16 * q][i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[q][c] = fmaf(a, w[c], acc[q][c]);
+      }
+    }
+    __syncthreads();
+  }
+  const int k = k0 + 4 * tx;
+  if (k >= d) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t t = t0 + ty + 16 * q;
+    if (t >= T) continue;
+    const uint2 gv = *reinterpret_cast<const uint2*>(G + t * d + k);
+    float v[4] = {__uint_as_float(gv.x << 16), __uint_as_float(gv.x & 0xFFFF0000u),
+                  __uint_as_float(gv.y << 16), __uint_as_float(gv.y & 0xFFFF0000u)};
+    if (!drop_mask[t]) {
+      const uint2 xv = *reinterpret_cast<const uint2*>(
+          dXe + ((int64_t)expert_idx[t] * C + position[t]) * d + k);
+      v[0] += __uint_as_float(xv.x << 16);
+      v[1] += __uint_as_float(xv.x & 0xFFFF0000u);
+      v[2] += __uint_as_float(xv.y << 16);
+      v[3] += __uint_as_float(xv.y & 0xFFFF0000u);
+    }
+    const uint2 o = make_uint2(f32x2_to_bf16x2_bits(v[0] + acc[q][0], v[1] + acc[q][1]),
+                               f32x2_to_bf16x2_bits(v[2] + acc[q][2], v[3] + acc[q][3]));
+    *reinterpret_cast<uint2*>(dx + t * d + k) = o;
+  }
 }
 
 // Zero fill (16-byte stores; bytes a multiple of 16).
@@ -287,21 +348,29 @@ void launch_router_bwd(const float* h, int64_t T, int N, int d, const void* G, c
                      drop_mask, load, loss_scale, dh);
 }
 
-void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d, float* dW_r,
-                         float* db, hipStream_t s) {
-  const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((N + 63) / 64));
-  hipLaunchKernelGGL(router_wgrad_kernel, grid, dim3(256), 0, s, dh, (const uint16_t*)x, T, N, d,
-                     dW_r, db);
+int64_t router_wgrad_slices(int64_t T) { return T > 0 ? (T + RW_SLICE - 1) / RW_SLICE : 0; }
+
+void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d, float* part,
+                         float* part_b, float* dW_r, float* db, hipStream_t s) {
+  const int64_t slices = router_wgrad_slices(T);
+  if (slices > 0) {
+    const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)slices);
+    hipLaunchKernelGGL(router_wgrad_kernel, grid, dim3(256), 0, s, dh, (const uint16_t*)x, T, N,
+                       d, part, part_b);
+  }
+  const int64_t n = (int64_t)N * d + N;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(router_wgrad_reduce, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                     dim3(256), 0, s, part, part_b, (int)slices, N, d, dW_r, db);
 }
 
 void launch_grad_x(const void* G, int64_t T, int d, const int32_t* expert_idx,
                    const int32_t* position, const uint8_t* drop_mask, int64_t C, const void* dXe,
                    const float* dh, const float* W_r, int N, void* dx, hipStream_t s) {
   if (T == 0) return;
-  const int rv = d / 8;
-  hipLaunchKernelGGL(grad_x_kernel, dim3((unsigned)((T * rv + 255) / 256)), dim3(256), 0, s,
-                     (const u32x4*)G, T, rv, expert_idx, position, drop_mask, C,
-                     (const u32x4*)dXe, dh, W_r, N, (u32x4*)dx);
+  const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((T + 63) / 64));
+  hipLaunchKernelGGL(grad_x_kernel, grid, dim3(256), 0, s, (const uint16_t*)G, T, d, expert_idx,
+                     position, drop_mask, C, (const uint16_t*)dXe, dh, W_r, N, (uint16_t*)dx);
 }
 
 }  // namespace swl

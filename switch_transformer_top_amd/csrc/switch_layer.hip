@@ -279,7 +279,8 @@ switch_status route_impl(switch_layer* L, const void* x, const float* given_logi
 // to 64: the weight-gradient matmuls run over the expert's rows as their K
 // dimension, zero-padded to whole K steps.
 struct BwdLayout {
-  size_t nkept, tok, gs, hbuf, ybuf, du, dxe, woutT, winT, gsT, hT, duT, xT, dh, total;
+  size_t nkept, tok, gs, hbuf, ybuf, du, dxe, woutT, winT, gsT, hT, duT, xT, dh, wpart, bpart,
+      total;
   int64_t Cb, Cbp;
 };
 
@@ -306,6 +307,9 @@ BwdLayout bwd_layout_of(const switch_layer* L, int64_t T) {
   lo.duT = take(2 * N * F * Cbp);
   lo.xT = take(2 * N * d * Cbp);
   lo.dh = take(4 * (size_t)T * N);
+  const size_t slices = (size_t)swl::router_wgrad_slices(T);
+  lo.wpart = take(4 * slices * N * d);
+  lo.bpart = take(4 * slices * N);
   lo.total = off;
   return lo;
 }
@@ -351,7 +355,8 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
         (float)((double)grad_aux * (double)c.alpha * (double)N / ((double)T * (double)T));
     swl::launch_router_bwd(logits, T, N, d, grad_out, ybuf, Cb, expert_idx, position, drop_mask,
                            load, loss_scale, dh, s);
-    swl::launch_router_wgrad(dh, x, T, N, d, grad_W_r, grad_b_r, s);
+    swl::launch_router_wgrad(dh, x, T, N, d, (float*)(w + lo.wpart), (float*)(w + lo.bpart),
+                             grad_W_r, grad_b_r, s);
     if (Cb > 0) {
       swl::prof_mark(P, s, "weight_transpose");
       void* woutT = w + lo.woutT;
@@ -404,7 +409,8 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
   }
   if (T == 0) {
     // no tokens: the router gradient sums are empty (the kernel writes zeros)
-    swl::launch_router_wgrad(dh, x, 0, N, d, grad_W_r, grad_b_r, s);
+    swl::launch_router_wgrad(dh, x, 0, N, d, (float*)(w + lo.wpart), (float*)(w + lo.bpart),
+                             grad_W_r, grad_b_r, s);
   }
   swl::prof_end(P, s);
   return hipGetLastError() == hipSuccess ? SWITCH_OK : SWITCH_E_HIP;
