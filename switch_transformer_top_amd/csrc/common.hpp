@@ -31,6 +31,15 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// ReLU on a packed pair of bf16 values: as 16-bit integers, exactly the
+// values with the sign bit set (negatives and -0) become +0.
+__device__ __forceinline__ uint32_t relu_bf16x2_bits(uint32_t p) {
+  typedef short shortx2 __attribute__((ext_vector_type(2)));
+  const shortx2 v = __builtin_bit_cast(shortx2, p);
+  const shortx2 z = {0, 0};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, z));
+}
+
 // out = x + g * y on eight bf16 values (16 bytes): fp32 fused multiply-add,
 // rounded to nearest even.  y is the expert output already rounded to bf16.
 __device__ __forceinline__ u32x4 combine_vec_bf16(u32x4 xv, u32x4 yv, float g) {

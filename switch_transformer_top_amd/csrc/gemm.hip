@@ -27,6 +27,33 @@ namespace swl {
 constexpr int GB_BK = 64, GB_PAD = 8;
 constexpr int GB_LDK = GB_BK + GB_PAD;  // LDS row stride in bf16 elements (144 bytes)
 
+// The MFMAs take the weight fragment as their first operand and the token
+// fragment as the second, so a 32 x 32 accumulator tile holds the transpose of
+// the output tile: lane l has output row (l % 32) and, for q < 4, the four
+// consecutive output columns 8 q + 4 (l / 32) .. + 3 in elements 4 q .. 4 q + 3.
+// A lane therefore rounds its values in pairs (v_cvt_pk_bf16_f32) and writes
+// 8 bytes of one row at a time.
+template <int TI, int TJ, int LD, bool RELU>
+__device__ __forceinline__ void stage_tile_bf16(const floatx16 (&acc)[TI][TJ], uint16_t* stage,
+                                                int lane) {
+  const int fr = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t lo = f32x2_to_bf16x2_bits(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+        uint32_t hi = f32x2_to_bf16x2_bits(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        if (RELU) {
+          lo = relu_bf16x2_bits(lo);
+          hi = relu_bf16x2_bits(hi);
+        }
+        *reinterpret_cast<uint2*>(stage + (i * 32 + fr) * LD + j * 32 + 8 * q + 4 * g) =
+            make_uint2(lo, hi);
+      }
+}
+
 // Epilogue shared by the bf16 kernels: a wave's TI x TJ grid of 32 x 32 fp32
 // accumulators goes through LDS (rows of TJ * 32 + 8 bf16, after the optional
 // ReLU and round-to-nearest-even) and then out in 16-byte row pieces, instead
@@ -37,17 +64,7 @@ __device__ __forceinline__ void store_tile_bf16(const floatx16 (&acc)[TI][TJ], u
                                                 int rows_e, int Nout, int lane,
                                                 const uint16_t* __restrict__ Me = nullptr) {
   constexpr int W = TJ * 32, LD = W + 8, CPR = W / 8;
-  const int fr = lane & 31, g = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float val = acc[i][j][v];
-        if (RELU) val = val > 0.f ? val : 0.f;
-        stage[(i * 32 + 8 * (v >> 2) + 4 * g + (v & 3)) * LD + j * 32 + fr] = f32_to_bf16_bits(val);
-      }
+  stage_tile_bf16<TI, TJ, LD, RELU>(acc, stage, lane);
 #pragma unroll 4
   for (int idx = lane; idx < TI * 32 * CPR; idx += kWave) {
     const int row = idx / CPR, ch = idx - row * CPR;
@@ -84,7 +101,6 @@ __device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ]
                                                    int rows_e, int d, int lane) {
   constexpr int W = TJ * 32, LD = W + 8, CPR = W / 8, NR = TI * 32 / kWave;
   static_assert(TI * 32 % kWave == 0, "whole waves of rows");
-  const int fr = lane & 31, g = lane >> 5;
   // lane l fetches the token and gate of rows l, l + 64, ... up front; the
   // store loop below takes them with a lane shuffle
   int tl[NR];
@@ -95,14 +111,7 @@ __device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ]
     tl[q] = r < rows_e ? tok_e[r] : 0;
     gl[q] = r < rows_e ? gate[tl[q]] : 0.f;
   }
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        stage[(i * 32 + 8 * (v >> 2) + 4 * g + (v & 3)) * LD + j * 32 + fr] =
-            f32_to_bf16_bits(acc[i][j][v]);
+  stage_tile_bf16<TI, TJ, LD, false>(acc, stage, lane);
 #pragma unroll
   for (int it = 0; it < TI * 32 * CPR / kWave; ++it) {
     const int idx = it * kWave + lane;
@@ -134,9 +143,11 @@ __device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ]
 // into registers (unconditionally: the last step re-reads its own tile) while
 // the current one is multiplied.
 //
-// MFMA 32x32x16 operand layout (per lane l): A row (l % 32) with 8 consecutive
-// k, B column (l % 32) with the same 8 k; the k group is (l / 32).  Result: lane
-// l holds column (l % 32) and rows 8 (v / 4) + 4 (l / 32) + (v % 4), v < 16.
+// MFMA 32x32x16 operand layout (per lane l): first operand row (l % 32) with 8
+// consecutive k, second operand column (l % 32) with the same 8 k; the k group
+// is (l / 32).  Result: lane l holds column (l % 32) and rows
+// 8 (v / 4) + 4 (l / 32) + (v % 4), v < 16.  The first operand is the weight
+// fragment, so those result rows are output columns (see stage_tile_bf16).
 template <int BM, int BN, bool RELU, int MODE>
 __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                         int64_t strideA,
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
     }
   }
 
@@ -362,7 +373,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
   };
 
   gload(0, NL, 0);
