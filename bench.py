@@ -94,9 +94,9 @@ def roofline_entry(stage: str, work: dict, ms: float) -> dict:
 
 
 # stage of the forward call -> (kernel name in the hardware-counter profiles, source file)
-STAGE_KERNEL = {"gemm1_relu": ("gemm_bf16_kernel<", "true, 1>", "gemm.hip"),
-                "gemm2": ("gemm_bf16_kernel<", "false, 0>", "gemm.hip"),
-                "gemm2_combine": ("gemm_bf16_kernel<", "false, 2>", "gemm.hip"),
+STAGE_KERNEL = {"gemm1_relu": ("gemm_bf16_", "true, 1>", "gemm.hip"),
+                "gemm2": ("gemm_bf16_", "false, 0>", "gemm.hip"),
+                "gemm2_combine": ("gemm_bf16_", "false, 2>", "gemm.hip"),
                 "router": ("router_", "", "router.hip"),
                 "dispatch": ("dispatch_index_kernel", "", "move.hip"),
                 "combine": ("combine_kernel<", "", "move.hip")}

@@ -203,13 +203,18 @@ __device__ __forceinline__ void split3(const float* w, bf16x8& hi, bf16x8& mid, 
 // [row * k + j].  Then thread e owns expert e and sums p_e over the chunk's
 // tokens in token order (fp64) for P_part; the logits leave in full coalesced
 // rows when requested.  Synchronises the block.
+//
+// With s_term (LDS, BT x NPAD doubles) each thread also stores its terms
+// exp(h_e - max) * (1 / S) there, so the P_part sums read them back instead of
+// evaluating the exponentials again (the same values, added in the same order).
 template <int BT, int NPAD, int LD>
 __device__ __forceinline__ void block_stats(const float* st, int N, int k, int64_t t0, int n_tok,
                                             float* __restrict__ logits,
                                             int32_t* __restrict__ expert_idx,
                                             float* __restrict__ gate,
                                             float* __restrict__ P_row, int32_t* s_idx,
-                                            float* s_m, double* s_inv) {
+                                            float* s_m, double* s_inv,
+                                            double* s_term = nullptr) {
   constexpr int TPR = 256 / BT;          // threads per token row
   constexpr int SPAN = NPAD / TPR;       // experts per thread
   static_assert(TPR >= 1 && TPR <= 16 && SPAN >= 1, "row split");
@@ -232,6 +237,13 @@ __device__ __forceinline__ void block_stats(const float* st, int N, int k, int64
   for (int i = 0; i < SPAN; ++i) ssum += (double)expf(rp[i] - m);
 #pragma unroll
   for (int o = TPR / 2; o >= 1; o >>= 1) ssum += shfl_xor_f64_w(ssum, o, TPR);
+  if (s_term) {
+    // every thread of the row holds the same sum after the butterfly
+    const double rinv = 1.0 / ssum;
+#pragma unroll 8
+    for (int i = 0; i < SPAN; ++i)
+      s_term[row * NPAD + part * SPAN + i] = (double)expf(rp[i] - m) * rinv;
+  }
   // second choice: the largest logit among the other experts (real ones only)
   float m2 = -__builtin_huge_valf();
   int mi2 = 0x7fffffff;
@@ -273,8 +285,30 @@ __device__ __forceinline__ void block_stats(const float* st, int N, int k, int64
   __syncthreads();
   for (int e = tid; e < N; e += 256) {
     double acc = 0.0;
-    for (int r = 0; r < n_tok; ++r) acc += (double)expf(st[r * LD + e] - s_m[r]) * s_inv[r];
+    if (s_term)
+      for (int r = 0; r < n_tok; ++r) acc += s_term[r * NPAD + e];
+    else
+      for (int r = 0; r < n_tok; ++r) acc += (double)expf(st[r * LD + e] - s_m[r]) * s_inv[r];
     P_row[e] = (float)acc;
+  }
+}
+
+// Ranks and histogram of a chunk of at most 64 assignments over at most 64
+// experts, by one wave (threads 64..127 of the block, so that it runs beside
+// wave 0's P_part sums): for each expert a ballot of the lanes holding it;
+// a lane's rank is the number of set bits below it (mbcnt), the histogram
+// entry the population count.  Same results as chunk_hist_rank.
+__device__ __forceinline__ void chunk_hist_rank_wave(const int32_t* s_idx, int n, int64_t a0,
+                                                     int N, int32_t* __restrict__ hist_row,
+                                                     int32_t* __restrict__ rank_local) {
+  const int lane = threadIdx.x & 63;
+  const int32_t e = lane < n ? s_idx[lane] : -1;
+  for (int i = 0; i < N; ++i) {
+    const uint64_t m = __ballot(e == i);
+    if (e == i)
+      rank_local[a0 + lane] = (int32_t)__builtin_amdgcn_mbcnt_hi(
+          (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (lane == 0) hist_row[i] = (int32_t)__popcll(m);
   }
 }
 
@@ -290,7 +324,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(
     int32_t* __restrict__ rank_local) {
   constexpr int NJ = NPAD / 16, BT = 16, NACC = NJ * 4, GRP = 8, LD = NPAD + 4;
   __shared__ int32_t s_idx[BT * kMaxTopK];
-  __shared__ int32_t cnt[NPAD];
+  __shared__ double s_term[BT * NPAD];
   __shared__ float red[3][NACC][kWave];
   __shared__ float st[BT * LD];
   __shared__ float s_m[BT];
@@ -376,8 +410,11 @@ __global__ __launch_bounds__(256) void router_small_kernel(
   }
   __syncthreads();
   block_stats<BT, NPAD, LD>(&st[0], N, k, t0, n_tok, logits, expert_idx, gate,
-                            P_part + (int64_t)blockIdx.x * N, s_idx, s_m, s_inv);
-  chunk_hist_rank(s_idx, n_tok * k, t0 * k, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
+                            P_part + (int64_t)blockIdx.x * N, s_idx, s_m, s_inv, s_term);
+  static_assert(BT * kMaxTopK <= kWave && NPAD <= kWave, "one wave ranks the chunk");
+  if (threadIdx.x >= kWave && threadIdx.x < 2 * kWave)
+    chunk_hist_rank_wave(s_idx, n_tok * k, t0 * k, N, hist + (int64_t)blockIdx.x * N,
+                         rank_local);
 }
 
 // More experts (32 < N): a block owns 64 * ROWT tokens and NPAD experts
