@@ -414,6 +414,162 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
                                   lane);
 }
 
+// Split-K variant of the 128 x 128 tile for launches with no more tiles than
+// CUs (the Switch-Base GEMM2 shape: about 240 tiles, K = 3072), where one
+// four-wave block per CU leaves the MFMA pipes idle while each wave waits on
+// LDS and barriers.  Eight waves, two per SIMD: waves 0-3 and 4-7 form two
+// groups owning the same 2 x 2 grid of 64 x 64 wave tiles; in every 64-wide K
+// step group 0 multiplies K sub-steps 0 and 1, group 1 sub-steps 2 and 3.  Two
+// LDS operand buffers, one barrier per step, the loads of step t + 2 in flight
+// during step t.  At the end group 1 hands its fp32 partial sums to group 0
+// through LDS and group 0 adds them (in that order) and runs the epilogue.
+constexpr int GS_STAGE = (128 + 128) * GB_LDK;                      // elements per buffer
+constexpr size_t kSplitRed = (size_t)4 * 16 * 64 * 16;              // bytes of partial sums
+constexpr size_t kSplitLds = kSplitRed + (size_t)4 * 64 * (64 + 8) * sizeof(uint16_t);
+
+template <bool RELU, int MODE>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
+    const uint16_t* __restrict__ A, int64_t strideA, const uint16_t* __restrict__ B,
+    int64_t strideB, uint16_t* __restrict__ Cout, int64_t strideC,
+    const int32_t* __restrict__ rows, int K, int Nout, int m_tiles, int n_tiles, int tiles,
+    GemmIO io, int64_t C) {
+  constexpr int BM = 128, BN = 128, BK = GB_BK, LDK = GB_LDK, TI = 2, TJ = 2;
+  static_assert(2 * GS_STAGE * sizeof(uint16_t) <= kSplitLds, "operand buffers fit");
+  static_assert(kSplitRed <= 2 * GS_STAGE * sizeof(uint16_t), "partial sums reuse the buffers");
+  extern __shared__ __attribute__((aligned(16))) uint16_t slds[];
+
+  const int per_xcd = (tiles + 7) >> 3;
+  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (tile >= tiles) return;
+  const int mt = tile % m_tiles;
+  const int nt = (tile / m_tiles) % n_tiles;
+  const int e = tile / (m_tiles * n_tiles);
+  const int rows_e = rows ? rows[e] : (int)C;
+  const int m0 = mt * BM;
+  if (m0 >= rows_e) return;
+  const int n0 = nt * BN;
+
+  const uint16_t* Ae = MODE == kRowsGather ? io.x : A + (int64_t)e * strideA;
+  const uint16_t* Be = B + (int64_t)e * strideB + (int64_t)n0 * K;
+  uint16_t* Ce = Cout + (int64_t)e * strideC;
+  const int32_t* tok_e = MODE == kRowsDense ? nullptr : io.tok + (int64_t)e * C;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2, wq = wave & 3, wm = wq >> 1, wn = wq & 1;
+  const int lrow = tid >> 3, lcol = (tid & 7) * 8;  // 64 rows per pass of 512 threads
+
+  int64_t go[4];  // element offsets: A rows (j < 2) from Ae, B rows (j >= 2) from Be
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int r = m0 + lrow + 64 * j;
+    r = r < rows_e ? r : rows_e - 1;  // rows past n_kept: any valid row, never stored
+    const int64_t src = MODE == kRowsGather ? (int64_t)tok_e[r] : (int64_t)r;
+    go[j] = src * K + lcol;
+    go[2 + j] = (int64_t)(lrow + 64 * j) * K + lcol;
+  }
+  const int lbase = lrow * LDK + lcol;
+  const int nk = K / BK;
+  u32x4 g[4];
+  auto gload = [&](int t) {
+    t = t < nk ? t : nk - 1;
+    const int k = t * BK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      g[j] = *reinterpret_cast<const u32x4*>((j < 2 ? Ae : Be) + go[j] + k);
+  };
+  auto gstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(
+          &slds[buf * GS_STAGE + lbase + ((j & 1) * 64 + (j < 2 ? 0 : BM)) * LDK]) = g[j];
+  };
+  floatx16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  bf16x8 fa[2][TI], fb[2][TJ];
+  auto frags = [&](int f, int buf, int ks) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+      fa[f][i] = *reinterpret_cast<const bf16x8*>(
+          &slds[buf * GS_STAGE + (wm * 64 + i * 32 + fr) * LDK + ks * 16 + fk]);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+      fb[f][j] = *reinterpret_cast<const bf16x8*>(
+          &slds[buf * GS_STAGE + (BM + wn * 64 + j * 32 + fr) * LDK + ks * 16 + fk]);
+  };
+  auto mfmas = [&](int f) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
+  };
+
+  const int ks0 = 2 * grp;
+  gload(0);
+  gstore(0);
+  gload(1);
+  __syncthreads();
+  for (int t = 0; t < nk; ++t) {
+    const int cur = t & 1, nxt = cur ^ 1;
+    // buffer nxt was last read in step t - 1, before the barrier that ended it
+    frags(0, cur, ks0);
+    frags(1, cur, ks0 + 1);
+    gstore(nxt);
+    gload(t + 2);
+    mfmas(0);
+    mfmas(1);
+    __syncthreads();
+  }
+
+  // group 1's partial sums, laid out [wave tile][i, j, q][lane][4 floats] so
+  // that each 16-byte LDS access of a wave covers consecutive addresses
+  float* red = reinterpret_cast<float*>(slds);
+  if (grp == 1) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]};
+          *reinterpret_cast<float4*>(red + ((wq * 16 + (i * TJ + j) * 4 + q) * 64 + lane) * 4) = v;
+        }
+  }
+  __syncthreads();
+  if (grp == 1) return;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(
+            red + ((wq * 16 + (i * TJ + j) * 4 + q) * 64 + lane) * 4);
+        acc[i][j][4 * q] += v.x;
+        acc[i][j][4 * q + 1] += v.y;
+        acc[i][j][4 * q + 2] += v.z;
+        acc[i][j][4 * q + 3] += v.w;
+      }
+  // epilogue staging lies past the partial sums
+  uint16_t* stage = slds + kSplitRed / sizeof(uint16_t) + wq * 64 * (64 + 8);
+  if (MODE == kRowsCombine)
+    store_tile_combine<TI, TJ>(acc, stage, tok_e, io.x, io.gate, io.out, m0 + wm * 64,
+                               n0 + wn * 64, rows_e, Nout, lane);
+  else if (MODE == kRowsMask)
+    store_tile_bf16<TI, TJ, false, true>(acc, stage, Ce, m0 + wm * 64, n0 + wn * 64, rows_e, Nout,
+                                         lane, io.mask + (int64_t)e * strideC);
+  else
+    store_tile_bf16<TI, TJ, RELU>(acc, stage, Ce, m0 + wm * 64, n0 + wn * 64, rows_e, Nout, lane);
+}
+
 // fp32 path (parity-sized fp32 layers): 32 x 32 tile, K in steps of 32, each
 // of 256 threads owns 4 rows of one column.  Any sizes (bounds-checked).
 template <bool RELU>
@@ -497,6 +653,38 @@ void launch_wide(const uint16_t* a, int64_t strideA, const uint16_t* b, int64_t 
                      n_experts);
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <bool RELU, int MODE>
+void launch_split(unsigned grid, const uint16_t* a, int64_t strideA, const uint16_t* b,
+                  int64_t strideB, uint16_t* c, int64_t strideC, const int32_t* rows, int K,
+                  int Nout, int mt, int nt, int tiles, const GemmIO& io, int64_t C,
+                  hipStream_t s) {
+  static uint64_t set_on = 0;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev < 64 && !(set_on >> dev & 1)) {
+    (void)hipFuncSetAttribute((const void*)gemm_bf16_split_kernel<RELU, MODE>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSplitLds);
+    set_on |= 1ull << dev;
+  }
+  hipLaunchKernelGGL((gemm_bf16_split_kernel<RELU, MODE>), dim3(grid), dim3(512), kSplitLds, s, a,
+                     strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
+}
+
 }  // namespace
 
 void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t strideA,
@@ -516,6 +704,24 @@ void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t st
   const int mt = (int)((C + BM - 1) / BM), nt = Nout / BN;
   const int tiles = mt * nt * n_experts;
   const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
+  if (tiles <= device_cus()) {
+    if (mode == kRowsGather && relu)
+      launch_split<true, kRowsGather>(grid, a, strideA, b, strideB, c, strideC, rows, K, Nout, mt,
+                                      nt, tiles, io, C, s);
+    else if (mode == kRowsCombine)
+      launch_split<false, kRowsCombine>(grid, a, strideA, b, strideB, c, strideC, rows, K, Nout,
+                                        mt, nt, tiles, io, C, s);
+    else if (mode == kRowsMask)
+      launch_split<false, kRowsMask>(grid, a, strideA, b, strideB, c, strideC, rows, K, Nout, mt,
+                                     nt, tiles, io, C, s);
+    else if (relu)
+      launch_split<true, kRowsDense>(grid, a, strideA, b, strideB, c, strideC, rows, K, Nout, mt,
+                                     nt, tiles, io, C, s);
+    else
+      launch_split<false, kRowsDense>(grid, a, strideA, b, strideB, c, strideC, rows, K, Nout, mt,
+                                      nt, tiles, io, C, s);
+    return;
+  }
   if (mode == kRowsGather && relu)
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true, kRowsGather>), dim3(grid), dim3(256), 0, s,
                        a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);

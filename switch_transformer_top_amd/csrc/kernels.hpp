@@ -59,6 +59,18 @@ void launch_route_rows(const float* h, int64_t T, int N, int k, int32_t* expert_
 void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T, int k,
                        int64_t C, float alpha, int32_t* load, int32_t* n_kept, double* terms,
                        float* aux, int32_t* tile_start, int tile_rows, hipStream_t s);
+// One launch for the chunk scan, the loss and the finalisation (N <= 256,
+// chunks of at least 16 tokens, nc * N <= kAssignMaxCells).  copy_mode 0: no
+// rows move; 1: rows of dropped tokens from x to dst (= out, top-1); 2: rows of
+// kept assignments from x to dst (= Xbuf [N, C, row]).  tok may be NULL.
+constexpr int64_t kAssignMaxCells = 1 << 16;
+bool assign_one_launch_ok(int N, int64_t nc, int64_t chunk);
+void launch_assign(const int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T, int k,
+                   int64_t chunk, int64_t C, float alpha, const int32_t* expert_idx,
+                   const int32_t* rank_local, int32_t* load, int32_t* n_kept, float* aux,
+                   int32_t* tile_start, int tile_rows, int32_t* position, uint8_t* drop_mask,
+                   int32_t* tok, int copy_mode, int row_bytes, const void* x, void* dst,
+                   hipStream_t s);
 void launch_finalize_positions(int64_t T, int k, const int32_t* expert_idx,
                                const int32_t* rank_local, const int32_t* offsets, int N,
                                int64_t chunk, int64_t C, int32_t* position, uint8_t* drop_mask,

@@ -124,6 +124,12 @@ struct Routed {
   int32_t* rank;
   int64_t chunk;
   int64_t Cb;
+  // set when the scan is left to the one-launch assignment (finish_assignment)
+  bool one_launch = false;
+  int64_t nc = 0;
+  float* ppart = nullptr;
+  float* aux = nullptr;
+  const int32_t* expert_idx = nullptr;
 };
 
 // Routing stage (logits, softmax / top-1 / gate, chunk statistics, scan and
@@ -165,10 +171,31 @@ Routed enqueue_routing(switch_layer* L, const void* x, const float* given_logits
     }
   }
   const int64_t nc = (T + r.chunk - 1) / r.chunk;
-  swl::prof_mark(P, s, "route_scan");
-  swl::launch_route_scan(r.offsets, ppart, nc, N, T, top_k(c), r.Cb, c.alpha, r.load, r.nkept,
-                         (double*)(ws + lo.terms), aux_loss, r.tile_start, swl::kWideTileRows, s);
+  r.nc = nc;
+  r.ppart = ppart;
+  r.aux = aux_loss;
+  r.expert_idx = expert_idx;
+  r.one_launch = T > 0 && swl::assign_one_launch_ok(N, nc, r.chunk);
+  if (!r.one_launch) {
+    swl::prof_mark(P, s, "route_scan");
+    swl::launch_route_scan(r.offsets, ppart, nc, N, T, top_k(c), r.Cb, c.alpha, r.load, r.nkept,
+                           (double*)(ws + lo.terms), aux_loss, r.tile_start, swl::kWideTileRows,
+                           s);
+  }
   return r;
+}
+
+// With the one-launch assignment: scan, loss, positions, drops, the slot
+// table (tok, may be NULL) and the row copies of copy_mode in one kernel.
+void finish_assignment(switch_layer* L, const Routed& r, int64_t T, int32_t* position,
+                       uint8_t* drop_mask, int32_t* tok, int copy_mode, const void* x, void* dst,
+                       hipStream_t s) {
+  const switch_config& c = L->cfg;
+  swl::prof_mark(&L->prof, s, "assign");
+  swl::launch_assign(r.offsets, r.ppart, r.nc, c.n_experts, T, top_k(c), r.chunk, r.Cb, c.alpha,
+                     r.expert_idx, r.rank, r.load, r.nkept, r.aux, r.tile_start,
+                     swl::kWideTileRows, position, drop_mask, tok, copy_mode,
+                     (int)(dtype_size(c.act_dtype) * (size_t)c.d_model), x, dst, s);
 }
 
 switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
@@ -214,9 +241,13 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
     io.gate = gate;
     io.out = (uint16_t*)out;
     const bool fused = !expert_out && k == 1;
-    swl::prof_mark(P, s, "dispatch");
-    swl::launch_dispatch_index(x, T, k, (int)(es * d), expert_idx, r.rank, r.offsets, N, r.chunk,
-                               Cb, position, drop_mask, tok, fused, out, s);
+    if (r.one_launch) {
+      finish_assignment(L, r, T, position, drop_mask, tok, fused ? 1 : 0, x, out, s);
+    } else {
+      swl::prof_mark(P, s, "dispatch");
+      swl::launch_dispatch_index(x, T, k, (int)(es * d), expert_idx, r.rank, r.offsets, N,
+                                 r.chunk, Cb, position, drop_mask, tok, fused, out, s);
+    }
     swl::prof_mark(P, s, "gemm1_relu");
     swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
                                  hbuf, Cb * F, r.nkept, N, Cb, d, F, io, s);
@@ -237,9 +268,13 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
       }
     }
   } else if (T > 0) {
-    swl::prof_mark(P, s, "dispatch");
-    swl::launch_dispatch(x, T, k, (int)(es * d), expert_idx, r.rank, r.offsets, N, r.chunk, Cb,
-                         position, drop_mask, xbuf, s);
+    if (r.one_launch) {
+      finish_assignment(L, r, T, position, drop_mask, nullptr, 2, x, xbuf, s);
+    } else {
+      swl::prof_mark(P, s, "dispatch");
+      swl::launch_dispatch(x, T, k, (int)(es * d), expert_idx, r.rank, r.offsets, N, r.chunk, Cb,
+                           position, drop_mask, xbuf, s);
+    }
     swl::prof_mark(P, s, "gemm1_relu");
     swl::launch_expert_gemm(bf16, true, xbuf, Cb * d, L->W_in, (int64_t)F * d, hbuf, Cb * F,
                             r.nkept, N, Cb, d, F, s);
@@ -266,7 +301,9 @@ switch_status route_impl(switch_layer* L, const void* x, const float* given_logi
   swl::prof_begin(&L->prof);
   Routed r = enqueue_routing(L, x, given_logits, T, logits_out, expert_idx, gate, aux_loss, load,
                              (char*)ws, lo, s);
-  if (T > 0) {
+  if (r.one_launch) {
+    finish_assignment(L, r, T, position, drop_mask, nullptr, 0, nullptr, nullptr, s);
+  } else if (T > 0) {
     swl::prof_mark(&L->prof, s, "finalize");
     swl::launch_finalize_positions(T, top_k(L->cfg), expert_idx, r.rank, r.offsets,
                                    L->cfg.n_experts, r.chunk, r.Cb, position, drop_mask, s);
