@@ -292,8 +292,10 @@ __global__ __launch_bounds__(256) void assign_kernel(
   for (int j = 0; j < AS_MAXCH; ++j)
     own[j] = (tid < N && j < ncb) ? hist[(cb0 + j) * N + tid] : 0;
   int32_t acc = 0;
-  if (el < N)
+  if (el < N) {
+#pragma unroll 4
     for (int64_t c = g; c < cb0; c += G) acc += hist[c * N + el];
+  }
   // tokens routed to each expert in the chunks before cb0
   int32_t* s_base = s_off + (AS_MAXCH - 1) * 256;  // reused once the walk has read it
   if (tid < N) s_base[tid] = 0;

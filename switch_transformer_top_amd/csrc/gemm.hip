@@ -99,8 +99,7 @@ __device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ]
                                                    const float* __restrict__ gate,
                                                    uint16_t* __restrict__ out, int r0, int c0,
                                                    int rows_e, int d, int lane) {
-  constexpr int W = TJ * 32, LD = W + 8, CPR = W / 8, NR = TI * 32 / kWave;
-  static_assert(TI * 32 % kWave == 0, "whole waves of rows");
+  constexpr int W = TJ * 32, LD = W + 8, CPR = W / 8, NR = (TI * 32 + kWave - 1) / kWave;
   // lane l fetches the token and gate of rows l, l + 64, ... up front; the
   // store loop below takes them with a lane shuffle
   int tl[NR];
@@ -108,8 +107,9 @@ __device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ]
 #pragma unroll
   for (int q = 0; q < NR; ++q) {
     const int r = r0 + q * kWave + lane;
-    tl[q] = r < rows_e ? tok_e[r] : 0;
-    gl[q] = r < rows_e ? gate[tl[q]] : 0.f;
+    const bool ok = q * kWave + lane < TI * 32 && r < rows_e;
+    tl[q] = ok ? tok_e[r] : 0;
+    gl[q] = ok ? gate[tl[q]] : 0.f;
   }
   stage_tile_bf16<TI, TJ, LD, false>(acc, stage, lane);
 #pragma unroll
@@ -421,11 +421,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
 // groups owning the same 2 x 2 grid of 64 x 64 wave tiles; in every 64-wide K
 // step group 0 multiplies K sub-steps 0 and 1, group 1 sub-steps 2 and 3.  Two
 // LDS operand buffers, one barrier per step, the loads of step t + 2 in flight
-// during step t.  At the end group 1 hands its fp32 partial sums to group 0
-// through LDS and group 0 adds them (in that order) and runs the epilogue.
+// during step t.  At the end the groups exchange halves of their fp32 partial
+// sums through LDS and each finishes half of the rows (epilogue included).
 constexpr int GS_STAGE = (128 + 128) * GB_LDK;                      // elements per buffer
-constexpr size_t kSplitRed = (size_t)4 * 16 * 64 * 16;              // bytes of partial sums
-constexpr size_t kSplitLds = kSplitRed + (size_t)4 * 64 * (64 + 8) * sizeof(uint16_t);
+constexpr size_t kSplitRed = (size_t)8 * 8 * 64 * 16;              // bytes of partial sums
+constexpr size_t kSplitLds = kSplitRed + (size_t)8 * 32 * (64 + 8) * sizeof(uint16_t);
 
 template <bool RELU, int MODE>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
@@ -528,46 +528,55 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
     __syncthreads();
   }
 
-  // group 1's partial sums, laid out [wave tile][i, j, q][lane][4 floats] so
-  // that each 16-byte LDS access of a wave covers consecutive addresses
+  // The two groups finish one half of the tile each: group 0 the first MFMA
+  // row tile (i = 0) of its wave tile, group 1 the second.  Each hands the
+  // other half of its partial sums over through LDS, laid out
+  // [wave][j][q][lane][4 floats] so that every 16-byte LDS access of a wave
+  // covers consecutive addresses, and adds the half it receives to its own
+  // (fp32 addition commutes, so the sum is the same whichever group adds).
   float* red = reinterpret_cast<float*>(slds);
-  if (grp == 1) {
+  auto send = [&](const floatx16 (&a)[TJ]) {
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                            acc[i][j][4 * q + 3]};
-          *reinterpret_cast<float4*>(red + ((wq * 16 + (i * TJ + j) * 4 + q) * 64 + lane) * 4) = v;
-        }
-  }
-  __syncthreads();
-  if (grp == 1) return;
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = {a[j][4 * q], a[j][4 * q + 1], a[j][4 * q + 2], a[j][4 * q + 3]};
+        *reinterpret_cast<float4*>(red + ((wave * TJ * 4 + j * 4 + q) * 64 + lane) * 4) = v;
+      }
+  };
+  // group g's partner wave is wave ^ 4 (same wave tile, other group)
+  auto take = [&](floatx16 (&a)[TJ]) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 v = *reinterpret_cast<const float4*>(
-            red + ((wq * 16 + (i * TJ + j) * 4 + q) * 64 + lane) * 4);
-        acc[i][j][4 * q] += v.x;
-        acc[i][j][4 * q + 1] += v.y;
-        acc[i][j][4 * q + 2] += v.z;
-        acc[i][j][4 * q + 3] += v.w;
+            red + (((wave ^ 4) * TJ * 4 + j * 4 + q) * 64 + lane) * 4);
+        a[j][4 * q] += v.x;
+        a[j][4 * q + 1] += v.y;
+        a[j][4 * q + 2] += v.z;
+        a[j][4 * q + 3] += v.w;
       }
-  // epilogue staging lies past the partial sums
-  uint16_t* stage = slds + kSplitRed / sizeof(uint16_t) + wq * 64 * (64 + 8);
-  if (MODE == kRowsCombine)
-    store_tile_combine<TI, TJ>(acc, stage, tok_e, io.x, io.gate, io.out, m0 + wm * 64,
-                               n0 + wn * 64, rows_e, Nout, lane);
-  else if (MODE == kRowsMask)
-    store_tile_bf16<TI, TJ, false, true>(acc, stage, Ce, m0 + wm * 64, n0 + wn * 64, rows_e, Nout,
-                                         lane, io.mask + (int64_t)e * strideC);
-  else
-    store_tile_bf16<TI, TJ, RELU>(acc, stage, Ce, m0 + wm * 64, n0 + wn * 64, rows_e, Nout, lane);
+  };
+  static_assert((size_t)8 * TJ * 4 * 64 * 16 <= kSplitRed, "partial sums fit");
+  if (grp == 0) send(acc[1]); else send(acc[0]);
+  __syncthreads();
+  // epilogue staging lies past the partial sums: 32 rows of 64 + 8 bf16 per wave
+  uint16_t* stage = slds + kSplitRed / sizeof(uint16_t) + wave * 32 * (64 + 8);
+  auto finish = [&](floatx16 (&a)[TJ], int half) {
+    take(a);
+    floatx16 (&t)[1][TJ] = *reinterpret_cast<floatx16 (*)[1][TJ]>(&a);
+    const int r0 = m0 + wm * 64 + half * 32, c0 = n0 + wn * 64;
+    if (MODE == kRowsCombine)
+      store_tile_combine<1, TJ>(t, stage, tok_e, io.x, io.gate, io.out, r0, c0, rows_e, Nout,
+                                lane);
+    else if (MODE == kRowsMask)
+      store_tile_bf16<1, TJ, false, true>(t, stage, Ce, r0, c0, rows_e, Nout, lane,
+                                          io.mask + (int64_t)e * strideC);
+    else
+      store_tile_bf16<1, TJ, RELU>(t, stage, Ce, r0, c0, rows_e, Nout, lane);
+  };
+  if (grp == 0) finish(acc[0], 0); else finish(acc[1], 1);
 }
 
 // fp32 path (parity-sized fp32 layers): 32 x 32 tile, K in steps of 32, each

@@ -63,7 +63,7 @@ void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, in
 // chunks of at least 16 tokens, nc * N <= kAssignMaxCells).  copy_mode 0: no
 // rows move; 1: rows of dropped tokens from x to dst (= out, top-1); 2: rows of
 // kept assignments from x to dst (= Xbuf [N, C, row]).  tok may be NULL.
-constexpr int64_t kAssignMaxCells = 1 << 16;
+constexpr int64_t kAssignMaxCells = 8192;  // every block re-reads up to nc * N counts
 bool assign_one_launch_ok(int N, int64_t nc, int64_t chunk);
 void launch_assign(const int32_t* hist, const float* P_part, int64_t nc, int N, int64_t T, int k,
                    int64_t chunk, int64_t C, float alpha, const int32_t* expert_idx,
