@@ -91,7 +91,67 @@ __device__ __forceinline__ void store_tile_bf16(const floatx16 (&acc)[TI][TJ], u
 // Combine epilogue: like store_tile_bf16 (no ReLU), but each 16-byte piece of
 // output row m goes to token t = tok_e[m]: out[t] = x[t] + gate[t] * y, with y
 // the expert output rounded to bf16 first (the same arithmetic as a separate
-// combine pass over a stored expert output).
+// combine pass over a stored expert output).  The reads it needs (slot table,
+// gates, residual rows) are issued by combine_prefetch, which a kernel may call
+// early so that their latency overlaps other work.
+template <int TI, int TJ>
+struct CombineRows {
+  static constexpr int W = TJ * 32, LD = W + 8, CPR = W / 8;
+  static constexpr int NR = (TI * 32 + kWave - 1) / kWave;   // rows per lane
+  static constexpr int IT = TI * 32 * CPR / kWave;            // 16-byte pieces per lane
+  static constexpr int RPI = kWave / CPR;                     // rows per piece round
+  int64_t at[IT];   // element offset of each piece in x and out (-1: row not stored)
+  float g[IT];
+  u32x4 xv[IT];
+};
+
+template <int TI, int TJ>
+__device__ __forceinline__ void combine_prefetch(CombineRows<TI, TJ>& cr,
+                                                 const int32_t* __restrict__ tok_e,
+                                                 const uint16_t* __restrict__ x,
+                                                 const float* __restrict__ gate, int r0, int c0,
+                                                 int rows_e, int d, int lane) {
+  using CR = CombineRows<TI, TJ>;
+  // lane l fetches the token and gate of rows l, l + 64, ...; the pieces take
+  // them with a lane shuffle
+  int tl[CR::NR];
+  float gl[CR::NR];
+#pragma unroll
+  for (int q = 0; q < CR::NR; ++q) {
+    const int r = r0 + q * kWave + lane;
+    const bool ok = q * kWave + lane < TI * 32 && r < rows_e;
+    tl[q] = ok ? tok_e[r] : 0;
+    gl[q] = ok ? gate[tl[q]] : 0.f;
+  }
+#pragma unroll
+  for (int it = 0; it < CR::IT; ++it) {
+    const int idx = it * kWave + lane;
+    const int row = idx / CR::CPR, ch = idx - row * CR::CPR;
+    const int q = it * CR::RPI / kWave;              // register holding this row
+    const int64_t t = __shfl(tl[q], row & (kWave - 1), kWave);
+    cr.g[it] = __shfl(gl[q], row & (kWave - 1), kWave);
+    cr.at[it] = r0 + row < rows_e ? t * d + c0 + ch * 8 : -1;
+    cr.xv[it] = cr.at[it] >= 0 ? *reinterpret_cast<const u32x4*>(x + cr.at[it]) : u32x4{0, 0, 0, 0};
+  }
+}
+
+template <int TI, int TJ>
+__device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ], uint16_t* stage,
+                                                   const CombineRows<TI, TJ>& cr,
+                                                   uint16_t* __restrict__ out, int lane) {
+  using CR = CombineRows<TI, TJ>;
+  stage_tile_bf16<TI, TJ, CR::LD, false>(acc, stage, lane);
+#pragma unroll
+  for (int it = 0; it < CR::IT; ++it) {
+    const int idx = it * kWave + lane;
+    const int row = idx / CR::CPR, ch = idx - row * CR::CPR;
+    if (cr.at[it] >= 0) {
+      const u32x4 yv = *reinterpret_cast<const u32x4*>(stage + row * CR::LD + ch * 8);
+      *reinterpret_cast<u32x4*>(out + cr.at[it]) = combine_vec_bf16(cr.xv[it], yv, cr.g[it]);
+    }
+  }
+}
+
 template <int TI, int TJ>
 __device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ], uint16_t* stage,
                                                    const int32_t* __restrict__ tok_e,
@@ -99,34 +159,9 @@ __device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ]
                                                    const float* __restrict__ gate,
                                                    uint16_t* __restrict__ out, int r0, int c0,
                                                    int rows_e, int d, int lane) {
-  constexpr int W = TJ * 32, LD = W + 8, CPR = W / 8, NR = (TI * 32 + kWave - 1) / kWave;
-  // lane l fetches the token and gate of rows l, l + 64, ... up front; the
-  // store loop below takes them with a lane shuffle
-  int tl[NR];
-  float gl[NR];
-#pragma unroll
-  for (int q = 0; q < NR; ++q) {
-    const int r = r0 + q * kWave + lane;
-    const bool ok = q * kWave + lane < TI * 32 && r < rows_e;
-    tl[q] = ok ? tok_e[r] : 0;
-    gl[q] = ok ? gate[tl[q]] : 0.f;
-  }
-  stage_tile_bf16<TI, TJ, LD, false>(acc, stage, lane);
-#pragma unroll
-  for (int it = 0; it < TI * 32 * CPR / kWave; ++it) {
-    const int idx = it * kWave + lane;
-    const int row = idx / CPR, ch = idx - row * CPR;
-    constexpr int RPI = kWave / CPR;                 // rows per iteration
-    const int q = it * RPI / kWave;                  // register holding this row
-    const int64_t t = __shfl(tl[q], row & (kWave - 1), kWave);
-    const float gt = __shfl(gl[q], row & (kWave - 1), kWave);
-    if (r0 + row < rows_e) {
-      const int64_t at = t * d + c0 + ch * 8;
-      const u32x4 yv = *reinterpret_cast<const u32x4*>(stage + row * LD + ch * 8);
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(x + at);
-      *reinterpret_cast<u32x4*>(out + at) = combine_vec_bf16(xv, yv, gt);
-    }
-  }
+  CombineRows<TI, TJ> cr;
+  combine_prefetch<TI, TJ>(cr, tok_e, x, gate, r0, c0, rows_e, d, lane);
+  store_tile_combine<TI, TJ>(acc, stage, cr, out, lane);
 }
 
 // Tile order: the grid is 1-D.  Workgroups are handed to the 8 XCDs round
@@ -559,6 +594,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
       }
   };
   static_assert((size_t)8 * TJ * 4 * 64 * 16 <= kSplitRed, "partial sums fit");
+  // the combine's reads go out before the exchange
+  const int rh = m0 + wm * 64 + grp * 32, ch0 = n0 + wn * 64;
+  CombineRows<1, TJ> cr;
+  if (MODE == kRowsCombine)
+    combine_prefetch<1, TJ>(cr, tok_e, io.x, io.gate, rh, ch0, rows_e, Nout, lane);
   if (grp == 0) send(acc[1]); else send(acc[0]);
   __syncthreads();
   // epilogue staging lies past the partial sums: 32 rows of 64 + 8 bf16 per wave
@@ -568,8 +608,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
     floatx16 (&t)[1][TJ] = *reinterpret_cast<floatx16 (*)[1][TJ]>(&a);
     const int r0 = m0 + wm * 64 + half * 32, c0 = n0 + wn * 64;
     if (MODE == kRowsCombine)
-      store_tile_combine<1, TJ>(t, stage, tok_e, io.x, io.gate, io.out, r0, c0, rows_e, Nout,
-                                lane);
+      store_tile_combine<1, TJ>(t, stage, cr, io.out, lane);
     else if (MODE == kRowsMask)
       store_tile_bf16<1, TJ, false, true>(t, stage, Ce, r0, c0, rows_e, Nout, lane,
                                           io.mask + (int64_t)e * strideC);
