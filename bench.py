@@ -63,7 +63,9 @@ def stage_work(stage: str, spec, kept: int, active_experts: int, k: int = 1) -> 
         return dict(flops=2.0 * kept * d * F,
                     bytes=active_experts * d * F * es + kept * (F + 2 * d) * es + 8 * kept,
                     peak_tflops=peak)
-    if stage == "dispatch":
+    if stage in ("dispatch", "assign"):
+        # assign: the one-launch form (chunk scan and loss included; their
+        # per-chunk counts are a few bytes per token and are left out)
         if spec.act == "bf16":
             # slot table only (the rows stay in place); at top-1 dropped rows copied to out
             rows = 2 * (T - kept) * d * es if k == 1 else 0
@@ -99,6 +101,7 @@ STAGE_KERNEL = {"gemm1_relu": ("gemm_bf16_", "true, 1>", "gemm.hip"),
                 "gemm2_combine": ("gemm_bf16_", "false, 2>", "gemm.hip"),
                 "router": ("router_", "", "router.hip"),
                 "dispatch": ("dispatch_index_kernel", "", "move.hip"),
+                "assign": ("assign_kernel", "", "assign.hip"),
                 "combine": ("combine_kernel<", "", "move.hip")}
 
 
@@ -361,7 +364,7 @@ def main():
         "dropped_assignments": spec.T * args.top_k - kept,
         "expert_tflops": round(expert_tflops, 2),
         "expert_mfma_frac": round(expert_tflops / PEAK_BF16_TFLOPS, 4),
-        "dispatch_hbm_frac": rooflines.get("dispatch", {}).get("frac"),
+        "dispatch_hbm_frac": rooflines.get("dispatch", rooflines.get("assign", {})).get("frac"),
         "combine_hbm_frac": rooflines.get("combine", {}).get("frac"),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "stage_rooflines": rooflines,
