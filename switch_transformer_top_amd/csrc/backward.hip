@@ -210,6 +210,73 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restri
     part_b[(int64_t)blockIdx.z * N + i0 + threadIdx.x] = bacc;
 }
 
+// Few experts (N <= 32): one wave per (256-column block, token slice); lane l
+// owns columns 4 l .. 4 l + 3 of the block and every expert, so one 8-byte
+// load of x feeds 4 NP fused multiply-adds.  The slice's dh rows pass through
+// LDS in steps of RS_TOK tokens and are read back as broadcasts.  Partial sums
+// go to part[s] like the general kernel's; the reduction is the same.
+constexpr int RS_TOK = 32;
+
+template <int NP>
+__global__ __launch_bounds__(64) void router_wgrad_small_kernel(const float* __restrict__ dh,
+                                                               const uint16_t* __restrict__ x,
+                                                               int64_t T, int N, int d,
+                                                               int64_t slice,
+                                                               float* __restrict__ part,
+                                                               float* __restrict__ part_b) {
+  __shared__ __attribute__((aligned(16))) float Dh[RS_TOK * NP];
+  const int lane = threadIdx.x;
+  const int c0 = blockIdx.x * 256 + lane * 4;
+  const bool has_cols = c0 < d;
+  const int64_t ts = (int64_t)blockIdx.y * slice;
+  const int64_t te = ts + slice < T ? ts + slice : T;
+  float acc[NP][4];
+#pragma unroll
+  for (int i = 0; i < NP; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[i][c] = 0.f;
+  float bacc = 0.f;
+  for (int64_t t0 = ts; t0 < te; t0 += RS_TOK) {
+    const int nt = (int)(te - t0 < RS_TOK ? te - t0 : RS_TOK);
+    for (int idx = lane; idx < RS_TOK * NP; idx += kWave) {
+      const int r = idx / NP, i = idx - r * NP;
+      Dh[idx] = (r < nt && i < N) ? dh[(t0 + r) * N + i] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < nt; ++r) {
+      float xv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (has_cols) {
+        const uint2 v = *reinterpret_cast<const uint2*>(x + (t0 + r) * d + c0);
+        xv[0] = __uint_as_float(v.x << 16);
+        xv[1] = __uint_as_float(v.x & 0xFFFF0000u);
+        xv[2] = __uint_as_float(v.y << 16);
+        xv[3] = __uint_as_float(v.y & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int i4 = 0; i4 < NP / 4; ++i4) {
+        const float4 w = *reinterpret_cast<const float4*>(&Dh[r * NP + 4 * i4]);
+        const float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[4 * i4 + q][c] = fmaf(wv[q], xv[c], acc[4 * i4 + q][c]);
+      }
+      if (blockIdx.x == 0 && lane < N) bacc += Dh[r * NP + lane];
+    }
+    __syncthreads();
+  }
+  float* ps = part + (int64_t)blockIdx.y * N * d;
+  if (has_cols) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      if (i < N)
+        *reinterpret_cast<float4*>(ps + (int64_t)i * d + c0) =
+            make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+  }
+  if (blockIdx.x == 0 && lane < N) part_b[(int64_t)blockIdx.y * N + lane] = bacc;
+}
+
 // dW_r = sum over slices of part[s] (slice order); db likewise (when db != NULL).
 __global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restrict__ part,
                                                            const float* __restrict__ part_b,
@@ -348,12 +415,36 @@ void launch_router_bwd(const float* h, int64_t T, int N, int d, const void* G, c
                      drop_mask, load, loss_scale, dh);
 }
 
-int64_t router_wgrad_slices(int64_t T) { return T > 0 ? (T + RW_SLICE - 1) / RW_SLICE : 0; }
+// Tokens per slice of the few-expert kernel: at least RS_TOK, and at most 256
+// slices in all (bounds the partial sums at 256 N d floats).
+static int64_t small_slice(int64_t T) {
+  int64_t sl = (T + 255) / 256;
+  sl = (sl + RS_TOK - 1) / RS_TOK * RS_TOK;
+  return sl < RS_TOK ? RS_TOK : sl;
+}
+
+int64_t router_wgrad_slices(int64_t T, int N) {
+  if (T <= 0) return 0;
+  if (N <= 32) return (T + small_slice(T) - 1) / small_slice(T);
+  return (T + RW_SLICE - 1) / RW_SLICE;
+}
 
 void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d, float* part,
                          float* part_b, float* dW_r, float* db, hipStream_t s) {
-  const int64_t slices = router_wgrad_slices(T);
-  if (slices > 0) {
+  const int64_t slices = router_wgrad_slices(T, N);
+  if (slices > 0 && N <= 32) {
+    const dim3 grid((unsigned)((d + 255) / 256), (unsigned)slices);
+    const int64_t sl = small_slice(T);
+    if (N <= 8)
+      hipLaunchKernelGGL(router_wgrad_small_kernel<8>, grid, dim3(64), 0, s, dh,
+                         (const uint16_t*)x, T, N, d, sl, part, part_b);
+    else if (N <= 16)
+      hipLaunchKernelGGL(router_wgrad_small_kernel<16>, grid, dim3(64), 0, s, dh,
+                         (const uint16_t*)x, T, N, d, sl, part, part_b);
+    else
+      hipLaunchKernelGGL(router_wgrad_small_kernel<32>, grid, dim3(64), 0, s, dh,
+                         (const uint16_t*)x, T, N, d, sl, part, part_b);
+  } else if (slices > 0) {
     const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)slices);
     hipLaunchKernelGGL(router_wgrad_kernel, grid, dim3(256), 0, s, dh, (const uint16_t*)x, T, N,
                        d, part, part_b);
