@@ -243,26 +243,33 @@ __global__ __launch_bounds__(64) void router_wgrad_small_kernel(const float* __r
       Dh[idx] = (r < nt && i < N) ? dh[(t0 + r) * N + i] : 0.f;
     }
     __syncthreads();
-#pragma unroll 4
-    for (int r = 0; r < nt; ++r) {
-      float xv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (has_cols) {
-        const uint2 v = *reinterpret_cast<const uint2*>(x + (t0 + r) * d + c0);
-        xv[0] = __uint_as_float(v.x << 16);
-        xv[1] = __uint_as_float(v.x & 0xFFFF0000u);
-        xv[2] = __uint_as_float(v.y << 16);
-        xv[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    // rows of x eight at a time, all eight in flight at once (rows past the
+    // slice read as 0)
+#pragma unroll 1
+    for (int rb = 0; rb < RS_TOK; rb += 8) {
+      uint2 xr[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        xr[u] = (has_cols && rb + u < nt)
+                    ? *reinterpret_cast<const uint2*>(x + (t0 + rb + u) * d + c0)
+                    : make_uint2(0u, 0u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = rb + u;
+        const uint2 v = xr[u];
+        const float xv[4] = {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                             __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
+#pragma unroll
+        for (int i4 = 0; i4 < NP / 4; ++i4) {
+          const float4 w = *reinterpret_cast<const float4*>(&Dh[r * NP + 4 * i4]);
+          const float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[4 * i4 + q][c] = fmaf(wv[q], xv[c], acc[4 * i4 + q][c]);
+        }
+        if (blockIdx.x == 0 && lane < N && r < nt) bacc += Dh[r * NP + lane];
       }
-#pragma unroll
-      for (int i4 = 0; i4 < NP / 4; ++i4) {
-        const float4 w = *reinterpret_cast<const float4*>(&Dh[r * NP + 4 * i4]);
-        const float wv[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc[4 * i4 + q][c] = fmaf(wv[q], xv[c], acc[4 * i4 + q][c]);
-      }
-      if (blockIdx.x == 0 && lane < N) bacc += Dh[r * NP + lane];
     }
     __syncthreads();
   }
@@ -277,24 +284,34 @@ __global__ __launch_bounds__(64) void router_wgrad_small_kernel(const float* __r
   if (blockIdx.x == 0 && lane < N) part_b[(int64_t)blockIdx.y * N + lane] = bacc;
 }
 
-// dW_r = sum over slices of part[s] (slice order); db likewise (when db != NULL).
+// dW_r = sum over slices of part[s]; db likewise (when db != NULL).  A block
+// takes 64 consecutive outputs; its four waves add every fourth slice (wave w:
+// slices w, w + 4, ...) in slice order, and the four partial sums are added in
+// wave order.  Fixed order throughout.
 __global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restrict__ part,
                                                            const float* __restrict__ part_b,
                                                            int slices, int N, int d,
                                                            float* __restrict__ dW_r,
                                                            float* __restrict__ db) {
+  __shared__ float red[4][64];
   const int64_t n = (int64_t)N * d;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n + N;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    float acc = 0.f;
-    if (i < n) {
-      for (int s = 0; s < slices; ++s) acc += part[(int64_t)s * n + i];
-      dW_r[i] = acc;
-    } else if (db) {
-      const int64_t j = i - n;
-      for (int s = 0; s < slices; ++s) acc += part_b[(int64_t)s * N + j];
-      db[j] = acc;
-    }
+  const int o = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + o;
+  float acc = 0.f;
+  if (i < n) {
+#pragma unroll 8
+    for (int sl = w; sl < slices; sl += 4) acc += part[(int64_t)sl * n + i];
+  } else if (i < n + N && db) {
+    const int64_t j = i - n;
+#pragma unroll 8
+    for (int sl = w; sl < slices; sl += 4) acc += part_b[(int64_t)sl * N + j];
+  }
+  red[w][o] = acc;
+  __syncthreads();
+  if (w == 0) {
+    const float v = ((red[0][o] + red[1][o]) + red[2][o]) + red[3][o];
+    if (i < n) dW_r[i] = v;
+    else if (i < n + N && db) db[i - n] = v;
   }
 }
 
@@ -450,9 +467,8 @@ void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d
                        d, part, part_b);
   }
   const int64_t n = (int64_t)N * d + N;
-  const int64_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(router_wgrad_reduce, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
-                     dim3(256), 0, s, part, part_b, (int)slices, N, d, dW_r, db);
+  hipLaunchKernelGGL(router_wgrad_reduce, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, part,
+                     part_b, (int)slices, N, d, dW_r, db);
 }
 
 void launch_grad_x(const void* G, int64_t T, int d, const int32_t* expert_idx,
