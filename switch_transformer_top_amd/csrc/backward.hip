@@ -23,10 +23,15 @@
 namespace swl {
 
 // n_kept[e] = min(load[e], C) (the forward's per-expert loads).
-__global__ __launch_bounds__(256) void bwd_rows_kernel(const int32_t* __restrict__ load, int N,
-                                                       int64_t C, int32_t* __restrict__ n_kept) {
-  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < N; e += gridDim.x * blockDim.x)
+__global__ __launch_bounds__(1024) void bwd_rows_kernel(const int32_t* __restrict__ load, int N,
+                                                        int64_t C, int32_t* __restrict__ n_kept,
+                                                        int32_t* __restrict__ tile_start,
+                                                        int tile_rows) {
+  __shared__ int32_t s_run[1024];
+  for (int e = threadIdx.x; e < N; e += blockDim.x)
     n_kept[e] = (int32_t)((int64_t)load[e] < C ? (int64_t)load[e] : C);
+  __syncthreads();
+  if (tile_start) tile_prefix_block(n_kept, N, tile_rows, tile_start, s_run);
 }
 
 // Slot table and scaled output gradient of every kept token:
@@ -398,9 +403,10 @@ void launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
                      0, s, (u32x4*)p, n);
 }
 
-void launch_bwd_rows(const int32_t* load, int N, int64_t C, int32_t* n_kept, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, load, N,
-                     C, n_kept);
+void launch_bwd_rows(const int32_t* load, int N, int64_t C, int32_t* n_kept,
+                     int32_t* tile_start, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_rows_kernel, dim3(1), dim3(1024), 0, s, load, N, C, n_kept, tile_start,
+                     kWideTileRows);
 }
 
 void launch_bwd_slots(const void* G, int64_t T, int d, const int32_t* expert_idx,

@@ -95,4 +95,33 @@ __device__ __forceinline__ void wave_argmax(float& v, int& idx) {
   }
 }
 
+// tile_start[e] = sum over e' < e of ceil(n_kept[e'] / tile_rows), and
+// tile_start[N] the total: the compact tile list of the grouped matmuls.  The
+// whole block calls it; each thread takes a contiguous run of experts.  s_run:
+// blockDim.x ints of LDS.
+__device__ __forceinline__ void tile_prefix_block(const int32_t* __restrict__ n_kept, int N, int tile_rows,
+                                  int32_t* __restrict__ tile_start, int32_t* s_run) {
+  const int tid = threadIdx.x;
+  const int nthr = (int)blockDim.x;
+  const int per = (N + nthr - 1) / nthr;
+  const int used = (N + per - 1) / per;             // threads that own experts
+  const int e0 = tid * per, e1 = (e0 + per < N) ? e0 + per : N;
+  int32_t sum = 0;
+  for (int e = e0; e < e1; ++e) sum += (n_kept[e] + tile_rows - 1) / tile_rows;
+  s_run[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < used; off <<= 1) {
+    const int32_t v = tid >= off ? s_run[tid - off] : 0;
+    __syncthreads();
+    s_run[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = s_run[tid] - sum;
+  for (int e = e0; e < e1; ++e) {
+    tile_start[e] = run;
+    run += (n_kept[e] + tile_rows - 1) / tile_rows;
+  }
+  if (tid == used - 1) tile_start[N] = s_run[tid];
+}
+
 }  // namespace swl

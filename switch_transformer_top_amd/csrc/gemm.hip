@@ -310,7 +310,10 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
 // 256-row M tiles, from the routing scan): block b takes list entry
 // (b % 8) * ceil(total / 8) + b / 8, so each XCD walks one stretch of the list
 // (order expert, N tile, M tile), and a grid sized for full capacity leaves
-// its extra blocks idle.  No XCD gets more tiles than its share.
+// its extra blocks idle.  No XCD gets more tiles than its share.  Without a
+// list every expert has the full count of M tiles (the weight-gradient
+// matmuls, whose rows are all valid).  Epilogue modes: plain (optional ReLU)
+// and the ReLU-derivative mask of the backward pass.
 constexpr int GW_BM = 256, GW_BN = 256;
 constexpr size_t kWideLds = (size_t)2 * (GW_BM + GW_BN) * GB_LDK * sizeof(uint16_t);
 
@@ -330,29 +333,41 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
   (void)tiles;
 
   const int32_t* ts = io.tile_start;
-  const int total = ts[n_exp] * n_tiles;
-  const int per_xcd = (total + 7) >> 3;
-  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if ((int)(blockIdx.x >> 3) >= per_xcd || tile >= total) return;
-  // expert: the last e with ts[e] * n_tiles <= tile (it has M tiles)
-  int lo = 0, hi = n_exp - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (ts[mid] * n_tiles <= tile) lo = mid; else hi = mid - 1;
+  int e, me, local, tile;
+  if (ts) {
+    const int total = ts[n_exp] * n_tiles;
+    const int per_xcd = (total + 7) >> 3;
+    tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if ((int)(blockIdx.x >> 3) >= per_xcd || tile >= total) return;
+    // expert: the last e with ts[e] * n_tiles <= tile (it has M tiles)
+    int lo = 0, hi = n_exp - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ts[mid] * n_tiles <= tile) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+    me = ts[e + 1] - ts[e];
+    local = tile - ts[e] * n_tiles;
+  } else {
+    // no tile list: every expert has m_tiles M tiles (rows past its count return)
+    const int per_xcd = (tiles + 7) >> 3;
+    tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (tile >= tiles) return;
+    me = m_tiles;
+    e = tile / (m_tiles * n_tiles);
+    local = tile - e * m_tiles * n_tiles;
   }
-  const int e = lo;
-  const int me = ts[e + 1] - ts[e];
-  const int local = tile - ts[e] * n_tiles;
   const int nt = local / me;
   const int mt = local - nt * me;
-  const int rows_e = rows[e];
+  const int rows_e = rows ? rows[e] : (int)C;
   const int m0 = mt * BM;
+  if (m0 >= rows_e) return;
   const int n0 = nt * BN;
 
   const uint16_t* Ae = MODE == kRowsGather ? io.x : A + (int64_t)e * strideA;
   const uint16_t* Be = B + (int64_t)e * strideB + (int64_t)n0 * K;
   uint16_t* Ce = Cout + (int64_t)e * strideC;
-  const int32_t* tok_e = MODE == kRowsDense ? nullptr : io.tok + (int64_t)e * C;
+  const int32_t* tok_e = MODE == kRowsGather ? io.tok + (int64_t)e * C : nullptr;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -441,9 +456,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
 
   __syncthreads();  // every wave is done with the LDS operand buffers
   uint16_t* stage = wlds + wave * 128 * (64 + 8);
-  if (MODE == kRowsCombine)
-    store_tile_combine<TI, TJ>(acc, stage, tok_e, io.x, io.gate, io.out, m0 + wm * 128,
-                               n0 + wn * 64, rows_e, Nout, lane);
+  static_assert(MODE != kRowsCombine, "the combine runs on the split-K and 128-row tiles");
+  if (MODE == kRowsMask)
+    store_tile_bf16<TI, TJ, false, true>(acc, stage, Ce, m0 + wm * 128, n0 + wn * 64, rows_e,
+                                         Nout, lane, io.mask + (int64_t)e * strideC);
   else
     store_tile_bf16<TI, TJ, RELU>(acc, stage, Ce, m0 + wm * 128, n0 + wn * 64, rows_e, Nout,
                                   lane);
@@ -673,11 +689,28 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 namespace {
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 // The wide tile pays off when experts hold at least two of its M tiles and N
-// splits into 256-column tiles.
-bool use_wide(int64_t C, int Nout, const GemmIO& io) {
+// splits into 256-column tiles; without a compact tile list (every expert at
+// full capacity) also only when there are tiles for at least two rounds of CUs.
+bool use_wide(int64_t C, int Nout, int n_experts, const GemmIO& io) {
   static_assert(GW_BM == kWideTileRows, "tile list and kernel agree");
-  return io.tile_start && C >= 2 * GW_BM && Nout % GW_BN == 0;
+  const int64_t tiles = (C + GW_BM - 1) / GW_BM * (Nout / GW_BN) * n_experts;
+  return C >= 2 * GW_BM && Nout % GW_BN == 0 && (io.tile_start || tiles >= 2 * device_cus());
 }
 
 template <bool RELU, int MODE>
@@ -699,21 +732,6 @@ void launch_wide(const uint16_t* a, int64_t strideA, const uint16_t* b, int64_t 
   hipLaunchKernelGGL((gemm_bf16_wide_kernel<RELU, MODE>), dim3(grid), dim3(512), kWideLds, s, a,
                      strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C,
                      n_experts);
-}
-
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  if (dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
 }
 
 template <bool RELU, int MODE>
@@ -743,9 +761,19 @@ void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t st
   const uint16_t* a = (const uint16_t*)A;
   const uint16_t* b = (const uint16_t*)B;
   uint16_t* c = (uint16_t*)Cout;
-  if (mode == kRowsGather && relu && use_wide(C, Nout, io)) {
-    launch_wide<true, kRowsGather>(a, strideA, b, strideB, c, strideC, rows, n_experts, C, K,
-                                   Nout, io, s);
+  if (mode != kRowsCombine && use_wide(C, Nout, n_experts, io)) {
+    if (mode == kRowsGather && relu)
+      launch_wide<true, kRowsGather>(a, strideA, b, strideB, c, strideC, rows, n_experts, C, K,
+                                     Nout, io, s);
+    else if (mode == kRowsMask)
+      launch_wide<false, kRowsMask>(a, strideA, b, strideB, c, strideC, rows, n_experts, C, K,
+                                    Nout, io, s);
+    else if (mode == kRowsDense && !relu)
+      launch_wide<false, kRowsDense>(a, strideA, b, strideB, c, strideC, rows, n_experts, C, K,
+                                     Nout, io, s);
+    else
+      launch_wide<true, kRowsDense>(a, strideA, b, strideB, c, strideC, rows, n_experts, C, K,
+                                    Nout, io, s);
     return;
   }
   constexpr int BM = 128, BN = 128;

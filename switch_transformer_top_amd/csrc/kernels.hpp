@@ -119,7 +119,10 @@ bool expert_gemm_shape_ok(bool bf16, int d, int F);
 constexpr int kWideTileRows = 256;   // M tile of the wide bf16 kernel
 
 // backward.hip
-void launch_bwd_rows(const int32_t* load, int N, int64_t C, int32_t* n_kept, hipStream_t s);
+// n_kept = min(load, C) and the compact tile list of kWideTileRows-row tiles
+// (tile_start may be NULL)
+void launch_bwd_rows(const int32_t* load, int N, int64_t C, int32_t* n_kept,
+                     int32_t* tile_start, hipStream_t s);
 void launch_bwd_slots(const void* G, int64_t T, int d, const int32_t* expert_idx,
                       const int32_t* position, const uint8_t* drop_mask, const float* gate,
                       int64_t C, int32_t* tok, void* Gs, hipStream_t s);

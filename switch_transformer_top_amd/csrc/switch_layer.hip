@@ -251,6 +251,9 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
     swl::prof_mark(P, s, "gemm1_relu");
     swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
                                  hbuf, Cb * F, r.nkept, N, Cb, d, F, io, s);
+    // GEMM2 runs on the same tiles with or without the fused combine (the
+    // tile list is GEMM1's), so both paths give the same expert outputs
+    io.tile_start = nullptr;
     if (fused) {
       swl::prof_mark(P, s, "gemm2_combine");
       swl::launch_expert_gemm_bf16(swl::kRowsCombine, false, hbuf, Cb * F, L->W_out,
@@ -316,8 +319,8 @@ switch_status route_impl(switch_layer* L, const void* x, const float* given_logi
 // to 64: the weight-gradient matmuls run over the expert's rows as their K
 // dimension, zero-padded to whole K steps.
 struct BwdLayout {
-  size_t nkept, tok, gs, hbuf, ybuf, du, dxe, woutT, winT, gsT, hT, duT, xT, dh, wpart, bpart,
-      total;
+  size_t nkept, tiles, tok, gs, hbuf, ybuf, du, dxe, woutT, winT, gsT, hT, duT, xT, dh, wpart,
+      bpart, total;
   int64_t Cb, Cbp;
 };
 
@@ -331,6 +334,7 @@ BwdLayout bwd_layout_of(const switch_layer* L, int64_t T) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes); return at; };
   lo.nkept = take(4 * N);
+  lo.tiles = take(4 * (N + 1));
   lo.tok = take(4 * N * Cb);
   lo.gs = take(2 * N * Cb * d);
   lo.hbuf = take(2 * N * Cb * F);
@@ -373,16 +377,21 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
   swl::prof_begin(P);
   if (T > 0) {
     swl::prof_mark(P, s, "bwd_slots");
-    swl::launch_bwd_rows(load, N, Cb, nkept, s);
+    int32_t* tiles = (int32_t*)(w + lo.tiles);
+    swl::launch_bwd_rows(load, N, Cb, nkept, tiles, s);
     swl::launch_bwd_slots(grad_out, T, d, expert_idx, position, drop_mask, gate, Cb, tok, gs, s);
+    // io_rows: products over the experts' token rows with F columns (the tile
+    // list of 256-row tiles applies); io: the rest
     swl::GemmIO io;
     io.tok = tok;
     io.x = (const uint16_t*)x;
+    swl::GemmIO io_rows = io;
+    io_rows.tile_start = tiles;
     if (Cb > 0) {
       // the forward's expert activations, recomputed
       swl::prof_mark(P, s, "recompute_h");
       swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
-                                   hbuf, Cb * F, nkept, N, Cb, d, F, io, s);
+                                   hbuf, Cb * F, nkept, N, Cb, d, F, io_rows, s);
       swl::prof_mark(P, s, "recompute_y");
       swl::launch_expert_gemm_bf16(swl::kRowsDense, false, hbuf, Cb * F, L->W_out,
                                    (int64_t)d * F, ybuf, Cb * d, nkept, N, Cb, F, d, io, s);
@@ -404,9 +413,9 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
                             (int64_t)d * F, F, N, s);
       // dU = (Gs W_out[e]) * [H > 0]
       swl::prof_mark(P, s, "grad_h");
-      io.mask = (const uint16_t*)hbuf;
+      io_rows.mask = (const uint16_t*)hbuf;
       swl::launch_expert_gemm_bf16(swl::kRowsMask, false, gs, Cb * d, woutT, (int64_t)F * d, du,
-                                   Cb * F, nkept, N, Cb, d, F, io, s);
+                                   Cb * F, nkept, N, Cb, d, F, io_rows, s);
       // dX = dU W_in[e]
       swl::prof_mark(P, s, "grad_x_expert");
       swl::launch_expert_gemm_bf16(swl::kRowsDense, false, du, Cb * F, winT, (int64_t)d * F, dxe,
