@@ -634,6 +634,221 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
   if (grp == 0) finish(acc[0], 0); else finish(acc[1], 1);
 }
 
+// ---------------------------------------------------------------------------
+// Grouped matmul with operands in either layout, for the backward pass, where
+// the products contract over a dimension that is not innermost in memory:
+// dU = Gs W_out[e] and dX = dU W_in[e] read the weights as stored ([K][N], N
+// innermost), dW_out = Gs^T H and dW_in = dU^T X read activations [rows][*]
+// with the rows as K.  A K-outer operand tile is staged in LDS as stored
+// ([64 k][R + 8] per K step, 16-byte row pieces) and its MFMA fragments come
+// from ds_read_b64_tr_b16: in each group of 16 lanes, source lane 4 q + p
+// addresses row q and columns 4 p .. 4 p + 3 of a 4 x 16 block and lane i
+// receives column i of rows 0..3, so two such reads give a lane its column's
+// 8 consecutive k.  K-contiguous operands are staged as in the kernels above.
+//
+// Tile BM x BN with BN / 64 x 2 waves, each (BM / 2) x 64; two LDS operand
+// buffers, one barrier per K step, the loads of step t + 2 in flight during
+// step t; tile order as the wide kernel (compact list, or every expert at full
+// capacity).  Rows of a K-outer operand at or past io.krows[e] read as zero
+// (the expert's rows beyond its kept count).
+// ---------------------------------------------------------------------------
+constexpr int KO_PAD = 8;
+
+template <int R, int NTHR, bool KOUTER>
+struct OpLayout {
+  static constexpr int PITCH = KOUTER ? R + KO_PAD : GB_LDK;      // LDS row pitch (elements)
+  static constexpr int ELEMS = KOUTER ? GB_BK * PITCH : R * GB_LDK;
+  static constexpr int P = R * GB_BK / 8 / NTHR;                   // 16-byte pieces per thread
+  // K-contiguous: thread -> (row, 8-wide k chunk); K-outer: (k row, 8-wide column chunk)
+  static constexpr int CPR = KOUTER ? R / 8 : GB_BK / 8;          // chunks per LDS row
+  static constexpr int RPP = NTHR / CPR;                           // LDS rows per pass
+  static_assert(P * NTHR * 8 == R * GB_BK && RPP * CPR == NTHR, "whole passes");
+};
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// Fragment of 32 columns starting at col of a K-outer LDS tile, K sub-step ks.
+__device__ __forceinline__ bf16x8 frag_kouter(const uint16_t* tile, int pitch, int ks, int col,
+                                              int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int row = ks * 16 + 8 * (g >> 1) + (j >> 2);
+  const int c = col + 16 * (g & 1) + 4 * (j & 3);
+  const uint16_t* p0 = tile + row * pitch + c;
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)p0);
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p0 + 4 * pitch));
+  typedef short shortx8 __attribute__((ext_vector_type(8)));
+  const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int BM, int BN, bool AKO, bool BKO, bool RELU, int MODE>
+__global__ __launch_bounds__(BN * 2, 1) void gemm_bf16_t_kernel(
+    const uint16_t* __restrict__ A, int64_t strideA, const uint16_t* __restrict__ B,
+    int64_t strideB, uint16_t* __restrict__ Cout, int64_t strideC,
+    const int32_t* __restrict__ rows, int K, int Nout, int m_tiles, int n_tiles, int tiles,
+    GemmIO io, int64_t C, int n_exp) {
+  constexpr int NTHR = BN * 2, WN = BN / 64, TI = BM / 64, TJ = 2;
+  using LA = OpLayout<BM, NTHR, AKO>;
+  using LB = OpLayout<BN, NTHR, BKO>;
+  constexpr int STAGE = LA::ELEMS + LB::ELEMS;
+  static_assert(MODE == kRowsDense || MODE == kRowsMask, "plain or masked epilogue");
+  extern __shared__ __attribute__((aligned(16))) uint16_t tlds[];
+
+  const int32_t* ts = io.tile_start;
+  int e, me, local, tile;
+  if (ts) {
+    const int total = ts[n_exp] * n_tiles;
+    const int per_xcd = (total + 7) >> 3;
+    tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if ((int)(blockIdx.x >> 3) >= per_xcd || tile >= total) return;
+    int lo = 0, hi = n_exp - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ts[mid] * n_tiles <= tile) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+    me = ts[e + 1] - ts[e];
+    local = tile - ts[e] * n_tiles;
+  } else {
+    const int per_xcd = (tiles + 7) >> 3;
+    tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (tile >= tiles) return;
+    me = m_tiles;
+    e = tile / (m_tiles * n_tiles);
+    local = tile - e * m_tiles * n_tiles;
+  }
+  const int nt = local / me;
+  const int mt = local - nt * me;
+  const int rows_e = rows ? rows[e] : (int)C;
+  const int m0 = mt * BM;
+  if (m0 >= rows_e) return;
+  const int n0 = nt * BN;
+  const int krows = io.krows ? io.krows[e] : K;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int nk = K / GB_BK;
+
+  // global element offsets of this thread's pieces at K step 0 and their LDS
+  // offsets; a K-outer piece also records its k row (for the krows test)
+  const uint16_t* Ae = A + (int64_t)e * strideA;
+  const uint16_t* Be = B + (int64_t)e * strideB;
+  int64_t ga[LA::P], gb[LB::P];
+  int la[LA::P], lb[LB::P], ka[LA::P], kb[LB::P];
+  const int64_t a_step = AKO ? (int64_t)GB_BK * io.lda : GB_BK;
+  const int64_t b_step = BKO ? (int64_t)GB_BK * io.ldb : GB_BK;
+#pragma unroll
+  for (int j = 0; j < LA::P; ++j) {
+    const int r = tid / LA::CPR + LA::RPP * j, c = (tid % LA::CPR) * 8;
+    if (AKO) {
+      ga[j] = (int64_t)r * io.lda + m0 + c;
+      ka[j] = r;
+    } else {
+      int row = m0 + r;
+      row = row < rows_e ? row : rows_e - 1;  // rows past the count: any valid row, never stored
+      ga[j] = (int64_t)row * K + c;
+      ka[j] = 0;
+    }
+    la[j] = r * LA::PITCH + c;
+  }
+#pragma unroll
+  for (int j = 0; j < LB::P; ++j) {
+    const int r = tid / LB::CPR + LB::RPP * j, c = (tid % LB::CPR) * 8;
+    if (BKO) {
+      gb[j] = (int64_t)r * io.ldb + n0 + c;
+      kb[j] = r;
+    } else {
+      gb[j] = (int64_t)(n0 + r) * K + c;
+      kb[j] = 0;
+    }
+    lb[j] = r * LB::PITCH + c;
+  }
+  u32x4 ra[LA::P], rb[LB::P];
+  auto gload = [&](int t) {
+    t = t < nk ? t : nk - 1;
+#pragma unroll
+    for (int j = 0; j < LA::P; ++j)
+      ra[j] = (!AKO || t * GB_BK + ka[j] < krows)
+                  ? *reinterpret_cast<const u32x4*>(Ae + ga[j] + t * a_step)
+                  : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < LB::P; ++j)
+      rb[j] = (!BKO || t * GB_BK + kb[j] < krows)
+                  ? *reinterpret_cast<const u32x4*>(Be + gb[j] + t * b_step)
+                  : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto gstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < LA::P; ++j)
+      *reinterpret_cast<u32x4*>(&tlds[buf * STAGE + la[j]]) = ra[j];
+#pragma unroll
+    for (int j = 0; j < LB::P; ++j)
+      *reinterpret_cast<u32x4*>(&tlds[buf * STAGE + LA::ELEMS + lb[j]]) = rb[j];
+  };
+  floatx16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  auto step = [&](int buf) {
+    const uint16_t* At = tlds + buf * STAGE;
+    const uint16_t* Bt = At + LA::ELEMS;
+#pragma unroll
+    for (int ks = 0; ks < GB_BK / 16; ++ks) {
+      bf16x8 a[TI], b[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        a[i] = AKO ? frag_kouter(At, LA::PITCH, ks, wm * (BM / 2) + i * 32, lane)
+                   : *reinterpret_cast<const bf16x8*>(
+                         &At[(wm * (BM / 2) + i * 32 + fr) * LA::PITCH + ks * 16 + fk]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        b[j] = BKO ? frag_kouter(Bt, LB::PITCH, ks, wn * 64 + j * 32, lane)
+                   : *reinterpret_cast<const bf16x8*>(
+                         &Bt[(wn * 64 + j * 32 + fr) * LB::PITCH + ks * 16 + fk]);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  gload(0);
+  gstore(0);
+  gload(1);
+  __syncthreads();
+  for (int t = 0; t < nk; ++t) {
+    const int cur = t & 1, nxt = cur ^ 1;
+    // buffer nxt was last read in step t - 1, before the barrier that ended it
+    gstore(nxt);
+    gload(t + 2);
+    step(cur);
+    __syncthreads();
+  }
+
+  uint16_t* stage = tlds + wave * (BM / 2) * (64 + 8);
+  uint16_t* Ce = Cout + (int64_t)e * strideC;
+  if (MODE == kRowsMask)
+    store_tile_bf16<TI, TJ, false, true>(acc, stage, Ce, m0 + wm * (BM / 2), n0 + wn * 64, rows_e,
+                                         Nout, lane, io.mask + (int64_t)e * strideC);
+  else
+    store_tile_bf16<TI, TJ, RELU>(acc, stage, Ce, m0 + wm * (BM / 2), n0 + wn * 64, rows_e, Nout,
+                                  lane);
+}
+
+template <int BM, int BN, bool AKO, bool BKO>
+constexpr size_t t_kernel_lds() {
+  constexpr size_t ops = 2 * (OpLayout<BM, BN * 2, AKO>::ELEMS + OpLayout<BN, BN * 2, BKO>::ELEMS);
+  constexpr size_t epi = (size_t)(BN / 64) * 2 * (BM / 2) * (64 + 8);
+  return (ops > epi ? ops : epi) * sizeof(uint16_t);
+}
+
 // fp32 path (parity-sized fp32 layers): 32 x 32 tile, K in steps of 32, each
 // of 256 threads owns 4 rows of one column.  Any sizes (bounds-checked).
 template <bool RELU>
@@ -751,7 +966,63 @@ void launch_split(unsigned grid, const uint16_t* a, int64_t strideA, const uint1
                      strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
 }
 
+template <int BM, int BN, bool AKO, bool BKO, bool RELU, int MODE>
+void launch_t(const uint16_t* a, int64_t strideA, const uint16_t* b, int64_t strideB,
+              uint16_t* c, int64_t strideC, const int32_t* rows, int n_experts, int64_t C, int K,
+              int Nout, const GemmIO& io, hipStream_t s) {
+  constexpr size_t lds = t_kernel_lds<BM, BN, AKO, BKO>();
+  auto kern = gemm_bf16_t_kernel<BM, BN, AKO, BKO, RELU, MODE>;
+  static uint64_t set_on = 0;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (lds > 65536 && dev < 64 && !(set_on >> dev & 1)) {
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+    set_on |= 1ull << dev;
+  }
+  const int mt = (int)((C + BM - 1) / BM), nt = Nout / BN;
+  const int tiles = mt * nt * n_experts;
+  const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(BN * 2), lds, s, a, strideA, b, strideB, c, strideC,
+                     rows, K, Nout, mt, nt, tiles, io, C, n_experts);
+}
+
+template <int BM, int BN>
+void launch_t_sized(GemmRows mode, bool relu, bool a_ko, bool b_ko, const uint16_t* a,
+                    int64_t strideA, const uint16_t* b, int64_t strideB, uint16_t* c,
+                    int64_t strideC, const int32_t* rows, int n_experts, int64_t C, int K,
+                    int Nout, const GemmIO& io, hipStream_t s) {
+#define SWL_T(AK, BK, RL, MD)                                                                    \
+  launch_t<BM, BN, AK, BK, RL, MD>(a, strideA, b, strideB, c, strideC, rows, n_experts, C, K, \
+                                   Nout, io, s)
+  if (mode == kRowsMask && !a_ko && b_ko) SWL_T(false, true, false, kRowsMask);
+  else if (mode == kRowsDense && !relu && !a_ko && b_ko) SWL_T(false, true, false, kRowsDense);
+  else if (mode == kRowsDense && !relu && a_ko && b_ko) SWL_T(true, true, false, kRowsDense);
+  else if (mode == kRowsDense && !relu && a_ko && !b_ko) SWL_T(true, false, false, kRowsDense);
+#undef SWL_T
+}
+
 }  // namespace
+
+void launch_expert_gemm_bf16_t(GemmRows mode, bool relu, bool a_kouter, bool b_kouter,
+                               const void* A, int64_t strideA, const void* B, int64_t strideB,
+                               void* Cout, int64_t strideC, const int32_t* rows, int n_experts,
+                               int64_t C, int K, int Nout, const GemmIO& io, hipStream_t s) {
+  if (C == 0 || n_experts == 0) return;
+  // a K-outer A is read in whole column tiles of the M range
+  const bool wide = use_wide(C, Nout, n_experts, io) && (!a_kouter || C % GW_BM == 0);
+  if (wide) {
+    launch_t_sized<GW_BM, GW_BN>(mode, relu, a_kouter, b_kouter, (const uint16_t*)A, strideA,
+                                 (const uint16_t*)B, strideB, (uint16_t*)Cout, strideC, rows,
+                                 n_experts, C, K, Nout, io, s);
+  } else {
+    GemmIO plain = io;  // a tile list counts 256-row tiles
+    plain.tile_start = nullptr;
+    launch_t_sized<128, 128>(mode, relu, a_kouter, b_kouter, (const uint16_t*)A, strideA,
+                             (const uint16_t*)B, strideB, (uint16_t*)Cout, strideC, rows,
+                             n_experts, C, K, Nout, plain, s);
+  }
+}
 
 void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t strideA,
                              const void* B, int64_t strideB, void* Cout, int64_t strideC,

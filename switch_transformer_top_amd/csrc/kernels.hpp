@@ -107,6 +107,10 @@ struct GemmIO {
   const uint16_t* x = nullptr;
   const float* gate = nullptr;
   uint16_t* out = nullptr;
+  // K-outer operands (launch_expert_gemm_bf16_t): row pitch in elements, and
+  // per-expert count of valid K rows (NULL: all K rows are valid)
+  int64_t lda = 0, ldb = 0;
+  const int32_t* krows = nullptr;
 };
 void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t strideA,
                              const void* B, int64_t strideB, void* Cout, int64_t strideC,
@@ -115,6 +119,14 @@ void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t st
 void launch_expert_gemm(bool bf16, bool relu, const void* A, int64_t strideA, const void* B,
                         int64_t strideB, void* Cout, int64_t strideC, const int32_t* rows,
                         int n_experts, int64_t C, int K, int Nout, hipStream_t s);
+// The same products with either operand stored K-outer (a_kouter: A is
+// [K][rows] per expert with pitch io.lda, the tile's M range a column range;
+// b_kouter: B is [K][Nout] with pitch io.ldb).  Modes kRowsDense (optional
+// ReLU) and kRowsMask.  K must be a multiple of 64.
+void launch_expert_gemm_bf16_t(GemmRows mode, bool relu, bool a_kouter, bool b_kouter,
+                               const void* A, int64_t strideA, const void* B, int64_t strideB,
+                               void* Cout, int64_t strideC, const int32_t* rows, int n_experts,
+                               int64_t C, int K, int Nout, const GemmIO& io, hipStream_t s);
 bool expert_gemm_shape_ok(bool bf16, int d, int F);
 constexpr int kWideTileRows = 256;   // M tile of the wide bf16 kernel
 

@@ -319,8 +319,7 @@ switch_status route_impl(switch_layer* L, const void* x, const float* given_logi
 // to 64: the weight-gradient matmuls run over the expert's rows as their K
 // dimension, zero-padded to whole K steps.
 struct BwdLayout {
-  size_t nkept, tiles, tok, gs, hbuf, ybuf, du, dxe, woutT, winT, gsT, hT, duT, xT, dh, wpart,
-      bpart, total;
+  size_t nkept, tiles, tok, gs, hbuf, ybuf, du, dxe, xT, dh, wpart, bpart, total;
   int64_t Cb, Cbp;
 };
 
@@ -341,11 +340,6 @@ BwdLayout bwd_layout_of(const switch_layer* L, int64_t T) {
   lo.ybuf = take(2 * N * Cb * d);
   lo.du = take(2 * N * Cb * F);
   lo.dxe = take(2 * N * Cb * d);
-  lo.woutT = take(2 * N * F * d);
-  lo.winT = take(2 * N * d * F);
-  lo.gsT = take(2 * N * d * Cbp);
-  lo.hT = take(2 * N * F * Cbp);
-  lo.duT = take(2 * N * F * Cbp);
   lo.xT = take(2 * N * d * Cbp);
   lo.dh = take(4 * (size_t)T * N);
   const size_t slices = (size_t)swl::router_wgrad_slices(T, (int)N);
@@ -404,45 +398,39 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
     swl::launch_router_wgrad(dh, x, T, N, d, (float*)(w + lo.wpart), (float*)(w + lo.bpart),
                              grad_W_r, grad_b_r, s);
     if (Cb > 0) {
-      swl::prof_mark(P, s, "weight_transpose");
-      void* woutT = w + lo.woutT;
-      void* winT = w + lo.winT;
-      swl::launch_transpose(L->W_out, (int64_t)d * F, F, d, F, nullptr, nullptr, woutT,
-                            (int64_t)F * d, d, N, s);
-      swl::launch_transpose(L->W_in, (int64_t)F * d, d, F, d, nullptr, nullptr, winT,
-                            (int64_t)d * F, F, N, s);
-      // dU = (Gs W_out[e]) * [H > 0]
+      // dU = (Gs W_out[e]) * [H > 0], W_out[e] read as stored ([d][F], K = d outer)
       swl::prof_mark(P, s, "grad_h");
       io_rows.mask = (const uint16_t*)hbuf;
-      swl::launch_expert_gemm_bf16(swl::kRowsMask, false, gs, Cb * d, woutT, (int64_t)F * d, du,
-                                   Cb * F, nkept, N, Cb, d, F, io_rows, s);
-      // dX = dU W_in[e]
+      io_rows.ldb = F;
+      swl::launch_expert_gemm_bf16_t(swl::kRowsMask, false, false, true, gs, Cb * d, L->W_out,
+                                     (int64_t)d * F, du, Cb * F, nkept, N, Cb, d, F, io_rows, s);
+      // dX = dU W_in[e], W_in[e] read as stored ([F][d], K = F outer)
       swl::prof_mark(P, s, "grad_x_expert");
-      swl::launch_expert_gemm_bf16(swl::kRowsDense, false, du, Cb * F, winT, (int64_t)d * F, dxe,
-                                   Cb * d, nkept, N, Cb, F, d, io, s);
-      // token-major operands of the weight gradients (K = the expert's rows)
-      swl::prof_mark(P, s, "act_transpose");
-      void* gsT = w + lo.gsT;
-      void* hT = w + lo.hT;
-      void* duT = w + lo.duT;
+      swl::GemmIO io_w = io;
+      io_w.ldb = d;
+      swl::launch_expert_gemm_bf16_t(swl::kRowsDense, false, false, true, du, Cb * F, L->W_in,
+                                     (int64_t)F * d, dxe, Cb * d, nkept, N, Cb, F, d, io_w, s);
+      // the gathered token rows, K (the expert's rows) innermost, zero past n_kept
+      swl::prof_mark(P, s, "x_transpose");
       void* xT = w + lo.xT;
-      swl::launch_transpose(gs, Cb * d, d, (int)Cb, d, nkept, nullptr, gsT, (int64_t)d * Cbp,
-                            (int)Cbp, N, s);
-      swl::launch_transpose(hbuf, Cb * F, F, (int)Cb, F, nkept, nullptr, hT, (int64_t)F * Cbp,
-                            (int)Cbp, N, s);
-      swl::launch_transpose(du, Cb * F, F, (int)Cb, F, nkept, nullptr, duT, (int64_t)F * Cbp,
-                            (int)Cbp, N, s);
       swl::launch_transpose(x, 0, d, (int)Cb, d, nkept, tok, xT, (int64_t)d * Cbp, (int)Cbp, N,
                             s);
-      // dW_out[e] = Gs^T H: [d, Cbp] x [F, Cbp]^T;  dW_in[e] = dU^T X: [F, Cbp] x [d, Cbp]^T
+      // dW_out[e] = Gs^T H and dW_in[e] = dU^T X over the expert's rows (K = Cbp,
+      // rows at or past n_kept read as zero): Gs, H and dU read as stored
+      swl::GemmIO io_g = io;
+      io_g.krows = nkept;
       swl::prof_mark(P, s, "grad_w_out");
-      swl::launch_expert_gemm_bf16(swl::kRowsDense, false, gsT, (int64_t)d * Cbp, hT,
-                                   (int64_t)F * Cbp, grad_W_out, (int64_t)d * F, nullptr, N, d,
-                                   (int)Cbp, F, io, s);
+      io_g.lda = d;
+      io_g.ldb = F;
+      swl::launch_expert_gemm_bf16_t(swl::kRowsDense, false, true, true, gs, Cb * d, hbuf, Cb * F,
+                                     grad_W_out, (int64_t)d * F, nullptr, N, d, (int)Cbp, F, io_g,
+                                     s);
       swl::prof_mark(P, s, "grad_w_in");
-      swl::launch_expert_gemm_bf16(swl::kRowsDense, false, duT, (int64_t)F * Cbp, xT,
-                                   (int64_t)d * Cbp, grad_W_in, (int64_t)F * d, nullptr, N, F,
-                                   (int)Cbp, d, io, s);
+      io_g.lda = F;
+      io_g.ldb = 0;
+      swl::launch_expert_gemm_bf16_t(swl::kRowsDense, false, true, false, du, Cb * F, xT,
+                                     (int64_t)d * Cbp, grad_W_in, (int64_t)F * d, nullptr, N, F,
+                                     (int)Cbp, d, io_g, s);
     }
     swl::prof_mark(P, s, "grad_x");
     swl::launch_grad_x(grad_out, T, d, expert_idx, position, drop_mask, Cb, dxe, dh, L->W_r, N,
