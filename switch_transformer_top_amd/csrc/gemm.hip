@@ -465,6 +465,38 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
                                   lane);
 }
 
+// K-outer LDS tiles: rows of R + KO_PAD elements.  A pitch of 32 mod 128
+// elements puts the four rows of a transposing read 16 banks apart.
+constexpr int KO_PAD = 32;
+
+template <int R, int NTHR, bool KOUTER>
+struct OpLayout {
+  static constexpr int PITCH = KOUTER ? R + KO_PAD : GB_LDK;      // LDS row pitch (elements)
+  static constexpr int ELEMS = KOUTER ? GB_BK * PITCH : R * GB_LDK;
+  static constexpr int P = R * GB_BK / 8 / NTHR;                   // 16-byte pieces per thread
+  // K-contiguous: thread -> (row, 8-wide k chunk); K-outer: (k row, 8-wide column chunk)
+  static constexpr int CPR = KOUTER ? R / 8 : GB_BK / 8;          // chunks per LDS row
+  static constexpr int RPP = NTHR / CPR;                           // LDS rows per pass
+  static_assert(P * NTHR * 8 == R * GB_BK && RPP * CPR == NTHR, "whole passes");
+};
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// Fragment of 32 columns starting at col of a K-outer LDS tile, K sub-step ks.
+__device__ __forceinline__ bf16x8 frag_kouter(const uint16_t* tile, int pitch, int ks, int col,
+                                              int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int row = ks * 16 + 8 * (g >> 1) + (j >> 2);
+  const int c = col + 16 * (g & 1) + 4 * (j & 3);
+  const uint16_t* p0 = tile + row * pitch + c;
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)p0);
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p0 + 4 * pitch));
+  typedef short shortx8 __attribute__((ext_vector_type(8)));
+  const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Split-K variant of the 128 x 128 tile for launches with no more tiles than
 // CUs (the Switch-Base GEMM2 shape: about 240 tiles, K = 3072), where one
 // four-wave block per CU leaves the MFMA pipes idle while each wave waits on
@@ -474,17 +506,20 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
 // LDS operand buffers, one barrier per step, the loads of step t + 2 in flight
 // during step t.  At the end the groups exchange halves of their fp32 partial
 // sums through LDS and each finishes half of the rows (epilogue included).
-constexpr int GS_STAGE = (128 + 128) * GB_LDK;                      // elements per buffer
+// BKO: B stored K-outer ([K][Nout] per expert, pitch io.ldb; the backward's
+// dX = dU W_in[e]).
 constexpr size_t kSplitRed = (size_t)8 * 8 * 64 * 16;              // bytes of partial sums
 constexpr size_t kSplitLds = kSplitRed + (size_t)8 * 32 * (64 + 8) * sizeof(uint16_t);
 
-template <bool RELU, int MODE>
+template <bool RELU, int MODE, bool BKO = false>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
     const uint16_t* __restrict__ A, int64_t strideA, const uint16_t* __restrict__ B,
     int64_t strideB, uint16_t* __restrict__ Cout, int64_t strideC,
     const int32_t* __restrict__ rows, int K, int Nout, int m_tiles, int n_tiles, int tiles,
     GemmIO io, int64_t C) {
   constexpr int BM = 128, BN = 128, BK = GB_BK, LDK = GB_LDK, TI = 2, TJ = 2;
+  using LB = OpLayout<BN, 512, BKO>;
+  constexpr int GS_STAGE = BM * GB_LDK + LB::ELEMS;                 // elements per buffer
   static_assert(2 * GS_STAGE * sizeof(uint16_t) <= kSplitLds, "operand buffers fit");
   static_assert(kSplitRed <= 2 * GS_STAGE * sizeof(uint16_t), "partial sums reuse the buffers");
   extern __shared__ __attribute__((aligned(16))) uint16_t slds[];
@@ -501,7 +536,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
   const int n0 = nt * BN;
 
   const uint16_t* Ae = MODE == kRowsGather ? io.x : A + (int64_t)e * strideA;
-  const uint16_t* Be = B + (int64_t)e * strideB + (int64_t)n0 * K;
+  const uint16_t* Be = B + (int64_t)e * strideB + (BKO ? (int64_t)n0 : (int64_t)n0 * K);
   uint16_t* Ce = Cout + (int64_t)e * strideC;
   const int32_t* tok_e = MODE == kRowsDense ? nullptr : io.tok + (int64_t)e * C;
 
@@ -510,30 +545,40 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
   const int grp = wave >> 2, wq = wave & 3, wm = wq >> 1, wn = wq & 1;
   const int lrow = tid >> 3, lcol = (tid & 7) * 8;  // 64 rows per pass of 512 threads
 
-  int64_t go[4];  // element offsets: A rows (j < 2) from Ae, B rows (j >= 2) from Be
+  // element offsets: A rows (j < 2) from Ae, B pieces (j >= 2) from Be; LDS offsets
+  int64_t go[4];
+  int lo_[4];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     int r = m0 + lrow + 64 * j;
     r = r < rows_e ? r : rows_e - 1;  // rows past n_kept: any valid row, never stored
     const int64_t src = MODE == kRowsGather ? (int64_t)tok_e[r] : (int64_t)r;
     go[j] = src * K + lcol;
-    go[2 + j] = (int64_t)(lrow + 64 * j) * K + lcol;
+    lo_[j] = (lrow + 64 * j) * LDK + lcol;
+    if (BKO) {
+      // K-outer B: k row tid / 16 + 32 j, columns 8 (tid % 16) .. + 7
+      const int kr = tid / LB::CPR + LB::RPP * j, c = (tid % LB::CPR) * 8;
+      go[2 + j] = (int64_t)kr * io.ldb + c;
+      lo_[2 + j] = BM * LDK + kr * LB::PITCH + c;
+    } else {
+      go[2 + j] = (int64_t)(lrow + 64 * j) * K + lcol;
+      lo_[2 + j] = BM * LDK + (lrow + 64 * j) * LDK + lcol;
+    }
   }
-  const int lbase = lrow * LDK + lcol;
+  static_assert(LB::P == 2, "two B pieces per thread");
   const int nk = K / BK;
+  const int64_t b_step = BKO ? (int64_t)BK * io.ldb : BK;
   u32x4 g[4];
   auto gload = [&](int t) {
     t = t < nk ? t : nk - 1;
-    const int k = t * BK;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      g[j] = *reinterpret_cast<const u32x4*>((j < 2 ? Ae : Be) + go[j] + k);
+      g[j] = j < 2 ? *reinterpret_cast<const u32x4*>(Ae + go[j] + (int64_t)t * BK)
+                   : *reinterpret_cast<const u32x4*>(Be + go[j] + t * b_step);
   };
   auto gstore = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4*>(
-          &slds[buf * GS_STAGE + lbase + ((j & 1) * 64 + (j < 2 ? 0 : BM)) * LDK]) = g[j];
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&slds[buf * GS_STAGE + lo_[j]]) = g[j];
   };
   floatx16 acc[TI][TJ];
 #pragma unroll
@@ -551,8 +596,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
           &slds[buf * GS_STAGE + (wm * 64 + i * 32 + fr) * LDK + ks * 16 + fk]);
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
-      fb[f][j] = *reinterpret_cast<const bf16x8*>(
-          &slds[buf * GS_STAGE + (BM + wn * 64 + j * 32 + fr) * LDK + ks * 16 + fk]);
+      fb[f][j] = BKO ? frag_kouter(slds + buf * GS_STAGE + BM * LDK, LB::PITCH, ks,
+                                   wn * 64 + j * 32, lane)
+                     : *reinterpret_cast<const bf16x8*>(
+                           &slds[buf * GS_STAGE + (BM + wn * 64 + j * 32 + fr) * LDK + ks * 16 +
+                                 fk]);
   };
   auto mfmas = [&](int f) {
 #pragma unroll
@@ -652,36 +700,6 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
 // capacity).  Rows of a K-outer operand at or past io.krows[e] read as zero
 // (the expert's rows beyond its kept count).
 // ---------------------------------------------------------------------------
-constexpr int KO_PAD = 8;
-
-template <int R, int NTHR, bool KOUTER>
-struct OpLayout {
-  static constexpr int PITCH = KOUTER ? R + KO_PAD : GB_LDK;      // LDS row pitch (elements)
-  static constexpr int ELEMS = KOUTER ? GB_BK * PITCH : R * GB_LDK;
-  static constexpr int P = R * GB_BK / 8 / NTHR;                   // 16-byte pieces per thread
-  // K-contiguous: thread -> (row, 8-wide k chunk); K-outer: (k row, 8-wide column chunk)
-  static constexpr int CPR = KOUTER ? R / 8 : GB_BK / 8;          // chunks per LDS row
-  static constexpr int RPP = NTHR / CPR;                           // LDS rows per pass
-  static_assert(P * NTHR * 8 == R * GB_BK && RPP * CPR == NTHR, "whole passes");
-};
-
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-
-// Fragment of 32 columns starting at col of a K-outer LDS tile, K sub-step ks.
-__device__ __forceinline__ bf16x8 frag_kouter(const uint16_t* tile, int pitch, int ks, int col,
-                                              int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const int row = ks * 16 + 8 * (g >> 1) + (j >> 2);
-  const int c = col + 16 * (g & 1) + 4 * (j & 3);
-  const uint16_t* p0 = tile + row * pitch + c;
-  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)p0);
-  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p0 + 4 * pitch));
-  typedef short shortx8 __attribute__((ext_vector_type(8)));
-  const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 template <int BM, int BN, bool AKO, bool BKO, bool RELU, int MODE>
 __global__ __launch_bounds__(BN * 2, 1) void gemm_bf16_t_kernel(
     const uint16_t* __restrict__ A, int64_t strideA, const uint16_t* __restrict__ B,
@@ -949,7 +967,7 @@ void launch_wide(const uint16_t* a, int64_t strideA, const uint16_t* b, int64_t 
                      n_experts);
 }
 
-template <bool RELU, int MODE>
+template <bool RELU, int MODE, bool BKO = false>
 void launch_split(unsigned grid, const uint16_t* a, int64_t strideA, const uint16_t* b,
                   int64_t strideB, uint16_t* c, int64_t strideC, const int32_t* rows, int K,
                   int Nout, int mt, int nt, int tiles, const GemmIO& io, int64_t C,
@@ -958,12 +976,12 @@ void launch_split(unsigned grid, const uint16_t* a, int64_t strideA, const uint1
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (dev < 64 && !(set_on >> dev & 1)) {
-    (void)hipFuncSetAttribute((const void*)gemm_bf16_split_kernel<RELU, MODE>,
+    (void)hipFuncSetAttribute((const void*)gemm_bf16_split_kernel<RELU, MODE, BKO>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSplitLds);
     set_on |= 1ull << dev;
   }
-  hipLaunchKernelGGL((gemm_bf16_split_kernel<RELU, MODE>), dim3(grid), dim3(512), kSplitLds, s, a,
-                     strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
+  hipLaunchKernelGGL((gemm_bf16_split_kernel<RELU, MODE, BKO>), dim3(grid), dim3(512), kSplitLds,
+                     s, a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
 }
 
 template <int BM, int BN, bool AKO, bool BKO, bool RELU, int MODE>
@@ -1011,6 +1029,23 @@ void launch_expert_gemm_bf16_t(GemmRows mode, bool relu, bool a_kouter, bool b_k
   if (C == 0 || n_experts == 0) return;
   // a K-outer A is read in whole column tiles of the M range
   const bool wide = use_wide(C, Nout, n_experts, io) && (!a_kouter || C % GW_BM == 0);
+  const int tiles128 = (int)((C + 127) / 128) * (Nout / 128) * n_experts;
+  if (!wide && !a_kouter && b_kouter && !relu && tiles128 <= device_cus()) {
+    const unsigned grid = (unsigned)(((tiles128 + 7) / 8) * 8);
+    GemmIO plain = io;
+    plain.tile_start = nullptr;
+    if (mode == kRowsMask)
+      launch_split<false, kRowsMask, true>(grid, (const uint16_t*)A, strideA, (const uint16_t*)B,
+                                           strideB, (uint16_t*)Cout, strideC, rows, K, Nout,
+                                           (int)((C + 127) / 128), Nout / 128, tiles128, plain,
+                                           C, s);
+    else
+      launch_split<false, kRowsDense, true>(grid, (const uint16_t*)A, strideA,
+                                            (const uint16_t*)B, strideB, (uint16_t*)Cout,
+                                            strideC, rows, K, Nout, (int)((C + 127) / 128),
+                                            Nout / 128, tiles128, plain, C, s);
+    return;
+  }
   if (wide) {
     launch_t_sized<GW_BM, GW_BN>(mode, relu, a_kouter, b_kouter, (const uint16_t*)A, strideA,
                                  (const uint16_t*)B, strideB, (uint16_t*)Cout, strideC, rows,
