@@ -694,14 +694,21 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
 // receives column i of rows 0..3, so two such reads give a lane its column's
 // 8 consecutive k.  K-contiguous operands are staged as in the kernels above.
 //
-// Tile BM x BN with BN / 64 x 2 waves, each (BM / 2) x 64; two LDS operand
-// buffers, one barrier per K step, the loads of step t + 2 in flight during
-// step t; tile order as the wide kernel (compact list, or every expert at full
-// capacity).  Rows of a K-outer operand at or past io.krows[e] read as zero
-// (the expert's rows beyond its kept count).
+// Tile BM x BN with BN / 64 x 2 waves, each (BM / 2) x 64; at 256 x 256 two
+// LDS operand buffers, one barrier per K step, the loads of step t + 2 in
+// flight during step t (at 128 x 128 see t_buffers); tile order as the wide
+// kernel (compact list, or every expert at full capacity). Rows of a K-outer
+// operand at or past io.krows[e] read as zero (the expert's rows beyond its
+// kept count).
 // ---------------------------------------------------------------------------
+
+// The 128 x 128 form stages through one LDS buffer (two barriers per K step,
+// the next step's loads in registers) so that three blocks fit on a CU.
+template <int BM, int BN>
+constexpr int t_buffers() { return BM == 128 ? 1 : 2; }
+
 template <int BM, int BN, bool AKO, bool BKO, bool RELU, int MODE>
-__global__ __launch_bounds__(BN * 2, 1) void gemm_bf16_t_kernel(
+__global__ __launch_bounds__(BN * 2, BM == 128 ? 3 : 1) void gemm_bf16_t_kernel(
     const uint16_t* __restrict__ A, int64_t strideA, const uint16_t* __restrict__ B,
     int64_t strideB, uint16_t* __restrict__ Cout, int64_t strideC,
     const int32_t* __restrict__ rows, int K, int Nout, int m_tiles, int n_tiles, int tiles,
@@ -837,17 +844,29 @@ __global__ __launch_bounds__(BN * 2, 1) void gemm_bf16_t_kernel(
     }
   };
 
-  gload(0);
-  gstore(0);
-  gload(1);
-  __syncthreads();
-  for (int t = 0; t < nk; ++t) {
-    const int cur = t & 1, nxt = cur ^ 1;
-    // buffer nxt was last read in step t - 1, before the barrier that ended it
-    gstore(nxt);
-    gload(t + 2);
-    step(cur);
+  if (t_buffers<BM, BN>() == 1) {
+    gload(0);
+    for (int t = 0; t < nk; ++t) {
+      __syncthreads();  // every wave is done with step t - 1's tile
+      gstore(0);
+      __syncthreads();
+      gload(t + 1);
+      step(0);
+    }
     __syncthreads();
+  } else {
+    gload(0);
+    gstore(0);
+    gload(1);
+    __syncthreads();
+    for (int t = 0; t < nk; ++t) {
+      const int cur = t & 1, nxt = cur ^ 1;
+      // buffer nxt was last read in step t - 1, before the barrier that ended it
+      gstore(nxt);
+      gload(t + 2);
+      step(cur);
+      __syncthreads();
+    }
   }
 
   uint16_t* stage = tlds + wave * (BM / 2) * (64 + 8);
@@ -862,7 +881,8 @@ __global__ __launch_bounds__(BN * 2, 1) void gemm_bf16_t_kernel(
 
 template <int BM, int BN, bool AKO, bool BKO>
 constexpr size_t t_kernel_lds() {
-  constexpr size_t ops = 2 * (OpLayout<BM, BN * 2, AKO>::ELEMS + OpLayout<BN, BN * 2, BKO>::ELEMS);
+  constexpr size_t ops = (size_t)t_buffers<BM, BN>() *
+                         (OpLayout<BM, BN * 2, AKO>::ELEMS + OpLayout<BN, BN * 2, BKO>::ELEMS);
   constexpr size_t epi = (size_t)(BN / 64) * 2 * (BM / 2) * (64 + 8);
   return (ops > epi ? ops : epi) * sizeof(uint16_t);
 }
