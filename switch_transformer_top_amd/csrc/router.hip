@@ -660,6 +660,115 @@ __global__ __launch_bounds__(256) void route_rows_kernel(const float* __restrict
   chunk_hist_rank(s_idx, rows * k, t0 * k, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
 }
 
+// Statistics from logits with each row read once (N <= 64 NPL): a wave takes
+// rows w, w + 4, ... of the block's 64; lane l holds experts l + 64 i of the row
+// in registers for the max, the sum, the second choice and its own running
+// sums of p over the wave's rows (fp64).  The four waves' sums are then added
+// as (w0 + w2) + (w1 + w3).  Same statistics as route_rows_kernel; the P sums
+// are the same terms added in another fixed order.
+template <int NPL>
+__global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __restrict__ h,
+                                                             int64_t T, int N, int k,
+                                                             int32_t* __restrict__ expert_idx,
+                                                             float* __restrict__ gate,
+                                                             float* __restrict__ P_part,
+                                                             int32_t* __restrict__ hist,
+                                                             int32_t* __restrict__ rank_local) {
+  extern __shared__ double rr_red[];  // [2][N] partial sums, then N ints of counts
+  __shared__ int32_t s_idx[RR_ROWS * kMaxTopK];
+  int32_t* cnt = reinterpret_cast<int32_t*>(rr_red + 2 * N);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * RR_ROWS;
+  const int rows = (int)((T - t0) < RR_ROWS ? (T - t0) : RR_ROWS);
+  double pacc[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) pacc[i] = 0.0;
+
+  for (int r = wave; r < rows; r += 4) {
+    const float* row = h + (t0 + r) * N;
+    float v[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + kWave * i;
+      v[i] = e < N ? row[e] : -__builtin_huge_valf();
+    }
+    float m = -__builtin_huge_valf();
+    int mi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + kWave * i < N && (v[i] > m || mi == 0x7fffffff)) {
+        m = v[i];
+        mi = lane + kWave * i;  // ascending within a lane: the first (lowest) index wins
+      }
+    wave_argmax(m, mi);
+    double sum = 0.0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) sum += (double)expf(v[i] - m);
+    sum = wave_sum_f64(sum);
+    const double inv = 1.0 / sum;
+    float m2 = -__builtin_huge_valf();
+    int mi2 = 0x7fffffff;
+    if (k > 1) {
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const int e = lane + kWave * i;
+        if (e < N && e != mi && (v[i] > m2 || mi2 == 0x7fffffff)) {
+          m2 = v[i];
+          mi2 = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float om = __shfl_xor(m2, o, kWave);
+        const int oi = __shfl_xor(mi2, o, kWave);
+        if (oi != 0x7fffffff && (mi2 == 0x7fffffff || om > m2 || (om == m2 && oi < mi2))) {
+          m2 = om;
+          mi2 = oi;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) pacc[i] += (double)expf(v[i] - m) * inv;
+    if (lane == 0) {
+      expert_idx[(t0 + r) * k] = mi;
+      gate[(t0 + r) * k] = (float)inv;
+      s_idx[r * k] = mi;
+      if (k > 1) {
+        expert_idx[(t0 + r) * k + 1] = mi2;
+        gate[(t0 + r) * k + 1] = (float)((double)expf(m2 - m) * inv);
+        s_idx[r * k + 1] = mi2;
+      }
+    }
+  }
+  // (w0 + w2) + (w1 + w3)
+  if (wave >= 2) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + kWave * i < N) rr_red[(wave - 2) * N + lane + kWave * i] = pacc[i];
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + kWave * i < N) pacc[i] += rr_red[wave * N + lane + kWave * i];
+  }
+  __syncthreads();
+  if (wave == 1) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + kWave * i < N) rr_red[lane + kWave * i] = pacc[i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + kWave * i;
+      if (e < N) P_part[(int64_t)blockIdx.x * N + e] = (float)(pacc[i] + rr_red[e]);
+    }
+  }
+  chunk_hist_rank(s_idx, rows * k, t0 * k, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
+}
+
 // ------------------------------------------------------------------ launchers
 
 constexpr int kTokRowt = 2;                 // router_tok_kernel: 128 tokens per block
@@ -712,9 +821,19 @@ void launch_router_fused(const uint16_t* x, const float* W_r, const float* b_r, 
 void launch_route_rows(const float* h, int64_t T, int N, int k, int32_t* expert_idx, float* gate,
                        float* P_part, int32_t* hist, int32_t* rank_local, hipStream_t s) {
   if (T == 0) return;
-  hipLaunchKernelGGL(route_rows_kernel, dim3((unsigned)((T + RR_ROWS - 1) / RR_ROWS)), dim3(256),
-                     sizeof(int32_t) * (size_t)N, s, h, T, N, k, expert_idx, gate, P_part, hist,
-                     rank_local);
+  const dim3 grid((unsigned)((T + RR_ROWS - 1) / RR_ROWS));
+  const size_t lds = (2 * sizeof(double) + sizeof(int32_t)) * (size_t)N;
+#define SWL_RR(NPL)                                                                              \
+  hipLaunchKernelGGL(route_rows_reg_kernel<NPL>, grid, dim3(256), lds, s, h, T, N, k, expert_idx, \
+                     gate, P_part, hist, rank_local)
+  if (N <= 4 * kWave) SWL_RR(4);
+  else if (N <= 8 * kWave) SWL_RR(8);
+  else if (N <= 16 * kWave) SWL_RR(16);
+  else if (N <= 32 * kWave) SWL_RR(32);
+  else
+    hipLaunchKernelGGL(route_rows_kernel, grid, dim3(256), sizeof(int32_t) * (size_t)N, s, h, T,
+                       N, k, expert_idx, gate, P_part, hist, rank_local);
+#undef SWL_RR
 }
 
 }  // namespace swl
