@@ -234,6 +234,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward pass (gradients of every input and weight) "
                          "after the forward, and report it beside the forward line's fields")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="steps timed one by one after writing a 512 MiB buffer (larger than the "
+                         "256 MB Infinity Cache), so every step starts with cold caches; 0: skip")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, run one device-to-device copy of 1 GiB "
                          "(reference for hardware byte counters)")
@@ -270,6 +273,25 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms_per_step = start.elapsed_time(stop) / args.steps
+
+    # cold caches: before each step a 512 MiB write evicts the weights, x and the
+    # workspace from L2 and the Infinity Cache; only the step itself is timed
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.cold_steps)]
+        for a, b in ev:
+            flush.fill_(1)
+            a.record(stream)
+            layer.forward(x, spec.T, bufs, stream=sp, with_logits=False)
+            b.record(stream)
+        torch.cuda.synchronize()
+        cold_ms = sum(a.elapsed_time(b) for a, b in ev) / args.cold_steps
+        cold = {"ms_per_step": round(cold_ms, 5),
+                "tokens_per_s": round(spec.T / (cold_ms * 1e-3), 1),
+                "steps": args.cold_steps, "flush_bytes": 512 << 20}
+        del flush
 
     # second pass of K steps: the library records HIP events around every kernel
     B.switch_profile_enable(layer.handle, args.steps)
@@ -370,6 +392,8 @@ def main():
         "stage_rooflines": rooflines,
         "wall_s_timed_region": round(wall, 4),
     }
+    if cold is not None:
+        result["cold_cache"] = cold
     if backward is not None:
         result["backward"] = backward
     if not args.no_cpu_baseline:
