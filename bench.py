@@ -95,14 +95,15 @@ def roofline_entry(stage: str, work: dict, ms: float) -> dict:
             if work["flops"] else None}
 
 
-# stage of the forward call -> (kernel name in the hardware-counter profiles, source file)
-STAGE_KERNEL = {"gemm1_relu": ("gemm_bf16_", "true, 1>", "gemm.hip"),
-                "gemm2": ("gemm_bf16_", "false, 0>", "gemm.hip"),
-                "gemm2_combine": ("gemm_bf16_", "false, 2>", "gemm.hip"),
-                "router": ("router_", "", "router.hip"),
-                "dispatch": ("dispatch_index_kernel", "", "move.hip"),
-                "assign": ("assign_kernel", "", "assign.hip"),
-                "combine": ("combine_kernel<", "", "move.hip")}
+# stage of the forward call -> (regular expression over the kernel's name in the
+# hardware-counter profiles, its source file)
+STAGE_KERNEL = {"gemm1_relu": (r"gemm_bf16_\w+<(\d+, \d+, )?true, 1(, false)?>", "gemm.hip"),
+                "gemm2": (r"gemm_bf16_\w+<(\d+, \d+, )?false, 0(, false)?>", "gemm.hip"),
+                "gemm2_combine": (r"gemm_bf16_\w+<(\d+, \d+, )?false, 2(, false)?>", "gemm.hip"),
+                "router": (r"router_\w+(<.*>)?", "router.hip"),
+                "dispatch": (r"dispatch_index_kernel", "move.hip"),
+                "assign": (r"assign_kernel", "assign.hip"),
+                "combine": (r"combine_kernel<.*>", "move.hip")}
 
 
 _TRAFFIC_LINE = re.compile(
@@ -116,7 +117,7 @@ def measured_traffic(stage: str, workload: str):
     kernel and workload or its source has changed since the counters were taken."""
     if stage not in STAGE_KERNEL:
         return None
-    prefix, suffix, src = STAGE_KERNEL[stage]
+    pattern, src = STAGE_KERNEL[stage]
     h = hashlib.sha256()
     for f in (src, "common.hpp"):
         with open(os.path.join(ROOT, "switch_transformer_top_amd", "csrc", f), "rb") as fh:
@@ -130,7 +131,7 @@ def measured_traffic(stage: str, workload: str):
                     continue
                 kv = m.groupdict()
                 k = kv.get("kernel", "")
-                if (kv.get("workload") == workload and k.startswith(prefix) and k.endswith(suffix)
+                if (kv.get("workload") == workload and re.fullmatch(pattern, k)
                         and kv.get("source_sha256") == digest):
                     return float(kv["bytes_per_launch"])
     return None
