@@ -7,8 +7,10 @@
 // kasblo explainer's "16 token、4 Expertで考える"; the overflow token of
 // "Switch Transformer by Hand" (step 7) is the third token routed to a full
 // expert.  All of it is integer work on per-chunk counts and is deterministic:
-// the router leaves hist[c, e] and in-chunk ranks; this kernel turns hist into
-// exclusive prefixes over chunks; the dispatch pass adds the two.
+// the router leaves hist[c, e] and in-chunk ranks; position = the exclusive
+// prefix of hist over earlier chunks + the rank.  assign_kernel does it all in
+// one launch; for large count tables route_scan_kernel rewrites hist into the
+// prefixes and the dispatch pass adds the two.
 //
 // Load-balancing loss (llm-papers-study close reading, section 3.3):
 // aux = alpha N sum_i f_i P_i, f_i = load_i / T, P_i = (1/T) sum_t p_i(t), with

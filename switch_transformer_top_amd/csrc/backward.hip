@@ -14,15 +14,17 @@
 //   every t:  dp_i = [i = e_t, kept] dg_t + g_aux alpha N load_i / T^2,
 //     dh = p * (dp - p . dp),  dW_r = dh^T x,  db = sum_t dh,
 //     dx_t = G_t + dX[e_t, p_t] + W_r^T dh_t.
-// The matmuls are the grouped bf16 kernels of gemm.hip (fp32 accumulation);
-// this file holds the slot/scale pass, the transposes that put their K
-// dimension innermost, the router backward and the assembly of dx.
+// The matmuls are the grouped bf16 kernels of gemm.hip (fp32 accumulation),
+// which read the weights and the per-slot activations as stored; this file
+// holds the slot/scale pass, the gather of the token rows with K (the expert's
+// rows) innermost for dW_in, the router backward and the assembly of dx.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace swl {
 
-// n_kept[e] = min(load[e], C) (the forward's per-expert loads).
+// n_kept[e] = min(load[e], C) (the forward's per-expert loads), and the
+// compact list of tile_rows-row tiles over them (one block).
 __global__ __launch_bounds__(1024) void bwd_rows_kernel(const int32_t* __restrict__ load, int N,
                                                         int64_t C, int32_t* __restrict__ n_kept,
                                                         int32_t* __restrict__ tile_start,
