@@ -65,6 +65,12 @@ def lib():
                                       _i32p, _f64p, ctypes.c_double, ctypes.c_double, _i64, _i64,
                                       _i64, _i64, _f64p, _f64p, _f64p, _f64p, _f64p, ctypes.c_int]
         L.oracle_backward.restype = None
+        L.oracle_backward_topk.argtypes = [_f32p, _f32p, _f32p, _f32p, _f64p, _i32p, _f64p,
+                                           _u8p, _i32p, _f64p, ctypes.c_double, ctypes.c_double,
+                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int64, _f64p, _f64p, _f64p,
+                                           _f64p, _f64p, ctypes.c_int]
+        L.oracle_backward_topk.restype = None
         _lib = L
     return _lib
 
@@ -193,4 +199,25 @@ def backward(x, W_r, W_in, W_out, h, expert_idx, gate, drop, load, G, g_aux: flo
                           _c(load, np.int32), _c(G, np.float64), g_aux, alpha, T, d, F, N,
                           r["dx"], r["dW_r"], r["db"], r["dW_in"], r["dW_out"],
                           nthreads or threads())
+    return r
+
+
+def backward_topk(x, W_r, W_in, W_out, h, expert_idx, gate, drop, load, G, g_aux: float = 0.0,
+                  alpha: float = 0.01, nthreads: int = 0) -> dict:
+    """Gradients of the top-k layer (expert_idx, gate, drop [T, k]) for dL/dout = G
+    and dL/daux = g_aux, at the forward's routing, logits h and loads."""
+    x = _c(x, np.float32)
+    T, d = x.shape
+    W_in = _c(W_in, np.float32)
+    W_out = _c(W_out, np.float32)
+    N, F = W_in.shape[0], W_in.shape[1]
+    expert_idx = _c(np.asarray(expert_idx).reshape(T, -1), np.int32)
+    k = expert_idx.shape[1]
+    r = dict(dx=np.empty((T, d)), dW_r=np.empty((N, d)), db=np.empty(N),
+             dW_in=np.empty((N, F, d)), dW_out=np.empty((N, d, F)))
+    lib().oracle_backward_topk(x, _c(W_r, np.float32), W_in, W_out, _c(h, np.float64),
+                               expert_idx, _c(np.asarray(gate).reshape(T, k), np.float64),
+                               _c(np.asarray(drop).reshape(T, k), np.uint8), _c(load, np.int32),
+                               _c(G, np.float64), g_aux, alpha, T, k, d, F, N, r["dx"],
+                               r["dW_r"], r["db"], r["dW_in"], r["dW_out"], nthreads or threads())
     return r

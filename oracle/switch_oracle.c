@@ -537,3 +537,148 @@ void oracle_backward(const float* x, const float* W_r, const float* W_in, const 
   free(dg);
   free(dh);
 }
+
+/* ------------------------------------------------------------------------
+ * Backward pass of the top-k layer (the classic routing the Switch layer
+ * reduces to k = 1; llm-papers-study section 3.1): the same chain rule with
+ * every kept choice j of token t contributing its own gated expert output,
+ *   out_t = x_t + sum_j [kept] g_tj E_{e_tj}(x_t),   g_tj = p_{e_tj}(h_t),
+ * and with f_i = load_i / (k T) in the loss (load_i counts assignments), so
+ *   dg_tj = G_t . E_{e_tj}(x_t),
+ *   dp_i = sum_j [i = e_tj and kept] dg_tj + g_aux alpha N load_i / (k T^2),
+ *   and each kept (t, j) adds its expert terms as in oracle_backward.
+ * expert_idx, gate and drop are [T, k] in (token, choice) order.
+ * ------------------------------------------------------------------------ */
+void oracle_backward_topk(const float* x, const float* W_r, const float* W_in,
+                          const float* W_out, const double* h, const int32_t* expert_idx,
+                          const double* gate, const uint8_t* drop, const int32_t* load,
+                          const double* G, double g_aux, double alpha, int64_t T, int64_t k,
+                          int64_t d, int64_t F, int64_t N, double* dx, double* dW_r, double* db,
+                          double* dW_in, double* dW_out, int nthreads) {
+  double* dg = (double*)calloc((size_t)(T > 0 ? T * k : 1), sizeof(double));
+  double* dh = (double*)calloc((size_t)(T > 0 ? T : 1) * (size_t)N, sizeof(double));
+
+  /* expert path of dx and dg, per token and kept choice */
+#pragma omp parallel for schedule(dynamic, 4) num_threads(NT(nthreads))
+  for (int64_t t = 0; t < T; ++t) {
+    const float* xt = x + t * d;
+    const double* Gt = G + t * d;
+    for (int64_t q = 0; q < d; ++q) dx[t * d + q] = Gt[q];
+    double* u = (double*)malloc(sizeof(double) * (size_t)F);
+    double* du = (double*)malloc(sizeof(double) * (size_t)F);
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t a = t * k + j;
+      if (drop[a]) continue;
+      const int64_t e = expert_idx[a];
+      const float* Wi = W_in + e * F * d;
+      const float* Wo = W_out + e * d * F;
+      for (int64_t f = 0; f < F; ++f) {
+        double acc = 0.0;
+        for (int64_t q = 0; q < d; ++q) acc += (double)Wi[f * d + q] * (double)xt[q];
+        u[f] = acc;
+      }
+      double s = 0.0;
+      for (int64_t i = 0; i < d; ++i) {
+        double E = 0.0;
+        for (int64_t f = 0; f < F; ++f) E += (double)Wo[i * F + f] * (u[f] > 0.0 ? u[f] : 0.0);
+        s += Gt[i] * E;
+      }
+      dg[a] = s;
+      for (int64_t f = 0; f < F; ++f) {
+        double acc = 0.0;
+        if (u[f] > 0.0)
+          for (int64_t i = 0; i < d; ++i) acc += (double)Wo[i * F + f] * gate[a] * Gt[i];
+        du[f] = acc;
+      }
+      for (int64_t q = 0; q < d; ++q) {
+        double acc = 0.0;
+        for (int64_t f = 0; f < F; ++f) acc += (double)Wi[f * d + q] * du[f];
+        dx[t * d + q] += acc;
+      }
+    }
+    free(u);
+    free(du);
+  }
+
+  /* router path: softmax Jacobian on each token's logits */
+#pragma omp parallel for schedule(static) num_threads(NT(nthreads))
+  for (int64_t t = 0; t < T; ++t) {
+    const double* ht = h + t * N;
+    double m = ht[0];
+    for (int64_t i = 1; i < N; ++i) m = ht[i] > m ? ht[i] : m;
+    double S = 0.0;
+    for (int64_t i = 0; i < N; ++i) S += exp(ht[i] - m);
+    double pdp = 0.0;
+    for (int64_t i = 0; i < N; ++i) {
+      const double p = exp(ht[i] - m) / S;
+      double dp = g_aux * alpha * (double)N * ((double)load[i] / ((double)k * (double)T)) /
+                  (double)T;
+      for (int64_t j = 0; j < k; ++j)
+        if (i == expert_idx[t * k + j] && !drop[t * k + j]) dp += dg[t * k + j];
+      dh[t * N + i] = dp;
+      pdp += p * dp;
+    }
+    for (int64_t i = 0; i < N; ++i) {
+      const double p = exp(ht[i] - m) / S;
+      dh[t * N + i] = p * (dh[t * N + i] - pdp);
+    }
+    for (int64_t q = 0; q < d; ++q) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < N; ++i) acc += (double)W_r[i * d + q] * dh[t * N + i];
+      dx[t * d + q] += acc;
+    }
+  }
+
+  /* router weight and bias gradients: sums over tokens, per expert row */
+#pragma omp parallel for schedule(static) num_threads(NT(nthreads))
+  for (int64_t i = 0; i < N; ++i) {
+    double bsum = 0.0;
+    for (int64_t q = 0; q < d; ++q) dW_r[i * d + q] = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      const double v = dh[t * N + i];
+      bsum += v;
+      for (int64_t q = 0; q < d; ++q) dW_r[i * d + q] += v * (double)x[t * d + q];
+    }
+    if (db) db[i] = bsum;
+  }
+
+  /* expert weight gradients: per expert, its kept assignments in (token, choice) order */
+#pragma omp parallel for schedule(dynamic, 1) num_threads(NT(nthreads))
+  for (int64_t e = 0; e < N; ++e) {
+    const float* Wi = W_in + e * F * d;
+    const float* Wo = W_out + e * d * F;
+    double* gWi = dW_in + e * F * d;
+    double* gWo = dW_out + e * d * F;
+    for (int64_t q = 0; q < F * d; ++q) gWi[q] = 0.0;
+    for (int64_t q = 0; q < d * F; ++q) gWo[q] = 0.0;
+    double* u = (double*)malloc(sizeof(double) * (size_t)F);
+    double* du = (double*)malloc(sizeof(double) * (size_t)F);
+    for (int64_t a = 0; a < T * k; ++a) {
+      if (drop[a] || expert_idx[a] != e) continue;
+      const int64_t t = a / k;
+      const float* xt = x + t * d;
+      const double* Gt = G + t * d;
+      for (int64_t f = 0; f < F; ++f) {
+        double acc = 0.0;
+        for (int64_t q = 0; q < d; ++q) acc += (double)Wi[f * d + q] * (double)xt[q];
+        u[f] = acc;
+      }
+      for (int64_t f = 0; f < F; ++f) {
+        double acc = 0.0;
+        if (u[f] > 0.0)
+          for (int64_t i = 0; i < d; ++i) acc += (double)Wo[i * F + f] * gate[a] * Gt[i];
+        du[f] = acc;
+      }
+      for (int64_t i = 0; i < d; ++i) {
+        const double dE = gate[a] * Gt[i];
+        for (int64_t f = 0; f < F; ++f) gWo[i * F + f] += dE * (u[f] > 0.0 ? u[f] : 0.0);
+      }
+      for (int64_t f = 0; f < F; ++f)
+        for (int64_t q = 0; q < d; ++q) gWi[f * d + q] += du[f] * (double)xt[q];
+    }
+    free(u);
+    free(du);
+  }
+  free(dg);
+  free(dh);
+}

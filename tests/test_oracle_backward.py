@@ -154,3 +154,77 @@ def test_loss_gradient_flows_through_p_only():
     dh = (ALPHA * N / T) * p * (f[None, :] - (p * f[None, :]).sum(axis=1, keepdims=True))
     assert np.allclose(grads["db"], dh.sum(axis=0), rtol=1e-12, atol=1e-15)
     assert np.all(grads["dW_in"] == 0) and np.all(grads["dW_out"] == 0)
+
+
+# ---------------------------------------------------------------------------
+# top-k (k = 2): the same chain rule with two gated experts per token
+
+
+def _loss_topk(x, W_r, b_r, W_in, W_out, G, c, g_aux, k):
+    h = oracle.logits(x, W_r, b_r)
+    r = oracle.route_topk(h, k, c, alpha=ALPHA)
+    out, _ = oracle.combine_topk(x, r["expert_idx"], r["gate"], r["drop"], W_in, W_out)
+    return float((G * out).sum() + g_aux * r["aux"]), r, h
+
+
+def _stable_topk(x, W_r, b_r, W_in, W_out, c, k):
+    """Margins between the k + 1 largest logits and the chosen experts' ReLU
+    inputs all clear of the perturbation."""
+    _, r, h = _loss_topk(x, W_r, b_r, W_in, W_out, np.zeros_like(x, dtype=np.float64), c, 0.0,
+                         k)
+    part = np.sort(h, axis=1)[:, ::-1]
+    if (part[:, :k] - part[:, 1:k + 1]).min() < 0.05:
+        return False
+    for t in range(x.shape[0]):
+        for j in range(k):
+            u = W_in[r["expert_idx"][t, j]].astype(np.float64) @ x[t].astype(np.float64)
+            if np.abs(u).min() < 0.05:
+                return False
+    return True
+
+
+@pytest.mark.parametrize("seed,g_aux", [(5, 0.0), (6, 1.0), (7, 3.0)])
+def test_topk_backward_matches_finite_differences(seed, g_aux):
+    k = 2
+    for s in range(seed, seed + 400, 4):
+        prob = _problem(s, T=7, d=4, F=5, N=4, c=0.7)
+        if _stable_topk(*prob[:5], prob[6], k):
+            break
+    else:
+        pytest.skip("no stable problem found")
+    x, W_r, b_r, W_in, W_out, G, c = prob
+    _, r, h = _loss_topk(x, W_r, b_r, W_in, W_out, G, c, g_aux, k)
+    assert r["drop"].any() and not r["drop"].all()     # both branches are exercised
+    grads = oracle.backward_topk(x, W_r, W_in, W_out, h, r["expert_idx"], r["gate"], r["drop"],
+                                 r["load"], G, g_aux, ALPHA)
+
+    def fd(arr, name):
+        out = np.empty(arr.shape)
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + EPS
+            lp, rp, _ = _loss_topk(x, W_r, b_r, W_in, W_out, G, c, g_aux, k)
+            arr[idx] = keep - EPS
+            lm, rm, _ = _loss_topk(x, W_r, b_r, W_in, W_out, G, c, g_aux, k)
+            arr[idx] = keep
+            assert np.array_equal(rp["expert_idx"], r["expert_idx"]), name
+            assert np.array_equal(rm["drop"], r["drop"]), name
+            out[idx] = (lp - lm) / (2 * EPS)
+        return out
+
+    for name, arr, got in (("x", x, grads["dx"]), ("W_r", W_r, grads["dW_r"]),
+                           ("b_r", b_r, grads["db"]), ("W_in", W_in, grads["dW_in"]),
+                           ("W_out", W_out, grads["dW_out"])):
+        want = fd(arr, name)
+        assert np.allclose(got, want, rtol=1e-6, atol=1e-7), \
+            f"{name}: max err {np.abs(got - want).max()}"
+
+
+def test_topk_backward_at_one_choice_is_the_top1_backward():
+    """k = 1: the same gradients as the top-1 backward."""
+    x, W_r, b_r, W_in, W_out, G, c = _problem(51, T=9, N=3)
+    grads1, r = _backward(x, W_r, b_r, W_in, W_out, G, c, 2.0)
+    gk = oracle.backward_topk(x, W_r, W_in, W_out, r["h"], r["expert_idx"][:, None],
+                              r["gate"][:, None], r["drop"][:, None], r["load"], G, 2.0, ALPHA)
+    for key in ("dx", "dW_r", "db", "dW_in", "dW_out"):
+        assert np.allclose(gk[key], grads1[key], rtol=1e-13, atol=1e-15), key
