@@ -304,8 +304,6 @@ def main():
 
     backward = None
     if args.backward:
-        if args.top_k != 1:
-            sys.exit("the backward pass is built for top-1 routing")
         # forward outputs (logits included) for the routing the backward differentiates at
         layer.forward(x, spec.T, bufs, stream=sp, with_logits=True)
         gen = torch.Generator(device=dev).manual_seed(1000 + spec.seed)   # seeded dL/dout
@@ -330,7 +328,7 @@ def main():
         torch.cuda.synchronize()
         bwd_kept = int((B.from_device(bufs["drop_mask"]) == 0).sum())
         # matmul work of the backward: two recomputed forward matmuls and four gradient
-        # matmuls over the kept rows (the weight-gradient K runs over padded rows)
+        # matmuls over the kept assignments (the weight-gradient K runs over padded rows)
         bwd_flops = 12.0 * bwd_kept * spec.d * spec.F
         backward = {"ms_per_step": round(bwd_ms, 5),
                     "tokens_per_s": round(spec.T / (bwd_ms * 1e-3), 1),

@@ -149,7 +149,7 @@ switch_status switch_forward(switch_layer* layer, const void* x, int64_t T, void
                              void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Backward pass of the top-1 layer (bf16 layers): gradients of a loss L given
+ * Backward pass of the layer (bf16 layers, top_k 1 or 2): gradients of a loss L given
  * grad_out = dL/dout and grad_aux = dL/daux_loss, at the routing of a forward
  * call on the same x.  The expert choice and the capacity cut carry no
  * gradient; the router learns through the gate p_{i*}(x) that scales the
@@ -163,18 +163,21 @@ switch_status switch_forward(switch_layer* layer, const void* x, int64_t T, void
  *   all t:   dp_i = [i = e_t, kept] dgate_t + grad_aux alpha N load_i / T^2,
  *            dh = p * (dp - p . dp),  dW_r += dh x_t^T,  db += dh,
  *            dx_t += grad_out_t + W_r^T dh.
+ * With top_k = 2 every kept choice (t, j) is a "kept t" above with its own
+ * gate, dp_i sums the dgate of the kept choices with e = i, and the loss term
+ * is grad_aux alpha N load_i / (2 T^2) (load counts assignments).
  *   x, grad_out   [T, d] bf16 (grad_x must overlap neither)
- *   logits [T, N] fp32, expert_idx, gate, position, drop_mask [T], load [N]:
- *                 the outputs of switch_forward / switch_route for this x
+ *   logits [T, N] fp32, expert_idx, gate, position, drop_mask [T] ([T, top_k]),
+ *                 load [N]: the outputs of switch_forward / switch_route for this x
  *   grad_x        [T, d] bf16 out
  *   grad_W_r      [N, d] fp32 out;  grad_b_r [N] fp32 out, or NULL
  *   grad_W_in     [N, F, d] bf16 out;  grad_W_out [N, d, F] bf16 out
  *   ws, ws_bytes  device workspace of at least switch_backward_workspace_bytes(T)
  * Weight gradients are fp32 sums over the expert's tokens rounded once to bf16;
  * grad_x is summed in fp32 and rounded once.  Every output is written (zeros
- * where nothing contributes).  SWITCH_E_UNSUPPORTED for fp32 layers or
- * top_k = 2.  The expert activations are recomputed (nothing is kept from the
- * forward call besides its listed outputs).
+ * where nothing contributes).  SWITCH_E_UNSUPPORTED for fp32 layers.  The
+ * expert activations are recomputed (nothing is kept from the forward call
+ * besides its listed outputs).
  */
 switch_status switch_backward(switch_layer* layer, const void* x, int64_t T, const void* grad_out,
                               float grad_aux, const float* logits, const int32_t* expert_idx,

@@ -36,11 +36,11 @@ __global__ __launch_bounds__(1024) void bwd_rows_kernel(const int32_t* __restric
   if (tile_start) tile_prefix_block(n_kept, N, tile_rows, tile_start, s_run);
 }
 
-// Slot table and scaled output gradient of every kept token:
-// tok[e * C + p] = t and Gs[e, p, :] = bf16(gate_t * G_t) (fp32 product,
+// Slot table and scaled output gradient of every kept assignment (t, j):
+// tok[e * C + p] = t and Gs[e, p, :] = bf16(gate_tj * G_t) (fp32 product,
 // rounded to nearest even).  One thread per 16-byte piece of a row.
 __global__ __launch_bounds__(256) void bwd_slots_kernel(const u32x4* __restrict__ G, int64_t T,
-                                                        int row_vec16,
+                                                        int topk, int row_vec16,
                                                         const int32_t* __restrict__ expert_idx,
                                                         const int32_t* __restrict__ position,
                                                         const uint8_t* __restrict__ drop_mask,
@@ -48,12 +48,13 @@ __global__ __launch_bounds__(256) void bwd_slots_kernel(const u32x4* __restrict_
                                                         int32_t* __restrict__ tok,
                                                         u32x4* __restrict__ Gs) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t t = gid / row_vec16;
-  const int c = (int)(gid - t * row_vec16);
-  if (t >= T || drop_mask[t]) return;
-  const int64_t slot = (int64_t)expert_idx[t] * C + position[t];
+  const int64_t a = gid / row_vec16;  // assignment (token t, choice j): a = t topk + j
+  const int c = (int)(gid - a * row_vec16);
+  if (a >= T * topk || drop_mask[a]) return;
+  const int64_t t = a / topk;
+  const int64_t slot = (int64_t)expert_idx[a] * C + position[a];
   if (c == 0) tok[slot] = (int32_t)t;
-  const float g = gate[t];
+  const float g = gate[a];
   const u32x4 v = G[t * row_vec16 + c];
   u32x4 o;
 #pragma unroll
@@ -111,11 +112,11 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
   }
 }
 
-// Router backward, one wave per token: dg = G_t . Y[e, p] (kept tokens),
-// p = softmax(h_t) (fp32 exponentials, fp64 sums as in the forward), dp, and
-// dh_t = p * (dp - p . dp) written to dh [T, N] (fp32).
+// Router backward, one wave per token: dg_j = G_t . Y[e_j, p_j] for each kept
+// choice j, p = softmax(h_t) (fp32 exponentials, fp64 sums as in the forward),
+// dp, and dh_t = p * (dp - p . dp) written to dh [T, N] (fp32).
 __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ h, int64_t T,
-                                                         int N, int d,
+                                                         int N, int d, int topk,
                                                          const uint16_t* __restrict__ G,
                                                          const uint16_t* __restrict__ Ybuf,
                                                          int64_t C,
@@ -128,14 +129,22 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int e = expert_idx[t];
-  const bool kept = drop_mask[t] == 0;
-  double dg = 0.0;
-  if (kept) {
-    const uint16_t* gt = G + t * d;
-    const uint16_t* yt = Ybuf + ((int64_t)e * C + position[t]) * d;
-    for (int k = lane; k < d; k += kWave) dg += (double)bf16_bits_to_f32(gt[k]) * bf16_bits_to_f32(yt[k]);
-    dg = wave_sum_f64(dg);
+  int ej[kMaxTopK];
+  bool kj[kMaxTopK];
+  double dg[kMaxTopK];
+  const uint16_t* gt = G + t * d;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    const int64_t a = t * topk + j;
+    ej[j] = j < topk ? expert_idx[a] : -1;
+    kj[j] = j < topk && drop_mask[a] == 0;
+    dg[j] = 0.0;
+    if (kj[j]) {
+      const uint16_t* yt = Ybuf + ((int64_t)ej[j] * C + position[a]) * d;
+      for (int q = lane; q < d; q += kWave)
+        dg[j] += (double)bf16_bits_to_f32(gt[q]) * bf16_bits_to_f32(yt[q]);
+      dg[j] = wave_sum_f64(dg[j]);
+    }
   }
   const float* ht = h + t * N;
   float m = -__builtin_huge_valf();
@@ -146,20 +155,21 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   for (int i = lane; i < N; i += kWave) S += (double)expf(ht[i] - m);
   S = wave_sum_f64(S);
   const double inv = 1.0 / S;
-  // dp_i = [i = e, kept] dg + loss_scale * load_i, loss_scale = g_aux alpha N / T^2
-  double pdp = 0.0;
-  for (int i = lane; i < N; i += kWave) {
-    const double p = (double)expf(ht[i] - m) * inv;
+  // dp_i = sum_j [i = e_j, kept] dg_j + loss_scale * load_i,
+  // loss_scale = g_aux alpha N / (k T^2)
+  auto dp_of = [&](int i) {
     double dp = (double)loss_scale * (double)load[i];
-    if (kept && i == e) dp += dg;
-    pdp += p * dp;
-  }
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (kj[j] && i == ej[j]) dp += dg[j];
+    return dp;
+  };
+  double pdp = 0.0;
+  for (int i = lane; i < N; i += kWave) pdp += (double)expf(ht[i] - m) * inv * dp_of(i);
   pdp = wave_sum_f64(pdp);
   for (int i = lane; i < N; i += kWave) {
     const double p = (double)expf(ht[i] - m) * inv;
-    double dp = (double)loss_scale * (double)load[i];
-    if (kept && i == e) dp += dg;
-    dh[t * N + i] = (float)(p * (dp - pdp));
+    dh[t * N + i] = (float)(p * (dp_of(i) - pdp));
   }
 }
 
@@ -322,12 +332,13 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restri
   }
 }
 
-// dx_t = G_t + dX[e_t, p_t] (kept) + sum_i dh[t, i] W_r[i, :], fp32 then one
-// rounding to bf16.  Block: 64 tokens x 64 columns; the router part is a
+// dx_t = G_t + sum over kept choices j of dX[e_tj, p_tj] + sum_i dh[t, i] W_r[i, :],
+// fp32 then one rounding to bf16.  Block: 64 tokens x 64 columns; the router part is a
 // small matmul with K = N, in steps of 32 experts through LDS; thread (ty, tx)
 // owns tokens ty + 16 q and the four columns 4 tx .. 4 tx + 3.
 __global__ __launch_bounds__(256) void grad_x_kernel(const uint16_t* __restrict__ G, int64_t T,
-                                                     int d, const int32_t* __restrict__ expert_idx,
+                                                     int d, int topk,
+                                                     const int32_t* __restrict__ expert_idx,
                                                      const int32_t* __restrict__ position,
                                                      const uint8_t* __restrict__ drop_mask,
                                                      int64_t C, const uint16_t* __restrict__ dXe,
@@ -374,9 +385,11 @@ __global__ __launch_bounds__(256) void grad_x_kernel(const uint16_t* __restrict_
     const uint2 gv = *reinterpret_cast<const uint2*>(G + t * d + k);
     float v[4] = {__uint_as_float(gv.x << 16), __uint_as_float(gv.x & 0xFFFF0000u),
                   __uint_as_float(gv.y << 16), __uint_as_float(gv.y & 0xFFFF0000u)};
-    if (!drop_mask[t]) {
+    for (int j = 0; j < topk; ++j) {  // the kept choices' expert parts, in choice order
+      const int64_t a = t * topk + j;
+      if (drop_mask[a]) continue;
       const uint2 xv = *reinterpret_cast<const uint2*>(
-          dXe + ((int64_t)expert_idx[t] * C + position[t]) * d + k);
+          dXe + ((int64_t)expert_idx[a] * C + position[a]) * d + k);
       v[0] += __uint_as_float(xv.x << 16);
       v[1] += __uint_as_float(xv.x & 0xFFFF0000u);
       v[2] += __uint_as_float(xv.y << 16);
@@ -411,13 +424,13 @@ void launch_bwd_rows(const int32_t* load, int N, int64_t C, int32_t* n_kept,
                      kWideTileRows);
 }
 
-void launch_bwd_slots(const void* G, int64_t T, int d, const int32_t* expert_idx,
+void launch_bwd_slots(const void* G, int64_t T, int d, int k, const int32_t* expert_idx,
                       const int32_t* position, const uint8_t* drop_mask, const float* gate,
                       int64_t C, int32_t* tok, void* Gs, hipStream_t s) {
   if (T == 0) return;
   const int rv = d / 8;
-  hipLaunchKernelGGL(bwd_slots_kernel, dim3((unsigned)((T * rv + 255) / 256)), dim3(256), 0, s,
-                     (const u32x4*)G, T, rv, expert_idx, position, drop_mask, gate, C, tok,
+  hipLaunchKernelGGL(bwd_slots_kernel, dim3((unsigned)((T * k * rv + 255) / 256)), dim3(256), 0,
+                     s, (const u32x4*)G, T, k, rv, expert_idx, position, drop_mask, gate, C, tok,
                      (u32x4*)Gs);
 }
 
@@ -430,13 +443,13 @@ void launch_transpose(const void* src, int64_t src_estride, int ld, int R, int C
                      ld, R, Ccols, valid, tok, (uint16_t*)dst, dst_estride, Rpad);
 }
 
-void launch_router_bwd(const float* h, int64_t T, int N, int d, const void* G, const void* Ybuf,
-                       int64_t C, const int32_t* expert_idx, const int32_t* position,
-                       const uint8_t* drop_mask, const int32_t* load, float loss_scale, float* dh,
-                       hipStream_t s) {
+void launch_router_bwd(const float* h, int64_t T, int N, int d, int k, const void* G,
+                       const void* Ybuf, int64_t C, const int32_t* expert_idx,
+                       const int32_t* position, const uint8_t* drop_mask, const int32_t* load,
+                       float loss_scale, float* dh, hipStream_t s) {
   if (T == 0) return;
   hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, h, T, N,
-                     d, (const uint16_t*)G, (const uint16_t*)Ybuf, C, expert_idx, position,
+                     d, k, (const uint16_t*)G, (const uint16_t*)Ybuf, C, expert_idx, position,
                      drop_mask, load, loss_scale, dh);
 }
 
@@ -479,13 +492,14 @@ void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d
                      part_b, (int)slices, N, d, dW_r, db);
 }
 
-void launch_grad_x(const void* G, int64_t T, int d, const int32_t* expert_idx,
+void launch_grad_x(const void* G, int64_t T, int d, int k, const int32_t* expert_idx,
                    const int32_t* position, const uint8_t* drop_mask, int64_t C, const void* dXe,
                    const float* dh, const float* W_r, int N, void* dx, hipStream_t s) {
   if (T == 0) return;
   const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((T + 63) / 64));
-  hipLaunchKernelGGL(grad_x_kernel, grid, dim3(256), 0, s, (const uint16_t*)G, T, d, expert_idx,
-                     position, drop_mask, C, (const uint16_t*)dXe, dh, W_r, N, (uint16_t*)dx);
+  hipLaunchKernelGGL(grad_x_kernel, grid, dim3(256), 0, s, (const uint16_t*)G, T, d, k,
+                     expert_idx, position, drop_mask, C, (const uint16_t*)dXe, dh, W_r, N,
+                     (uint16_t*)dx);
 }
 
 }  // namespace swl

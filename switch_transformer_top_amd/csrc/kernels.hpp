@@ -135,21 +135,21 @@ constexpr int kWideTileRows = 256;   // M tile of the wide bf16 kernel
 // (tile_start may be NULL)
 void launch_bwd_rows(const int32_t* load, int N, int64_t C, int32_t* n_kept,
                      int32_t* tile_start, hipStream_t s);
-void launch_bwd_slots(const void* G, int64_t T, int d, const int32_t* expert_idx,
+void launch_bwd_slots(const void* G, int64_t T, int d, int k, const int32_t* expert_idx,
                       const int32_t* position, const uint8_t* drop_mask, const float* gate,
                       int64_t C, int32_t* tok, void* Gs, hipStream_t s);
 void launch_transpose(const void* src, int64_t src_estride, int ld, int R, int Ccols,
                       const int32_t* valid, const int32_t* tok, void* dst, int64_t dst_estride,
                       int Rpad, int n_experts, hipStream_t s);
-void launch_router_bwd(const float* h, int64_t T, int N, int d, const void* G, const void* Ybuf,
-                       int64_t C, const int32_t* expert_idx, const int32_t* position,
-                       const uint8_t* drop_mask, const int32_t* load, float loss_scale, float* dh,
-                       hipStream_t s);
+void launch_router_bwd(const float* h, int64_t T, int N, int d, int k, const void* G,
+                       const void* Ybuf, int64_t C, const int32_t* expert_idx,
+                       const int32_t* position, const uint8_t* drop_mask, const int32_t* load,
+                       float loss_scale, float* dh, hipStream_t s);
 // part [slices, N, d] and part_b [slices, N] fp32 scratch, slices = router_wgrad_slices(T, N)
 int64_t router_wgrad_slices(int64_t T, int N);
 void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d, float* part,
                          float* part_b, float* dW_r, float* db, hipStream_t s);
-void launch_grad_x(const void* G, int64_t T, int d, const int32_t* expert_idx,
+void launch_grad_x(const void* G, int64_t T, int d, int k, const int32_t* expert_idx,
                    const int32_t* position, const uint8_t* drop_mask, int64_t C, const void* dXe,
                    const float* dh, const float* W_r, int N, void* dx, hipStream_t s);
 void launch_fill_zero(void* p, size_t bytes, hipStream_t s);

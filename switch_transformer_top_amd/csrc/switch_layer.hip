@@ -373,7 +373,9 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
     swl::prof_mark(P, s, "bwd_slots");
     int32_t* tiles = (int32_t*)(w + lo.tiles);
     swl::launch_bwd_rows(load, N, Cb, nkept, tiles, s);
-    swl::launch_bwd_slots(grad_out, T, d, expert_idx, position, drop_mask, gate, Cb, tok, gs, s);
+    const int k = top_k(c);
+    swl::launch_bwd_slots(grad_out, T, d, k, expert_idx, position, drop_mask, gate, Cb, tok, gs,
+                          s);
     // io_rows: products over the experts' token rows with F columns (the tile
     // list of 256-row tiles applies); io: the rest
     swl::GemmIO io;
@@ -391,10 +393,11 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
                                    (int64_t)d * F, ybuf, Cb * d, nkept, N, Cb, F, d, io, s);
     }
     swl::prof_mark(P, s, "router_bwd");
-    const float loss_scale =
-        (float)((double)grad_aux * (double)c.alpha * (double)N / ((double)T * (double)T));
-    swl::launch_router_bwd(logits, T, N, d, grad_out, ybuf, Cb, expert_idx, position, drop_mask,
-                           load, loss_scale, dh, s);
+    // d aux / d p_i(t) = alpha N f_i / T with f_i = load_i / (k T)
+    const float loss_scale = (float)((double)grad_aux * (double)c.alpha * (double)N /
+                                     ((double)k * (double)T * (double)T));
+    swl::launch_router_bwd(logits, T, N, d, k, grad_out, ybuf, Cb, expert_idx, position,
+                           drop_mask, load, loss_scale, dh, s);
     swl::launch_router_wgrad(dh, x, T, N, d, (float*)(w + lo.wpart), (float*)(w + lo.bpart),
                              grad_W_r, grad_b_r, s);
     if (Cb > 0) {
@@ -433,7 +436,7 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
                                      (int)Cbp, d, io_g, s);
     }
     swl::prof_mark(P, s, "grad_x");
-    swl::launch_grad_x(grad_out, T, d, expert_idx, position, drop_mask, Cb, dxe, dh, L->W_r, N,
+    swl::launch_grad_x(grad_out, T, d, k, expert_idx, position, drop_mask, Cb, dxe, dh, L->W_r, N,
                        grad_x, s);
   }
   if (T == 0 || Cb == 0) {
@@ -567,7 +570,7 @@ switch_status switch_backward(switch_layer* L, const void* x, int64_t T, const v
                               void* grad_W_out, void* ws, size_t ws_bytes, void* stream) {
   if (!L || T < 0 || T > L->cfg.t_max) return SWITCH_E_INVALID;
   const switch_config& c = L->cfg;
-  if (c.act_dtype != SWITCH_BF16 || top_k(c) != 1) return SWITCH_E_UNSUPPORTED;
+  if (c.act_dtype != SWITCH_BF16) return SWITCH_E_UNSUPPORTED;
   if (!isfinite(grad_aux)) return SWITCH_E_INVALID;
   if (T > 0 && (!x || !grad_out || !logits || !expert_idx || !gate || !position || !drop_mask ||
                 !grad_x))

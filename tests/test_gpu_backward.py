@@ -60,24 +60,31 @@ def _within(got, ref, bound, tag):
 
 
 def _bounds(spec, host, f, Gf, ref, g_aux):
-    """Error bounds of the GPU gradients (see the module docstring)."""
+    """Error bounds of the GPU gradients (see the module docstring).  Routing
+    arrays are [T] (top-1) or [T, k]; each kept assignment (t, j) contributes
+    like a kept token of the top-1 layer."""
     xf = S.to_f32(host["x"], spec.act).astype(np.float64)
     W_in = S.to_f32(host["W_in"], spec.expert).astype(np.float64)
     W_out = S.to_f32(host["W_out"], spec.expert).astype(np.float64)
     W_r = host["W_r"].astype(np.float64)
     T, d, N, F = spec.T, spec.d, spec.N, spec.F
-    gate = f["gate"].astype(np.float64)
-    kept = f["drop_mask"] == 0
+    eidx = f["expert_idx"].reshape(T, -1)
+    k = eidx.shape[1]
+    ea = eidx.reshape(-1)                                  # per assignment a = t k + j
+    gate = f["gate"].astype(np.float64).reshape(-1)
+    kept = (f["drop_mask"].reshape(-1) == 0)
+    tok = np.repeat(np.arange(T), k)
     b = dict(dW_out=np.zeros((N, d, F)), dW_in=np.zeros((N, F, d)), dx=np.zeros((T, d)))
-    ddg = np.zeros(T)           # bound on the error of dg_t = G_t . Y_t
-    dg_abs = np.zeros(T)        # bound on |dg_t|
+    ddg = np.zeros(T * k)       # bound on the error of dg_a = G_t . Y_a
+    dg_abs = np.zeros(T * k)    # bound on |dg_a|
     for e in range(N):
-        rows = np.flatnonzero(kept & (f["expert_idx"] == e))
+        rows = np.flatnonzero(kept & (ea == e))
         if rows.size == 0:
             continue
-        X = xf[rows]
+        t_r = tok[rows]                                    # distinct: one choice per expert
+        X = xf[t_r]
         n = rows.size
-        Sg = gate[rows, None] * Gf[rows]
+        Sg = gate[rows, None] * Gf[t_r]
         U = X @ W_in[e].T
         A = np.maximum(U, 0)
         XW = np.abs(X) @ np.abs(W_in[e]).T             # |X| |W_in|^T: scale of U
@@ -93,20 +100,25 @@ def _bounds(spec, host, f, Gf, ref, g_aux):
         b["dW_in"][e] = ((ddu.T @ np.abs(X)) + _gamma(n) * (DAabs.T @ np.abs(X))
                          + U16 * np.abs(ref["dW_in"][e]))
         dXe_abs = DAabs @ np.abs(W_in[e])
-        b["dx"][rows] += ddu @ np.abs(W_in[e]) + (U16 + _gamma(F)) * dXe_abs
-        ddg[rows] = (np.abs(Gf[rows]) * Yerr).sum(1) + _gamma(d) * (np.abs(Gf[rows]) * AW).sum(1)
-        dg_abs[rows] = (np.abs(Gf[rows]) * AW).sum(1)
+        b["dx"][t_r] += ddu @ np.abs(W_in[e]) + (U16 + _gamma(F)) * dXe_abs
+        ddg[rows] = (np.abs(Gf[t_r]) * Yerr).sum(1) + _gamma(d) * (np.abs(Gf[t_r]) * AW).sum(1)
+        dg_abs[rows] = (np.abs(Gf[t_r]) * AW).sum(1)
     h = f["logits"].astype(np.float64)
     p = np.exp(h - h.max(axis=1, keepdims=True))
     p /= p.sum(axis=1, keepdims=True)
-    e_t = f["expert_idx"]
-    onehot = np.zeros((T, N))
-    onehot[np.arange(T), e_t] = kept
-    pe = p[np.arange(T), e_t]
-    c = abs(g_aux) * spec.alpha * N * f["load"].astype(np.float64) / (T * T)
-    dp_abs = onehot * dg_abs[:, None] + c[None, :]
+    c = abs(g_aux) * spec.alpha * N * f["load"].astype(np.float64) / (k * T * T)
+    dp_abs = np.zeros((T, N)) + c[None, :]
+    ddh = np.zeros((T, N))
+    for j in range(k):
+        a = np.arange(T) * k + j
+        kj = kept[a].astype(np.float64)
+        onehot = np.zeros((T, N))
+        onehot[np.arange(T), eidx[:, j]] = kj
+        dp_abs += onehot * dg_abs[a][:, None]
+        pe = p[np.arange(T), eidx[:, j]]
+        ddh += p * np.abs(onehot - (pe * kj)[:, None]) * ddg[a][:, None]
     dh_abs = p * (dp_abs + (p * dp_abs).sum(1, keepdims=True))
-    ddh = p * np.abs(onehot - pe[:, None] * kept[:, None]) * ddg[:, None] + 1e-6 * dh_abs
+    ddh += 1e-6 * dh_abs
     b["dW_r"] = ddh.T @ np.abs(xf) + 2 * _gamma(T) * (dh_abs.T @ np.abs(xf))
     b["db"] = ddh.sum(0) + 2 * _gamma(T) * dh_abs.sum(0)
     b["dx"] += ddh @ np.abs(W_r) + 2 * _gamma(N) * (dh_abs @ np.abs(W_r))
@@ -114,9 +126,9 @@ def _bounds(spec, host, f, Gf, ref, g_aux):
     return b
 
 
-def _run(B, spec, g_aux=1.0, seed=0):
+def _run(B, spec, g_aux=1.0, seed=0, top_k=1):
     host = S.host_inputs(spec)
-    layer = B.SwitchLayer.from_host(spec, host)
+    layer = B.SwitchLayer.from_host(spec, host, top_k=top_k)
     print(f"[case] backward {spec.name} T={spec.T} d={spec.d} F={spec.F} N={spec.N} c={spec.c}",
           flush=True)
     T, d = spec.T, spec.d
@@ -139,9 +151,9 @@ def _check(spec, host, f, g, G_bits, g_aux, tag):
     W_in = S.to_f32(host["W_in"], spec.expert)
     W_out = S.to_f32(host["W_out"], spec.expert)
     Gf = S.to_f32(G_bits, "bf16").astype(np.float64)
-    ref = oracle.backward(xf, host["W_r"], W_in, W_out, f["logits"].astype(np.float64),
-                          f["expert_idx"], f["gate"].astype(np.float64), f["drop_mask"],
-                          f["load"], Gf, g_aux, spec.alpha)
+    args = (xf, host["W_r"], W_in, W_out, f["logits"].astype(np.float64), f["expert_idx"],
+            f["gate"].astype(np.float64), f["drop_mask"], f["load"], Gf, g_aux, spec.alpha)
+    ref = oracle.backward(*args) if f["expert_idx"].ndim == 1 else oracle.backward_topk(*args)
     b = _bounds(spec, host, f, Gf, ref, g_aux)
     _within(S.to_f32(g["grad_W_out"], "bf16"), ref["dW_out"], b["dW_out"], f"{tag} grad_W_out")
     _within(S.to_f32(g["grad_W_in"], "bf16"), ref["dW_in"], b["dW_in"], f"{tag} grad_W_in")
@@ -211,3 +223,23 @@ def test_backward_deterministic(B):
     torch.cuda.synchronize()
     for k in ("grad_x", "grad_W_r", "grad_b_r", "grad_W_in", "grad_W_out"):
         assert np.array_equal(B.from_device(again[k]), g[k]), k
+
+
+@pytest.mark.parametrize("T,N,d,F,c,seed", [
+    (1000, 8, 256, 512, 1.0, 91),      # several M tiles, drops of either choice
+    (130, 16, 128, 256, 0.5, 92),      # heavy overflow: tokens with both choices dropped
+    (700, 48, 128, 256, 1.0, 93),      # 32 < N <= 256 router
+    (600, 300, 128, 128, 1.0, 94),     # N > 256 router (logits in HBM)
+])
+def test_backward_top2_shapes(B, T, N, d, F, c, seed):
+    """Top-2 routing: two gated experts per token, loss term over k T assignments."""
+    spec = S.Spec(f"bwd2-{T}-{N}", T=T, d=d, F=F, N=N, c=c, seed=seed)
+    host, *_, f, g, G_bits = _run(B, spec, g_aux=2.0, top_k=2)
+    assert f["expert_idx"].shape == (T, 2)
+    _check(spec, host, f, g, G_bits, 2.0, spec.name)
+
+
+def test_backward_top2_switch_base_shape(B):
+    spec = S.CONFIGS[2]
+    host, *_, f, g, G_bits = _run(B, spec, top_k=2)
+    _check(spec, host, f, g, G_bits, 1.0, "bwd2-base")
