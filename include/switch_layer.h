@@ -173,18 +173,22 @@ switch_status switch_forward(switch_layer* layer, const void* x, int64_t T, void
  *   grad_W_r      [N, d] fp32 out;  grad_b_r [N] fp32 out, or NULL
  *   grad_W_in     [N, F, d] bf16 out;  grad_W_out [N, d, F] bf16 out
  *   ws, ws_bytes  device workspace of at least switch_backward_workspace_bytes(T)
+ *   fwd_ws, fwd_ws_bytes  the workspace of that forward call (switch_forward,
+ *                 unchanged since; at least switch_workspace_bytes(T)), whose
+ *                 expert activations H are then read instead of recomputed
+ *                 (the same values), or NULL
  * Weight gradients are fp32 sums over the expert's tokens rounded once to bf16;
  * grad_x is summed in fp32 and rounded once.  Every output is written (zeros
  * where nothing contributes).  SWITCH_E_UNSUPPORTED for fp32 layers.  The
- * expert activations are recomputed (nothing is kept from the forward call
- * besides its listed outputs).
+ * expert outputs Y are recomputed, and H too when fwd_ws is NULL.
  */
 switch_status switch_backward(switch_layer* layer, const void* x, int64_t T, const void* grad_out,
                               float grad_aux, const float* logits, const int32_t* expert_idx,
                               const float* gate, const int32_t* position,
                               const uint8_t* drop_mask, const int32_t* load, void* grad_x,
                               float* grad_W_r, float* grad_b_r, void* grad_W_in,
-                              void* grad_W_out, void* ws, size_t ws_bytes, void* stream);
+                              void* grad_W_out, void* ws, size_t ws_bytes, const void* fwd_ws,
+                              size_t fwd_ws_bytes, void* stream);
 
 /* Bytes of device workspace a switch_backward call with T tokens needs (0 on a
  * NULL handle or T outside [0, t_max]). */

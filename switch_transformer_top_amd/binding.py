@@ -66,7 +66,7 @@ lib.switch_forward_debug.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _v
                                      _sz, _vp, _vp]
 lib.switch_forward_debug.restype = ctypes.c_int
 lib.switch_backward.argtypes = [_vp, _vp, _i64, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp,
-                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp]
 lib.switch_backward.restype = ctypes.c_int
 lib.switch_backward_workspace_bytes.argtypes = [_vp, _i64]
 lib.switch_backward_workspace_bytes.restype = _sz
@@ -150,11 +150,12 @@ def switch_forward_debug(handle, x, T, out, expert_idx, gate, position, drop_mas
 
 def switch_backward(handle, x, T, grad_out, grad_aux, logits, expert_idx, gate, position,
                     drop_mask, load, grad_x, grad_W_r, grad_b_r, grad_W_in, grad_W_out, ws,
-                    ws_bytes, stream=0) -> int:
+                    ws_bytes, fwd_ws=None, fwd_ws_bytes=0, stream=0) -> int:
     return lib.switch_backward(handle, _ptr(x), T, _ptr(grad_out), float(grad_aux), _ptr(logits),
                                _ptr(expert_idx), _ptr(gate), _ptr(position), _ptr(drop_mask),
                                _ptr(load), _ptr(grad_x), _ptr(grad_W_r), _ptr(grad_b_r),
-                               _ptr(grad_W_in), _ptr(grad_W_out), _ptr(ws), ws_bytes, stream)
+                               _ptr(grad_W_in), _ptr(grad_W_out), _ptr(ws), ws_bytes,
+                               _ptr(fwd_ws), fwd_ws_bytes, stream)
 
 
 def switch_backward_workspace_bytes(handle: int, T: int) -> int:
@@ -283,14 +284,20 @@ class SwitchLayer:
             ws=torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev), ws_bytes=nbytes)
 
     def backward(self, x, T: int, grad_out, grad_aux: float, fwd: dict, grads: dict,
-                 stream: int = 0):
+                 stream: int = 0, reuse_forward: bool = False):
         """Gradients at the routing of a forward call whose outputs are in fwd (logits
-        included)."""
+        included).  With reuse_forward the forward's workspace (fwd["ws"]) supplies the
+        expert activations H instead of a recomputation: every alloc() of a layer shares
+        that workspace, so no other forward or routing call of the layer may run between
+        the two."""
         g = grads
+        fws = fwd["ws"] if reuse_forward else None
+        fwb = fwd["ws_bytes"] if reuse_forward else 0
         _check(switch_backward(self.handle, x, T, grad_out, grad_aux, fwd["logits"],
                                fwd["expert_idx"], fwd["gate"], fwd["position"], fwd["drop_mask"],
                                fwd["load"], g["grad_x"], g["grad_W_r"], g["grad_b_r"],
-                               g["grad_W_in"], g["grad_W_out"], g["ws"], g["ws_bytes"], stream),
+                               g["grad_W_in"], g["grad_W_out"], g["ws"], g["ws_bytes"], fws, fwb,
+                               stream),
                "switch_backward")
 
     def forward_host(self, x_host: np.ndarray, debug: bool = False) -> dict:

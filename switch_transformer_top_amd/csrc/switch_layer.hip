@@ -353,7 +353,8 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
                             float grad_aux, const float* logits, const int32_t* expert_idx,
                             const float* gate, const int32_t* position, const uint8_t* drop_mask,
                             const int32_t* load, void* grad_x, float* grad_W_r, float* grad_b_r,
-                            void* grad_W_in, void* grad_W_out, void* ws, hipStream_t s) {
+                            void* grad_W_in, void* grad_W_out, void* ws, const void* fwd_ws,
+                            hipStream_t s) {
   const switch_config& c = L->cfg;
   const int N = c.n_experts, d = c.d_model, F = c.d_ff;
   const BwdLayout lo = bwd_layout_of(L, T);
@@ -362,7 +363,11 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
   int32_t* nkept = (int32_t*)(w + lo.nkept);
   int32_t* tok = (int32_t*)(w + lo.tok);
   void* gs = w + lo.gs;
-  void* hbuf = w + lo.hbuf;
+  // the forward call's H when its workspace is given (the same tiles computed
+  // it, so it equals the recomputation bit for bit); else recomputed here
+  const bool have_h = fwd_ws != nullptr;
+  void* hbuf = have_h ? (void*)((const char*)fwd_ws + layout_of(L, T).hbuf)
+                      : (void*)(w + lo.hbuf);
   void* ybuf = w + lo.ybuf;
   void* du = w + lo.du;
   void* dxe = w + lo.dxe;
@@ -384,10 +389,11 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
     swl::GemmIO io_rows = io;
     io_rows.tile_start = tiles;
     if (Cb > 0) {
-      // the forward's expert activations, recomputed
-      swl::prof_mark(P, s, "recompute_h");
-      swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
-                                   hbuf, Cb * F, nkept, N, Cb, d, F, io_rows, s);
+      if (!have_h) {
+        swl::prof_mark(P, s, "recompute_h");
+        swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
+                                     hbuf, Cb * F, nkept, N, Cb, d, F, io_rows, s);
+      }
       swl::prof_mark(P, s, "recompute_y");
       swl::launch_expert_gemm_bf16(swl::kRowsDense, false, hbuf, Cb * F, L->W_out,
                                    (int64_t)d * F, ybuf, Cb * d, nkept, N, Cb, F, d, io, s);
@@ -567,7 +573,8 @@ switch_status switch_backward(switch_layer* L, const void* x, int64_t T, const v
                               const float* gate, const int32_t* position,
                               const uint8_t* drop_mask, const int32_t* load, void* grad_x,
                               float* grad_W_r, float* grad_b_r, void* grad_W_in,
-                              void* grad_W_out, void* ws, size_t ws_bytes, void* stream) {
+                              void* grad_W_out, void* ws, size_t ws_bytes, const void* fwd_ws,
+                              size_t fwd_ws_bytes, void* stream) {
   if (!L || T < 0 || T > L->cfg.t_max) return SWITCH_E_INVALID;
   const switch_config& c = L->cfg;
   if (c.act_dtype != SWITCH_BF16) return SWITCH_E_UNSUPPORTED;
@@ -582,13 +589,15 @@ switch_status switch_backward(switch_layer* L, const void* x, int64_t T, const v
       !aligned(grad_W_in, 16) || !aligned(grad_W_out, 16) || !aligned(ws, 16))
     return SWITCH_E_INVALID;
   if (ws_bytes < bwd_layout_of(L, T).total) return SWITCH_E_INVALID;
+  if (fwd_ws && (!aligned(fwd_ws, 16) || fwd_ws_bytes < layout_of(L, T).total))
+    return SWITCH_E_INVALID;
   const size_t xbytes = (size_t)T * (size_t)c.d_model * 2;
   if (overlaps(grad_x, xbytes, x, xbytes) || overlaps(grad_x, xbytes, grad_out, xbytes))
     return SWITCH_E_INVALID;
   switch_status st = check_device(L);
   if (st != SWITCH_OK) return st;
   return backward_impl(L, x, T, grad_out, grad_aux, logits, expert_idx, gate, position, drop_mask,
-                       load, grad_x, grad_W_r, grad_b_r, grad_W_in, grad_W_out, ws,
+                       load, grad_x, grad_W_r, grad_b_r, grad_W_in, grad_W_out, ws, fwd_ws,
                        (hipStream_t)stream);
 }
 

@@ -243,3 +243,27 @@ def test_backward_top2_switch_base_shape(B):
     spec = S.CONFIGS[2]
     host, *_, f, g, G_bits = _run(B, spec, top_k=2)
     _check(spec, host, f, g, G_bits, 1.0, "bwd2-base")
+
+
+@pytest.mark.parametrize("top_k,T,N,d,F,c,seed", [
+    (1, 1000, 8, 256, 512, 1.0, 95),
+    (1, 4096, 64, 512, 1024, 1.0, 96),
+    (2, 700, 48, 128, 256, 1.0, 97),
+])
+def test_backward_reads_forward_h(B, top_k, T, N, d, F, c, seed):
+    """H taken from the forward call's workspace gives the gradients of the
+    recomputation bit for bit; a forward workspace that is too small is refused."""
+    spec = S.Spec(f"bwd-reuse-{top_k}-{T}", T=T, d=d, F=F, N=N, c=c, seed=seed)
+    host, layer, x, G, fwd, grads, f, g, G_bits = _run(B, spec, top_k=top_k)
+    again = layer.alloc_backward(T)
+    layer.backward(x, T, G, 1.0, fwd, again, reuse_forward=True)
+    torch.cuda.synchronize()
+    for k in ("grad_x", "grad_W_r", "grad_b_r", "grad_W_in", "grad_W_out"):
+        assert np.array_equal(B.from_device(again[k]), g[k]), k
+    a = again
+    st = B.switch_backward(layer.handle, x, T, G, 1.0, fwd["logits"], fwd["expert_idx"],
+                           fwd["gate"], fwd["position"], fwd["drop_mask"], fwd["load"],
+                           a["grad_x"], a["grad_W_r"], a["grad_b_r"], a["grad_W_in"],
+                           a["grad_W_out"], a["ws"], a["ws_bytes"], fwd["ws"],
+                           fwd["ws_bytes"] - 1)
+    assert st == B.SWITCH_E_INVALID
