@@ -172,6 +172,7 @@ def _check(spec, host, f, g, G_bits, g_aux, tag):
     (700, 48, 128, 256, 1.0, 75),      # 32 < N <= 256 router
     (600, 300, 128, 128, 1.0, 76),     # N > 256 router (logits in HBM)
     (4096, 64, 512, 1024, 1.0, 81),    # weight gradients on 256 x 256 tiles, operands K-outer
+    (1500, 4, 128, 512, 1.0, 82),      # capacity 375: 256-row tiles from the tile list
 ])
 def test_backward_shapes(B, T, N, d, F, c, seed):
     spec = S.Spec(f"bwd-{T}-{N}", T=T, d=d, F=F, N=N, c=c, seed=seed)
