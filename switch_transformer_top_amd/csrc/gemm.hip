@@ -135,12 +135,12 @@ __device__ __forceinline__ void combine_prefetch(CombineRows<TI, TJ>& cr,
   }
 }
 
+// The combine of a tile already staged in LDS (stage_tile_bf16 with CR::LD).
 template <int TI, int TJ>
-__device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ], uint16_t* stage,
+__device__ __forceinline__ void combine_from_stage(const uint16_t* stage,
                                                    const CombineRows<TI, TJ>& cr,
                                                    uint16_t* __restrict__ out, int lane) {
   using CR = CombineRows<TI, TJ>;
-  stage_tile_bf16<TI, TJ, CR::LD, false>(acc, stage, lane);
 #pragma unroll
   for (int it = 0; it < CR::IT; ++it) {
     const int idx = it * kWave + lane;
@@ -150,6 +150,14 @@ __device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ]
       *reinterpret_cast<u32x4*>(out + cr.at[it]) = combine_vec_bf16(cr.xv[it], yv, cr.g[it]);
     }
   }
+}
+
+template <int TI, int TJ>
+__device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ], uint16_t* stage,
+                                                   const CombineRows<TI, TJ>& cr,
+                                                   uint16_t* __restrict__ out, int lane) {
+  stage_tile_bf16<TI, TJ, CombineRows<TI, TJ>::LD, false>(acc, stage, lane);
+  combine_from_stage<TI, TJ>(stage, cr, out, lane);
 }
 
 template <int TI, int TJ>
@@ -387,7 +395,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
   const uint16_t* Ae = MODE == kRowsGather ? io.x : A + (int64_t)e * strideA;
   const uint16_t* Be = B + (int64_t)e * strideB + (int64_t)n0 * K;
   uint16_t* Ce = Cout + (int64_t)e * strideC;
-  const int32_t* tok_e = MODE == kRowsGather ? io.tok + (int64_t)e * C : nullptr;
+  const int32_t* tok_e =
+      MODE == kRowsGather || MODE == kRowsCombine ? io.tok + (int64_t)e * C : nullptr;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -476,8 +485,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
 
   __syncthreads();  // every wave is done with the LDS operand buffers
   uint16_t* stage = wlds + wave * 128 * (64 + 8);
-  static_assert(MODE != kRowsCombine, "the combine runs on the split-K and 128-row tiles");
-  if (MODE == kRowsMask)
+  if (MODE == kRowsCombine) {
+    // the accumulators go to LDS first, so the residual rows and gates fetched
+    // next do not have to share the registers with them
+    stage_tile_bf16<TI, TJ, CombineRows<TI, TJ>::LD, false>(acc, stage, lane);
+    CombineRows<TI, TJ> cr;
+    combine_prefetch<TI, TJ>(cr, tok_e, io.x, io.gate, m0 + wm * 128, n0 + wn * 64, rows_e,
+                             Nout, lane);
+    combine_from_stage<TI, TJ>(stage, cr, io.out, lane);
+  } else if (MODE == kRowsMask)
     store_tile_bf16<TI, TJ, false, true>(acc, stage, Ce, m0 + wm * 128, n0 + wn * 64, rows_e,
                                          Nout, lane, io.mask + (int64_t)e * strideC);
   else
@@ -1005,15 +1021,18 @@ int device_cus() {
 // The wide tile pays off when N splits into 256-column tiles and the experts
 // hold at least two of its M tiles; without a compact tile list (every expert
 // at full capacity) also only with tiles for at least two rounds of CUs.
-// one_tile: with the tile list, one full M tile of capacity suffices (the
-// forward-layout products: at the Switch-Large shape, 188-320 rows per expert,
-// the first matmul is 6% faster than on 128-row tiles despite the padding of
-// the second M tile, while the backward's masked K-outer product is slower).
+// one_tile (the forward-layout products): with the tile list, one full M tile
+// of capacity suffices when the experts' tiles at full capacity would fill the
+// CUs (at the Switch-Large shape, 188-320 rows per expert, both matmuls beat
+// 128-row tiles despite the padding of the second M tile; at the Switch-Base
+// second matmul, 72 tiles, the split-K kernel wins), while the backward's
+// masked K-outer product is slower on them.
 bool use_wide(int64_t C, int Nout, int n_experts, const GemmIO& io, bool one_tile = false) {
   static_assert(GW_BM == kWideTileRows, "tile list and kernel agree");
   const int64_t tiles = (C + GW_BM - 1) / GW_BM * (Nout / GW_BN) * n_experts;
   if (Nout % GW_BN != 0) return false;
-  if (io.tile_start) return C >= (one_tile ? GW_BM : 2 * GW_BM);
+  if (io.tile_start && one_tile) return C >= GW_BM && tiles >= device_cus();
+  if (io.tile_start) return C >= 2 * GW_BM;
   return C >= 2 * GW_BM && tiles >= 2 * device_cus();
 }
 
@@ -1138,8 +1157,11 @@ void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t st
   const uint16_t* a = (const uint16_t*)A;
   const uint16_t* b = (const uint16_t*)B;
   uint16_t* c = (uint16_t*)Cout;
-  if (mode != kRowsCombine && use_wide(C, Nout, n_experts, io, true)) {
-    if (mode == kRowsGather && relu)
+  if (use_wide(C, Nout, n_experts, io, true)) {
+    if (mode == kRowsCombine)
+      launch_wide<false, kRowsCombine>(a, strideA, b, strideB, c, strideC, rows, n_experts, C, K,
+                                       Nout, io, s);
+    else if (mode == kRowsGather && relu)
       launch_wide<true, kRowsGather>(a, strideA, b, strideB, c, strideC, rows, n_experts, C, K,
                                      Nout, io, s);
     else if (mode == kRowsMask)

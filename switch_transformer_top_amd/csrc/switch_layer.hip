@@ -251,9 +251,9 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
     swl::prof_mark(P, s, "gemm1_relu");
     swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
                                  hbuf, Cb * F, r.nkept, N, Cb, d, F, io, s);
-    // GEMM2 runs on the same tiles with or without the fused combine (the
-    // tile list is GEMM1's), so both paths give the same expert outputs
-    io.tile_start = nullptr;
+    // GEMM2 runs on the same tiles with or without the fused combine, so both
+    // paths give the same expert outputs (the tile list of 256-row tiles
+    // applies when the wide kernel is chosen)
     if (fused) {
       swl::prof_mark(P, s, "gemm2_combine");
       swl::launch_expert_gemm_bf16(swl::kRowsCombine, false, hbuf, Cb * F, L->W_out,
