@@ -218,8 +218,10 @@ switch_status switch_forward_debug(switch_layer* layer, const void* x, int64_t T
 
 /*
  * Per-kernel timing for measurement.  switch_profile_enable(layer, n) makes the
- * next n switch_forward / switch_route calls record a HIP event before every
- * kernel they launch and one after the last, on the call's stream, without
+ * next n switch_forward / switch_route / switch_backward calls time each stage
+ * (a kernel, or a few kernels in a row) with HIP events that the kernel
+ * dispatches themselves record (hipExtLaunchKernel: the start of the stage's
+ * first kernel, the end of its last), on the call's stream, without
  * synchronising (n = 0 turns recording off and frees the events; calls past
  * the n-th are not recorded).  switch_profile_read waits for the last
  * recorded call to finish and writes, for each stage in launch order, the mean

@@ -325,15 +325,15 @@ void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, in
   if (N <= 1024) {
     int EG = 1;
     while (EG < N) EG <<= 1;
-    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, P_part, nc, N, EG, T,
+    launch_k(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, P_part, nc, N, EG, T,
                        k, C, alpha, load, n_kept, nullptr, aux, tile_start, tile_rows);
     return;
   }
   constexpr int EG = 64;
-  hipLaunchKernelGGL(route_scan_kernel, dim3((unsigned)((N + EG - 1) / EG)), dim3(1024), 0, s,
+  launch_k(route_scan_kernel, dim3((unsigned)((N + EG - 1) / EG)), dim3(1024), 0, s,
                      hist, P_part, nc, N, EG, T, k, C, alpha, load, n_kept, terms, aux, nullptr,
                      tile_rows);
-  hipLaunchKernelGGL(aux_kernel, dim3(1), dim3(1024), 0, s, terms, N, T, k, alpha, aux, n_kept,
+  launch_k(aux_kernel, dim3(1), dim3(1024), 0, s, terms, N, T, k, alpha, aux, n_kept,
                      tile_start, tile_rows);
 }
 
@@ -343,7 +343,7 @@ void launch_finalize_positions(int64_t T, int k, const int32_t* expert_idx,
                                hipStream_t s) {
   if (T == 0) return;
   const int64_t n = T * k;
-  hipLaunchKernelGGL(finalize_positions_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+  launch_k(finalize_positions_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                      s, T, k, expert_idx, rank_local, offsets, N, chunk, C, position, drop_mask);
 }
 
@@ -359,7 +359,7 @@ void launch_assign(const int32_t* hist, const float* P_part, int64_t nc, int N, 
                    int32_t* tok, int copy_mode, int row_bytes, const void* x, void* dst,
                    hipStream_t s) {
   const int64_t nb = (T + AS_TOK - 1) / AS_TOK;
-  hipLaunchKernelGGL(assign_kernel, dim3((unsigned)(nb + 1)), dim3(256), 0, s, hist, P_part, nc,
+  launch_k(assign_kernel, dim3((unsigned)(nb + 1)), dim3(256), 0, s, hist, P_part, nc,
                      N, T, k, chunk, C, alpha, expert_idx, rank_local, load, n_kept, aux,
                      tile_start, tile_rows, position, drop_mask, tok, copy_mode, row_bytes / 16,
                      (const uint4*)x, (uint4*)dst);

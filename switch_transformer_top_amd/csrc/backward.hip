@@ -414,13 +414,13 @@ void launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   const int64_t n = (int64_t)(bytes / 16);
   if (n == 0) return;
   const int64_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
+  launch_k(fill_zero_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
                      0, s, (u32x4*)p, n);
 }
 
 void launch_bwd_rows(const int32_t* load, int N, int64_t C, int32_t* n_kept,
                      int32_t* tile_start, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_rows_kernel, dim3(1), dim3(1024), 0, s, load, N, C, n_kept, tile_start,
+  launch_k(bwd_rows_kernel, dim3(1), dim3(1024), 0, s, load, N, C, n_kept, tile_start,
                      kWideTileRows);
 }
 
@@ -429,7 +429,7 @@ void launch_bwd_slots(const void* G, int64_t T, int d, int k, const int32_t* exp
                       int64_t C, int32_t* tok, void* Gs, hipStream_t s) {
   if (T == 0) return;
   const int rv = d / 8;
-  hipLaunchKernelGGL(bwd_slots_kernel, dim3((unsigned)((T * k * rv + 255) / 256)), dim3(256), 0,
+  launch_k(bwd_slots_kernel, dim3((unsigned)((T * k * rv + 255) / 256)), dim3(256), 0,
                      s, (const u32x4*)G, T, k, rv, expert_idx, position, drop_mask, gate, C, tok,
                      (u32x4*)Gs);
 }
@@ -439,7 +439,7 @@ void launch_transpose(const void* src, int64_t src_estride, int ld, int R, int C
                       int Rpad, int n_experts, hipStream_t s) {
   if (Ccols == 0 || Rpad == 0 || n_experts == 0) return;
   const dim3 grid((unsigned)((Ccols + 63) / 64), (unsigned)(Rpad / 64), (unsigned)n_experts);
-  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, (const uint16_t*)src, src_estride,
+  launch_k(transpose_kernel, grid, dim3(256), 0, s, (const uint16_t*)src, src_estride,
                      ld, R, Ccols, valid, tok, (uint16_t*)dst, dst_estride, Rpad);
 }
 
@@ -448,7 +448,7 @@ void launch_router_bwd(const float* h, int64_t T, int N, int d, int k, const voi
                        const int32_t* position, const uint8_t* drop_mask, const int32_t* load,
                        float loss_scale, float* dh, hipStream_t s) {
   if (T == 0) return;
-  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, h, T, N,
+  launch_k(router_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, h, T, N,
                      d, k, (const uint16_t*)G, (const uint16_t*)Ybuf, C, expert_idx, position,
                      drop_mask, load, loss_scale, dh);
 }
@@ -474,21 +474,21 @@ void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d
     const dim3 grid((unsigned)((d + 255) / 256), (unsigned)slices);
     const int64_t sl = small_slice(T);
     if (N <= 8)
-      hipLaunchKernelGGL(router_wgrad_small_kernel<8>, grid, dim3(64), 0, s, dh,
+      launch_k(router_wgrad_small_kernel<8>, grid, dim3(64), 0, s, dh,
                          (const uint16_t*)x, T, N, d, sl, part, part_b);
     else if (N <= 16)
-      hipLaunchKernelGGL(router_wgrad_small_kernel<16>, grid, dim3(64), 0, s, dh,
+      launch_k(router_wgrad_small_kernel<16>, grid, dim3(64), 0, s, dh,
                          (const uint16_t*)x, T, N, d, sl, part, part_b);
     else
-      hipLaunchKernelGGL(router_wgrad_small_kernel<32>, grid, dim3(64), 0, s, dh,
+      launch_k(router_wgrad_small_kernel<32>, grid, dim3(64), 0, s, dh,
                          (const uint16_t*)x, T, N, d, sl, part, part_b);
   } else if (slices > 0) {
     const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)slices);
-    hipLaunchKernelGGL(router_wgrad_kernel, grid, dim3(256), 0, s, dh, (const uint16_t*)x, T, N,
+    launch_k(router_wgrad_kernel, grid, dim3(256), 0, s, dh, (const uint16_t*)x, T, N,
                        d, part, part_b);
   }
   const int64_t n = (int64_t)N * d + N;
-  hipLaunchKernelGGL(router_wgrad_reduce, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, part,
+  launch_k(router_wgrad_reduce, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, part,
                      part_b, (int)slices, N, d, dW_r, db);
 }
 
@@ -497,7 +497,7 @@ void launch_grad_x(const void* G, int64_t T, int d, int k, const int32_t* expert
                    const float* dh, const float* W_r, int N, void* dx, hipStream_t s) {
   if (T == 0) return;
   const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((T + 63) / 64));
-  hipLaunchKernelGGL(grad_x_kernel, grid, dim3(256), 0, s, (const uint16_t*)G, T, d, k,
+  launch_k(grad_x_kernel, grid, dim3(256), 0, s, (const uint16_t*)G, T, d, k,
                      expert_idx, position, drop_mask, C, (const uint16_t*)dXe, dh, W_r, N,
                      (uint16_t*)dx);
 }

@@ -1050,7 +1050,7 @@ void launch_wide(const uint16_t* a, int64_t strideA, const uint16_t* b, int64_t 
   const int mt = (int)((C + GW_BM - 1) / GW_BM), nt = Nout / GW_BN;
   const int tiles = mt * nt * n_experts;
   const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
-  hipLaunchKernelGGL((gemm_bf16_wide_kernel<RELU, MODE>), dim3(grid), dim3(512), kWideLds, s, a,
+  launch_k((gemm_bf16_wide_kernel<RELU, MODE>), dim3(grid), dim3(512), kWideLds, s, a,
                      strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C,
                      n_experts);
 }
@@ -1068,7 +1068,7 @@ void launch_split(unsigned grid, const uint16_t* a, int64_t strideA, const uint1
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSplitLds);
     set_on |= 1ull << dev;
   }
-  hipLaunchKernelGGL((gemm_bf16_split_kernel<RELU, MODE, BKO>), dim3(grid), dim3(512), kSplitLds,
+  launch_k((gemm_bf16_split_kernel<RELU, MODE, BKO>), dim3(grid), dim3(512), kSplitLds,
                      s, a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
 }
 
@@ -1089,7 +1089,7 @@ void launch_t(const uint16_t* a, int64_t strideA, const uint16_t* b, int64_t str
   const int mt = (int)((C + BM - 1) / BM), nt = Nout / BN;
   const int tiles = mt * nt * n_experts;
   const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(BN * 2), lds, s, a, strideA, b, strideB, c, strideC,
+  launch_k(kern, dim3(grid), dim3(BN * 2), lds, s, a, strideA, b, strideB, c, strideC,
                      rows, K, Nout, mt, nt, tiles, io, C, n_experts);
 }
 
@@ -1196,19 +1196,19 @@ void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t st
     return;
   }
   if (mode == kRowsGather && relu)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true, kRowsGather>), dim3(grid), dim3(256), 0, s,
+    launch_k((gemm_bf16_kernel<BM, BN, true, kRowsGather>), dim3(grid), dim3(256), 0, s,
                        a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
   else if (mode == kRowsCombine)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false, kRowsCombine>), dim3(grid), dim3(256), 0,
+    launch_k((gemm_bf16_kernel<BM, BN, false, kRowsCombine>), dim3(grid), dim3(256), 0,
                        s, a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
   else if (mode == kRowsMask)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false, kRowsMask>), dim3(grid), dim3(256), 0, s,
+    launch_k((gemm_bf16_kernel<BM, BN, false, kRowsMask>), dim3(grid), dim3(256), 0, s,
                        a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
   else if (relu)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true, kRowsDense>), dim3(grid), dim3(256), 0, s,
+    launch_k((gemm_bf16_kernel<BM, BN, true, kRowsDense>), dim3(grid), dim3(256), 0, s,
                        a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false, kRowsDense>), dim3(grid), dim3(256), 0, s,
+    launch_k((gemm_bf16_kernel<BM, BN, false, kRowsDense>), dim3(grid), dim3(256), 0, s,
                        a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
 }
 
@@ -1222,10 +1222,10 @@ void launch_expert_gemm(bool bf16, bool relu, const void* A, int64_t strideA, co
   } else {
     dim3 grid((unsigned)((Nout + 31) / 32), (unsigned)((C + 31) / 32), (unsigned)n_experts);
     if (relu)
-      hipLaunchKernelGGL(gemm_f32_kernel<true>, grid, dim3(256), 0, s, (const float*)A, strideA,
+      launch_k(gemm_f32_kernel<true>, grid, dim3(256), 0, s, (const float*)A, strideA,
                          (const float*)B, strideB, (float*)Cout, strideC, rows, K, Nout);
     else
-      hipLaunchKernelGGL(gemm_f32_kernel<false>, grid, dim3(256), 0, s, (const float*)A, strideA,
+      launch_k(gemm_f32_kernel<false>, grid, dim3(256), 0, s, (const float*)A, strideA,
                          (const float*)B, strideB, (float*)Cout, strideC, rows, K, Nout);
   }
 }

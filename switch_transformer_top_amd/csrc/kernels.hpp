@@ -1,40 +1,85 @@
 // Launchers of the Switch-layer kernels (host side) and the per-stage event
 // profiler used for measurement.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace swl {
 
-// Records a HIP event on the launch stream before each stage of a call and
-// one after its last stage, for up to max_calls calls (no synchronisation).
+// Per-stage timing of a call, for measurement.  While a profiled call runs,
+// the first kernel a stage launches records the stage's start event and every
+// kernel its stop event on the dispatch itself (hipExtLaunchKernel), so a
+// stage's time is its kernels' execution from the first start to the last end,
+// with no event packets of their own on the stream.  Up to max_calls calls are
+// recorded; nothing synchronises.
+struct StageEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool launched = false;
+};
+// the open stage of the profiled call in progress on this thread, or NULL
+extern thread_local StageEvents* g_stage;
+
 struct Profiler {
   static constexpr int kMax = 24;   // stages per call
   bool on = false;
   int max_calls = 0;
   int calls = 0;                    // calls recorded so far
-  int n = 0;                        // stages recorded in the current call
+  int n = 0;                        // stages opened in the current call
   bool active = false;              // the current call is being recorded
-  hipEvent_t* ev = nullptr;         // max_calls * (kMax + 1)
+  hipEvent_t* ev = nullptr;         // max_calls * kMax * 2: start and stop per stage
   const char* names[kMax];
+  StageEvents cur;                  // the stage open now
 };
 
+// A stage that launched no kernel gets both events recorded where it ends.
+inline void prof_close(Profiler* p, hipStream_t s) {
+  if (g_stage != &p->cur) return;
+  if (!p->cur.launched) {
+    (void)hipEventRecord(p->cur.start, s);
+    (void)hipEventRecord(p->cur.stop, s);
+  }
+  g_stage = nullptr;
+}
 inline void prof_begin(Profiler* p) {
+  g_stage = nullptr;
   if (!p || !p->on) return;
   p->active = p->calls < p->max_calls;
   p->n = 0;
 }
 inline void prof_mark(Profiler* p, hipStream_t s, const char* name) {
   if (!p || !p->on || !p->active || p->n >= Profiler::kMax) return;
+  prof_close(p, s);
   p->names[p->n] = name;
-  (void)hipEventRecord(p->ev[p->calls * (Profiler::kMax + 1) + p->n], s);
+  hipEvent_t* e = p->ev + 2 * (p->calls * Profiler::kMax + p->n);
+  p->cur.start = e[0];
+  p->cur.stop = e[1];
+  p->cur.launched = false;
+  g_stage = &p->cur;
   p->n += 1;
 }
 inline void prof_end(Profiler* p, hipStream_t s) {
-  if (!p || !p->on || !p->active || p->n == 0) return;
-  (void)hipEventRecord(p->ev[p->calls * (Profiler::kMax + 1) + p->n], s);
+  if (!p || !p->on || !p->active || p->n == 0) {
+    g_stage = nullptr;
+    return;
+  }
+  prof_close(p, s);
   p->calls += 1;
   p->active = false;
+}
+
+// Every kernel of the library is launched through here.
+template <typename F, typename... Args>
+inline void launch_k(F kernel, const dim3& grid, const dim3& block, uint32_t lds, hipStream_t s,
+                     Args... args) {
+  StageEvents* st = g_stage;
+  if (st) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, st->launched ? nullptr : st->start,
+                          st->stop, 0, args...);
+    st->launched = true;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  }
 }
 
 // Experts per token: 1 (the Switch layer) or 2 (classic top-2 MoE routing).

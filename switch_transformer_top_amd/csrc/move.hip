@@ -169,7 +169,7 @@ void launch_dispatch(const void* x, int64_t T, int k, int row_bytes, const int32
                      const int32_t* rank_local, const int32_t* offsets, int N, int64_t chunk,
                      int64_t C, int32_t* position, uint8_t* drop_mask, void* Xbuf, hipStream_t s) {
   if (T == 0) return;
-  hipLaunchKernelGGL(dispatch_kernel, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
+  launch_k(dispatch_kernel, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
                      (const uint4*)x, T, k, row_bytes / 16, expert_idx, rank_local, offsets, N,
                      chunk, C, position, drop_mask, (uint4*)Xbuf);
 }
@@ -180,7 +180,7 @@ void launch_dispatch_index(const void* x, int64_t T, int k, int row_bytes,
                            int32_t* position, uint8_t* drop_mask, int32_t* tok, bool copy_dropped,
                            void* out, hipStream_t s) {
   if (T == 0) return;
-  hipLaunchKernelGGL(dispatch_index_kernel, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
+  launch_k(dispatch_index_kernel, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
                      (const uint4*)x, T, k, row_bytes / 16, expert_idx, rank_local, offsets, N,
                      chunk, C, position, drop_mask, tok, copy_dropped && k == 1, (uint4*)out);
 }
@@ -190,11 +190,11 @@ void launch_combine(const void* x, bool bf16, int64_t T, int k, int row_bytes,
                     const float* gate, int64_t C, const void* Ybuf, void* out, hipStream_t s) {
   if (T == 0) return;
   if (bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
+    launch_k(combine_kernel<true>, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
                        (const uint4*)x, T, k, row_bytes / 16, expert_idx, position, drop_mask,
                        gate, C, (const uint4*)Ybuf, (uint4*)out);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
+    launch_k(combine_kernel<false>, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
                        (const uint4*)x, T, k, row_bytes / 16, expert_idx, position, drop_mask,
                        gate, C, (const uint4*)Ybuf, (uint4*)out);
 }
@@ -202,7 +202,7 @@ void launch_combine(const void* x, bool bf16, int64_t T, int k, int row_bytes,
 void launch_copy_expert_rows(const void* Ybuf, const int32_t* n_kept, int N, int64_t C,
                              int row_bytes, void* dst, hipStream_t s) {
   if (C == 0 || N == 0) return;
-  hipLaunchKernelGGL(copy_expert_rows_kernel, dim3((unsigned)((C + 3) / 4), (unsigned)N),
+  launch_k(copy_expert_rows_kernel, dim3((unsigned)((C + 3) / 4), (unsigned)N),
                      dim3(256), 0, s, (const uint4*)Ybuf, n_kept, C, row_bytes / 16, (uint4*)dst);
 }
 

@@ -787,13 +787,13 @@ void launch_router_logits(const void* x, bool x_bf16, const float* W_r, const fl
     // MFMA logits in expert tiles of 256, statistics by route_rows_kernel
     constexpr int BT = 64 * kTokRowt;
     const dim3 grid((unsigned)((T + BT - 1) / BT), (unsigned)((N + 255) / 256));
-    hipLaunchKernelGGL((router_tok_kernel<256, kTokRowt, false>), grid, dim3(256), 0, s,
+    launch_k((router_tok_kernel<256, kTokRowt, false>), grid, dim3(256), 0, s,
                        (const uint16_t*)x, W_r, b_r, T, d, N, 1, h, nullptr, nullptr, nullptr,
                        nullptr, nullptr);
     return;
   }
   dim3 grid((unsigned)((T + RT_BT - 1) / RT_BT), (unsigned)((N + RT_BE - 1) / RT_BE));
-  hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, s, (const float*)x, W_r,
+  launch_k(router_logits_kernel<float>, grid, dim3(256), 0, s, (const float*)x, W_r,
                      b_r, h, T, d, N);
 }
 
@@ -804,10 +804,10 @@ void launch_router_fused(const uint16_t* x, const float* W_r, const float* b_r, 
   const int64_t ch = route_chunk_tokens(true, N);
   const dim3 grid((unsigned)((T + ch - 1) / ch));
 #define SWL_SMALL(NP)                                                                           \
-  hipLaunchKernelGGL((router_small_kernel<NP>), grid, dim3(256), 0, s, x, W_r, b_r, T, d, N, k, \
+  launch_k((router_small_kernel<NP>), grid, dim3(256), 0, s, x, W_r, b_r, T, d, N, k, \
                      logits, expert_idx, gate, P_part, hist, rank_local)
 #define SWL_TOK(NP)                                                                             \
-  hipLaunchKernelGGL((router_tok_kernel<NP, kTokRowt, true>), grid, dim3(256), 0, s, x, W_r,    \
+  launch_k((router_tok_kernel<NP, kTokRowt, true>), grid, dim3(256), 0, s, x, W_r,    \
                      b_r, T, d, N, k, logits, expert_idx, gate, P_part, hist, rank_local)
   if (N <= 16) SWL_SMALL(16);
   else if (N <= 32) SWL_SMALL(32);
@@ -824,14 +824,14 @@ void launch_route_rows(const float* h, int64_t T, int N, int k, int32_t* expert_
   const dim3 grid((unsigned)((T + RR_ROWS - 1) / RR_ROWS));
   const size_t lds = (2 * sizeof(double) + sizeof(int32_t)) * (size_t)N;
 #define SWL_RR(NPL)                                                                              \
-  hipLaunchKernelGGL(route_rows_reg_kernel<NPL>, grid, dim3(256), lds, s, h, T, N, k, expert_idx, \
+  launch_k(route_rows_reg_kernel<NPL>, grid, dim3(256), lds, s, h, T, N, k, expert_idx, \
                      gate, P_part, hist, rank_local)
   if (N <= 4 * kWave) SWL_RR(4);
   else if (N <= 8 * kWave) SWL_RR(8);
   else if (N <= 16 * kWave) SWL_RR(16);
   else if (N <= 32 * kWave) SWL_RR(32);
   else
-    hipLaunchKernelGGL(route_rows_kernel, grid, dim3(256), sizeof(int32_t) * (size_t)N, s, h, T,
+    launch_k(route_rows_kernel, grid, dim3(256), sizeof(int32_t) * (size_t)N, s, h, T,
                        N, k, expert_idx, gate, P_part, hist, rank_local);
 #undef SWL_RR
 }

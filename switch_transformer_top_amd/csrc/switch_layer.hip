@@ -461,6 +461,10 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
 
 }  // namespace
 
+namespace swl {
+thread_local StageEvents* g_stage = nullptr;
+}
+
 extern "C" {
 
 switch_status switch_layer_create(const switch_config* cfg, const float* W_r, const float* b_r,
@@ -604,8 +608,9 @@ switch_status switch_backward(switch_layer* L, const void* x, int64_t T, const v
 switch_status switch_profile_enable(switch_layer* L, int max_calls) {
   if (!L || max_calls < 0) return SWITCH_E_INVALID;
   swl::Profiler& P = L->prof;
+  if (swl::g_stage == &P.cur) swl::g_stage = nullptr;
   if (P.ev) {
-    for (int i = 0; i < P.max_calls * (swl::Profiler::kMax + 1); ++i) (void)hipEventDestroy(P.ev[i]);
+    for (int i = 0; i < P.max_calls * swl::Profiler::kMax * 2; ++i) (void)hipEventDestroy(P.ev[i]);
     delete[] P.ev;
     P.ev = nullptr;
   }
@@ -614,7 +619,7 @@ switch_status switch_profile_enable(switch_layer* L, int max_calls) {
   P.calls = 0;
   P.n = 0;
   if (max_calls == 0) return SWITCH_OK;
-  const int count = max_calls * (swl::Profiler::kMax + 1);
+  const int count = max_calls * swl::Profiler::kMax * 2;
   P.ev = new (std::nothrow) hipEvent_t[count];
   if (!P.ev) return SWITCH_E_INVALID;
   for (int i = 0; i < count; ++i) {
@@ -634,16 +639,16 @@ int switch_profile_read(switch_layer* L, float* ms, const char** names, int cap)
   if (!L || !L->prof.ev || cap < 0) return -1;
   swl::Profiler& P = L->prof;
   if (P.calls == 0) return 0;
-  const int stride = swl::Profiler::kMax + 1;
+  const int stride = swl::Profiler::kMax * 2;
   // every recorded call of this session has the same stages (the last one's)
   const int n = P.n;
-  if (hipEventSynchronize(P.ev[(P.calls - 1) * stride + n]) != hipSuccess) return -1;
+  if (hipEventSynchronize(P.ev[(P.calls - 1) * stride + 2 * (n - 1) + 1]) != hipSuccess) return -1;
   for (int i = 0; i < n && i < cap; ++i) {
     double sum = 0.0;
     for (int c = 0; c < P.calls; ++c) {
       float t = 0.f;
-      if (hipEventElapsedTime(&t, P.ev[c * stride + i], P.ev[c * stride + i + 1]) != hipSuccess)
-        return -1;
+      const hipEvent_t* e = P.ev + c * stride + 2 * i;
+      if (hipEventElapsedTime(&t, e[0], e[1]) != hipSuccess) return -1;
       sum += t;
     }
     if (ms) ms[i] = (float)(sum / P.calls);
