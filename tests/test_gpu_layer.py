@@ -69,6 +69,7 @@ def test_tiny_fp32_config(B):
     (2100, 4, 256, 768, 1.0, 27),      # 256-row tiles with a ragged last tile and drops
     (1500, 4, 128, 512, 1.0, 28),      # capacity 375: one full 256-row tile and a ragged one
     (9600, 32, 1024, 256, 1.0, 29),    # capacity 300: second matmul on 256-row tiles, combine fused
+    (8192, 256, 256, 256, 1.0, 30),    # capacity 32 with more tiles than CUs: 64-row tiles
 ])
 def test_bf16_ragged_shapes(B, T, N, d, F, c, seed):
     spec = S.Spec(f"bf16-{T}-{N}", T=T, d=d, F=F, N=N, c=c, seed=seed)
