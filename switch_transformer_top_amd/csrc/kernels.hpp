@@ -25,7 +25,7 @@ struct Profiler {
   bool on = false;
   int max_calls = 0;
   int calls = 0;                    // calls recorded so far
-  int n = 0;                        // stages opened in the current call
+  int n = 0;                        // stages of the call being (or last) recorded
   bool active = false;              // the current call is being recorded
   hipEvent_t* ev = nullptr;         // max_calls * kMax * 2: start and stop per stage
   const char* names[kMax];
@@ -45,7 +45,7 @@ inline void prof_begin(Profiler* p) {
   g_stage = nullptr;
   if (!p || !p->on) return;
   p->active = p->calls < p->max_calls;
-  p->n = 0;
+  if (p->active) p->n = 0;  // calls past the recorded ones keep the recorded stage count
 }
 inline void prof_mark(Profiler* p, hipStream_t s, const char* name) {
   if (!p || !p->on || !p->active || p->n >= Profiler::kMax) return;

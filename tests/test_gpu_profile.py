@@ -1,0 +1,88 @@
+"""GPU tests of the per-stage timing hooks (switch_profile_enable / switch_profile_read):
+stage names in launch order with positive times taken from the kernel dispatches,
+the same results with and without recording, stages that launch nothing, and
+the recording state released when it is turned off or the layer is destroyed."""
+import numpy as np
+import pytest
+
+import synthetic as S
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from switch_transformer_top_amd import binding
+    return binding
+
+
+KEYS = ("out", "expert_idx", "gate", "position", "drop_mask", "load", "aux_loss")
+
+
+def _layer(B, spec):
+    host = S.host_inputs(spec)
+    layer = B.SwitchLayer.from_host(spec, host)
+    x = B.to_device(host["x"], layer.device)
+    return layer, x
+
+
+def _outputs(B, bufs):
+    return {k: B.from_device(bufs[k]) for k in KEYS}
+
+
+def test_stage_times_and_same_results(B):
+    spec = S.Spec("prof", T=2100, d=256, F=768, N=4, c=1.0, seed=41)
+    layer, x = _layer(B, spec)
+    print(f"[case] profile {spec.name}", flush=True)
+    plain = layer.alloc(spec.T)
+    layer.forward(x, spec.T, plain)
+    torch.cuda.synchronize()
+    ref = _outputs(B, plain)
+
+    B.switch_profile_enable(layer.handle, 3)
+    for _ in range(5):                       # the last two are not recorded
+        bufs = layer.alloc(spec.T)
+        layer.forward(x, spec.T, bufs)
+    stages = B.switch_profile_read(layer.handle)
+    torch.cuda.synchronize()
+    got = _outputs(B, bufs)
+    for k in KEYS:
+        assert np.array_equal(got[k], ref[k]), k
+    names = [n for n, _ in stages]
+    assert names == ["router", "assign", "gemm1_relu", "gemm2_combine"], names
+    for n, ms in stages:
+        assert 0.0 < ms < 50.0, (n, ms)
+    B.switch_profile_enable(layer.handle, 0)
+    assert B.lib.switch_profile_read(layer.handle, None, None, 4) == -1
+
+
+def test_stage_without_kernels_and_release(B):
+    """Capacity 0: the matmul stages launch nothing, and their times read as 0;
+    recording is released by switch_profile_enable(0) and by destroying the layer."""
+    spec = S.Spec("prof-c0", T=300, d=128, F=256, N=4, c=0.0, seed=42)
+    layer, x = _layer(B, spec)
+    print(f"[case] profile {spec.name}", flush=True)
+    B.switch_profile_enable(layer.handle, 2)
+    bufs = layer.alloc(spec.T)
+    layer.forward(x, spec.T, bufs)
+    stages = dict(B.switch_profile_read(layer.handle))
+    assert "router" in stages and stages["router"] > 0.0
+    for n, ms in stages.items():
+        assert ms >= 0.0, (n, ms)
+    torch.cuda.synchronize()
+    assert np.array_equal(B.from_device(bufs["out"]), B.from_device(x))
+
+    # a layer destroyed while recording leaves nothing behind for the next one
+    B.switch_profile_enable(layer.handle, 2)
+    del layer, bufs
+    import gc
+    gc.collect()
+    other, x2 = _layer(B, spec.with_(c=1.0, seed=43))
+    b2 = other.alloc(spec.T)
+    other.forward(x2, spec.T, b2)
+    torch.cuda.synchronize()
+    assert B.switch_last_async_error() == B.SWITCH_OK
+    assert int(B.from_device(b2["drop_mask"]).size) == spec.T
