@@ -73,3 +73,40 @@ def test_no_writes_past_the_end(B, T, N, d, F, c, k, seed):
     assert np.array_equal(B.from_device(bufs["expert_idx"]), ref["expert_idx"])
     assert np.array_equal(B.from_device(bufs["position"]), ref["position"])
     assert np.array_equal(B.from_device(bufs["drop_mask"]), ref["drop"])
+
+
+@pytest.mark.parametrize("T,N,d,F,c,k,seed", [
+    (4096, 8, 768, 3072, 1.25, 1, 121),     # Switch-Base: 256 x 256 and split-K products
+    (777, 5, 128, 384, 1.25, 1, 122),       # odd expert count, ragged K of the weight gradients
+    (600, 300, 128, 128, 1.0, 1, 123),      # N > 256: logits router, many small experts
+    (1000, 8, 256, 512, 1.0, 2, 124),       # top-2
+])
+def test_backward_no_writes_past_the_end(B, T, N, d, F, c, k, seed):
+    spec = S.Spec(f"guard-bwd-{T}-{N}-k{k}", T=T, d=d, F=F, N=N, c=c, seed=seed)
+    host = S.host_inputs(spec)
+    layer = B.SwitchLayer.from_host(spec, host, top_k=k)
+    print(f"[case] {spec.name}", flush=True)
+    x = B.to_device(host["x"], layer.device)
+    fwd = layer.alloc(T)
+    layer.forward(x, T, fwd)
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((T, d)).astype(np.float32)
+    G = B.to_device((g.view(np.uint32) >> 16).astype(np.uint16), layer.device)  # truncated to bf16
+    grads = layer.alloc_backward(T)
+    fills = {"grad_x": 0x3C3C, "grad_W_r": -1.25, "grad_b_r": -2.5, "grad_W_in": 0x3C3C,
+             "grad_W_out": 0x3C3C}
+    bigs = {}
+    for key, fill in fills.items():
+        bigs[key], grads[key] = _guarded(grads[key], fill)
+    ws_big = torch.full((grads["ws_bytes"] + GUARD,), 0x5A, dtype=torch.uint8,
+                        device=layer.device)
+    grads["ws"] = ws_big[:grads["ws_bytes"]]
+    for reuse in (False, True):
+        layer.backward(x, T, G, 1.0, fwd, grads, reuse_forward=reuse)
+        torch.cuda.synchronize()
+        for key, fill in fills.items():
+            tail = B.from_device(bigs[key][grads[key].numel():])
+            assert np.all(tail == np.asarray(fill).astype(tail.dtype)), \
+                f"{spec.name}: {key} written past its end"
+        assert np.all(B.from_device(ws_big[grads["ws_bytes"]:]) == 0x5A), \
+            f"{spec.name}: backward workspace written past its end"
