@@ -132,7 +132,10 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   int ej[kMaxTopK];
   bool kj[kMaxTopK];
   double dg[kMaxTopK];
-  const uint16_t* gt = G + t * d;
+  // dg_j = <G[t], Y[e_j, position]> in fp64 over 16-byte pieces (d is a
+  // multiple of 128, so rows are whole pieces); bf16 products are exact
+  const u32x4* gt = reinterpret_cast<const u32x4*>(G + t * d);
+  const int nv = d / 8;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     const int64_t a = t * topk + j;
@@ -140,10 +143,19 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
     kj[j] = j < topk && drop_mask[a] == 0;
     dg[j] = 0.0;
     if (kj[j]) {
-      const uint16_t* yt = Ybuf + ((int64_t)ej[j] * C + position[a]) * d;
-      for (int q = lane; q < d; q += kWave)
-        dg[j] += (double)bf16_bits_to_f32(gt[q]) * bf16_bits_to_f32(yt[q]);
-      dg[j] = wave_sum_f64(dg[j]);
+      const u32x4* yt =
+          reinterpret_cast<const u32x4*>(Ybuf + ((int64_t)ej[j] * C + position[a]) * d);
+      double acc = 0.0;
+      for (int q = lane; q < nv; q += kWave) {
+        const u32x4 gv = gt[q], yv = yt[q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc += (double)__uint_as_float(gv[i] << 16) * (double)__uint_as_float(yv[i] << 16);
+          acc += (double)__uint_as_float(gv[i] & 0xFFFF0000u) *
+                 (double)__uint_as_float(yv[i] & 0xFFFF0000u);
+        }
+      }
+      dg[j] = wave_sum_f64(acc);
     }
   }
   const float* ht = h + t * N;
