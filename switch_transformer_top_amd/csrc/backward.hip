@@ -185,58 +185,126 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   }
 }
 
-// dW_r[i, k] = sum_t dh[t, i] x[t, k] and db[i] = sum_t dh[t, i] (fp32).
-// Block (k tile, i tile, s): 64 experts x 64 columns over the tokens of slice
-// s (RW_SLICE consecutive tokens), 256 threads each 4 x 4 outputs, the slice
-// in steps of 32 tokens through LDS.  Each slice writes its partial sums to
-// part[s] ([N, d], and part_b[s] [N] from the k-tile-0 blocks);
-// router_wgrad_reduce adds the slices in slice order.  Fixed order throughout.
-constexpr int RW_SLICE = 256;
+// dW_r[i, k] = sum_t dh[t, i] x[t, k] and db[i] = sum_t dh[t, i] (fp32), for
+// more than 32 experts, on fp32 MFMA (v_mfma_f32_32x32x2_f32: every lane holds
+// one k of each operand, A[i][k] at lane i + 32 k and B[k][j] at lane j + 32 k,
+// so token-major tiles are read as stored).  Block (128-column tile, 128-expert
+// tile, token slice s): four waves of 64 experts x 64 columns (2 x 2 MFMA
+// tiles); the slice in steps of 32 tokens, dh [32][128] and x [32][128] (as
+// fp32) staged in two LDS buffers, the next step's loads in registers while the
+// current one is multiplied.  Each slice writes its partial sums to part[s]
+// ([N, d], and part_b[s] [N] from the column-tile-0 blocks, added in token
+// order); router_wgrad_reduce adds the slices in slice order.
+constexpr int RW_TOK = 32, RW_LD = 132;
 
-__global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restrict__ dh,
-                                                           const uint16_t* __restrict__ x,
-                                                           int64_t T, int N, int d,
-                                                           float* __restrict__ part,
-                                                           float* __restrict__ part_b) {
-  __shared__ float Ds[32][68];
-  __shared__ float Xs[32][68];
-  const int i0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
-  const int64_t ts = (int64_t)blockIdx.z * RW_SLICE;
-  const int64_t te = ts + RW_SLICE < T ? ts + RW_SLICE : T;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4] = {};
+__device__ __forceinline__ void rw_load(const float* __restrict__ dh,
+                                        const uint16_t* __restrict__ x, int64_t ts, int64_t te,
+                                        int N, int d, int i0, int k0, float (&dv)[16],
+                                        u32x4 (&xv)[2]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int idx = tid + 256 * u, r = idx >> 7, c = idx & 127;
+    const int64_t t = ts + r;
+    dv[u] = (t < te && i0 + c < N) ? dh[t * N + i0 + c] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = tid + 256 * u, r = idx >> 4, c = (idx & 15) * 8;
+    const int64_t t = ts + r;
+    xv[u] = t < te ? *reinterpret_cast<const u32x4*>(x + t * d + k0 + c) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ void rw_store(float (*Ds)[RW_LD], float (*Xs)[RW_LD],
+                                         const float (&dv)[16], const u32x4 (&xv)[2]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int idx = tid + 256 * u;
+    Ds[idx >> 7][idx & 127] = dv[u];
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = tid + 256 * u, r = idx >> 4, c = (idx & 15) * 8;
+    const u32x4 v = xv[u];
+    *reinterpret_cast<float4*>(&Xs[r][c]) =
+        make_float4(__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u),
+                    __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u));
+    *reinterpret_cast<float4*>(&Xs[r][c + 4]) =
+        make_float4(__uint_as_float(v[2] << 16), __uint_as_float(v[2] & 0xFFFF0000u),
+                    __uint_as_float(v[3] << 16), __uint_as_float(v[3] & 0xFFFF0000u));
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void router_wgrad_kernel(const float* __restrict__ dh,
+                                                              const uint16_t* __restrict__ x,
+                                                              int64_t T, int N, int d,
+                                                              int64_t slice,
+                                                              float* __restrict__ part,
+                                                              float* __restrict__ part_b) {
+  __shared__ __attribute__((aligned(16))) float Ds[2][RW_TOK][RW_LD];
+  __shared__ __attribute__((aligned(16))) float Xs[2][RW_TOK][RW_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1, col = lane & 31, kh = lane >> 5;
+  const int k0 = blockIdx.x * 128, i0 = blockIdx.y * 128;
+  const int64_t ts = (int64_t)blockIdx.z * slice;
+  const int64_t te = ts + slice < T ? ts + slice : T;
+  const int steps = (int)((te - ts + RW_TOK - 1) / RW_TOK);
+  const bool bias = blockIdx.x == 0 && tid < 128;
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.f;
   float bacc = 0.f;
-  for (int64_t t0 = ts; t0 < te; t0 += 32) {
-    for (int idx = threadIdx.x; idx < 32 * 64; idx += 256) {
-      const int r = idx >> 6, c = idx & 63;
-      const int64_t t = t0 + r;
-      Ds[r][c] = (t < te && i0 + c < N) ? dh[t * N + i0 + c] : 0.f;
-      Xs[r][c] = (t < te && k0 + c < d) ? bf16_bits_to_f32(x[t * d + k0 + c]) : 0.f;
-    }
-    __syncthreads();
+
+  float dv[16];
+  u32x4 xv[2];
+  rw_load(dh, x, ts, te, N, d, i0, k0, dv, xv);
+  rw_store(Ds[0], Xs[0], dv, xv);
+  __syncthreads();
+  for (int st = 0; st < steps; ++st) {
+    const int b = st & 1;
+    if (st + 1 < steps) rw_load(dh, x, ts + (int64_t)(st + 1) * RW_TOK, te, N, d, i0, k0, dv, xv);
 #pragma unroll 4
-    for (int r = 0; r < 32; ++r) {
-      float a[4], b[4];
+    for (int kk = 0; kk < RW_TOK / 2; ++kk) {
+      const int r = 2 * kk + kh;
+      float a[2], bv[2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { a[q] = Ds[r][ty + 16 * q]; b[q] = Xs[r][tx + 16 * q]; }
+      for (int m = 0; m < 2; ++m) a[m] = Ds[b][r][64 * wm + 32 * m + col];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int n = 0; n < 2; ++n) bv[n] = Xs[b][r][64 * wn + 32 * n + col];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) acc[q][w] = fmaf(a[q], b[w], acc[q][w]);
-      if (blockIdx.x == 0 && threadIdx.x < 64) bacc += Ds[r][threadIdx.x];
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[m], bv[n], acc[m][n], 0, 0, 0);
     }
+    if (bias) {
+#pragma unroll 8
+      for (int r = 0; r < RW_TOK; ++r) bacc += Ds[b][r][tid];
+    }
+    if (st + 1 < steps) rw_store(Ds[b ^ 1], Xs[b ^ 1], dv, xv);
     __syncthreads();
   }
+  // acc[m][n][v]: expert i0 + 64 wm + 32 m + 8 (v / 4) + 4 kh + v % 4,
+  // column k0 + 64 wn + 32 n + col
   float* ps = part + (int64_t)blockIdx.z * N * d;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int i = i0 + ty + 16 * q, k = k0 + tx + 16 * w;
-      if (i < N && k < d) ps[(int64_t)i * d + k] = acc[q][w];
+    for (int v = 0; v < 16; ++v) {
+      const int i = i0 + 64 * wm + 32 * m + 8 * (v >> 2) + 4 * kh + (v & 3);
+      if (i < N) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) ps[(int64_t)i * d + k0 + 64 * wn + 32 * n + col] = acc[m][n][v];
+      }
     }
-  if (blockIdx.x == 0 && threadIdx.x < 64 && i0 + threadIdx.x < N)
-    part_b[(int64_t)blockIdx.z * N + i0 + threadIdx.x] = bacc;
+  if (bias && i0 + tid < N) part_b[(int64_t)blockIdx.z * N + i0 + tid] = bacc;
 }
 
 // Few experts (N <= 32): one wave per (256-column block, token slice); lane l
@@ -345,9 +413,50 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restri
 }
 
 // dx_t = G_t + sum over kept choices j of dX[e_tj, p_tj] + sum_i dh[t, i] W_r[i, :],
-// fp32 then one rounding to bf16.  Block: 64 tokens x 64 columns; the router part is a
-// small matmul with K = N, in steps of 32 experts through LDS; thread (ty, tx)
-// owns tokens ty + 16 q and the four columns 4 tx .. 4 tx + 3.
+// fp32 then one rounding to bf16.  Block: 64 tokens x 128 columns.  The router
+// part is D[k][t] = sum_i W_r[i][k] dh[t][i] on fp32 MFMA
+// (v_mfma_f32_32x32x2_f32, one i per lane in each operand, so W_r's rows and
+// dh's rows are read as stored), in steps of 32 experts staged in two LDS
+// buffers (experts past N read as 0).  Wave w owns columns 64 (w & 1) .. +64
+// (two 32-column MFMA tiles) and tokens 32 (w >> 1) .. +32; lane l holds token
+// l % 32 and, per tile, columns 8 b + 4 (l / 32) .. +3 for b = 0..3, whose G and
+// dX rows it loads before the products start.
+constexpr int GX_TOK = 64, GX_EXP = 32, GX_WLD = 132, GX_DLD = GX_EXP + 1;
+
+__device__ __forceinline__ void gx_load(const float* __restrict__ dh,
+                                        const float* __restrict__ W_r, int64_t T, int N, int d,
+                                        int64_t t0, int k0, int i0, float4 (&wv)[4],
+                                        float (&dv)[8]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = tid + 256 * u, r = idx >> 5, c = (idx & 31) * 4;
+    wv[u] = i0 + r < N ? *reinterpret_cast<const float4*>(W_r + (int64_t)(i0 + r) * d + k0 + c)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int idx = tid + 256 * u, r = idx >> 5, c = idx & 31;
+    const int64_t t = t0 + r;
+    dv[u] = (t < T && i0 + c < N) ? dh[t * N + i0 + c] : 0.f;
+  }
+}
+
+__device__ __forceinline__ void gx_store(float (*Ws)[GX_WLD], float (*Ds)[GX_DLD],
+                                         const float4 (&wv)[4], const float (&dv)[8]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = tid + 256 * u;
+    *reinterpret_cast<float4*>(&Ws[idx >> 5][(idx & 31) * 4]) = wv[u];
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int idx = tid + 256 * u;
+    Ds[idx >> 5][idx & 31] = dv[u];
+  }
+}
+
 __global__ __launch_bounds__(256) void grad_x_kernel(const uint16_t* __restrict__ G, int64_t T,
                                                      int d, int topk,
                                                      const int32_t* __restrict__ expert_idx,
@@ -357,60 +466,93 @@ __global__ __launch_bounds__(256) void grad_x_kernel(const uint16_t* __restrict_
                                                      const float* __restrict__ dh,
                                                      const float* __restrict__ W_r, int N,
                                                      uint16_t* __restrict__ dx) {
-  __shared__ float Ds[64][33];
-  __shared__ float Ws[32][68];
-  const int64_t t0 = (int64_t)blockIdx.y * 64;
-  const int k0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4] = {};
-  for (int i0 = 0; i0 < N; i0 += 32) {
-    for (int idx = threadIdx.x; idx < 64 * 32; idx += 256) {
-      const int r = idx >> 5, c = idx & 31;
-      const int64_t t = t0 + r;
-      Ds[r][c] = (t < T && i0 + c < N) ? dh[t * N + i0 + c] : 0.f;
-    }
-    for (int idx = threadIdx.x; idx < 32 * 64; idx += 256) {
-      const int r = idx >> 6, c = idx & 63;
-      Ws[r][c] = (i0 + r < N && k0 + c < d) ? W_r[(int64_t)(i0 + r) * d + k0 + c] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
-      float w[4];
+  __shared__ __attribute__((aligned(16))) float Ws[2][GX_EXP][GX_WLD];
+  __shared__ float Ds[2][GX_TOK][GX_DLD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1, col = lane & 31, kh = lane >> 5;
+  const int64_t t0 = (int64_t)blockIdx.y * GX_TOK;
+  const int k0 = blockIdx.x * 128;
+  const int64_t t = t0 + 32 * wn + col;
+  const bool tv = t < T;
+  // the lane's columns: kc(m, b) = k0 + 64 wm + 32 m + 8 b + 4 kh .. +3
+  const int kb = k0 + 64 * wm + 4 * kh;
+
+  // epilogue inputs first: G and the kept choices' dX rows of the lane's token
+  uint2 gin[2][4];
+  uint2 xin[kMaxTopK][2][4];
+  bool kept[kMaxTopK];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) w[c] = Ws[i][4 * tx + c];
+  for (int j = 0; j < kMaxTopK; ++j) kept[j] = false;
+  if (tv) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a = Ds[ty + 16 * q][i];
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[q][c] = fmaf(a, w[c], acc[q][c]);
-      }
-    }
-    __syncthreads();
-  }
-  const int k = k0 + 4 * tx;
-  if (k >= d) return;
+      for (int b = 0; b < 4; ++b)
+        gin[m][b] = *reinterpret_cast<const uint2*>(G + t * d + kb + 32 * m + 8 * b);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t t = t0 + ty + 16 * q;
-    if (t >= T) continue;
-    const uint2 gv = *reinterpret_cast<const uint2*>(G + t * d + k);
-    float v[4] = {__uint_as_float(gv.x << 16), __uint_as_float(gv.x & 0xFFFF0000u),
-                  __uint_as_float(gv.y << 16), __uint_as_float(gv.y & 0xFFFF0000u)};
-    for (int j = 0; j < topk; ++j) {  // the kept choices' expert parts, in choice order
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= topk) break;
       const int64_t a = t * topk + j;
-      if (drop_mask[a]) continue;
-      const uint2 xv = *reinterpret_cast<const uint2*>(
-          dXe + ((int64_t)expert_idx[a] * C + position[a]) * d + k);
-      v[0] += __uint_as_float(xv.x << 16);
-      v[1] += __uint_as_float(xv.x & 0xFFFF0000u);
-      v[2] += __uint_as_float(xv.y << 16);
-      v[3] += __uint_as_float(xv.y & 0xFFFF0000u);
+      kept[j] = drop_mask[a] == 0;
+      if (!kept[j]) continue;
+      const uint16_t* xr = dXe + ((int64_t)expert_idx[a] * C + position[a]) * d + kb;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          xin[j][m][b] = *reinterpret_cast<const uint2*>(xr + 32 * m + 8 * b);
     }
-    const uint2 o = make_uint2(f32x2_to_bf16x2_bits(v[0] + acc[q][0], v[1] + acc[q][1]),
-                               f32x2_to_bf16x2_bits(v[2] + acc[q][2], v[3] + acc[q][3]));
-    *reinterpret_cast<uint2*>(dx + t * d + k) = o;
   }
+
+  floatx16 acc[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[m][v] = 0.f;
+  const int steps = (N + GX_EXP - 1) / GX_EXP;
+  float4 wv[4];
+  float dv[8];
+  gx_load(dh, W_r, T, N, d, t0, k0, 0, wv, dv);
+  gx_store(Ws[0], Ds[0], wv, dv);
+  __syncthreads();
+  for (int st = 0; st < steps; ++st) {
+    const int b = st & 1, i0 = st * GX_EXP;
+    if (st + 1 < steps) gx_load(dh, W_r, T, N, d, t0, k0, i0 + GX_EXP, wv, dv);
+    const int left = N - i0 < GX_EXP ? N - i0 : GX_EXP;
+    const int npair = (left + 1) >> 1;  // an odd last expert pairs with a zero row
+    for (int kk = 0; kk < npair; ++kk) {
+      const int r = 2 * kk + kh;
+      const float bv = Ds[b][32 * wn + col][r];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ws[b][r][64 * wm + 32 * m + col], bv,
+                                                      acc[m], 0, 0, 0);
+    }
+    if (st + 1 < steps) gx_store(Ws[b ^ 1], Ds[b ^ 1], wv, dv);
+    __syncthreads();
+  }
+  if (!tv) return;
+  // acc[m][4 b + q]: column kb + 32 m + 8 b + q of token t
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint2 gv = gin[m][b];
+      float v[4] = {__uint_as_float(gv.x << 16), __uint_as_float(gv.x & 0xFFFF0000u),
+                    __uint_as_float(gv.y << 16), __uint_as_float(gv.y & 0xFFFF0000u)};
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {  // the kept choices' expert parts, in choice order
+        if (!kept[j]) continue;
+        const uint2 xv = xin[j][m][b];
+        v[0] += __uint_as_float(xv.x << 16);
+        v[1] += __uint_as_float(xv.x & 0xFFFF0000u);
+        v[2] += __uint_as_float(xv.y << 16);
+        v[3] += __uint_as_float(xv.y & 0xFFFF0000u);
+      }
+      const uint2 o = make_uint2(f32x2_to_bf16x2_bits(v[0] + acc[m][4 * b], v[1] + acc[m][4 * b + 1]),
+                                 f32x2_to_bf16x2_bits(v[2] + acc[m][4 * b + 2], v[3] + acc[m][4 * b + 3]));
+      *reinterpret_cast<uint2*>(dx + t * d + kb + 32 * m + 8 * b) = o;
+    }
 }
 
 // Zero fill (16-byte stores; bytes a multiple of 16).
@@ -473,15 +615,26 @@ static int64_t small_slice(int64_t T) {
   return sl < RS_TOK ? RS_TOK : sl;
 }
 
-int64_t router_wgrad_slices(int64_t T, int N) {
+// Tokens per slice of the MFMA kernel: about 512 blocks over the
+// (128-column, 128-expert) tiles, slices of whole 32-token steps.
+static int64_t mfma_slice(int64_t T, int N, int d) {
+  const int64_t tiles = (int64_t)((d + 127) / 128) * ((N + 127) / 128);
+  const int64_t most = (T + RW_TOK - 1) / RW_TOK;
+  int64_t want = (512 + tiles - 1) / tiles;
+  want = want < most ? want : most;
+  const int64_t sl = (T + want - 1) / want;
+  return (sl + RW_TOK - 1) / RW_TOK * RW_TOK;
+}
+
+int64_t router_wgrad_slices(int64_t T, int N, int d) {
   if (T <= 0) return 0;
-  if (N <= 32) return (T + small_slice(T) - 1) / small_slice(T);
-  return (T + RW_SLICE - 1) / RW_SLICE;
+  const int64_t sl = N <= 32 ? small_slice(T) : mfma_slice(T, N, d);
+  return (T + sl - 1) / sl;
 }
 
 void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d, float* part,
                          float* part_b, float* dW_r, float* db, hipStream_t s) {
-  const int64_t slices = router_wgrad_slices(T, N);
+  const int64_t slices = router_wgrad_slices(T, N, d);
   if (slices > 0 && N <= 32) {
     const dim3 grid((unsigned)((d + 255) / 256), (unsigned)slices);
     const int64_t sl = small_slice(T);
@@ -495,9 +648,10 @@ void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d
       launch_k(router_wgrad_small_kernel<32>, grid, dim3(64), 0, s, dh,
                          (const uint16_t*)x, T, N, d, sl, part, part_b);
   } else if (slices > 0) {
-    const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)slices);
+    // d is a multiple of 128 (bf16 layers): whole column tiles
+    const dim3 grid((unsigned)(d / 128), (unsigned)((N + 127) / 128), (unsigned)slices);
     launch_k(router_wgrad_kernel, grid, dim3(256), 0, s, dh, (const uint16_t*)x, T, N,
-                       d, part, part_b);
+                       d, mfma_slice(T, N, d), part, part_b);
   }
   const int64_t n = (int64_t)N * d + N;
   launch_k(router_wgrad_reduce, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, part,
@@ -508,7 +662,8 @@ void launch_grad_x(const void* G, int64_t T, int d, int k, const int32_t* expert
                    const int32_t* position, const uint8_t* drop_mask, int64_t C, const void* dXe,
                    const float* dh, const float* W_r, int N, void* dx, hipStream_t s) {
   if (T == 0) return;
-  const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((T + 63) / 64));
+  // d is a multiple of 128 (bf16 layers): whole column tiles
+  const dim3 grid((unsigned)(d / 128), (unsigned)((T + GX_TOK - 1) / GX_TOK));
   launch_k(grad_x_kernel, grid, dim3(256), 0, s, (const uint16_t*)G, T, d, k,
                      expert_idx, position, drop_mask, C, (const uint16_t*)dXe, dh, W_r, N,
                      (uint16_t*)dx);

@@ -190,8 +190,8 @@ void launch_router_bwd(const float* h, int64_t T, int N, int d, int k, const voi
                        const void* Ybuf, int64_t C, const int32_t* expert_idx,
                        const int32_t* position, const uint8_t* drop_mask, const int32_t* load,
                        float loss_scale, float* dh, hipStream_t s);
-// part [slices, N, d] and part_b [slices, N] fp32 scratch, slices = router_wgrad_slices(T, N)
-int64_t router_wgrad_slices(int64_t T, int N);
+// part [slices, N, d] and part_b [slices, N] fp32 scratch, slices = router_wgrad_slices(T, N, d)
+int64_t router_wgrad_slices(int64_t T, int N, int d);
 void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d, float* part,
                          float* part_b, float* dW_r, float* db, hipStream_t s);
 void launch_grad_x(const void* G, int64_t T, int d, int k, const int32_t* expert_idx,

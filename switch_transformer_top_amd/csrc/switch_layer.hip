@@ -342,7 +342,7 @@ BwdLayout bwd_layout_of(const switch_layer* L, int64_t T) {
   lo.dxe = take(2 * N * Cb * d);
   lo.xT = take(2 * N * d * Cbp);
   lo.dh = take(4 * (size_t)T * N);
-  const size_t slices = (size_t)swl::router_wgrad_slices(T, (int)N);
+  const size_t slices = (size_t)swl::router_wgrad_slices(T, (int)N, (int)d);
   lo.wpart = take(4 * slices * N * d);
   lo.bpart = take(4 * slices * N);
   lo.total = off;
