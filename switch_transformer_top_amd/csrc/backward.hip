@@ -418,9 +418,9 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restri
 // (v_mfma_f32_32x32x2_f32, one i per lane in each operand, so W_r's rows and
 // dh's rows are read as stored), in steps of 32 experts staged in two LDS
 // buffers (experts past N read as 0).  Wave w owns columns 64 (w & 1) .. +64
-// (two 32-column MFMA tiles) and tokens 32 (w >> 1) .. +32; lane l holds token
-// l % 32 and, per tile, columns 8 b + 4 (l / 32) .. +3 for b = 0..3, whose G and
-// dX rows it loads before the products start.
+// (two 32-column MFMA tiles) and tokens 32 (w >> 1) .. +32.  The sums go
+// through LDS as a [64][128] fp32 tile, and G, the dX rows and dx move in
+// 16-byte row pieces (thread: pieces tid + 256 u, token tid / 16 + 16 u).
 constexpr int GX_TOK = 64, GX_EXP = 32, GX_WLD = 132, GX_DLD = GX_EXP + 1;
 
 __device__ __forceinline__ void gx_load(const float* __restrict__ dh,
@@ -472,37 +472,7 @@ __global__ __launch_bounds__(256) void grad_x_kernel(const uint16_t* __restrict_
   const int wm = wave & 1, wn = wave >> 1, col = lane & 31, kh = lane >> 5;
   const int64_t t0 = (int64_t)blockIdx.y * GX_TOK;
   const int k0 = blockIdx.x * 128;
-  const int64_t t = t0 + 32 * wn + col;
-  const bool tv = t < T;
-  // the lane's columns: kc(m, b) = k0 + 64 wm + 32 m + 8 b + 4 kh .. +3
-  const int kb = k0 + 64 * wm + 4 * kh;
-
-  // epilogue inputs first: G and the kept choices' dX rows of the lane's token
-  uint2 gin[2][4];
-  uint2 xin[kMaxTopK][2][4];
-  bool kept[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) kept[j] = false;
-  if (tv) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        gin[m][b] = *reinterpret_cast<const uint2*>(G + t * d + kb + 32 * m + 8 * b);
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j >= topk) break;
-      const int64_t a = t * topk + j;
-      kept[j] = drop_mask[a] == 0;
-      if (!kept[j]) continue;
-      const uint16_t* xr = dXe + ((int64_t)expert_idx[a] * C + position[a]) * d + kb;
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          xin[j][m][b] = *reinterpret_cast<const uint2*>(xr + 32 * m + 8 * b);
-    }
-  }
+  const int pc = k0 + 8 * (tid & 15);  // the thread's piece columns
 
   floatx16 acc[2];
 #pragma unroll
@@ -531,28 +501,69 @@ __global__ __launch_bounds__(256) void grad_x_kernel(const uint16_t* __restrict_
     if (st + 1 < steps) gx_store(Ws[b ^ 1], Ds[b ^ 1], wv, dv);
     __syncthreads();
   }
-  if (!tv) return;
-  // acc[m][4 b + q]: column kb + 32 m + 8 b + q of token t
+  // G and the kept choices' dX rows of the thread's pieces
+  u32x4 gin[4];
+  u32x4 xin[kMaxTopK][4];
+  bool kept[kMaxTopK][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t t = t0 + (tid >> 4) + 16 * u;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) kept[j][u] = false;
+    if (t >= T) continue;
+    gin[u] = *reinterpret_cast<const u32x4*>(G + t * d + pc);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= topk) break;
+      const int64_t a = t * topk + j;
+      kept[j][u] = drop_mask[a] == 0;
+      if (kept[j][u])
+        xin[j][u] = *reinterpret_cast<const u32x4*>(
+            dXe + ((int64_t)expert_idx[a] * C + position[a]) * d + pc);
+    }
+  }
+
+  // acc[m][4 b + q]: column 64 wm + 32 m + 8 b + 4 kh + q of token 32 wn + col; the
+  // [64][GX_WLD] fp32 tile takes the place of the W_r buffers
+  static_assert(GX_TOK * GX_WLD <= 2 * GX_EXP * GX_WLD, "the sum tile fits the W_r buffers");
+  float (*Ys)[GX_WLD] = reinterpret_cast<float (*)[GX_WLD]>(&Ws[0][0][0]);
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint2 gv = gin[m][b];
-      float v[4] = {__uint_as_float(gv.x << 16), __uint_as_float(gv.x & 0xFFFF0000u),
-                    __uint_as_float(gv.y << 16), __uint_as_float(gv.y & 0xFFFF0000u)};
+    for (int b = 0; b < 4; ++b)
+      *reinterpret_cast<float4*>(&Ys[32 * wn + col][64 * wm + 32 * m + 8 * b + 4 * kh]) =
+          make_float4(acc[m][4 * b], acc[m][4 * b + 1], acc[m][4 * b + 2], acc[m][4 * b + 3]);
+  __syncthreads();
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {  // the kept choices' expert parts, in choice order
-        if (!kept[j]) continue;
-        const uint2 xv = xin[j][m][b];
-        v[0] += __uint_as_float(xv.x << 16);
-        v[1] += __uint_as_float(xv.x & 0xFFFF0000u);
-        v[2] += __uint_as_float(xv.y << 16);
-        v[3] += __uint_as_float(xv.y & 0xFFFF0000u);
-      }
-      const uint2 o = make_uint2(f32x2_to_bf16x2_bits(v[0] + acc[m][4 * b], v[1] + acc[m][4 * b + 1]),
-                                 f32x2_to_bf16x2_bits(v[2] + acc[m][4 * b + 2], v[3] + acc[m][4 * b + 3]));
-      *reinterpret_cast<uint2*>(dx + t * d + kb + 32 * m + 8 * b) = o;
+  for (int u = 0; u < 4; ++u) {
+    const int r = (tid >> 4) + 16 * u;
+    const int64_t t = t0 + r;
+    if (t >= T) continue;
+    const u32x4 gv = gin[u];
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(gv[i] << 16);
+      v[2 * i + 1] = __uint_as_float(gv[i] & 0xFFFF0000u);
     }
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {  // the kept choices' expert parts, in choice order
+      if (!kept[j][u]) continue;
+      const u32x4 xv = xin[j][u];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] += __uint_as_float(xv[i] << 16);
+        v[2 * i + 1] += __uint_as_float(xv[i] & 0xFFFF0000u);
+      }
+    }
+    const float4 s0 = *reinterpret_cast<const float4*>(&Ys[r][8 * (tid & 15)]);
+    const float4 s1 = *reinterpret_cast<const float4*>(&Ys[r][8 * (tid & 15) + 4]);
+    const u32x4 o = {f32x2_to_bf16x2_bits(v[0] + s0.x, v[1] + s0.y),
+                     f32x2_to_bf16x2_bits(v[2] + s0.z, v[3] + s0.w),
+                     f32x2_to_bf16x2_bits(v[4] + s1.x, v[5] + s1.y),
+                     f32x2_to_bf16x2_bits(v[6] + s1.z, v[7] + s1.w)};
+    *reinterpret_cast<u32x4*>(dx + t * d + pc) = o;
+  }
 }
 
 // Zero fill (16-byte stores; bytes a multiple of 16).
