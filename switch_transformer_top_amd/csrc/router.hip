@@ -417,33 +417,41 @@ __global__ __launch_bounds__(256) void router_small_kernel(
                          rank_local);
 }
 
-// More experts (32 < N): a block owns 64 * ROWT tokens and NPAD experts
-// starting at e0 = blockIdx.y * NPAD; each wave takes 16 * ROWT of the tokens
-// and the whole K.  Every 32-wide K chunk of W_r is loaded once per block,
-// split into its three bf16 planes and stored in LDS (double buffered, rows of
-// 40 bf16), where all four waves read their B fragments; the next chunk is
-// loaded into registers while the current one is multiplied.
-// FUSED (N <= NPAD, one expert tile): routing statistics and the chunk
-// histogram / ranks follow; otherwise only the logits are written.
-template <int NPAD, int ROWT, bool FUSED>
-__global__ __launch_bounds__(256) void router_tok_kernel(
+// More experts (32 < N): a block of WAVES waves owns 16 * ROWT * WAVES tokens
+// and NPAD experts starting at e0 = blockIdx.y * NPAD; each wave takes
+// 16 * ROWT of the tokens and the whole K.  Every 32-wide K chunk of W_r is
+// loaded once per block, split into its three bf16 planes and stored in LDS
+// (double buffered, rows of 40 bf16), where all the waves read their B
+// fragments; the next chunk is loaded into registers while the current one is
+// multiplied.  Each block streams its NPAD rows of W_r once, so more tokens per
+// block mean less weight traffic.
+// FUSED (N <= NPAD, one expert tile, four waves): routing statistics and the
+// chunk histogram / ranks follow; otherwise only the logits are written, the
+// tile staged through LDS a group of four waves at a time.
+template <int NPAD, int ROWT, bool FUSED, int WAVES = 4>
+__global__ __launch_bounds__(64 * WAVES) void router_tok_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ W_r, const float* __restrict__ b_r,
     int64_t T, int d, int N, int k, float* __restrict__ logits, int32_t* __restrict__ expert_idx,
     float* __restrict__ gate, float* __restrict__ P_part, int32_t* __restrict__ hist,
     int32_t* __restrict__ rank_local) {
-  constexpr int NJ = NPAD / 16, BT = 64 * ROWT, WLD = 40, LD = NPAD + 4;
-  constexpr int WL = NPAD * 8 / 256;  // float4 loads per thread per K chunk
-  static_assert(WL >= 1, "at least one expert row per 32 threads");
-  // the weight planes during the K loop, then the block's logit tile
-  constexpr int PLANES = 2 * 3 * NPAD * WLD * 2, TILE = BT * LD * 4;
+  constexpr int NTHR = 64 * WAVES, NJ = NPAD / 16, BT = 16 * ROWT * WAVES, WLD = 40,
+                LD = NPAD + 4;
+  constexpr int WL = NPAD * 8 / NTHR;  // float4 loads per thread per K chunk
+  constexpr int WROWS = NTHR / 8;      // W_r rows per loader pass
+  static_assert(WL >= 1 && WL * WROWS == NPAD, "whole loader passes over the expert rows");
+  static_assert(!FUSED || WAVES == 4, "the statistics take a four-wave block");
+  static_assert(WAVES % 4 == 0, "groups of four waves");
+  constexpr int GROUPS = WAVES / 4;    // the logit tile goes through LDS a group at a time
+  // the weight planes during the K loop, then a group's logit tile
+  constexpr int PLANES = 2 * 3 * NPAD * WLD * 2, TILE = (BT / GROUPS) * LD * 4;
   __shared__ __attribute__((aligned(16))) unsigned char raw[PLANES > TILE ? PLANES : TILE];
   typedef uint16_t PlaneArr[3][NPAD * WLD];
   PlaneArr* wpl = reinterpret_cast<PlaneArr*>(raw);
   float* st = reinterpret_cast<float*>(raw);
   __shared__ int32_t s_idx[FUSED ? BT * kMaxTopK : 1];
   __shared__ int32_t cnt[FUSED ? NPAD : 1];
-  __shared__ float s_m[BT];
-  __shared__ double s_inv[BT];
+  __shared__ float s_m[FUSED ? BT : 1];
+  __shared__ double s_inv[FUSED ? BT : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * BT;
@@ -465,13 +473,13 @@ __global__ __launch_bounds__(256) void router_tok_kernel(
     t = t < T ? t : T - 1;  // rows past T: any valid row, never stored
     xrow[r] = x + t * d + fk;
   }
-  // W loader: thread covers expert row (tid / 8) + 32 q and k offset 4 (tid % 8)
+  // W loader: thread covers expert row (tid / 8) + WROWS q and k offset 4 (tid % 8)
   const int wr = tid >> 3, wk = (tid & 7) * 4;
   const float* wsrc[WL];
   bool wok[WL];
 #pragma unroll
   for (int q = 0; q < WL; ++q) {
-    const int e = e0 + wr + 32 * q;
+    const int e = e0 + wr + WROWS * q;
     wok[q] = e < N;
     wsrc[q] = W_r + (int64_t)(e < N ? e : 0) * d + wk;
   }
@@ -510,7 +518,7 @@ __global__ __launch_bounds__(256) void router_tok_kernel(
         mv[h] = mb[0] | ((uint32_t)mb[1] << 16);
         lv[h] = lb[0] | ((uint32_t)lb[1] << 16);
       }
-      const int off = (wr + 32 * q) * WLD + wk;
+      const int off = (wr + WROWS * q) * WLD + wk;
       *reinterpret_cast<uint2*>(&wpl[buf][0][off]) = make_uint2(hv[0], hv[1]);
       *reinterpret_cast<uint2*>(&wpl[buf][1][off]) = make_uint2(mv[0], mv[1]);
       *reinterpret_cast<uint2*>(&wpl[buf][2][off]) = make_uint2(lv[0], lv[1]);
@@ -550,32 +558,41 @@ __global__ __launch_bounds__(256) void router_tok_kernel(
     }
   }
 
-  // logit tile (+ bias, padded experts at -inf) into LDS over the weight planes
-  __syncthreads();
-  {
-    const int g = lane >> 4;
+  // logit tile (+ bias, padded experts at -inf) into LDS over the weight planes,
+  // one group of four waves (64 ROWT tokens) at a time
+  constexpr int GT = BT / GROUPS;
+  const int grp = wave >> 2;
+#pragma unroll 1
+  for (int gi = 0; gi < GROUPS; ++gi) {
+    __syncthreads();
+    if (grp == gi) {
+      const int g = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = e0 + 16 * j + fr;
-      const float bias = (e < N && b_r) ? b_r[e] : 0.f;
+      for (int j = 0; j < NJ; ++j) {
+        const int e = e0 + 16 * j + fr;
+        const float bias = (e < N && b_r) ? b_r[e] : 0.f;
 #pragma unroll
-      for (int r = 0; r < ROWT; ++r)
+        for (int r = 0; r < ROWT; ++r)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          st[(wave * 16 * ROWT + 16 * r + 4 * g + i) * LD + 16 * j + fr] =
-              e < N ? acc[r][j][i] + bias : -__builtin_huge_valf();
+          for (int i = 0; i < 4; ++i)
+            st[((wave & 3) * 16 * ROWT + 16 * r + 4 * g + i) * LD + 16 * j + fr] =
+                e < N ? acc[r][j][i] + bias : -__builtin_huge_valf();
+      }
+    }
+    __syncthreads();
+    if (!FUSED) {
+      // logits only, in full rows of the group's tokens; statistics come from
+      // route_rows_kernel
+      const int ne = (N - e0) < NPAD ? (N - e0) : NPAD;
+      const int r0 = gi * GT;
+      const int nr = n_tok - r0 < GT ? n_tok - r0 : GT;
+      for (int idx = tid; idx < nr * ne; idx += NTHR) {
+        const int r = idx / ne, e = idx - r * ne;
+        logits[(t0 + r0 + r) * N + e0 + e] = st[r * LD + e];
+      }
     }
   }
-  __syncthreads();
-  if (!FUSED) {
-    // logits only, in full rows of the tile; statistics come from route_rows_kernel
-    const int ne = (N - e0) < NPAD ? (N - e0) : NPAD;
-    for (int idx = tid; idx < n_tok * ne; idx += 256) {
-      const int r = idx / ne, e = idx - r * ne;
-      logits[(t0 + r) * N + e0 + e] = st[r * LD + e];
-    }
-    return;
-  }
+  if (!FUSED) return;
   block_stats<BT, NPAD, LD>(st, N, k, t0, n_tok, logits, expert_idx, gate,
                             P_part + (int64_t)blockIdx.x * N, s_idx, s_m, s_inv);
   chunk_hist_rank(s_idx, n_tok * k, t0 * k, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
@@ -772,6 +789,7 @@ __global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __rest
 // ------------------------------------------------------------------ launchers
 
 constexpr int kTokRowt = 2;                 // router_tok_kernel: 128 tokens per block
+constexpr int kLogitWaves = 8;              // logits only: 256 tokens per block
 
 bool router_fused_ok(bool x_bf16, int N) { return x_bf16 && N <= 256; }
 
@@ -785,9 +803,9 @@ void launch_router_logits(const void* x, bool x_bf16, const float* W_r, const fl
   if (T == 0) return;
   if (x_bf16) {
     // MFMA logits in expert tiles of 256, statistics by route_rows_kernel
-    constexpr int BT = 64 * kTokRowt;
+    constexpr int BT = 16 * kTokRowt * kLogitWaves;
     const dim3 grid((unsigned)((T + BT - 1) / BT), (unsigned)((N + 255) / 256));
-    launch_k((router_tok_kernel<256, kTokRowt, false>), grid, dim3(256), 0, s,
+    launch_k((router_tok_kernel<256, kTokRowt, false, kLogitWaves>), grid, dim3(64 * kLogitWaves), 0, s,
                        (const uint16_t*)x, W_r, b_r, T, d, N, 1, h, nullptr, nullptr, nullptr,
                        nullptr, nullptr);
     return;
