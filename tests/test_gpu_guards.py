@@ -42,6 +42,7 @@ def _guarded(t, fill):
     (8192, 256, 256, 256, 1.0, 1, 114),     # two-launch assignment, 64-row tiles
     (12000, 128, 128, 512, 1.25, 1, 115),   # 128-row tiles with more tiles than CUs
     (600, 300, 128, 128, 1.0, 1, 116),      # logits router (N > 256)
+    (1000, 520, 128, 256, 1.0, 1, 118),     # logits router, partial expert tile and token group
     (4096, 8, 768, 3072, 1.25, 2, 117),     # top-2: wide GEMM1, 128-row GEMM2, the combine pass
 ])
 def test_no_writes_past_the_end(B, T, N, d, F, c, k, seed):

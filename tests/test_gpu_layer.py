@@ -70,6 +70,8 @@ def test_tiny_fp32_config(B):
     (1500, 4, 128, 512, 1.0, 28),      # capacity 375: one full 256-row tile and a ragged one
     (9600, 32, 1024, 256, 1.0, 29),    # capacity 300: second matmul on 256-row tiles, combine fused
     (8192, 256, 256, 256, 1.0, 30),    # capacity 32 with more tiles than CUs: 64-row tiles
+    (1000, 520, 128, 256, 1.0, 31),    # logits router: three expert tiles (the last of 8), a
+                                       # 256-token block whose second 128-token group is partial
 ])
 def test_bf16_ragged_shapes(B, T, N, d, F, c, seed):
     spec = S.Spec(f"bf16-{T}-{N}", T=T, d=d, F=F, N=N, c=c, seed=seed)
