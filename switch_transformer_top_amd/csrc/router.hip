@@ -789,7 +789,7 @@ __global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __rest
 // ------------------------------------------------------------------ launchers
 
 constexpr int kTokRowt = 2;                 // router_tok_kernel: 128 tokens per block
-constexpr int kLogitWaves = 8;              // logits only: 256 tokens per block
+constexpr int kLogitRowt = 2, kLogitWaves = 8;  // logits only: 256 tokens per block
 
 bool router_fused_ok(bool x_bf16, int N) { return x_bf16 && N <= 256; }
 
@@ -803,9 +803,10 @@ void launch_router_logits(const void* x, bool x_bf16, const float* W_r, const fl
   if (T == 0) return;
   if (x_bf16) {
     // MFMA logits in expert tiles of 256, statistics by route_rows_kernel
-    constexpr int BT = 16 * kTokRowt * kLogitWaves;
+    constexpr int BT = 16 * kLogitRowt * kLogitWaves;
     const dim3 grid((unsigned)((T + BT - 1) / BT), (unsigned)((N + 255) / 256));
-    launch_k((router_tok_kernel<256, kTokRowt, false, kLogitWaves>), grid, dim3(64 * kLogitWaves), 0, s,
+    launch_k((router_tok_kernel<256, kLogitRowt, false, kLogitWaves>), grid,
+             dim3(64 * kLogitWaves), 0, s,
                        (const uint16_t*)x, W_r, b_r, T, d, N, 1, h, nullptr, nullptr, nullptr,
                        nullptr, nullptr);
     return;
