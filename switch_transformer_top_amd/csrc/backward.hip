@@ -185,55 +185,79 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   }
 }
 
-// dW_r[i, k] = sum_t dh[t, i] x[t, k] and db[i] = sum_t dh[t, i] (fp32), for
-// more than 32 experts, on fp32 MFMA (v_mfma_f32_32x32x2_f32: every lane holds
-// one k of each operand, A[i][k] at lane i + 32 k and B[k][j] at lane j + 32 k,
-// so token-major tiles are read as stored).  Block (128-column tile, 128-expert
-// tile, token slice s): four waves of 64 experts x 64 columns (2 x 2 MFMA
-// tiles); the slice in steps of 32 tokens, dh [32][128] and x [32][128] (as
-// fp32) staged in two LDS buffers, the next step's loads in registers while the
-// current one is multiplied.  Each slice writes its partial sums to part[s]
-// ([N, d], and part_b[s] [N] from the column-tile-0 blocks, added in token
-// order); router_wgrad_reduce adds the slices in slice order.
-constexpr int RW_TOK = 32, RW_LD = 132;
+// dW_r[i, k] = sum_t dh[t, i] x[t, k] and db[i] = sum_t dh[t, i], for more
+// than 32 experts, on bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+// each dh value is split into three bf16 planes, hi = bf16(v), mid =
+// bf16(v - hi), lo = bf16(v - hi - mid), which hold its 24 significant bits (the
+// forward router splits W_r the same way), and x is exact in bf16, so
+// dW_r = sum over the planes of plane^T x.  Both operands are token-major (the
+// contraction runs over tokens): they are staged in LDS as stored, [32
+// tokens][128 + KO_PAD], and read with the transposing fragment read.  Block
+// (128-column tile, 128-expert tile, token slice s): four waves of 64 experts x
+// 64 columns (2 x 2 MFMA tiles); the slice in steps of 32 tokens, one LDS
+// buffer, the next step's loads in registers while the current one is
+// multiplied.  db sums the fp32 dh values, each thread over its row group's
+// tokens, then the eight groups in order.  Each slice writes its
+// partial sums to part[s] ([N, d]; part_b[s] [N] from the column-tile-0
+// blocks); router_wgrad_reduce adds the slices in slice order.
+constexpr int RW_TOK = 32, RW_PITCH = 128 + KO_PAD;
 
+// dh rows t0 .. t0 + 32 of experts i0 .. i0 + 128 (thread: column quad tid % 32,
+// tokens tid / 32 + 8 u) and x rows (16-byte pieces tid + 256 u)
 __device__ __forceinline__ void rw_load(const float* __restrict__ dh,
                                         const uint16_t* __restrict__ x, int64_t ts, int64_t te,
-                                        int N, int d, int i0, int k0, float (&dv)[16],
-                                        u32x4 (&xv)[2]) {
-  const int tid = threadIdx.x;
+                                        int N, int d, int i0, int k0, bool vec4,
+                                        float4 (&dv)[4], u32x4 (&xv)[2]) {
+  const int tid = threadIdx.x, c = i0 + 4 * (tid & 31);
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int idx = tid + 256 * u, r = idx >> 7, c = idx & 127;
-    const int64_t t = ts + r;
-    dv[u] = (t < te && i0 + c < N) ? dh[t * N + i0 + c] : 0.f;
+  for (int u = 0; u < 4; ++u) {
+    const int64_t t = ts + (tid >> 5) + 8 * u;
+    const float* row = dh + t * N + c;
+    if (t >= te) {
+      dv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else if (vec4 && c + 3 < N) {
+      dv[u] = *reinterpret_cast<const float4*>(row);
+    } else {
+      dv[u] = make_float4(c < N ? row[0] : 0.f, c + 1 < N ? row[1] : 0.f,
+                          c + 2 < N ? row[2] : 0.f, c + 3 < N ? row[3] : 0.f);
+    }
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int idx = tid + 256 * u, r = idx >> 4, c = (idx & 15) * 8;
+    const int idx = threadIdx.x + 256 * u, r = idx >> 4, cc = (idx & 15) * 8;
     const int64_t t = ts + r;
-    xv[u] = t < te ? *reinterpret_cast<const u32x4*>(x + t * d + k0 + c) : u32x4{0u, 0u, 0u, 0u};
+    xv[u] = t < te ? *reinterpret_cast<const u32x4*>(x + t * d + k0 + cc)
+                   : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-__device__ __forceinline__ void rw_store(float (*Ds)[RW_LD], float (*Xs)[RW_LD],
-                                         const float (&dv)[16], const u32x4 (&xv)[2]) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void rw_store(uint16_t (*Ps)[RW_TOK * RW_PITCH], uint16_t* Xs,
+                                         const float4 (&dv)[4], const u32x4 (&xv)[2]) {
+  const int tid = threadIdx.x, c = 4 * (tid & 31);
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int idx = tid + 256 * u;
-    Ds[idx >> 7][idx & 127] = dv[u];
+  for (int u = 0; u < 4; ++u) {
+    const int r = (tid >> 5) + 8 * u;
+    const float w[4] = {dv[u].x, dv[u].y, dv[u].z, dv[u].w};
+    uint16_t hb[4], mb[4], lb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hb[q] = f32_to_bf16_bits(w[q]);
+      const float r1 = w[q] - bf16_bits_to_f32(hb[q]);
+      mb[q] = f32_to_bf16_bits(r1);
+      lb[q] = f32_to_bf16_bits(r1 - bf16_bits_to_f32(mb[q]));
+    }
+    const int off = r * RW_PITCH + c;
+    *reinterpret_cast<uint2*>(&Ps[0][off]) =
+        make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
+    *reinterpret_cast<uint2*>(&Ps[1][off]) =
+        make_uint2(mb[0] | ((uint32_t)mb[1] << 16), mb[2] | ((uint32_t)mb[3] << 16));
+    *reinterpret_cast<uint2*>(&Ps[2][off]) =
+        make_uint2(lb[0] | ((uint32_t)lb[1] << 16), lb[2] | ((uint32_t)lb[3] << 16));
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int idx = tid + 256 * u, r = idx >> 4, c = (idx & 15) * 8;
-    const u32x4 v = xv[u];
-    *reinterpret_cast<float4*>(&Xs[r][c]) =
-        make_float4(__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u),
-                    __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u));
-    *reinterpret_cast<float4*>(&Xs[r][c + 4]) =
-        make_float4(__uint_as_float(v[2] << 16), __uint_as_float(v[2] & 0xFFFF0000u),
-                    __uint_as_float(v[3] << 16), __uint_as_float(v[3] & 0xFFFF0000u));
+    const int idx = tid + 256 * u;
+    *reinterpret_cast<u32x4*>(&Xs[(idx >> 4) * RW_PITCH + (idx & 15) * 8]) = xv[u];
   }
 }
 
@@ -243,15 +267,16 @@ __global__ __launch_bounds__(256, 2) void router_wgrad_kernel(const float* __res
                                                               int64_t slice,
                                                               float* __restrict__ part,
                                                               float* __restrict__ part_b) {
-  __shared__ __attribute__((aligned(16))) float Ds[2][RW_TOK][RW_LD];
-  __shared__ __attribute__((aligned(16))) float Xs[2][RW_TOK][RW_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[3][RW_TOK * RW_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[RW_TOK * RW_PITCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1, col = lane & 31, kh = lane >> 5;
   const int k0 = blockIdx.x * 128, i0 = blockIdx.y * 128;
   const int64_t ts = (int64_t)blockIdx.z * slice;
   const int64_t te = ts + slice < T ? ts + slice : T;
   const int steps = (int)((te - ts + RW_TOK - 1) / RW_TOK);
-  const bool bias = blockIdx.x == 0 && tid < 128;
+  const bool bias = blockIdx.x == 0;
+  const bool vec4 = (N & 3) == 0;
 
   floatx16 acc[2][2];
 #pragma unroll
@@ -260,36 +285,44 @@ __global__ __launch_bounds__(256, 2) void router_wgrad_kernel(const float* __res
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.f;
-  float bacc = 0.f;
+  // db: this thread's column quad over its row group's tokens (see the end)
+  float4 bacc = make_float4(0.f, 0.f, 0.f, 0.f);
 
-  float dv[16];
+  float4 dv[4];
   u32x4 xv[2];
-  rw_load(dh, x, ts, te, N, d, i0, k0, dv, xv);
-  rw_store(Ds[0], Xs[0], dv, xv);
-  __syncthreads();
+  rw_load(dh, x, ts, te, N, d, i0, k0, vec4, dv, xv);
   for (int st = 0; st < steps; ++st) {
-    const int b = st & 1;
-    if (st + 1 < steps) rw_load(dh, x, ts + (int64_t)(st + 1) * RW_TOK, te, N, d, i0, k0, dv, xv);
-#pragma unroll 4
-    for (int kk = 0; kk < RW_TOK / 2; ++kk) {
-      const int r = 2 * kk + kh;
-      float a[2], bv[2];
+    if (st > 0) __syncthreads();  // the previous step's fragments are read
+    rw_store(Ps, Xs, dv, xv);
+    if (bias) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) a[m] = Ds[b][r][64 * wm + 32 * m + col];
+      for (int u = 0; u < 4; ++u) {
+        bacc.x += dv[u].x;
+        bacc.y += dv[u].y;
+        bacc.z += dv[u].z;
+        bacc.w += dv[u].w;
+      }
+    }
+    __syncthreads();
+    if (st + 1 < steps)
+      rw_load(dh, x, ts + (int64_t)(st + 1) * RW_TOK, te, N, d, i0, k0, vec4, dv, xv);
 #pragma unroll
-      for (int n = 0; n < 2; ++n) bv[n] = Xs[b][r][64 * wn + 32 * n + col];
+    for (int ks = 0; ks < RW_TOK / 16; ++ks) {
+      bf16x8 a[2][3], b[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[m], bv[n], acc[m][n], 0, 0, 0);
+        for (int p = 0; p < 3; ++p) a[m][p] = frag_kouter(Ps[p], RW_PITCH, ks, 64 * wm + 32 * m, lane);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) b[n] = frag_kouter(Xs, RW_PITCH, ks, 64 * wn + 32 * n, lane);
+#pragma unroll
+      for (int p = 2; p >= 0; --p)  // small planes first
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m][p], b[n], acc[m][n], 0, 0, 0);
     }
-    if (bias) {
-#pragma unroll 8
-      for (int r = 0; r < RW_TOK; ++r) bacc += Ds[b][r][tid];
-    }
-    if (st + 1 < steps) rw_store(Ds[b ^ 1], Xs[b ^ 1], dv, xv);
-    __syncthreads();
   }
   // acc[m][n][v]: expert i0 + 64 wm + 32 m + 8 (v / 4) + 4 kh + v % 4,
   // column k0 + 64 wn + 32 n + col
@@ -304,7 +337,23 @@ __global__ __launch_bounds__(256, 2) void router_wgrad_kernel(const float* __res
         for (int n = 0; n < 2; ++n) ps[(int64_t)i * d + k0 + 64 * wn + 32 * n + col] = acc[m][n][v];
       }
     }
-  if (bias && i0 + tid < N) part_b[(int64_t)blockIdx.z * N + i0 + tid] = bacc;
+  if (bias) {
+    // thread (g, q) = (tid / 32, tid % 32) summed columns 4 q .. 4 q + 3 over the
+    // tokens 32 st + g + 8 u; the eight row groups are added in group order
+    __shared__ float s_g[8][128];
+    const int q = tid & 31, g = tid >> 5;
+    s_g[g][4 * q] = bacc.x;
+    s_g[g][4 * q + 1] = bacc.y;
+    s_g[g][4 * q + 2] = bacc.z;
+    s_g[g][4 * q + 3] = bacc.w;
+    __syncthreads();
+    if (tid < 128 && i0 + tid < N) {
+      float v = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < 8; ++gg) v += s_g[gg][tid];
+      part_b[(int64_t)blockIdx.z * N + i0 + tid] = v;
+    }
+  }
 }
 
 // Few experts (N <= 32): one wave per (256-column block, token slice); lane l

@@ -124,4 +124,31 @@ __device__ __forceinline__ void tile_prefix_block(const int32_t* __restrict__ n_
   if (tid == used - 1) tile_start[N] = s_run[tid];
 }
 
+// K-outer LDS tiles ([k][columns], columns innermost): rows of R + KO_PAD
+// elements.  A pitch of 32 mod 128 elements puts the four rows of a
+// transposing read 16 banks apart.
+constexpr int KO_PAD = 32;
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// MFMA fragment (v_mfma_f32_32x32x16_bf16 operand) of the 32 columns starting at
+// col of a K-outer LDS tile, K sub-step ks: lane l receives column col + l % 32,
+// rows 16 ks + 8 (l / 32) .. +7.  ds_read_b64_tr_b16: in each group of 16 lanes,
+// source lane 4 q + p addresses row q and columns 4 p .. 4 p + 3 of a 4 x 16
+// block and lane i receives column i of rows 0..3, so two such reads give a
+// lane its column's 8 consecutive k.
+__device__ __forceinline__ bf16x8 frag_kouter(const uint16_t* tile, int pitch, int ks, int col,
+                                              int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int row = ks * 16 + 8 * (g >> 1) + (j >> 2);
+  const int c = col + 16 * (g & 1) + 4 * (j & 3);
+  const uint16_t* p0 = tile + row * pitch + c;
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)p0);
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p0 + 4 * pitch));
+  typedef short shortx8 __attribute__((ext_vector_type(8)));
+  const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 }  // namespace swl

@@ -501,9 +501,6 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
                                   lane);
 }
 
-// K-outer LDS tiles: rows of R + KO_PAD elements.  A pitch of 32 mod 128
-// elements puts the four rows of a transposing read 16 banks apart.
-constexpr int KO_PAD = 32;
 
 template <int R, int NTHR, bool KOUTER>
 struct OpLayout {
@@ -516,22 +513,6 @@ struct OpLayout {
   static_assert(P * NTHR * 8 == R * GB_BK && RPP * CPR == NTHR, "whole passes");
 };
 
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-
-// Fragment of 32 columns starting at col of a K-outer LDS tile, K sub-step ks.
-__device__ __forceinline__ bf16x8 frag_kouter(const uint16_t* tile, int pitch, int ks, int col,
-                                              int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const int row = ks * 16 + 8 * (g >> 1) + (j >> 2);
-  const int c = col + 16 * (g & 1) + 4 * (j & 3);
-  const uint16_t* p0 = tile + row * pitch + c;
-  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)p0);
-  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p0 + 4 * pitch));
-  typedef short shortx8 __attribute__((ext_vector_type(8)));
-  const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
 
 // Split-K variant of the 128 x 128 tile for launches with no more tiles than
 // CUs (the Switch-Base GEMM2 shape: about 240 tiles, K = 3072), where one
