@@ -463,18 +463,28 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restri
 
 // dx_t = G_t + sum over kept choices j of dX[e_tj, p_tj] + sum_i dh[t, i] W_r[i, :],
 // fp32 then one rounding to bf16.  Block: 64 tokens x 128 columns.  The router
-// part is D[k][t] = sum_i W_r[i][k] dh[t][i] on fp32 MFMA
-// (v_mfma_f32_32x32x2_f32, one i per lane in each operand, so W_r's rows and
-// dh's rows are read as stored), in steps of 32 experts staged in two LDS
-// buffers (experts past N read as 0).  Wave w owns columns 64 (w & 1) .. +64
-// (two 32-column MFMA tiles) and tokens 32 (w >> 1) .. +32.  The sums go
-// through LDS as a [64][128] fp32 tile, and G, the dX rows and dx move in
-// 16-byte row pieces (thread: pieces tid + 256 u, token tid / 16 + 16 u).
-constexpr int GX_TOK = 64, GX_EXP = 32, GX_WLD = 132, GX_DLD = GX_EXP + 1;
+// part D[k][t] = sum_i W_r[i][k] dh[t][i] runs on bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation) with both operands split into
+// two bf16 planes, v = hi + mid + r, |r| <= 2^-16 |v|, as
+// hi(W) hi(dh) + hi(W) mid(dh) + mid(W) hi(dh): an error of about 2^-16 of
+// sum_i |W_r[i][k] dh[t][i]|, far below the final bf16 rounding of dx (2^-9).
+// Steps of 32 experts (two 16-deep sub-steps; experts past N read as 0): the W_r
+// planes staged as stored, [32 experts][128 + KO_PAD] (read with the transposing
+// fragment read), the dh planes as [64 tokens][32 + 8] (experts innermost, read
+// directly); one LDS buffer, the next step's loads in registers.  Wave w owns
+// columns 64 (w & 1) .. +64 (two 32-column MFMA tiles) and tokens
+// 32 (w >> 1) .. +32.  The sums go through LDS as a [64][128] fp32 tile, and G,
+// the dX rows and dx move in 16-byte row pieces (thread: pieces tid + 256 u,
+// token tid / 16 + 16 u).
+constexpr int GX_TOK = 64, GX_EXP = 32, GX_WP = 128 + KO_PAD, GX_DP = GX_EXP + 8,
+              GX_YLD = 132;
 
+// W_r rows i0 .. i0 + 32, columns k0 .. k0 + 128 (thread: float4 pieces tid + 256 u)
+// and dh experts i0 .. i0 + 32 of tokens t0 .. t0 + 64 (thread: token tid / 4,
+// experts 8 (tid % 4) .. +7)
 __device__ __forceinline__ void gx_load(const float* __restrict__ dh,
                                         const float* __restrict__ W_r, int64_t T, int N, int d,
-                                        int64_t t0, int k0, int i0, float4 (&wv)[4],
+                                        int64_t t0, int k0, int i0, bool vec4, float4 (&wv)[4],
                                         float (&dv)[8]) {
   const int tid = threadIdx.x;
 #pragma unroll
@@ -483,27 +493,52 @@ __device__ __forceinline__ void gx_load(const float* __restrict__ dh,
     wv[u] = i0 + r < N ? *reinterpret_cast<const float4*>(W_r + (int64_t)(i0 + r) * d + k0 + c)
                        : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  const int64_t t = t0 + (tid >> 2);
+  const int c = i0 + 8 * (tid & 3);
+  const float* row = dh + t * N + c;
+  if (t < T && vec4 && c + 7 < N) {
+    const float4 a = *reinterpret_cast<const float4*>(row);
+    const float4 b = *reinterpret_cast<const float4*>(row + 4);
+    dv[0] = a.x; dv[1] = a.y; dv[2] = a.z; dv[3] = a.w;
+    dv[4] = b.x; dv[5] = b.y; dv[6] = b.z; dv[7] = b.w;
+  } else {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int idx = tid + 256 * u, r = idx >> 5, c = idx & 31;
-    const int64_t t = t0 + r;
-    dv[u] = (t < T && i0 + c < N) ? dh[t * N + i0 + c] : 0.f;
+    for (int j = 0; j < 8; ++j) dv[j] = (t < T && c + j < N) ? row[j] : 0.f;
   }
 }
 
-__device__ __forceinline__ void gx_store(float (*Ws)[GX_WLD], float (*Ds)[GX_DLD],
-                                         const float4 (&wv)[4], const float (&dv)[8]) {
+// hi = bf16(v), mid = bf16(v - hi)
+__device__ __forceinline__ void split2(float v, uint16_t& hi, uint16_t& mid) {
+  hi = f32_to_bf16_bits(v);
+  mid = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+}
+
+__device__ __forceinline__ void gx_store(uint16_t (*Wp)[GX_EXP * GX_WP],
+                                         uint16_t (*Dp)[GX_TOK * GX_DP], const float4 (&wv)[4],
+                                         const float (&dv)[8]) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int idx = tid + 256 * u;
-    *reinterpret_cast<float4*>(&Ws[idx >> 5][(idx & 31) * 4]) = wv[u];
-  }
+    const int idx = tid + 256 * u, r = idx >> 5, c = (idx & 31) * 4;
+    const float w[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+    uint16_t h[4], m[4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int idx = tid + 256 * u;
-    Ds[idx >> 5][idx & 31] = dv[u];
+    for (int q = 0; q < 4; ++q) split2(w[q], h[q], m[q]);
+    *reinterpret_cast<uint2*>(&Wp[0][r * GX_WP + c]) =
+        make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+    *reinterpret_cast<uint2*>(&Wp[1][r * GX_WP + c]) =
+        make_uint2(m[0] | ((uint32_t)m[1] << 16), m[2] | ((uint32_t)m[3] << 16));
   }
+  uint16_t h[8], m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) split2(dv[j], h[j], m[j]);
+  const int off = (tid >> 2) * GX_DP + 8 * (tid & 3);
+  *reinterpret_cast<u32x4*>(&Dp[0][off]) =
+      u32x4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+            h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
+  *reinterpret_cast<u32x4*>(&Dp[1][off]) =
+      u32x4{m[0] | ((uint32_t)m[1] << 16), m[2] | ((uint32_t)m[3] << 16),
+            m[4] | ((uint32_t)m[5] << 16), m[6] | ((uint32_t)m[7] << 16)};
 }
 
 __global__ __launch_bounds__(256) void grad_x_kernel(const uint16_t* __restrict__ G, int64_t T,
@@ -515,13 +550,19 @@ __global__ __launch_bounds__(256) void grad_x_kernel(const uint16_t* __restrict_
                                                      const float* __restrict__ dh,
                                                      const float* __restrict__ W_r, int N,
                                                      uint16_t* __restrict__ dx) {
-  __shared__ __attribute__((aligned(16))) float Ws[2][GX_EXP][GX_WLD];
-  __shared__ float Ds[2][GX_TOK][GX_DLD];
+  // the operand planes during the products, then the [64][GX_YLD] fp32 sum tile
+  constexpr int PLANES = (2 * GX_EXP * GX_WP + 2 * GX_TOK * GX_DP) * 2, SUMS = GX_TOK * GX_YLD * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char raw[PLANES > SUMS ? PLANES : SUMS];
+  typedef uint16_t WArr[GX_EXP * GX_WP];
+  typedef uint16_t DArr[GX_TOK * GX_DP];
+  WArr* Wp = reinterpret_cast<WArr*>(raw);
+  DArr* Dp = reinterpret_cast<DArr*>(raw + 2 * GX_EXP * GX_WP * 2);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1, col = lane & 31, kh = lane >> 5;
   const int64_t t0 = (int64_t)blockIdx.y * GX_TOK;
   const int k0 = blockIdx.x * 128;
   const int pc = k0 + 8 * (tid & 15);  // the thread's piece columns
+  const bool vec4 = (N & 3) == 0;
 
   floatx16 acc[2];
 #pragma unroll
@@ -531,25 +572,32 @@ __global__ __launch_bounds__(256) void grad_x_kernel(const uint16_t* __restrict_
   const int steps = (N + GX_EXP - 1) / GX_EXP;
   float4 wv[4];
   float dv[8];
-  gx_load(dh, W_r, T, N, d, t0, k0, 0, wv, dv);
-  gx_store(Ws[0], Ds[0], wv, dv);
-  __syncthreads();
+  gx_load(dh, W_r, T, N, d, t0, k0, 0, vec4, wv, dv);
   for (int st = 0; st < steps; ++st) {
-    const int b = st & 1, i0 = st * GX_EXP;
-    if (st + 1 < steps) gx_load(dh, W_r, T, N, d, t0, k0, i0 + GX_EXP, wv, dv);
-    const int left = N - i0 < GX_EXP ? N - i0 : GX_EXP;
-    const int npair = (left + 1) >> 1;  // an odd last expert pairs with a zero row
-    for (int kk = 0; kk < npair; ++kk) {
-      const int r = 2 * kk + kh;
-      const float bv = Ds[b][32 * wn + col][r];
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ws[b][r][64 * wm + 32 * m + col], bv,
-                                                      acc[m], 0, 0, 0);
-    }
-    if (st + 1 < steps) gx_store(Ws[b ^ 1], Ds[b ^ 1], wv, dv);
+    const int i0 = st * GX_EXP;
+    if (st > 0) __syncthreads();  // the previous step's fragments are read
+    gx_store(Wp, Dp, wv, dv);
     __syncthreads();
+    if (st + 1 < steps) gx_load(dh, W_r, T, N, d, t0, k0, i0 + GX_EXP, vec4, wv, dv);
+    const int left = N - i0 < GX_EXP ? N - i0 : GX_EXP;
+    const int nsub = (left + 15) >> 4;  // 16-deep sub-steps holding experts
+    for (int ks = 0; ks < nsub; ++ks) {
+      bf16x8 a[2][2], b[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) a[p][m] = frag_kouter(Wp[p], GX_WP, ks, 64 * wm + 32 * m, lane);
+        b[p] = *reinterpret_cast<const bf16x8*>(&Dp[p][(32 * wn + col) * GX_DP + 16 * ks + 8 * kh]);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][m], b[0], acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][m], b[1], acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][m], b[0], acc[m], 0, 0, 0);
+      }
+    }
   }
+  __syncthreads();  // the planes are read: the sum tile takes their place
   // G and the kept choices' dX rows of the thread's pieces
   u32x4 gin[4];
   u32x4 xin[kMaxTopK][4];
@@ -572,10 +620,8 @@ __global__ __launch_bounds__(256) void grad_x_kernel(const uint16_t* __restrict_
     }
   }
 
-  // acc[m][4 b + q]: column 64 wm + 32 m + 8 b + 4 kh + q of token 32 wn + col; the
-  // [64][GX_WLD] fp32 tile takes the place of the W_r buffers
-  static_assert(GX_TOK * GX_WLD <= 2 * GX_EXP * GX_WLD, "the sum tile fits the W_r buffers");
-  float (*Ys)[GX_WLD] = reinterpret_cast<float (*)[GX_WLD]>(&Ws[0][0][0]);
+  // acc[m][4 b + q]: column 64 wm + 32 m + 8 b + 4 kh + q of token 32 wn + col
+  float (*Ys)[GX_YLD] = reinterpret_cast<float (*)[GX_YLD]>(raw);
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
