@@ -23,22 +23,11 @@
 
 namespace swl {
 
-// n_kept[e] = min(load[e], C) (the forward's per-expert loads), and the
-// compact list of tile_rows-row tiles over them (one block).
-__global__ __launch_bounds__(1024) void bwd_rows_kernel(const int32_t* __restrict__ load, int N,
-                                                        int64_t C, int32_t* __restrict__ n_kept,
-                                                        int32_t* __restrict__ tile_start,
-                                                        int tile_rows) {
-  __shared__ int32_t s_run[1024];
-  for (int e = threadIdx.x; e < N; e += blockDim.x)
-    n_kept[e] = (int32_t)((int64_t)load[e] < C ? (int64_t)load[e] : C);
-  __syncthreads();
-  if (tile_start) tile_prefix_block(n_kept, N, tile_rows, tile_start, s_run);
-}
-
 // Slot table and scaled output gradient of every kept assignment (t, j):
 // tok[e * C + p] = t and Gs[e, p, :] = bf16(gate_tj * G_t) (fp32 product,
-// rounded to nearest even).  One thread per 16-byte piece of a row.
+// rounded to nearest even).  One thread per 16-byte piece of a row.  The last
+// block instead writes n_kept[e] = min(load[e], C) (the forward's per-expert
+// loads) and the compact list of tile_rows-row tiles over them.
 __global__ __launch_bounds__(256) void bwd_slots_kernel(const u32x4* __restrict__ G, int64_t T,
                                                         int topk, int row_vec16,
                                                         const int32_t* __restrict__ expert_idx,
@@ -46,7 +35,19 @@ __global__ __launch_bounds__(256) void bwd_slots_kernel(const u32x4* __restrict_
                                                         const uint8_t* __restrict__ drop_mask,
                                                         const float* __restrict__ gate, int64_t C,
                                                         int32_t* __restrict__ tok,
-                                                        u32x4* __restrict__ Gs) {
+                                                        u32x4* __restrict__ Gs,
+                                                        const int32_t* __restrict__ load, int N,
+                                                        int32_t* __restrict__ n_kept,
+                                                        int32_t* __restrict__ tile_start,
+                                                        int tile_rows) {
+  if (blockIdx.x == gridDim.x - 1) {
+    __shared__ int32_t s_run[256];
+    for (int e = threadIdx.x; e < N; e += blockDim.x)
+      n_kept[e] = (int32_t)((int64_t)load[e] < C ? (int64_t)load[e] : C);
+    __syncthreads();
+    if (tile_start) tile_prefix_block(n_kept, N, tile_rows, tile_start, s_run);
+    return;
+  }
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t a = gid / row_vec16;  // assignment (token t, choice j): a = t topk + j
   const int c = (int)(gid - a * row_vec16);
@@ -678,20 +679,16 @@ void launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
                      0, s, (u32x4*)p, n);
 }
 
-void launch_bwd_rows(const int32_t* load, int N, int64_t C, int32_t* n_kept,
-                     int32_t* tile_start, hipStream_t s) {
-  launch_k(bwd_rows_kernel, dim3(1), dim3(1024), 0, s, load, N, C, n_kept, tile_start,
-                     kWideTileRows);
-}
-
 void launch_bwd_slots(const void* G, int64_t T, int d, int k, const int32_t* expert_idx,
                       const int32_t* position, const uint8_t* drop_mask, const float* gate,
-                      int64_t C, int32_t* tok, void* Gs, hipStream_t s) {
-  if (T == 0) return;
+                      int64_t C, int32_t* tok, void* Gs, const int32_t* load, int N,
+                      int32_t* n_kept, int32_t* tile_start, hipStream_t s) {
   const int rv = d / 8;
-  launch_k(bwd_slots_kernel, dim3((unsigned)((T * k * rv + 255) / 256)), dim3(256), 0,
-                     s, (const u32x4*)G, T, k, rv, expert_idx, position, drop_mask, gate, C, tok,
-                     (u32x4*)Gs);
+  // the slot blocks, then the block for n_kept and the tile list
+  const int64_t nb = (T * k * rv + 255) / 256 + 1;
+  launch_k(bwd_slots_kernel, dim3((unsigned)nb), dim3(256), 0, s, (const u32x4*)G, T, k, rv,
+           expert_idx, position, drop_mask, gate, C, tok, (u32x4*)Gs, load, N, n_kept,
+           tile_start, kWideTileRows);
 }
 
 void launch_transpose(const void* src, int64_t src_estride, int ld, int R, int Ccols,

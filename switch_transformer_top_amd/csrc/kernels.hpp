@@ -178,11 +178,10 @@ constexpr int kWideTileRows = 256;   // M tile of the wide bf16 kernel
 // backward.hip
 // n_kept = min(load, C) and the compact tile list of kWideTileRows-row tiles
 // (tile_start may be NULL)
-void launch_bwd_rows(const int32_t* load, int N, int64_t C, int32_t* n_kept,
-                     int32_t* tile_start, hipStream_t s);
 void launch_bwd_slots(const void* G, int64_t T, int d, int k, const int32_t* expert_idx,
                       const int32_t* position, const uint8_t* drop_mask, const float* gate,
-                      int64_t C, int32_t* tok, void* Gs, hipStream_t s);
+                      int64_t C, int32_t* tok, void* Gs, const int32_t* load, int N,
+                      int32_t* n_kept, int32_t* tile_start, hipStream_t s);
 void launch_transpose(const void* src, int64_t src_estride, int ld, int R, int Ccols,
                       const int32_t* valid, const int32_t* tok, void* dst, int64_t dst_estride,
                       int Rpad, int n_experts, hipStream_t s);

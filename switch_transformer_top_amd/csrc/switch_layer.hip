@@ -377,10 +377,9 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
   if (T > 0) {
     swl::prof_mark(P, s, "bwd_slots");
     int32_t* tiles = (int32_t*)(w + lo.tiles);
-    swl::launch_bwd_rows(load, N, Cb, nkept, tiles, s);
     const int k = top_k(c);
     swl::launch_bwd_slots(grad_out, T, d, k, expert_idx, position, drop_mask, gate, Cb, tok, gs,
-                          s);
+                          load, N, nkept, tiles, s);
     // io_rows: products over the experts' token rows with F columns (the tile
     // list of 256-row tiles applies); io: the rest
     swl::GemmIO io;
