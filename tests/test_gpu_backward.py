@@ -17,7 +17,10 @@ element, summed the way each gradient sums its terms (abs values, per expert):
                 1e-6 relative allowance for the fp32 softmax; grad_W_r and
                 grad_b_r sum |dh errors| |x| (and 2 gamma_T of the fp32 sum)
   grad_x        the expert part |W_in|^T |dU error| + u |dX| + the router part
-                |dh error| |W_r| + u |ref| for the final rounding
+                |dh error| |W_r| + u |ref| for the final rounding; the router part's
+                products take two bf16 pieces of W_r and of dh (hi + mid, the
+                rest below u^2 of the value) and leave out mid * mid and the rests,
+                at most 3.1 u^2 |W_r| |dh| per product, on top of the fp32 sum
 """
 import numpy as np
 import pytest
@@ -121,7 +124,7 @@ def _bounds(spec, host, f, Gf, ref, g_aux):
     ddh += 1e-6 * dh_abs
     b["dW_r"] = ddh.T @ np.abs(xf) + 2 * _gamma(T) * (dh_abs.T @ np.abs(xf))
     b["db"] = ddh.sum(0) + 2 * _gamma(T) * dh_abs.sum(0)
-    b["dx"] += ddh @ np.abs(W_r) + 2 * _gamma(N) * (dh_abs @ np.abs(W_r))
+    b["dx"] += ddh @ np.abs(W_r) + (3.2 * U16 ** 2 + 2 * _gamma(N)) * (dh_abs @ np.abs(W_r))
     b["dx"] += U16 * np.abs(ref["dx"]) + 4 * U32 * (np.abs(Gf) + b["dx"])
     return b
 
