@@ -121,3 +121,67 @@ def test_switch_c_share_config_sampled(B):
     if props.total_memory < 150 * 2 ** 30:
         pytest.skip("needs ~110 GB of device memory")
     _check_large(B, S.CONFIGS[5], "switch-c-share")
+
+
+def test_switch_large_backward_sampled(B):
+    """The backward at full size (every kernel over all 32768 tokens, 128 experts and the
+    weight-gradient slices), checked exactly where the oracle can afford it: with the loss
+    weight 0 and dL/dout nonzero only on a sampled token set, no other token contributes to
+    any gradient, so the oracle's backward of the sampled tokens alone (at the GPU forward's
+    routing) is the whole answer; everything else must be exactly 0."""
+    import test_gpu_backward as tb
+    spec = S.CONFIGS[4]
+    T, d, F, N = spec.T, spec.d, spec.F, spec.N
+    print(f"[case] switch-large backward T={T} d={d} F={F} N={N}", flush=True)
+    host, layer = _device_layer(B, spec)
+    x = B.to_device(host["x"], layer.device)
+    fwd = layer.alloc(T)
+    layer.forward(x, T, fwd)
+    f = {k: B.from_device(fwd[k]) for k in ("expert_idx", "gate", "drop_mask", "logits", "load")}
+    rng = np.random.default_rng(spec.seed + 9)
+    experts = rng.choice(N, size=4, replace=False)
+    toks = []
+    for e in experts:
+        kept = np.flatnonzero((f["expert_idx"] == e) & (f["drop_mask"] == 0))
+        toks += list(rng.choice(kept, size=min(8, kept.size), replace=False))
+    dropped = np.flatnonzero(f["drop_mask"] == 1)
+    toks += list(dropped[:4]) + list(rng.choice(T, size=4, replace=False))
+    sel = np.unique(np.array(toks, dtype=np.int64))
+    G_bits = np.zeros((T, d), dtype=np.uint16)
+    G_bits[sel] = tb._bf16_bits(rng.standard_normal((sel.size, d)).astype(np.float32))
+    G = B.to_device(G_bits, layer.device)
+    grads = layer.alloc_backward(T)
+    layer.backward(x, T, G, 0.0, fwd, grads, reuse_forward=True)
+    torch.cuda.synchronize()
+    print(f"[case] switch-large backward: {sel.size} sampled tokens, backward done", flush=True)
+
+    # the sampled tokens' sub-problem: full router, the experts' weights where it reads them
+    used = np.unique(f["expert_idx"][sel][f["drop_mask"][sel] == 0])
+    w_in = {int(e): S.expert_slice(spec, S.TENSOR_WIN, int(e)) for e in used}
+    w_out = {int(e): S.expert_slice(spec, S.TENSOR_WOUT, int(e)) for e in used}
+    dt = next(iter(w_in.values())).dtype
+    W_in = np.zeros((N, F, d), dtype=dt)     # experts the sampled tokens never reach stay 0:
+    W_out = np.zeros((N, d, F), dtype=dt)    # the oracle reads only the kept tokens' experts
+    for e in used:
+        W_in[e] = w_in[int(e)]
+        W_out[e] = w_out[int(e)]
+    sub = S.Spec("switch-large-sampled", T=int(sel.size), d=d, F=F, N=N, c=spec.c, seed=spec.seed)
+    sub_host = {"x": host["x"][sel], "W_r": host["W_r"], "b_r": host["b_r"], "W_in": W_in,
+                "W_out": W_out}
+    sub_f = {k: f[k][sel] for k in ("expert_idx", "gate", "drop_mask", "logits")}
+    sub_f["load"] = f["load"]
+    sub_g = {"grad_x": B.from_device(grads["grad_x"])[sel],
+             "grad_W_r": B.from_device(grads["grad_W_r"]), "grad_b_r": B.from_device(grads["grad_b_r"]),
+             "grad_W_in": B.from_device(grads["grad_W_in"]),
+             "grad_W_out": B.from_device(grads["grad_W_out"])}
+    tb._check(sub, sub_host, sub_f, sub_g, G_bits[sel], 0.0, "switch-large backward")
+    # no other token and no other expert gets anything
+    rest = np.ones(T, dtype=bool)
+    rest[sel] = False
+    gx = S.to_f32(B.from_device(grads["grad_x"])[rest], "bf16")
+    assert not np.any(gx != 0), "grad_x nonzero outside the sampled tokens"
+    other = np.setdiff1d(np.arange(N), used)
+    for key in ("grad_W_in", "grad_W_out"):
+        assert not np.any(S.to_f32(sub_g[key][other], "bf16") != 0), f"{key} of another expert"
+    del layer, grads, fwd
+    _free()
