@@ -431,19 +431,31 @@ __global__ __launch_bounds__(64) void router_wgrad_small_kernel(const float* __r
   if (blockIdx.x == 0 && lane < N) part_b[(int64_t)blockIdx.y * N + lane] = bacc;
 }
 
-// dW_r = sum over slices of part[s]; db likewise (when db != NULL).  A block
-// takes 64 consecutive outputs; its four waves add every fourth slice (wave w:
-// slices w, w + 4, ...) in slice order, and the four partial sums are added in
-// wave order.  Fixed order throughout.
-__global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restrict__ part,
-                                                           const float* __restrict__ part_b,
-                                                           int slices, int N, int d,
-                                                           float* __restrict__ dW_r,
-                                                           float* __restrict__ db) {
+// dW_r = sum over slices of part[s]; db likewise (when db != NULL).  Block
+// number blk (256 threads) takes the 64 consecutive outputs from 64 blk; its
+// four waves add every fourth slice (wave w: slices w, w + 4, ...) in slice
+// order, and the four partial sums are added in wave order.  Fixed order
+// throughout.  Runs as its own kernel (no tokens) or as the last blocks of the
+// dx kernel.
+struct WgradSums {
+  const float* part;
+  const float* part_b;
+  int slices;
+  float* dW_r;
+  float* db;
+};
+
+__device__ __forceinline__ void wgrad_reduce_block(const WgradSums& ws, int N, int d,
+                                                   int64_t blk) {
   __shared__ float red[4][64];
+  const float* __restrict__ part = ws.part;
+  const float* __restrict__ part_b = ws.part_b;
+  const int slices = ws.slices;
+  float* __restrict__ dW_r = ws.dW_r;
+  float* __restrict__ db = ws.db;
   const int64_t n = (int64_t)N * d;
   const int o = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t i = (int64_t)blockIdx.x * 64 + o;
+  const int64_t i = blk * 64 + o;
   float acc = 0.f;
   if (i < n) {
 #pragma unroll 8
@@ -460,6 +472,10 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restri
     if (i < n) dW_r[i] = v;
     else if (i < n + N && db) db[i - n] = v;
   }
+}
+
+__global__ __launch_bounds__(256) void router_wgrad_reduce(WgradSums ws, int N, int d) {
+  wgrad_reduce_block(ws, N, d, blockIdx.x);
 }
 
 // dx_t = G_t + sum over kept choices j of dX[e_tj, p_tj] + sum_i dh[t, i] W_r[i, :],
@@ -550,7 +566,12 @@ __global__ __launch_bounds__(256) void grad_x_kernel(const uint16_t* __restrict_
                                                      int64_t C, const uint16_t* __restrict__ dXe,
                                                      const float* __restrict__ dh,
                                                      const float* __restrict__ W_r, int N,
-                                                     uint16_t* __restrict__ dx) {
+                                                     uint16_t* __restrict__ dx, int tok_tiles,
+                                                     WgradSums wsum) {
+  if ((int)blockIdx.y >= tok_tiles) {  // the blocks past the token tiles add the dW_r slices
+    wgrad_reduce_block(wsum, N, d, (int64_t)(blockIdx.y - tok_tiles) * gridDim.x + blockIdx.x);
+    return;
+  }
   // the operand planes during the products, then the [64][GX_YLD] fp32 sum tile
   constexpr int PLANES = (2 * GX_EXP * GX_WP + 2 * GX_TOK * GX_DP) * 2, SUMS = GX_TOK * GX_YLD * 4;
   __shared__ __attribute__((aligned(16))) unsigned char raw[PLANES > SUMS ? PLANES : SUMS];
@@ -736,7 +757,7 @@ int64_t router_wgrad_slices(int64_t T, int N, int d) {
 }
 
 void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d, float* part,
-                         float* part_b, float* dW_r, float* db, hipStream_t s) {
+                         float* part_b, float* dW_r, float* db, bool reduce, hipStream_t s) {
   const int64_t slices = router_wgrad_slices(T, N, d);
   if (slices > 0 && N <= 32) {
     const dim3 grid((unsigned)((d + 255) / 256), (unsigned)slices);
@@ -756,20 +777,27 @@ void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d
     launch_k(router_wgrad_kernel, grid, dim3(256), 0, s, dh, (const uint16_t*)x, T, N,
                        d, mfma_slice(T, N, d), part, part_b);
   }
+  if (!reduce) return;  // the dx kernel's last blocks add the slices
   const int64_t n = (int64_t)N * d + N;
-  launch_k(router_wgrad_reduce, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, part,
-                     part_b, (int)slices, N, d, dW_r, db);
+  launch_k(router_wgrad_reduce, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s,
+           WgradSums{part, part_b, (int)slices, dW_r, db}, N, d);
 }
 
 void launch_grad_x(const void* G, int64_t T, int d, int k, const int32_t* expert_idx,
                    const int32_t* position, const uint8_t* drop_mask, int64_t C, const void* dXe,
-                   const float* dh, const float* W_r, int N, void* dx, hipStream_t s) {
+                   const float* dh, const float* W_r, int N, void* dx, const float* part,
+                   const float* part_b, float* dW_r, float* db, hipStream_t s) {
   if (T == 0) return;
-  // d is a multiple of 128 (bf16 layers): whole column tiles
-  const dim3 grid((unsigned)(d / 128), (unsigned)((T + GX_TOK - 1) / GX_TOK));
-  launch_k(grad_x_kernel, grid, dim3(256), 0, s, (const uint16_t*)G, T, d, k,
-                     expert_idx, position, drop_mask, C, (const uint16_t*)dXe, dh, W_r, N,
-                     (uint16_t*)dx);
+  // d is a multiple of 128 (bf16 layers): whole column tiles; then enough rows of
+  // blocks for the router weight-gradient sums (64 outputs each)
+  const int64_t tok_tiles = (T + GX_TOK - 1) / GX_TOK;
+  const int64_t n = (int64_t)N * d + N, sum_blocks = (n + 63) / 64;
+  const int64_t sum_rows = (sum_blocks + d / 128 - 1) / (d / 128);
+  const dim3 grid((unsigned)(d / 128), (unsigned)(tok_tiles + sum_rows));
+  const WgradSums ws{part, part_b, (int)router_wgrad_slices(T, N, d), dW_r, db};
+  launch_k(grad_x_kernel, grid, dim3(256), 0, s, (const uint16_t*)G, T, d, k, expert_idx,
+           position, drop_mask, C, (const uint16_t*)dXe, dh, W_r, N, (uint16_t*)dx,
+           (int)tok_tiles, ws);
 }
 
 }  // namespace swl

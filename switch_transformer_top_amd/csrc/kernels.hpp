@@ -191,11 +191,14 @@ void launch_router_bwd(const float* h, int64_t T, int N, int d, int k, const voi
                        float loss_scale, float* dh, hipStream_t s);
 // part [slices, N, d] and part_b [slices, N] fp32 scratch, slices = router_wgrad_slices(T, N, d)
 int64_t router_wgrad_slices(int64_t T, int N, int d);
+// reduce = false leaves the slice sums to launch_grad_x (called later with the
+// same part, part_b, T, N and d)
 void launch_router_wgrad(const float* dh, const void* x, int64_t T, int N, int d, float* part,
-                         float* part_b, float* dW_r, float* db, hipStream_t s);
+                         float* part_b, float* dW_r, float* db, bool reduce, hipStream_t s);
 void launch_grad_x(const void* G, int64_t T, int d, int k, const int32_t* expert_idx,
                    const int32_t* position, const uint8_t* drop_mask, int64_t C, const void* dXe,
-                   const float* dh, const float* W_r, int N, void* dx, hipStream_t s);
+                   const float* dh, const float* W_r, int N, void* dx, const float* part,
+                   const float* part_b, float* dW_r, float* db, hipStream_t s);
 void launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace swl

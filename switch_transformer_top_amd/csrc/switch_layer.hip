@@ -403,8 +403,9 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
                                      ((double)k * (double)T * (double)T));
     swl::launch_router_bwd(logits, T, N, d, k, grad_out, ybuf, Cb, expert_idx, position,
                            drop_mask, load, loss_scale, dh, s);
+    // the slices' partial sums; launch_grad_x adds them into grad_W_r and grad_b_r
     swl::launch_router_wgrad(dh, x, T, N, d, (float*)(w + lo.wpart), (float*)(w + lo.bpart),
-                             grad_W_r, grad_b_r, s);
+                             grad_W_r, grad_b_r, false, s);
     if (Cb > 0) {
       // dU = (Gs W_out[e]) * [H > 0], W_out[e] read as stored ([d][F], K = d outer)
       swl::prof_mark(P, s, "grad_h");
@@ -442,7 +443,8 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
     }
     swl::prof_mark(P, s, "grad_x");
     swl::launch_grad_x(grad_out, T, d, k, expert_idx, position, drop_mask, Cb, dxe, dh, L->W_r, N,
-                       grad_x, s);
+                       grad_x, (const float*)(w + lo.wpart), (const float*)(w + lo.bpart),
+                       grad_W_r, grad_b_r, s);
   }
   if (T == 0 || Cb == 0) {
     // no token reached an expert: the expert weights get no gradient
@@ -452,7 +454,7 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
   if (T == 0) {
     // no tokens: the router gradient sums are empty (the kernel writes zeros)
     swl::launch_router_wgrad(dh, x, 0, N, d, (float*)(w + lo.wpart), (float*)(w + lo.bpart),
-                             grad_W_r, grad_b_r, s);
+                             grad_W_r, grad_b_r, true, s);
   }
   swl::prof_end(P, s);
   return hipGetLastError() == hipSuccess ? SWITCH_OK : SWITCH_E_HIP;
