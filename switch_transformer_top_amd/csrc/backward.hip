@@ -200,7 +200,8 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
 // multiplied.  db sums the fp32 dh values, each thread over its row group's
 // tokens, then the eight groups in order.  Each slice writes its
 // partial sums to part[s] ([N, d]; part_b[s] [N] from the column-tile-0
-// blocks); router_wgrad_reduce adds the slices in slice order.
+// blocks); wgrad_reduce_block adds the slices in slice order (the dx kernel's
+// last blocks, or router_wgrad_reduce when there are no tokens).
 constexpr int RW_TOK = 32, RW_PITCH = 128 + KO_PAD;
 
 // dh rows t0 .. t0 + 32 of experts i0 .. i0 + 128 (thread: column quad tid % 32,
@@ -483,8 +484,9 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce(WgradSums ws, int N, 
 // part D[k][t] = sum_i W_r[i][k] dh[t][i] runs on bf16 MFMA
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulation) with both operands split into
 // two bf16 planes, v = hi + mid + r, |r| <= 2^-16 |v|, as
-// hi(W) hi(dh) + hi(W) mid(dh) + mid(W) hi(dh): an error of about 2^-16 of
-// sum_i |W_r[i][k] dh[t][i]|, far below the final bf16 rounding of dx (2^-9).
+// hi(W) hi(dh) + hi(W) mid(dh) + mid(W) hi(dh), which leaves out mid * mid and
+// the rests: at most 3.1 * 2^-16 of sum_i |W_r[i][k] dh[t][i]|, far below the
+// final bf16 rounding of dx (unit roundoff 2^-8).
 // Steps of 32 experts (two 16-deep sub-steps; experts past N read as 0): the W_r
 // planes staged as stored, [32 experts][128 + KO_PAD] (read with the transposing
 // fragment read), the dh planes as [64 tokens][32 + 8] (experts innermost, read
@@ -492,7 +494,8 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce(WgradSums ws, int N, 
 // columns 64 (w & 1) .. +64 (two 32-column MFMA tiles) and tokens
 // 32 (w >> 1) .. +32.  The sums go through LDS as a [64][128] fp32 tile, and G,
 // the dX rows and dx move in 16-byte row pieces (thread: pieces tid + 256 u,
-// token tid / 16 + 16 u).
+// token tid / 16 + 16 u).  The block rows past the token tiles add the dW_r
+// slices (wgrad_reduce_block) instead.
 constexpr int GX_TOK = 64, GX_EXP = 32, GX_WP = 128 + KO_PAD, GX_DP = GX_EXP + 8,
               GX_YLD = 132;
 
