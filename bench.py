@@ -304,8 +304,20 @@ def main():
 
     backward = None
     if args.backward:
-        # forward outputs (logits included) for the routing the backward differentiates at
-        layer.forward(x, spec.T, bufs, stream=sp, with_logits=True)
+        # the training forward: logits for the backward's routing, and the expert
+        # outputs kept in its workspace (switch_set_keep_expert_out), timed on its own
+        B.switch_set_keep_expert_out(layer.handle, True)
+        for _ in range(args.warmup):
+            layer.forward(x, spec.T, bufs, stream=sp, with_logits=True)
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(args.steps):
+            layer.forward(x, spec.T, bufs, stream=sp, with_logits=True)
+        f1.record(stream)
+        torch.cuda.synchronize()
+        train_fwd_ms = f0.elapsed_time(f1) / args.steps
+        B.switch_set_keep_expert_out(layer.handle, False)
         gen = torch.Generator(device=dev).manual_seed(1000 + spec.seed)   # seeded dL/dout
         g_out = torch.randn((spec.T, spec.d), device=dev, generator=gen).to(torch.bfloat16)
         g_out = g_out.view(torch.int16)
@@ -327,13 +339,14 @@ def main():
         B.switch_profile_enable(layer.handle, 0)
         torch.cuda.synchronize()
         bwd_kept = int((B.from_device(bufs["drop_mask"]) == 0).sum())
-        # matmul work of the backward: the recomputed expert outputs (H comes from the
-        # forward call's workspace) and four gradient matmuls over the kept assignments
-        # (the weight-gradient K runs over padded rows)
-        bwd_flops = 10.0 * bwd_kept * spec.d * spec.F
+        # matmul work of the backward: four gradient matmuls over the kept assignments
+        # (H and Y come from the training forward's workspace; the weight-gradient K
+        # runs over padded rows)
+        bwd_flops = 8.0 * bwd_kept * spec.d * spec.F
         backward = {"ms_per_step": round(bwd_ms, 5),
                     "tokens_per_s": round(spec.T / (bwd_ms * 1e-3), 1),
-                    "fwd_bwd_tokens_per_s": round(spec.T / ((bwd_ms + ms_per_step) * 1e-3), 1),
+                    "train_forward_ms": round(train_fwd_ms, 5),
+                    "fwd_bwd_tokens_per_s": round(spec.T / ((bwd_ms + train_fwd_ms) * 1e-3), 1),
                     "matmul_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
                     "stage_ms": {k: round(v, 5) for k, v in bwd_stages.items()}}
 

@@ -180,7 +180,10 @@ switch_status switch_forward(switch_layer* layer, const void* x, int64_t T, void
  * Weight gradients are fp32 sums over the expert's tokens rounded once to bf16;
  * grad_x is summed in fp32 and rounded once.  Every output is written (zeros
  * where nothing contributes).  SWITCH_E_UNSUPPORTED for fp32 layers.  The
- * expert outputs Y are recomputed, and H too when fwd_ws is NULL.
+ * expert outputs Y are read from fwd_ws when that forward call kept them (see
+ * switch_set_keep_expert_out; the call's second matmul writes a flag word into
+ * its workspace, which the backward's kernels read on the device), else
+ * recomputed; H is recomputed when fwd_ws is NULL.
  */
 switch_status switch_backward(switch_layer* layer, const void* x, int64_t T, const void* grad_out,
                               float grad_aux, const float* logits, const int32_t* expert_idx,
@@ -193,6 +196,19 @@ switch_status switch_backward(switch_layer* layer, const void* x, int64_t T, con
 /* Bytes of device workspace a switch_backward call with T tokens needs (0 on a
  * NULL handle or T outside [0, t_max]). */
 size_t switch_backward_workspace_bytes(const switch_layer* layer, int64_t T);
+
+/*
+ * Training forward.  The gate's gradient needs the chosen expert's output Y
+ * (dL/dgate = dL/dout . Y: the gradient reaches the router through the gate
+ * that scales that output; kasblo explainer, section
+ * "argmaxは離散なのに、Routerはなぜ学習できるのか").  keep = 1 makes the
+ * following switch_forward calls of this layer also store Y in their workspace
+ * (a few MB of extra writes from the combine epilogue), so that a
+ * switch_backward given that workspace reads it instead of recomputing it;
+ * keep = 0 (the default) stores nothing extra.  Outputs are the same either
+ * way.  SWITCH_E_INVALID for a NULL handle or keep other than 0 or 1.
+ */
+switch_status switch_set_keep_expert_out(switch_layer* layer, int keep);
 
 /*
  * Test hook: the routing stage from given fp32 logits [T, N] (device), with the

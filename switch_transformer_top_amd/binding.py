@@ -23,7 +23,7 @@ EXPORTS = ("switch_layer_create", "switch_layer_destroy", "switch_capacity",
            "switch_workspace_bytes", "switch_route", "switch_forward",
            "switch_route_from_logits", "switch_forward_debug", "switch_profile_enable",
            "switch_profile_read", "switch_status_string", "switch_last_async_error",
-           "switch_backward", "switch_backward_workspace_bytes")
+           "switch_backward", "switch_backward_workspace_bytes", "switch_set_keep_expert_out")
 
 
 class switch_config(ctypes.Structure):
@@ -72,6 +72,8 @@ lib.switch_backward_workspace_bytes.argtypes = [_vp, _i64]
 lib.switch_backward_workspace_bytes.restype = _sz
 lib.switch_profile_enable.argtypes = [_vp, ctypes.c_int]
 lib.switch_profile_enable.restype = ctypes.c_int
+lib.switch_set_keep_expert_out.argtypes = [_vp, ctypes.c_int]
+lib.switch_set_keep_expert_out.restype = ctypes.c_int
 lib.switch_profile_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_float),
                                     ctypes.POINTER(ctypes.c_char_p), ctypes.c_int]
 lib.switch_profile_read.restype = ctypes.c_int
@@ -160,6 +162,12 @@ def switch_backward(handle, x, T, grad_out, grad_aux, logits, expert_idx, gate, 
 
 def switch_backward_workspace_bytes(handle: int, T: int) -> int:
     return lib.switch_backward_workspace_bytes(handle, T)
+
+
+def switch_set_keep_expert_out(handle: int, keep: bool) -> None:
+    """Training forward: later forward calls also store the expert outputs in their
+    workspace, for a backward given that workspace."""
+    _check(lib.switch_set_keep_expert_out(handle, 1 if keep else 0), "switch_set_keep_expert_out")
 
 
 def switch_profile_enable(handle: int, max_calls: int) -> None:

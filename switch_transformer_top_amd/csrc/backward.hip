@@ -120,6 +120,8 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
                                                          int N, int d, int topk,
                                                          const uint16_t* __restrict__ G,
                                                          const uint16_t* __restrict__ Ybuf,
+                                                         const uint16_t* __restrict__ Yfwd,
+                                                         const int32_t* __restrict__ yflag,
                                                          int64_t C,
                                                          const int32_t* __restrict__ expert_idx,
                                                          const int32_t* __restrict__ position,
@@ -130,6 +132,8 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  // Y from the forward's buffer when that call kept it, else as recomputed
+  const uint16_t* __restrict__ Y = (yflag && *yflag != 0) ? Yfwd : Ybuf;
   int ej[kMaxTopK];
   bool kj[kMaxTopK];
   double dg[kMaxTopK];
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
     dg[j] = 0.0;
     if (kj[j]) {
       const u32x4* yt =
-          reinterpret_cast<const u32x4*>(Ybuf + ((int64_t)ej[j] * C + position[a]) * d);
+          reinterpret_cast<const u32x4*>(Y + ((int64_t)ej[j] * C + position[a]) * d);
       double acc = 0.0;
       for (int q = lane; q < nv; q += kWave) {
         const u32x4 gv = gt[q], yv = yt[q];
@@ -725,12 +729,14 @@ void launch_transpose(const void* src, int64_t src_estride, int ld, int R, int C
 }
 
 void launch_router_bwd(const float* h, int64_t T, int N, int d, int k, const void* G,
-                       const void* Ybuf, int64_t C, const int32_t* expert_idx,
+                       const void* Ybuf, const void* Yfwd, const int32_t* yflag, int64_t C,
+                       const int32_t* expert_idx,
                        const int32_t* position, const uint8_t* drop_mask, const int32_t* load,
                        float loss_scale, float* dh, hipStream_t s) {
   if (T == 0) return;
   launch_k(router_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, h, T, N,
-                     d, k, (const uint16_t*)G, (const uint16_t*)Ybuf, C, expert_idx, position,
+                     d, k, (const uint16_t*)G, (const uint16_t*)Ybuf,
+                     (const uint16_t*)Yfwd, yflag, C, expert_idx, position,
                      drop_mask, load, loss_scale, dh);
 }
 

@@ -137,9 +137,13 @@ __device__ __forceinline__ void combine_prefetch(CombineRows<TI, TJ>& cr,
 
 // The combine of a tile already staged in LDS (stage_tile_bf16 with CR::LD).
 template <int TI, int TJ>
+// With yk (the tile's first row and column in the kept Y buffer, row pitch
+// ld_y) the staged Y rows are stored there too.
 __device__ __forceinline__ void combine_from_stage(const uint16_t* stage,
                                                    const CombineRows<TI, TJ>& cr,
-                                                   uint16_t* __restrict__ out, int lane) {
+                                                   uint16_t* __restrict__ out, int lane,
+                                                   uint16_t* __restrict__ yk = nullptr,
+                                                   int ld_y = 0) {
   using CR = CombineRows<TI, TJ>;
 #pragma unroll
   for (int it = 0; it < CR::IT; ++it) {
@@ -148,6 +152,7 @@ __device__ __forceinline__ void combine_from_stage(const uint16_t* stage,
     if (cr.at[it] >= 0) {
       const u32x4 yv = *reinterpret_cast<const u32x4*>(stage + row * CR::LD + ch * 8);
       *reinterpret_cast<u32x4*>(out + cr.at[it]) = combine_vec_bf16(cr.xv[it], yv, cr.g[it]);
+      if (yk) *reinterpret_cast<u32x4*>(yk + (int64_t)row * ld_y + ch * 8) = yv;
     }
   }
 }
@@ -155,9 +160,11 @@ __device__ __forceinline__ void combine_from_stage(const uint16_t* stage,
 template <int TI, int TJ>
 __device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ], uint16_t* stage,
                                                    const CombineRows<TI, TJ>& cr,
-                                                   uint16_t* __restrict__ out, int lane) {
+                                                   uint16_t* __restrict__ out, int lane,
+                                                   uint16_t* __restrict__ yk = nullptr,
+                                                   int ld_y = 0) {
   stage_tile_bf16<TI, TJ, CombineRows<TI, TJ>::LD, false>(acc, stage, lane);
-  combine_from_stage<TI, TJ>(stage, cr, out, lane);
+  combine_from_stage<TI, TJ>(stage, cr, out, lane, yk, ld_y);
 }
 
 template <int TI, int TJ>
@@ -166,10 +173,26 @@ __device__ __forceinline__ void store_tile_combine(const floatx16 (&acc)[TI][TJ]
                                                    const uint16_t* __restrict__ x,
                                                    const float* __restrict__ gate,
                                                    uint16_t* __restrict__ out, int r0, int c0,
-                                                   int rows_e, int d, int lane) {
+                                                   int rows_e, int d, int lane,
+                                                   uint16_t* __restrict__ yk = nullptr) {
   CombineRows<TI, TJ> cr;
   combine_prefetch<TI, TJ>(cr, tok_e, x, gate, r0, c0, rows_e, d, lane);
-  store_tile_combine<TI, TJ>(acc, stage, cr, out, lane);
+  store_tile_combine<TI, TJ>(acc, stage, cr, out, lane, yk, d);
+}
+
+// The kept-Y origin of a combine tile (rows r0.., columns c0.. of expert e), or
+// NULL when the forward keeps no Y.
+__device__ __forceinline__ uint16_t* ykeep_at(const GemmIO& io, int e, int64_t C, int r0, int c0,
+                                              int Nout) {
+  return io.ykeep ? io.ykeep + ((int64_t)e * C + r0) * Nout + c0 : nullptr;
+}
+
+// First statements of the forward's second matmul and the backward's Y
+// recomputation: block 0 records whether Y is kept; a recomputation whose Y is
+// already kept exits.  True: the block returns.
+__device__ __forceinline__ bool y_prologue(const GemmIO& io) {
+  if (io.yflag && blockIdx.x == 0 && threadIdx.x == 0) *io.yflag = io.yflag_value;
+  return io.yskip && *io.yskip != 0;
 }
 
 // Tile order: the grid is 1-D.  Workgroups are handed to the 8 XCDs round
@@ -201,6 +224,7 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
                                                         const int32_t* __restrict__ rows, int K,
                                                         int Nout, int m_tiles, int n_tiles,
                                                         int tiles, GemmIO io, int64_t C) {
+  if (y_prologue(io)) return;
   constexpr int LA = BM / 32, LB = BN / 32;   // 16-byte loads per thread per operand
   constexpr int TI = BM / 64, TJ = BN / 64;   // MFMA tiles per wave
   // one buffer holding the A rows then the B rows; reused by the epilogue
@@ -298,7 +322,8 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
   __syncthreads();  // every wave is done with the LDS operand tiles
   if (MODE == kRowsCombine)
     store_tile_combine<TI, TJ>(acc, lds + wave * (BM / 2) * (BN / 2 + 8), tok_e, io.x, io.gate,
-                               io.out, m0 + wm * (BM / 2), n0 + wn * (BN / 2), rows_e, Nout, lane);
+                               io.out, m0 + wm * (BM / 2), n0 + wn * (BN / 2), rows_e, Nout, lane,
+                               ykeep_at(io, e, C, m0 + wm * (BM / 2), n0 + wn * (BN / 2), Nout));
   else if (MODE == kRowsMask)
     store_tile_bf16<TI, TJ, false, true>(acc, lds + wave * (BM / 2) * (BN / 2 + 8), Ce,
                                          m0 + wm * (BM / 2), n0 + wn * (BN / 2), rows_e, Nout,
@@ -351,6 +376,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
     int64_t strideB, uint16_t* __restrict__ Cout, int64_t strideC,
     const int32_t* __restrict__ rows, int K, int Nout, int m_tiles, int n_tiles, int tiles,
     GemmIO io, int64_t C, int n_exp) {
+  if (y_prologue(io)) return;
   constexpr int BM = GW_BM, BN = GW_BN, BK = GB_BK, LDK = GB_LDK;
   constexpr int TI = 4, TJ = 2;
   constexpr int STAGE = (BM + BN) * LDK;
@@ -492,7 +518,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
     CombineRows<TI, TJ> cr;
     combine_prefetch<TI, TJ>(cr, tok_e, io.x, io.gate, m0 + wm * 128, n0 + wn * 64, rows_e,
                              Nout, lane);
-    combine_from_stage<TI, TJ>(stage, cr, io.out, lane);
+    combine_from_stage<TI, TJ>(stage, cr, io.out, lane,
+                               ykeep_at(io, e, C, m0 + wm * 128, n0 + wn * 64, Nout), Nout);
   } else if (MODE == kRowsMask)
     store_tile_bf16<TI, TJ, false, true>(acc, stage, Ce, m0 + wm * 128, n0 + wn * 64, rows_e,
                                          Nout, lane, io.mask + (int64_t)e * strideC);
@@ -534,6 +561,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
     int64_t strideB, uint16_t* __restrict__ Cout, int64_t strideC,
     const int32_t* __restrict__ rows, int K, int Nout, int m_tiles, int n_tiles, int tiles,
     GemmIO io, int64_t C) {
+  if (y_prologue(io)) return;
   constexpr int BM = 128, BN = 128, BK = GB_BK, LDK = GB_LDK, TI = 2, TJ = 2;
   using LB = OpLayout<BN, 512, BKO>;
   constexpr int GS_STAGE = BM * GB_LDK + LB::ELEMS;                 // elements per buffer
@@ -712,7 +740,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_split_kernel(
     floatx16 (&t)[1][TJ] = *reinterpret_cast<floatx16 (*)[1][TJ]>(&a);
     const int r0 = m0 + wm * 64 + half * 32, c0 = n0 + wn * 64;
     if (MODE == kRowsCombine)
-      store_tile_combine<1, TJ>(t, stage, cr, io.out, lane);
+      store_tile_combine<1, TJ>(t, stage, cr, io.out, lane, ykeep_at(io, e, C, r0, c0, Nout),
+                                Nout);
     else if (MODE == kRowsMask)
       store_tile_bf16<1, TJ, false, true>(t, stage, Ce, r0, c0, rows_e, Nout, lane,
                                           io.mask + (int64_t)e * strideC);

@@ -156,6 +156,15 @@ struct GemmIO {
   // per-expert count of valid K rows (NULL: all K rows are valid)
   int64_t lda = 0, ldb = 0;
   const int32_t* krows = nullptr;
+  // expert output kept by a training forward: the combine also stores Y into
+  // ykeep ([experts][C][Nout], the dense layout), and block 0 of a forward's
+  // second matmul writes yflag_value to *yflag (1: Y is in the forward's Y
+  // buffer).  yskip: the kernel exits at once when *yskip is nonzero (the
+  // backward's recomputation of Y, when the forward kept it).
+  uint16_t* ykeep = nullptr;
+  int32_t* yflag = nullptr;
+  int32_t yflag_value = 0;
+  const int32_t* yskip = nullptr;
 };
 void launch_expert_gemm_bf16(GemmRows mode, bool relu, const void* A, int64_t strideA,
                              const void* B, int64_t strideB, void* Cout, int64_t strideC,
@@ -185,8 +194,10 @@ void launch_bwd_slots(const void* G, int64_t T, int d, int k, const int32_t* exp
 void launch_transpose(const void* src, int64_t src_estride, int ld, int R, int Ccols,
                       const int32_t* valid, const int32_t* tok, void* dst, int64_t dst_estride,
                       int Rpad, int n_experts, hipStream_t s);
+// Y from Yfwd when *yflag is nonzero (yflag may be NULL), else from Ybuf
 void launch_router_bwd(const float* h, int64_t T, int N, int d, int k, const void* G,
-                       const void* Ybuf, int64_t C, const int32_t* expert_idx,
+                       const void* Ybuf, const void* Yfwd, const int32_t* yflag, int64_t C,
+                       const int32_t* expert_idx,
                        const int32_t* position, const uint8_t* drop_mask, const int32_t* load,
                        float loss_scale, float* dh, hipStream_t s);
 // part [slices, N, d] and part_b [slices, N] fp32 scratch, slices = router_wgrad_slices(T, N, d)

@@ -18,6 +18,7 @@ struct switch_layer {
   const void* W_out;
   int device;
   swl::Profiler prof;
+  int keep_y = 0;  // forward: also store the expert outputs for switch_backward
 };
 
 namespace {
@@ -49,7 +50,7 @@ int64_t buffer_rows(const switch_config& c, int64_t T) {
 }
 
 struct Layout {
-  size_t logits, ppart, hist, rank, load, nkept, terms, tiles, tok, xbuf, hbuf, ybuf, total;
+  size_t logits, ppart, hist, rank, load, nkept, terms, tiles, tok, xbuf, hbuf, ybuf, yflag, total;
 };
 
 // Chunks of the routing statistics: the fused router uses small chunks, the
@@ -83,6 +84,7 @@ Layout layout_of(const switch_layer* L, int64_t T) {
   lo.xbuf = take(gather_copy ? es * (size_t)N * (size_t)Cb * (size_t)c.d_model : 0);
   lo.hbuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_ff);
   lo.ybuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_model);
+  lo.yflag = take(sizeof(int32_t));  // 1: ybuf holds this call's expert outputs
   lo.total = off;
   return lo;
 }
@@ -254,14 +256,21 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
     // GEMM2 runs on the same tiles with or without the fused combine, so both
     // paths give the same expert outputs (the tile list of 256-row tiles
     // applies when the wide kernel is chosen)
+    // the second matmul records in the workspace whether ybuf holds Y: always
+    // on the dense path, on the fused path when the layer keeps it
+    swl::GemmIO io2 = io;
+    io2.yflag = (int32_t*)(w + lo.yflag);
     if (fused) {
       swl::prof_mark(P, s, "gemm2_combine");
+      io2.yflag_value = L->keep_y ? 1 : 0;
+      io2.ykeep = L->keep_y ? (uint16_t*)ybuf : nullptr;
       swl::launch_expert_gemm_bf16(swl::kRowsCombine, false, hbuf, Cb * F, L->W_out,
-                                   (int64_t)d * F, nullptr, 0, r.nkept, N, Cb, F, d, io, s);
+                                   (int64_t)d * F, nullptr, 0, r.nkept, N, Cb, F, d, io2, s);
     } else {
       swl::prof_mark(P, s, "gemm2");
+      io2.yflag_value = 1;
       swl::launch_expert_gemm_bf16(swl::kRowsDense, false, hbuf, Cb * F, L->W_out, (int64_t)d * F,
-                                   ybuf, Cb * d, r.nkept, N, Cb, F, d, io, s);
+                                   ybuf, Cb * d, r.nkept, N, Cb, F, d, io2, s);
       swl::prof_mark(P, s, "combine");
       swl::launch_combine(x, bf16, T, k, (int)(es * d), expert_idx, position, drop_mask, gate, Cb,
                           ybuf, out, s);
@@ -369,6 +378,11 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
   void* hbuf = have_h ? (void*)((const char*)fwd_ws + layout_of(L, T).hbuf)
                       : (void*)(w + lo.hbuf);
   void* ybuf = w + lo.ybuf;
+  // its expert outputs too, when it kept them (decided on the device: the flag
+  // word the forward's second matmul wrote)
+  const Layout flo = layout_of(L, T);
+  const int32_t* yflag_fwd = have_h ? (const int32_t*)((const char*)fwd_ws + flo.yflag) : nullptr;
+  const void* ybuf_fwd = have_h ? (const void*)((const char*)fwd_ws + flo.ybuf) : nullptr;
   void* du = w + lo.du;
   void* dxe = w + lo.dxe;
   float* dh = (float*)(w + lo.dh);
@@ -393,16 +407,20 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
         swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
                                      hbuf, Cb * F, nkept, N, Cb, d, F, io_rows, s);
       }
+      // Y again, unless the forward call whose workspace is given kept it (its
+      // flag word; the kernel's blocks then exit at once)
       swl::prof_mark(P, s, "recompute_y");
+      swl::GemmIO ioy = io;
+      ioy.yskip = yflag_fwd;
       swl::launch_expert_gemm_bf16(swl::kRowsDense, false, hbuf, Cb * F, L->W_out,
-                                   (int64_t)d * F, ybuf, Cb * d, nkept, N, Cb, F, d, io, s);
+                                   (int64_t)d * F, ybuf, Cb * d, nkept, N, Cb, F, d, ioy, s);
     }
     swl::prof_mark(P, s, "router_bwd");
     // d aux / d p_i(t) = alpha N f_i / T with f_i = load_i / (k T)
     const float loss_scale = (float)((double)grad_aux * (double)c.alpha * (double)N /
                                      ((double)k * (double)T * (double)T));
-    swl::launch_router_bwd(logits, T, N, d, k, grad_out, ybuf, Cb, expert_idx, position,
-                           drop_mask, load, loss_scale, dh, s);
+    swl::launch_router_bwd(logits, T, N, d, k, grad_out, ybuf, ybuf_fwd, yflag_fwd, Cb,
+                           expert_idx, position, drop_mask, load, loss_scale, dh, s);
     // the slices' partial sums; launch_grad_x adds them into grad_W_r and grad_b_r
     swl::launch_router_wgrad(dh, x, T, N, d, (float*)(w + lo.wpart), (float*)(w + lo.bpart),
                              grad_W_r, grad_b_r, false, s);
@@ -604,6 +622,12 @@ switch_status switch_backward(switch_layer* L, const void* x, int64_t T, const v
   return backward_impl(L, x, T, grad_out, grad_aux, logits, expert_idx, gate, position, drop_mask,
                        load, grad_x, grad_W_r, grad_b_r, grad_W_in, grad_W_out, ws, fwd_ws,
                        (hipStream_t)stream);
+}
+
+switch_status switch_set_keep_expert_out(switch_layer* L, int keep) {
+  if (!L || (keep != 0 && keep != 1)) return SWITCH_E_INVALID;
+  L->keep_y = keep;
+  return SWITCH_OK;
 }
 
 switch_status switch_profile_enable(switch_layer* L, int max_calls) {

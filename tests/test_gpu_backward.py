@@ -271,3 +271,50 @@ def test_backward_reads_forward_h(B, top_k, T, N, d, F, c, seed):
                            a["grad_W_out"], a["ws"], a["ws_bytes"], fwd["ws"],
                            fwd["ws_bytes"] - 1)
     assert st == B.SWITCH_E_INVALID
+
+
+@pytest.mark.parametrize("top_k,T,N,d,F,c,seed", [
+    (1, 4096, 8, 768, 3072, 1.25, 131),   # Switch-Base: split-K second matmul with the combine
+    (1, 1000, 8, 256, 512, 1.0, 132),     # 128-row tiles
+    (1, 4096, 64, 512, 1024, 1.0, 133),   # 64 experts
+    (1, 9600, 32, 1024, 256, 1.0, 134),   # 256 x 256 second matmul with the combine
+    (2, 700, 48, 128, 256, 1.0, 135),     # top-2: Y is always in the forward's buffer
+])
+def test_backward_reads_kept_y(B, top_k, T, N, d, F, c, seed):
+    """A training forward (switch_set_keep_expert_out) gives the same outputs, and a
+    backward given its workspace reads Y from it instead of recomputing it: the same
+    gradients bit for bit.  A later forward that keeps nothing leaves the workspace
+    marked so that the backward recomputes Y again."""
+    spec = S.Spec(f"bwd-keep-y-{top_k}-{T}", T=T, d=d, F=F, N=N, c=c, seed=seed)
+    host, layer, x, G, fwd, grads, f, g, G_bits = _run(B, spec, top_k=top_k)
+    print(f"[case] kept Y {spec.name}", flush=True)
+    keys = ("out", "expert_idx", "gate", "position", "drop_mask", "aux_loss", "logits", "load")
+    plain = {k: B.from_device(fwd[k]) for k in keys}
+    B.switch_set_keep_expert_out(layer.handle, True)
+    kept = layer.alloc(T)
+    layer.forward(x, T, kept)
+    B.switch_set_keep_expert_out(layer.handle, False)
+    torch.cuda.synchronize()
+    for k in keys:
+        assert np.array_equal(B.from_device(kept[k]), plain[k]), k
+    again = layer.alloc_backward(T)
+    layer.backward(x, T, G, 1.0, kept, again, reuse_forward=True)
+    torch.cuda.synchronize()
+    for k in ("grad_x", "grad_W_r", "grad_b_r", "grad_W_in", "grad_W_out"):
+        assert np.array_equal(B.from_device(again[k]), g[k]), k
+    # the same workspace after a forward of another input that keeps nothing: its
+    # buffer still holds the first input's Y, and the backward must recompute Y
+    if top_k == 1:
+        x2 = B.to_device(np.ascontiguousarray(host["x"][::-1]), layer.device)
+        layer.forward(x2, T, kept)
+        fresh = layer.alloc(T)
+        layer.forward(x2, T, fresh)
+        ref2 = layer.alloc_backward(T)
+        layer.backward(x2, T, G, 1.0, fresh, ref2)
+        third = layer.alloc_backward(T)
+        layer.backward(x2, T, G, 1.0, kept, third, reuse_forward=True)
+        torch.cuda.synchronize()
+        for k in ("grad_x", "grad_W_r", "grad_b_r", "grad_W_in", "grad_W_out"):
+            assert np.array_equal(B.from_device(third[k]), B.from_device(ref2[k])), k
+    assert B.lib.switch_set_keep_expert_out(layer.handle, 2) == B.SWITCH_E_INVALID
+    assert B.lib.switch_set_keep_expert_out(None, 1) == B.SWITCH_E_INVALID
