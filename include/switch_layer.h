@@ -47,7 +47,8 @@
  *     Results are valid once the stream has reached that point.
  *   - Nothing is launched when a call returns an error status.  No call
  *     aborts the process, and no call allocates device memory: all scratch
- *     lives in the caller's workspace.
+ *     lives in the caller's workspace (switch_forward_noalloc: in a fixed
+ *     array of the library).
  *   - Calls do not synchronise the stream; one handle may be used on several
  *     streams concurrently only with distinct workspaces and outputs.
  *   - Inputs must be finite.
@@ -67,7 +68,9 @@ typedef enum {
   SWITCH_E_INVALID = 1,      /* bad size, NULL required pointer, misalignment, T > t_max,
                                 workspace too small */
   SWITCH_E_UNSUPPORTED = 2,  /* dtype combination or shape the kernels do not handle */
-  SWITCH_E_HIP = 3           /* a HIP runtime call or kernel launch failed */
+  SWITCH_E_HIP = 3,          /* a HIP runtime call or kernel launch failed */
+  SWITCH_E_TOO_LARGE = 4     /* switch_forward_noalloc: the call needs more scratch than the
+                                library's fixed array holds */
 } switch_status;
 
 typedef enum { SWITCH_F32 = 0, SWITCH_BF16 = 1 } switch_dtype;
@@ -248,6 +251,30 @@ switch_status switch_forward_debug(switch_layer* layer, const void* x, int64_t T
  */
 switch_status switch_profile_enable(switch_layer* layer, int max_calls);
 int switch_profile_read(switch_layer* layer, float* ms, const char** names, int cap);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): switch_forward with the
+ * same arguments and results minus the workspace.  Its scratch is a fixed device
+ * array inside the library, SWITCH_NOALLOC_SCRATCH_BYTES (64 MiB), one copy per
+ * GPU: it is resolved when the first handle is created on that GPU and held until
+ * the process ends.  The call itself allocates nothing.
+ *   - Returns SWITCH_E_TOO_LARGE, launching nothing, when the call would need more
+ *     than the array holds (switch_workspace_bytes(layer, T) > the maximum; the
+ *     Switch-Base shape, 4096 tokens of d = 768, F = 3072 over 8 experts, needs
+ *     about 40 MB).  SWITCH_E_HIP if the array's address could not be resolved.
+ *   - Every call on one GPU, from any handle, stream or thread, uses that GPU's one
+ *     array: calls that overlap on one GPU race, and the caller must order them
+ *     (one stream, or events).  The array keeps the last call's contents; the
+ *     forward writes everything it reads there, so nothing must start at zero.
+ *   - The array is not a forward workspace for switch_backward (its address is not
+ *     exported).
+ */
+#define SWITCH_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+switch_status switch_forward_noalloc(switch_layer* layer, const void* x, int64_t T, void* out,
+                                     int32_t* expert_idx, float* gate, int32_t* position,
+                                     uint8_t* drop_mask, float* aux_loss, float* logits,
+                                     int32_t* load, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* switch_status_string(switch_status s);

@@ -17,13 +17,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libswitch_layer.so")
 
 SWITCH_OK, SWITCH_E_INVALID, SWITCH_E_UNSUPPORTED, SWITCH_E_HIP = 0, 1, 2, 3
+SWITCH_E_TOO_LARGE = 4
+SWITCH_NOALLOC_SCRATCH_BYTES = 64 << 20   # include/switch_layer.h
 SWITCH_F32, SWITCH_BF16 = 0, 1
 
 EXPORTS = ("switch_layer_create", "switch_layer_destroy", "switch_capacity",
            "switch_workspace_bytes", "switch_route", "switch_forward",
            "switch_route_from_logits", "switch_forward_debug", "switch_profile_enable",
            "switch_profile_read", "switch_status_string", "switch_last_async_error",
-           "switch_backward", "switch_backward_workspace_bytes", "switch_set_keep_expert_out")
+           "switch_backward", "switch_backward_workspace_bytes", "switch_set_keep_expert_out",
+           "switch_forward_noalloc")
 
 
 class switch_config(ctypes.Structure):
@@ -59,6 +62,9 @@ lib.switch_route.restype = ctypes.c_int
 lib.switch_forward.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                _vp]
 lib.switch_forward.restype = ctypes.c_int
+lib.switch_forward_noalloc.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp]
+lib.switch_forward_noalloc.restype = ctypes.c_int
 lib.switch_route_from_logits.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                          _vp]
 lib.switch_route_from_logits.restype = ctypes.c_int
@@ -133,6 +139,13 @@ def switch_forward(handle, x, T, out, expert_idx, gate, position, drop_mask, aux
     return lib.switch_forward(handle, _ptr(x), T, _ptr(out), _ptr(expert_idx), _ptr(gate),
                               _ptr(position), _ptr(drop_mask), _ptr(aux_loss), _ptr(logits),
                               _ptr(load), _ptr(ws), ws_bytes, stream)
+
+
+def switch_forward_noalloc(handle, x, T, out, expert_idx, gate, position, drop_mask, aux_loss,
+                           logits, load, stream=0) -> int:
+    return lib.switch_forward_noalloc(handle, _ptr(x), T, _ptr(out), _ptr(expert_idx), _ptr(gate),
+                                      _ptr(position), _ptr(drop_mask), _ptr(aux_loss),
+                                      _ptr(logits), _ptr(load), stream)
 
 
 def switch_route_from_logits(handle, logits, T, expert_idx, gate, position, drop_mask, aux_loss,

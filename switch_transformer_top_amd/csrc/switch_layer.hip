@@ -5,6 +5,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "kernels.hpp"
@@ -19,7 +20,13 @@ struct switch_layer {
   int device;
   swl::Profiler prof;
   int keep_y = 0;  // forward: also store the expert outputs for switch_backward
+  void* scratch = nullptr;  // this device's copy of `scratch` (switch_forward_noalloc)
 };
+
+// Scratch of switch_forward_noalloc, for callers that cannot allocate: one copy
+// per GPU, in the code object's data, resolved once per device by scratch_on.
+// In host code the name is only a stand-in; kernels get the device address.
+static __device__ __align__(256) unsigned char scratch[SWITCH_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -90,6 +97,29 @@ Layout layout_of(const switch_layer* L, int64_t T) {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Device address of the current device's copy of `scratch`, looked up once per
+// device (hipGetSymbolAddress with that device current); NULL if the lookup
+// failed.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+bool g_scratch_done[kMaxDevices];
+
+void* scratch_on(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_done[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      p = nullptr;
+      (void)hipGetLastError();  // reported by switch_forward_noalloc as SWITCH_E_HIP
+    }
+    g_scratch_ptr[dev] = p;
+    g_scratch_done[dev] = true;
+  }
+  return g_scratch_ptr[dev];
+}
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -519,6 +549,7 @@ switch_status switch_layer_create(const switch_config* cfg, const float* W_r, co
   L->W_in = W_in;
   L->W_out = W_out;
   L->device = dev;
+  L->scratch = scratch_on(dev);
   *out = L;
   return SWITCH_OK;
 }
@@ -572,6 +603,19 @@ switch_status switch_forward(switch_layer* L, const void* x, int64_t T, void* ou
                              void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(L, x, T, out, expert_idx, gate, position, drop_mask, aux_loss, logits, load,
                       ws, ws_bytes, nullptr, (hipStream_t)stream);
+}
+
+switch_status switch_forward_noalloc(switch_layer* L, const void* x, int64_t T, void* out,
+                                     int32_t* expert_idx, float* gate, int32_t* position,
+                                     uint8_t* drop_mask, float* aux_loss, float* logits,
+                                     int32_t* load, void* stream) {
+  if (!L || T < 0 || T > L->cfg.t_max) return SWITCH_E_INVALID;
+  if (layout_of(L, T).total > SWITCH_NOALLOC_SCRATCH_BYTES) return SWITCH_E_TOO_LARGE;
+  switch_status st = check_device(L);
+  if (st != SWITCH_OK) return st;
+  if (!L->scratch) return SWITCH_E_HIP;
+  return forward_impl(L, x, T, out, expert_idx, gate, position, drop_mask, aux_loss, logits, load,
+                      L->scratch, SWITCH_NOALLOC_SCRATCH_BYTES, nullptr, (hipStream_t)stream);
 }
 
 switch_status switch_forward_debug(switch_layer* L, const void* x, int64_t T, void* out,
@@ -688,6 +732,8 @@ const char* switch_status_string(switch_status s) {
     case SWITCH_E_INVALID: return "SWITCH_E_INVALID: invalid argument";
     case SWITCH_E_UNSUPPORTED: return "SWITCH_E_UNSUPPORTED: unsupported dtype or shape";
     case SWITCH_E_HIP: return "SWITCH_E_HIP: HIP runtime error";
+    case SWITCH_E_TOO_LARGE:
+      return "SWITCH_E_TOO_LARGE: the call needs more than the no-allocation scratch array";
   }
   return "unknown switch_status";
 }
