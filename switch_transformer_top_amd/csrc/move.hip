@@ -15,11 +15,10 @@
 
 namespace swl {
 
-// One thread per 16-byte piece of a row: every row's index loads and data
-// moves run concurrently across the grid instead of row after row.
 // row_vec16 = bytes of one row / 16 (rows are a multiple of 16 bytes).
 
-// Dispatch also finalises the routing: position = chunk offset + in-chunk
+// Row gather of the fp32 path (into Xbuf), one thread per 16-byte piece of a
+// row.  Dispatch also finalises the routing: position = chunk offset + in-chunk
 // rank, drop = position >= C; kept rows are copied to their expert slot.  With
 // k choices per token, assignment a = t * k + j goes to expert_idx[a]; thread
 // c < k of a token finalises choice c, and every thread copies its piece of the
@@ -50,9 +49,19 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const uint4* __restrict__
   }
 }
 
+// Lanes per row of the row-wise kernels below: a power of two, at most a wave,
+// no more than the row's 16-byte pieces need.
+__host__ __device__ constexpr int lanes_per_row(int row_vec16) {
+  return row_vec16 >= 64 ? 64 : row_vec16 >= 32 ? 32 : row_vec16 >= 16 ? 16 : row_vec16 >= 8 ? 8
+         : row_vec16 >= 4 ? 4 : row_vec16 >= 2 ? 2 : 1;
+}
+
 // out[t] = x[t] + sum over kept choices j of gate[t, j] * Y[e_tj, position_tj]:
 // fp32 fused multiply-adds in choice order, then one rounding (bf16 layers).
-// A token with no kept choice leaves bit for bit.
+// A token with no kept choice leaves bit for bit.  R = lanes_per_row lanes own
+// a row: they read the token's routing once (the same addresses, one request
+// per wave) and move its 16-byte pieces c, c + R, ...; rows t, t + rows in
+// flight, ... in a grid-stride loop.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ x, int64_t T,
                                                       int k, int row_vec16,
@@ -62,58 +71,72 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       const float* __restrict__ gate, int64_t C,
                                                       const uint4* __restrict__ Ybuf,
                                                       uint4* __restrict__ out) {
+  const int R = lanes_per_row(row_vec16);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t t = gid / row_vec16;
-  const int c = (int)(gid - t * row_vec16);
-  if (t >= T) return;
-  const uint4 xv = x[t * row_vec16 + c];
+  const int sub = (int)(gid % R);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x / R;
   constexpr int NV = BF16 ? 8 : 4;   // values per 16-byte piece
-  float acc[NV];
-  const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (BF16) {
-      acc[2 * i] = __uint_as_float(xs[i] << 16);
-      acc[2 * i + 1] = __uint_as_float(xs[i] & 0xFFFF0000u);
-    } else {
-      acc[i] = __uint_as_float(xs[i]);
+  for (int64_t t = gid / R; t < T; t += stride) {
+    const uint4* xr = x + t * row_vec16;
+    uint4* orow = out + t * row_vec16;
+    // the token's kept choices (at most kMaxTopK): gate and source row in Ybuf
+    float g[kMaxTopK];
+    const uint4* yr[kMaxTopK];
+    int nk = 0;
+    for (int j = 0; j < k; ++j) {
+      const int64_t a = t * k + j;
+      if (drop_mask[a]) continue;
+      g[nk] = gate[a];
+      yr[nk] = Ybuf + ((int64_t)expert_idx[a] * C + position[a]) * row_vec16;
+      ++nk;
     }
-  }
-  bool any = false;
-  for (int j = 0; j < k; ++j) {
-    const int64_t a = t * k + j;
-    if (drop_mask[a]) continue;
-    any = true;
-    const float g = gate[a];
-    const uint4 yv = Ybuf[((int64_t)expert_idx[a] * C + position[a]) * row_vec16 + c];
-    const uint32_t ys[4] = {yv.x, yv.y, yv.z, yv.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (BF16) {
-        acc[2 * i] = fmaf(g, __uint_as_float(ys[i] << 16), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(g, __uint_as_float(ys[i] & 0xFFFF0000u), acc[2 * i + 1]);
-      } else {
-        acc[i] = fmaf(g, __uint_as_float(ys[i]), acc[i]);
+    for (int c = sub; c < row_vec16; c += R) {
+      const uint4 xv = xr[c];
+      if (nk == 0) {
+        orow[c] = xv;
+        continue;
       }
+      float acc[NV];
+      const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (BF16) {
+          acc[2 * i] = __uint_as_float(xs[i] << 16);
+          acc[2 * i + 1] = __uint_as_float(xs[i] & 0xFFFF0000u);
+        } else {
+          acc[i] = __uint_as_float(xs[i]);
+        }
+      }
+      for (int j = 0; j < nk; ++j) {
+        const uint4 yv = yr[j][c];
+        const uint32_t ys[4] = {yv.x, yv.y, yv.z, yv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (BF16) {
+            acc[2 * i] = fmaf(g[j], __uint_as_float(ys[i] << 16), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(g[j], __uint_as_float(ys[i] & 0xFFFF0000u), acc[2 * i + 1]);
+          } else {
+            acc[i] = fmaf(g[j], __uint_as_float(ys[i]), acc[i]);
+          }
+        }
+      }
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = BF16 ? f32x2_to_bf16x2_bits(acc[2 * i], acc[2 * i + 1]) : __float_as_uint(acc[i]);
+      orow[c] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
-  if (!any) {
-    out[t * row_vec16 + c] = xv;
-    return;
-  }
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o[i] = BF16 ? f32x2_to_bf16x2_bits(acc[2 * i], acc[2 * i + 1]) : __float_as_uint(acc[i]);
-  out[t * row_vec16 + c] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // Dispatch by index (bf16 path): the expert matmuls read the rows of x in
 // place, so dispatch only finalises the routing and records, for every kept
 // assignment, which token sits in slot (e, position): tok[e * C + position] = t.
-// With the fused combine (k = 1) a dropped token leaves the layer unchanged:
-// its row of x is copied to out here, and the combine never touches it.
-// Thread c < k of a token handles choice c.
+// One wave per 64 assignments: lane i finalises assignment 64 w + i (position
+// = chunk offset + in-chunk rank, drop = position >= C).  With the fused
+// combine (k = 1) a dropped token leaves the layer unchanged: the wave then
+// copies the row of each dropped token among its 64 from x to out, its 16-byte
+// pieces spread over the lanes, and the combine never touches it.
 __global__ __launch_bounds__(256) void dispatch_index_kernel(const uint4* __restrict__ x, int64_t T,
                                                              int k, int row_vec16,
                                                              const int32_t* __restrict__ expert_idx,
@@ -125,23 +148,28 @@ __global__ __launch_bounds__(256) void dispatch_index_kernel(const uint4* __rest
                                                              int32_t* __restrict__ tok,
                                                              bool copy_dropped,
                                                              uint4* __restrict__ out) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t t = gid / row_vec16;
-  const int c = (int)(gid - t * row_vec16);
-  if (t >= T) return;
-  if (c < k) {
-    const int64_t a = t * k + c;
+  const int lane = threadIdx.x & 63;
+  const int64_t a0 = (((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6) * kWave;
+  const int64_t a = a0 + lane;
+  bool dropped = false;
+  if (a < T * k) {
+    const int64_t t = a / k;
     const int32_t e = expert_idx[a];
     const int32_t pos = offsets[(t / chunk) * N + e] + rank_local[a];
-    const bool dropped = (int64_t)pos >= C;
+    dropped = (int64_t)pos >= C;
     position[a] = pos;
     drop_mask[a] = dropped ? 1 : 0;
     if (!dropped) tok[(int64_t)e * C + pos] = (int32_t)t;
   }
-  if (copy_dropped) {
-    const int32_t e = expert_idx[t];
-    const int32_t pos = offsets[(t / chunk) * N + e] + rank_local[t];
-    if ((int64_t)pos >= C) out[t * row_vec16 + c] = x[t * row_vec16 + c];
+  if (!copy_dropped) return;  // uniform: only with k = 1, where assignment a is token a
+  uint64_t m = __ballot(dropped);
+  while (m) {
+    const int64_t t = a0 + __builtin_ctzll(m);
+    m &= m - 1;
+    const uint4* src = x + t * row_vec16;
+    uint4* dst = out + t * row_vec16;
+#pragma unroll 4
+    for (int c = lane; c < row_vec16; c += kWave) dst[c] = src[c];
   }
 }
 
@@ -180,7 +208,8 @@ void launch_dispatch_index(const void* x, int64_t T, int k, int row_bytes,
                            int32_t* position, uint8_t* drop_mask, int32_t* tok, bool copy_dropped,
                            void* out, hipStream_t s) {
   if (T == 0) return;
-  launch_k(dispatch_index_kernel, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
+  const int64_t waves = (T * k + kWave - 1) / kWave;
+  launch_k(dispatch_index_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
                      (const uint4*)x, T, k, row_bytes / 16, expert_idx, rank_local, offsets, N,
                      chunk, C, position, drop_mask, tok, copy_dropped && k == 1, (uint4*)out);
 }
@@ -189,12 +218,17 @@ void launch_combine(const void* x, bool bf16, int64_t T, int k, int row_bytes,
                     const int32_t* expert_idx, const int32_t* position, const uint8_t* drop_mask,
                     const float* gate, int64_t C, const void* Ybuf, void* out, hipStream_t s) {
   if (T == 0) return;
+  // one row per R lanes, up to 8 rows per 256-thread block in each pass; the
+  // grid-stride loop takes the rest (about 16 blocks per compute unit)
+  const int64_t R = lanes_per_row(row_bytes / 16);
+  const int64_t want = (T * R + 255) / 256;
+  const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
   if (bf16)
-    launch_k(combine_kernel<true>, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
+    launch_k(combine_kernel<true>, dim3(grid), dim3(256), 0, s,
                        (const uint4*)x, T, k, row_bytes / 16, expert_idx, position, drop_mask,
                        gate, C, (const uint4*)Ybuf, (uint4*)out);
   else
-    launch_k(combine_kernel<false>, dim3(move_blocks(T, row_bytes)), dim3(256), 0, s,
+    launch_k(combine_kernel<false>, dim3(grid), dim3(256), 0, s,
                        (const uint4*)x, T, k, row_bytes / 16, expert_idx, position, drop_mask,
                        gate, C, (const uint4*)Ybuf, (uint4*)out);
 }
