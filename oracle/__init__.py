@@ -26,11 +26,12 @@ _vp = ctypes.c_void_p
 
 
 def threads() -> int:
+    """Every core the process may run on (its affinity mask)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+    return max(1, n)
 
 
 def lib():

@@ -14,10 +14,13 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wall", "-Wno-unused-function"]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(LIBDIR, exist_ok=True)
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", LIB + ".tmp"]
+# attainable-peak probes of the measurement (a library of their own)
+PEAKS_LIB = os.path.join(LIBDIR, "libswitch_peaks.so")
+
+
+def _hipcc(srcs, out, verbose):
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o",
+           out + ".tmp"]
     if verbose:
         print(" ".join(cmd))
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -27,7 +30,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err.strip():
         print(err)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(LIBDIR, exist_ok=True)
+    _hipcc([os.path.join(CSRC, s) for s in SOURCES], LIB, verbose)
+    _hipcc([os.path.join(CSRC, "peaks.hip")], PEAKS_LIB, verbose)
     return LIB
 
 
