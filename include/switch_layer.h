@@ -94,7 +94,12 @@ typedef struct {
 typedef struct switch_layer switch_layer;
 
 /*
- * Create a layer handle over caller-owned device weights.  Nothing is copied:
+ * Create a layer handle over caller-owned device weights: the router W_r (one
+ * row per expert, llm-papers-study section 3.1, h(x) = W_r x) and N experts,
+ * each the dense FFN it replaces (kasblo explainer, section
+ * "TransformerのどこへSwitch layerが入るのか"), relu(x W_in^T) W_out^T with no
+ * biases.  The capacity factor and alpha are those of llm-papers-study sections
+ * 3.4 and 3.3.  Nothing is copied:
  * the weights are BORROWED and must stay valid and unchanged for the life of
  * the handle.
  *   W_r   [N, d] fp32 router weights (one row per expert)
@@ -121,7 +126,10 @@ size_t switch_workspace_bytes(const switch_layer* layer, int64_t T);
 
 /*
  * Routing stage only: router logits, softmax, top-1, capacity positions,
- * drops, per-expert loads and the load-balancing loss.
+ * drops, per-expert loads and the load-balancing loss (llm-papers-study
+ * sections 3.1 to 3.4: logits and softmax, the top-1 choice and its gate, the
+ * auxiliary loss, capacity and overflow; positions in token order as the
+ * Incredible.AI blog's MoE layer assigns them, section "MoE Layer").
  *   x          [T, d]  act_dtype input tokens
  *   logits     [T, N]  fp32 router logits, or NULL if not wanted
  *   expert_idx [T]     int32 chosen expert
@@ -140,7 +148,12 @@ switch_status switch_route(switch_layer* layer, const void* x, int64_t T, float*
                            size_t ws_bytes, void* stream);
 
 /*
- * The whole layer: everything switch_route returns, plus
+ * The whole layer (kasblo explainer, section "tokenをExpertへ送って戻す
+ * forward pass": route, send each token to its expert, run the expert, bring
+ * the result back scaled by the gate; llm-papers-study section 3.2 for
+ * y = p_{i*} E_{i*}(x), section 3.4 and "Switch Transformer by Hand" step 13
+ * for dropped tokens leaving on the residual): everything switch_route
+ * returns, plus
  *   out [T, d] act_dtype layer output x + gate * E(x) (dropped tokens: x
  *   unchanged).  `out` must not overlap `x`.
  * Expert activations are rounded to bf16 between the two expert matmuls and
@@ -279,9 +292,15 @@ switch_status switch_forward_noalloc(switch_layer* layer, const void* x, int64_t
 /* Human-readable name of a status code (static string). */
 const char* switch_status_string(switch_status s);
 
-/* Status of the most recent asynchronous HIP error seen on this thread
- * (hipGetLastError, which also clears it): SWITCH_OK or SWITCH_E_HIP. */
-switch_status switch_last_async_error(void);
+/*
+ * Error state of the work this library enqueued for `layer` on `stream`, without
+ * waiting: SWITCH_E_HIP if a launch on this thread failed since the last check
+ * (hipGetLastError, which also clears it) or the stream reports a failed kernel
+ * (hipStreamQuery); SWITCH_OK otherwise, also while the work is still running.
+ * SWITCH_E_INVALID for a NULL layer or when the current device is not the
+ * layer's.
+ */
+switch_status switch_last_async_error(switch_layer* layer, void* stream);
 
 #ifdef __cplusplus
 }

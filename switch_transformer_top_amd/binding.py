@@ -85,7 +85,7 @@ lib.switch_profile_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_float),
 lib.switch_profile_read.restype = ctypes.c_int
 lib.switch_status_string.argtypes = [ctypes.c_int]
 lib.switch_status_string.restype = ctypes.c_char_p
-lib.switch_last_async_error.argtypes = []
+lib.switch_last_async_error.argtypes = [_vp, _vp]
 lib.switch_last_async_error.restype = ctypes.c_int
 
 
@@ -196,8 +196,8 @@ def switch_profile_read(handle: int, cap: int = 24):
     return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]
 
 
-def switch_last_async_error() -> int:
-    return lib.switch_last_async_error()
+def switch_last_async_error(handle, stream=0) -> int:
+    return lib.switch_last_async_error(handle, stream)
 
 
 # ------------------------------------------------------------------ convenience wrapper

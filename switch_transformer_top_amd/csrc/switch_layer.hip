@@ -738,8 +738,14 @@ const char* switch_status_string(switch_status s) {
   return "unknown switch_status";
 }
 
-switch_status switch_last_async_error(void) {
-  return hipGetLastError() == hipSuccess ? SWITCH_OK : SWITCH_E_HIP;
+switch_status switch_last_async_error(switch_layer* L, void* stream) {
+  if (!L) return SWITCH_E_INVALID;
+  const switch_status st = check_device(L);
+  if (st != SWITCH_OK) return st;
+  const hipError_t launch = hipGetLastError();
+  const hipError_t q = hipStreamQuery((hipStream_t)stream);
+  if (launch != hipSuccess || (q != hipSuccess && q != hipErrorNotReady)) return SWITCH_E_HIP;
+  return SWITCH_OK;
 }
 
 }  // extern "C"

@@ -82,6 +82,24 @@ def test_bf16_ragged_shapes(B, T, N, d, F, c, seed):
         assert res["aux_loss"] == pytest.approx(spec.alpha, rel=1e-6)
 
 
+def test_more_than_2048_experts(B):
+    """N = 3000 (create accepts up to 8192) takes the statistics kernel that walks each
+    logit row in pieces (more than 32 logits per lane): the layer end to end against
+    the oracle, then the routing stage alone from the same logits through
+    switch_route_from_logits, which must give the same bits."""
+    spec = S.Spec("bf16-2000-3000", T=2000, d=128, F=128, N=3000, c=1.0, seed=34)
+    host, layer, res = _run(B, spec)
+    _full_check(spec, host, res, spec.name)
+    bufs = layer.alloc(spec.T)
+    hl = torch.from_numpy(np.ascontiguousarray(res["logits"])).cuda()
+    print(f"[case] route_from_logits N={spec.N}", flush=True)
+    layer.route_from_logits(hl, spec.T, bufs)
+    torch.cuda.synchronize()
+    for k in ("expert_idx", "gate", "position", "drop_mask", "load"):
+        assert np.array_equal(B.from_device(bufs[k]), res[k]), k
+    assert float(bufs["aux_loss"].item()) == res["aux_loss"]
+
+
 def test_switch_base_config_full(B):
     spec = S.CONFIGS[2]
     host, _, res = _run(B, spec)

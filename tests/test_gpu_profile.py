@@ -84,5 +84,7 @@ def test_stage_without_kernels_and_release(B):
     b2 = other.alloc(spec.T)
     other.forward(x2, spec.T, b2)
     torch.cuda.synchronize()
-    assert B.switch_last_async_error() == B.SWITCH_OK
+    stream = torch.cuda.current_stream().cuda_stream
+    assert B.switch_last_async_error(other.handle, stream) == B.SWITCH_OK
+    assert B.switch_last_async_error(None, stream) == B.SWITCH_E_INVALID
     assert int(B.from_device(b2["drop_mask"]).size) == spec.T
