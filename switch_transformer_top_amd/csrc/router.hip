@@ -599,6 +599,163 @@ __global__ __launch_bounds__(64 * WAVES) void router_tok_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Logits of many experts (N > 256, bf16 tokens): a dense fp32-exact GEMM
+// h[T, N] = x W_r^T + b on bf16 MFMA over the three-plane split of W_r (see
+// split3), written to memory for the statistics kernel below.
+//
+// Block: 512 threads = 8 waves, tile 256 tokens x 256 experts; waves in a
+// 2 x 4 grid (token half, expert quarter), each 128 tokens x 64 experts = 4 x 2
+// tiles of v_mfma_f32_32x32x16_bf16 with the weight plane as the first operand,
+// so lane l ends up holding token (l % 32) of a tile and 16 of its 32 experts:
+// rows 8 (v / 4) + 4 (l / 32) + (v % 4), which leave as four 16-byte stores.
+// K steps of 32: the block loads x [256][32] (bf16) and W_r [256][32] (fp32),
+// splits W into its three bf16 planes once and stores x and the planes to LDS
+// (double buffered, one barrier per step); every x fragment then serves three
+// MFMAs (one per plane) and every plane fragment four token tiles.  LDS rows
+// are 32 elements (64 bytes) with the 16-byte chunk c of row r stored at
+// c ^ ((r >> 2) & 3): the 16 rows one fragment read touches per chunk fall on
+// 16 distinct 16-byte slots of the 256-byte bank space.
+// Tile order: block b takes expert tile b % n_et and token tile b / n_et, so
+// with 8 expert tiles each XCD (b % 8) keeps one 2 MB slice of W_r in its L2
+// while it walks the tokens.
+// ---------------------------------------------------------------------------
+constexpr int RG_BT = 256, RG_BE = 256, RG_BK = 32;
+constexpr int RG_XS = RG_BT * RG_BK;            // x tile (elements)
+constexpr int RG_PS = RG_BE * RG_BK;            // one weight plane
+constexpr int RG_STAGE = RG_XS + 3 * RG_PS;     // one LDS buffer (elements)
+constexpr size_t kRouterGemmLds = (size_t)2 * RG_STAGE * sizeof(uint16_t);  // 128 KiB
+
+// element offset of 16-byte chunk c (0..3) of row r in a swizzled [rows][32] tile
+__device__ __forceinline__ int rg_at(int r, int c) { return r * RG_BK + ((c ^ ((r >> 2) & 3)) << 3); }
+
+__global__ __launch_bounds__(512, 1) void router_gemm_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ W_r, const float* __restrict__ b_r,
+    float* __restrict__ h, int64_t T, int d, int N, int n_et, bool vec) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t rlds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wt = wave >> 2, we = wave & 3;
+  const int et = (int)(blockIdx.x % (unsigned)n_et);
+  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)n_et) * RG_BT;
+  const int e0 = et * RG_BE;
+
+  // loaders: thread -> row tid / 2, half (tid & 1) of the 32-wide K step: 16
+  // fp32 weights (four 16-byte loads) and 16 bf16 token values (two loads)
+  const int lr = tid >> 1, lh = tid & 1;
+  int64_t tr = t0 + lr;
+  tr = tr < T ? tr : T - 1;  // rows past T: any valid row, never stored
+  const uint16_t* xsrc = x + tr * d + lh * 16;
+  const bool wok = e0 + lr < N;
+  const float* wsrc = W_r + (int64_t)(wok ? e0 + lr : 0) * d + lh * 16;
+  const int nk = d / RG_BK;
+  // one register stage: step t + 1 waits in xr / wr while step t is multiplied
+  u32x4 xr[2];
+  float4 wr[4];
+  auto gload = [&](int kc) {
+    const int k = (kc < nk ? kc : nk - 1) * RG_BK;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) xr[q] = *reinterpret_cast<const u32x4*>(xsrc + k + 8 * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wr[q] = *reinterpret_cast<const float4*>(wsrc + k + 4 * q);
+  };
+  auto split_store = [&](int buf) {
+    uint16_t* xs = rlds + buf * RG_STAGE;
+    uint16_t* ps = xs + RG_XS;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) *reinterpret_cast<u32x4*>(xs + rg_at(lr, 2 * lh + q)) = xr[q];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {   // 8 weights -> one 16-byte chunk per plane
+      const float4 a = wr[2 * q], b = wr[2 * q + 1];
+      float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      if (!wok) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = 0.f;
+      }
+      bf16x8 hi, mid, lo;
+      split3(w, hi, mid, lo);
+      const int at = rg_at(lr, 2 * lh + q);
+      *reinterpret_cast<bf16x8*>(ps + at) = hi;
+      *reinterpret_cast<bf16x8*>(ps + RG_PS + at) = mid;
+      *reinterpret_cast<bf16x8*>(ps + 2 * RG_PS + at) = lo;
+    }
+  };
+
+  floatx16 acc[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
+  const int fr = lane & 31, fc = lane >> 5;
+  auto compute = [&](int buf) {
+    const uint16_t* xs = rlds + buf * RG_STAGE;
+    const uint16_t* ps = xs + RG_XS;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = 2 * s + fc;
+      bf16x8 xb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xb[i] = *reinterpret_cast<const bf16x8*>(xs + rg_at(wt * 128 + i * 32 + fr, c));
+      // smallest pieces first: lo, mid, hi
+#pragma unroll
+      for (int p = 2; p >= 0; --p) {
+        bf16x8 wp[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          wp[j] = *reinterpret_cast<const bf16x8*>(ps + p * RG_PS +
+                                                   rg_at(we * 64 + j * 32 + fr, c));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wp[j], xb[i], acc[j][i], 0, 0, 0);
+      }
+    }
+  };
+
+  gload(0);
+  split_store(0);
+  gload(1);
+  __syncthreads();
+  for (int t = 0; t < nk; ++t) {
+    // buffer (t + 1) & 1 was last read in step t - 1, before the barrier that
+    // ended it; the registers then take step t + 2
+    if (t + 1 < nk) split_store((t + 1) & 1);
+    gload(t + 2);
+    compute(t & 1);
+    __syncthreads();
+  }
+
+  // logits + bias: lane l of tile (j, i) holds token wt*128 + 32 i + l % 32 and
+  // experts we*64 + 32 j + 8 q + 4 (l / 32) + (0..3), q < 4; vec: 16-byte stores
+  // (h 16-byte aligned and N a multiple of 4)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + wt * 128 + i * 32 + fr;
+    if (t >= T) continue;
+    float* hrow = h + t * N;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = e0 + we * 64 + j * 32 + 8 * q + 4 * fc;
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          v[u] = acc[j][i][4 * q + u] + ((b_r && e + u < N) ? b_r[e + u] : 0.f);
+        if (vec && e + 3 < N) {
+          *reinterpret_cast<float4*>(hrow + e) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (e + u < N) hrow[e + u] = v[u];
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Routing statistics from logits in memory (fp32 routers, N > 256, and the
 // test entry point that takes logits).  Block: 256 threads, one chunk of 64
 // tokens.  Each wave takes 16 tokens: lanes stride over the N logits of a row;
@@ -802,13 +959,20 @@ void launch_router_logits(const void* x, bool x_bf16, const float* W_r, const fl
                           float* h, int64_t T, int d, int N, hipStream_t s) {
   if (T == 0) return;
   if (x_bf16) {
-    // MFMA logits in expert tiles of 256, statistics by route_rows_kernel
-    constexpr int BT = 16 * kLogitRowt * kLogitWaves;
-    const dim3 grid((unsigned)((T + BT - 1) / BT), (unsigned)((N + 255) / 256));
-    launch_k((router_tok_kernel<256, kLogitRowt, false, kLogitWaves>), grid,
-             dim3(64 * kLogitWaves), 0, s,
-                       (const uint16_t*)x, W_r, b_r, T, d, N, 1, h, nullptr, nullptr, nullptr,
-                       nullptr, nullptr);
+    // MFMA logits in 256 x 256 tiles, statistics by route_rows_kernel
+    static uint64_t set_on = 0;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev < 64 && !(set_on >> dev & 1)) {
+      (void)hipFuncSetAttribute((const void*)router_gemm_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRouterGemmLds);
+      set_on |= 1ull << dev;
+    }
+    const int n_et = (N + RG_BE - 1) / RG_BE;
+    const int64_t n_tt = (T + RG_BT - 1) / RG_BT;
+    const bool vec = (N & 3) == 0 && ((uintptr_t)h & 15) == 0;
+    launch_k(router_gemm_kernel, dim3((unsigned)(n_tt * n_et)), dim3(512), kRouterGemmLds, s,
+             (const uint16_t*)x, W_r, b_r, h, T, d, N, n_et, vec);
     return;
   }
   dim3 grid((unsigned)((T + RT_BT - 1) / RT_BT), (unsigned)((N + RT_BE - 1) / RT_BE));
