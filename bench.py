@@ -67,6 +67,12 @@ def stage_work(stage: str, spec, kept: int, active_experts: int, k: int = 1) -> 
         return dict(flops=2.0 * kept * d * F,
                     bytes=active_experts * d * F * es + kept * (F + 2 * d) * es + 8 * kept,
                     peak_tflops=peak)
+    if stage == "ffn_fused":
+        # both matmuls with the combine, H on chip: the weights of the experts in
+        # use, the kept rows of x in, the residual rows in and the outputs out
+        return dict(flops=4.0 * kept * d * F,
+                    bytes=2 * active_experts * d * F * es + 3 * kept * d * es + 8 * kept,
+                    peak_tflops=peak)
     if stage in ("dispatch", "assign"):
         # assign: the one-launch form (chunk scan and loss included; their
         # per-chunk counts are a few bytes per token and are left out)
@@ -123,7 +129,7 @@ def measured_traffic(stage: str, workload: str):
         return None
     pattern, src = STAGE_KERNEL[stage]
     h = hashlib.sha256()
-    for f in (src, "common.hpp"):
+    for f in (src, "common.hpp", "epilogue.hpp"):
         with open(os.path.join(ROOT, "switch_transformer_top_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     digest = h.hexdigest()
@@ -294,7 +300,8 @@ def attainable_peaks(torch, dev, stream) -> dict:
 
 # stages whose HBM traffic is almost all reads (weights, tokens, logits): their
 # attainable reference is the read stream; the movers' is the copy stream
-READ_STAGES = ("router", "router_logits", "route_rows", "gemm1_relu", "gemm2", "gemm2_combine")
+READ_STAGES = ("router", "router_logits", "route_rows", "gemm1_relu", "gemm2", "gemm2_combine",
+               "ffn_fused")
 
 
 def with_attainable(entry: dict, peaks) -> dict:
@@ -360,6 +367,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, run one device-to-device copy of 1 GiB "
                          "(reference for hardware byte counters)")
+    ap.add_argument("--ffn", choices=("auto", "fused", "unfused"), default="auto",
+                    help="expert FFN variant: the library's choice (default), the fused kernel "
+                         "(H on chip), or the two matmul launches")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run only W warm-up and this many plain steps (for rocprofv3)")
     args = ap.parse_args()
@@ -381,6 +391,8 @@ def main():
     bufs = layer.alloc(spec.T)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
+    B.switch_set_ffn_mode(layer.handle, {"auto": B.SWITCH_FFN_AUTO, "fused": B.SWITCH_FFN_FUSED,
+                                         "unfused": B.SWITCH_FFN_UNFUSED}[args.ffn])
 
     def step():
         layer.forward(x, spec.T, bufs, stream=sp, with_logits=False)
@@ -481,10 +493,10 @@ def main():
 
     rooflines = {k: entry(k, v) for k, v in stage_ms.items()
                  if k in ("router", "router_logits", "route_rows", "gemm1_relu", "gemm2",
-                          "gemm2_combine", "dispatch", "assign", "combine")}
+                          "gemm2_combine", "ffn_fused", "dispatch", "assign", "combine")}
     dominant = max(rooflines, key=lambda k: stage_ms[k])
     gemm_ms = (stage_ms.get("gemm1_relu", 0) + stage_ms.get("gemm2", 0)
-               + stage_ms.get("gemm2_combine", 0))
+               + stage_ms.get("gemm2_combine", 0) + stage_ms.get("ffn_fused", 0))
     expert_tflops = 4.0 * kept * spec.d * spec.F / (gemm_ms * 1e-3) / 1e12 if gemm_ms else 0.0
     slot_stage = "dispatch" if "dispatch" in rooflines else "assign"
     combine_entry = rooflines.get("combine")
@@ -512,6 +524,7 @@ def main():
         "config": {"workload": workload, "T": spec.T, "d_model": spec.d, "d_ff": spec.F,
                    "n_experts": spec.N, "capacity_factor": spec.c, "capacity": C,
                    "router": "fp32", "experts": spec.expert, "parallelism": "single-gpu",
+                   "ffn": "fused" if "ffn_fused" in stage_ms else "two launches",
                    "timing": "median of K steps, each after a 512 MiB cache-evicting write "
                              "(cold caches)"},
         "roofline": rooflines[dominant],

@@ -75,6 +75,15 @@ typedef enum {
 
 typedef enum { SWITCH_F32 = 0, SWITCH_BF16 = 1 } switch_dtype;
 
+/* How the expert FFN runs (switch_set_ffn_mode). */
+typedef enum {
+  SWITCH_FFN_AUTO = 0,     /* the library's choice (the default): the faster form measured
+                              for the shape, at present the two-launch form */
+  SWITCH_FFN_UNFUSED = 1,  /* two matmul launches, H [rows, F] through the workspace */
+  SWITCH_FFN_FUSED = 2     /* one launch, H kept on chip (bf16, top-1, d a multiple of 256
+                              up to 1024, F a multiple of 256) */
+} switch_ffn_mode;
+
 typedef struct {
   int64_t t_max;            /* largest T any call on this handle may pass (>= 0) */
   int32_t d_model;          /* d; a multiple of 8 (of 128 for bf16 layers) */
@@ -192,7 +201,9 @@ switch_status switch_forward(switch_layer* layer, const void* x, int64_t T, void
  *   fwd_ws, fwd_ws_bytes  the workspace of that forward call (switch_forward,
  *                 unchanged since; at least switch_workspace_bytes(T)), whose
  *                 expert activations H are then read instead of recomputed
- *                 (the same values), or NULL
+ *                 (the same values), or NULL.  A forward that ran the fused
+ *                 expert FFN left no H there (a flag word in the workspace says
+ *                 so): the backward then recomputes H into that workspace
  * Weight gradients are fp32 sums over the expert's tokens rounded once to bf16;
  * grad_x is summed in fp32 and rounded once.  Every output is written (zeros
  * where nothing contributes).  SWITCH_E_UNSUPPORTED for fp32 layers.  The
@@ -206,12 +217,28 @@ switch_status switch_backward(switch_layer* layer, const void* x, int64_t T, con
                               const float* gate, const int32_t* position,
                               const uint8_t* drop_mask, const int32_t* load, void* grad_x,
                               float* grad_W_r, float* grad_b_r, void* grad_W_in,
-                              void* grad_W_out, void* ws, size_t ws_bytes, const void* fwd_ws,
+                              void* grad_W_out, void* ws, size_t ws_bytes, void* fwd_ws,
                               size_t fwd_ws_bytes, void* stream);
 
 /* Bytes of device workspace a switch_backward call with T tokens needs (0 on a
  * NULL handle or T outside [0, t_max]). */
 size_t switch_backward_workspace_bytes(const switch_layer* layer, int64_t T);
+
+/*
+ * Expert FFN variant of the following forward calls of this layer.  Both compute
+ * relu(x W_in[e]^T) rounded to bf16, its product with W_out[e]^T rounded to
+ * bf16, and the combine, in fp32 sums; the fused variant keeps H on chip
+ * instead of writing it to the workspace between two launches (the single-
+ * device forward pass of the kasblo explainer, section
+ * "tokenをExpertへ送って戻すforward pass", done in one pass over each expert's
+ * tokens), and its sums run in another order, so the two agree within
+ * rounding, not bit for bit.  Calls that must return or keep the expert outputs
+ * (switch_forward_debug, switch_set_keep_expert_out(1)) and top-2 layers always
+ * run the two-launch form.  SWITCH_E_UNSUPPORTED for SWITCH_FFN_FUSED on a
+ * layer whose shape or type the fused kernel does not take; SWITCH_E_INVALID for
+ * a NULL handle or another mode.
+ */
+switch_status switch_set_ffn_mode(switch_layer* layer, int mode);
 
 /*
  * Training forward.  The gate's gradient needs the chosen expert's output Y

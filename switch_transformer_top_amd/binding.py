@@ -20,13 +20,14 @@ SWITCH_OK, SWITCH_E_INVALID, SWITCH_E_UNSUPPORTED, SWITCH_E_HIP = 0, 1, 2, 3
 SWITCH_E_TOO_LARGE = 4
 SWITCH_NOALLOC_SCRATCH_BYTES = 64 << 20   # include/switch_layer.h
 SWITCH_F32, SWITCH_BF16 = 0, 1
+SWITCH_FFN_AUTO, SWITCH_FFN_UNFUSED, SWITCH_FFN_FUSED = 0, 1, 2
 
 EXPORTS = ("switch_layer_create", "switch_layer_destroy", "switch_capacity",
            "switch_workspace_bytes", "switch_route", "switch_forward",
            "switch_route_from_logits", "switch_forward_debug", "switch_profile_enable",
            "switch_profile_read", "switch_status_string", "switch_last_async_error",
            "switch_backward", "switch_backward_workspace_bytes", "switch_set_keep_expert_out",
-           "switch_forward_noalloc")
+           "switch_forward_noalloc", "switch_set_ffn_mode")
 
 
 class switch_config(ctypes.Structure):
@@ -78,6 +79,8 @@ lib.switch_backward_workspace_bytes.argtypes = [_vp, _i64]
 lib.switch_backward_workspace_bytes.restype = _sz
 lib.switch_profile_enable.argtypes = [_vp, ctypes.c_int]
 lib.switch_profile_enable.restype = ctypes.c_int
+lib.switch_set_ffn_mode.argtypes = [_vp, ctypes.c_int]
+lib.switch_set_ffn_mode.restype = ctypes.c_int
 lib.switch_set_keep_expert_out.argtypes = [_vp, ctypes.c_int]
 lib.switch_set_keep_expert_out.restype = ctypes.c_int
 lib.switch_profile_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_float),
@@ -181,6 +184,11 @@ def switch_set_keep_expert_out(handle: int, keep: bool) -> None:
     """Training forward: later forward calls also store the expert outputs in their
     workspace, for a backward given that workspace."""
     _check(lib.switch_set_keep_expert_out(handle, 1 if keep else 0), "switch_set_keep_expert_out")
+
+
+def switch_set_ffn_mode(handle: int, mode: int) -> None:
+    """Expert FFN variant of later forward calls: SWITCH_FFN_AUTO, _UNFUSED or _FUSED."""
+    _check(lib.switch_set_ffn_mode(handle, int(mode)), "switch_set_ffn_mode")
 
 
 def switch_profile_enable(handle: int, max_calls: int) -> None:

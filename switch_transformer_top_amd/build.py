@@ -8,7 +8,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libswitch_layer.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["switch_layer.hip", "router.hip", "assign.hip", "move.hip", "gemm.hip", "backward.hip"]
+SOURCES = ["switch_layer.hip", "router.hip", "assign.hip", "move.hip", "gemm.hip", "ffn.hip",
+           "backward.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]

@@ -184,6 +184,17 @@ void launch_expert_gemm_bf16_t(GemmRows mode, bool relu, bool a_kouter, bool b_k
 bool expert_gemm_shape_ok(bool bf16, int d, int F);
 constexpr int kWideTileRows = 256;   // M tile of the wide bf16 kernel
 
+// ffn.hip: the fused expert FFN (both matmuls, the ReLU and the combine, H
+// kept on chip) over the compact list of kFfnTileRows-row tiles; d a multiple
+// of 256 up to 1024, F a multiple of 256, bf16, top-1.  Block 0 writes 0 to
+// *yflag and *hflag (neither Y nor H is left in the workspace).
+constexpr int kFfnTileRows = 64;
+bool ffn_fused_shape_ok(int d, int F);
+void launch_ffn_fused(const void* x, const void* W_in, const void* W_out, const int32_t* n_kept,
+                      const int32_t* tile_start, const int32_t* tok, const float* gate,
+                      void* out, int d, int F, int64_t C, int n_exp, int32_t* yflag,
+                      int32_t* hflag, hipStream_t s);
+
 // backward.hip
 // n_kept = min(load, C) and the compact tile list of kWideTileRows-row tiles
 // (tile_start may be NULL)

@@ -162,14 +162,35 @@ __global__ __launch_bounds__(256) void dispatch_index_kernel(const uint4* __rest
     if (!dropped) tok[(int64_t)e * C + pos] = (int32_t)t;
   }
   if (!copy_dropped) return;  // uniform: only with k = 1, where assignment a is token a
+  // the wave's dropped tokens, four rows at a time: every lane issues its loads
+  // of all four rows (16-byte pieces c = lane + 64 i) before any store
   uint64_t m = __ballot(dropped);
   while (m) {
-    const int64_t t = a0 + __builtin_ctzll(m);
-    m &= m - 1;
-    const uint4* src = x + t * row_vec16;
-    uint4* dst = out + t * row_vec16;
-#pragma unroll 4
-    for (int c = lane; c < row_vec16; c += kWave) dst[c] = src[c];
+    int64_t row[4];
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      row[j] = m ? (a0 + __builtin_ctzll(m)) * row_vec16 : 0;
+      n += m ? 1 : 0;
+      m &= m - 1;
+    }
+    for (int c0 = 0; c0 < row_vec16; c0 += 4 * kWave) {
+      uint4 v[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = c0 + lane + kWave * i;
+          if (j < n && c < row_vec16) v[j][i] = x[row[j] + c];
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = c0 + lane + kWave * i;
+          if (j < n && c < row_vec16) out[row[j] + c] = v[j][i];
+        }
+    }
   }
 }
 

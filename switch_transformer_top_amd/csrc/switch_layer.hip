@@ -20,6 +20,7 @@ struct switch_layer {
   int device;
   swl::Profiler prof;
   int keep_y = 0;  // forward: also store the expert outputs for switch_backward
+  int ffn_mode = SWITCH_FFN_AUTO;  // fused or two-launch expert FFN (switch_set_ffn_mode)
   void* scratch = nullptr;  // this device's copy of `scratch` (switch_forward_noalloc)
 };
 
@@ -57,7 +58,8 @@ int64_t buffer_rows(const switch_config& c, int64_t T) {
 }
 
 struct Layout {
-  size_t logits, ppart, hist, rank, load, nkept, terms, tiles, tok, xbuf, hbuf, ybuf, yflag, total;
+  size_t logits, ppart, hist, rank, load, nkept, terms, tiles, tok, xbuf, hbuf, ybuf, yflag, hflag,
+      total;
 };
 
 // Chunks of the routing statistics: the fused router uses small chunks, the
@@ -92,6 +94,7 @@ Layout layout_of(const switch_layer* L, int64_t T) {
   lo.hbuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_ff);
   lo.ybuf = take(es * (size_t)N * (size_t)Cb * (size_t)c.d_model);
   lo.yflag = take(sizeof(int32_t));  // 1: ybuf holds this call's expert outputs
+  lo.hflag = take(sizeof(int32_t));  // 1: hbuf holds this call's hidden activations
   lo.total = off;
   return lo;
 }
@@ -162,6 +165,7 @@ struct Routed {
   float* ppart = nullptr;
   float* aux = nullptr;
   const int32_t* expert_idx = nullptr;
+  int tile_rows = swl::kWideTileRows;  // rows per tile of the compact tile list
 };
 
 // Routing stage (logits, softmax / top-1 / gate, chunk statistics, scan and
@@ -170,7 +174,8 @@ struct Routed {
 // call, by finalize_positions otherwise.
 Routed enqueue_routing(switch_layer* L, const void* x, const float* given_logits, int64_t T,
                        float* logits_out, int32_t* expert_idx, float* gate, float* aux_loss,
-                       int32_t* load, char* ws, const Layout& lo, hipStream_t s) {
+                       int32_t* load, char* ws, const Layout& lo, hipStream_t s,
+                       int tile_rows = swl::kWideTileRows) {
   const switch_config& c = L->cfg;
   const int N = c.n_experts;
   const bool bf16 = c.act_dtype == SWITCH_BF16;
@@ -208,11 +213,11 @@ Routed enqueue_routing(switch_layer* L, const void* x, const float* given_logits
   r.aux = aux_loss;
   r.expert_idx = expert_idx;
   r.one_launch = T > 0 && swl::assign_one_launch_ok(N, nc, r.chunk);
+  r.tile_rows = tile_rows;
   if (!r.one_launch) {
     swl::prof_mark(P, s, "route_scan");
     swl::launch_route_scan(r.offsets, ppart, nc, N, T, top_k(c), r.Cb, c.alpha, r.load, r.nkept,
-                           (double*)(ws + lo.terms), aux_loss, r.tile_start, swl::kWideTileRows,
-                           s);
+                           (double*)(ws + lo.terms), aux_loss, r.tile_start, tile_rows, s);
   }
   return r;
 }
@@ -226,8 +231,21 @@ void finish_assignment(switch_layer* L, const Routed& r, int64_t T, int32_t* pos
   swl::prof_mark(&L->prof, s, "assign");
   swl::launch_assign(r.offsets, r.ppart, r.nc, c.n_experts, T, top_k(c), r.chunk, r.Cb, c.alpha,
                      r.expert_idx, r.rank, r.load, r.nkept, r.aux, r.tile_start,
-                     swl::kWideTileRows, position, drop_mask, tok, copy_mode,
+                     r.tile_rows, position, drop_mask, tok, copy_mode,
                      (int)(dtype_size(c.act_dtype) * (size_t)c.d_model), x, dst, s);
+}
+
+// Whether a forward call runs the fused expert FFN (H kept on chip): bf16 top-1
+// layers of a shape the kernel takes, when the caller wants neither the expert
+// outputs (debug hook) nor Y kept for a backward, and the layer asks for it.
+// The automatic mode keeps the two-launch matmuls: on every workload measured
+// (Switch-Base, Zipf overflow, Switch-Large shapes) they are faster.
+bool fused_ffn(const switch_layer* L, int64_t T, bool want_y) {
+  const switch_config& c = L->cfg;
+  (void)T;
+  if (c.act_dtype != SWITCH_BF16 || top_k(c) != 1 || want_y || L->keep_y) return false;
+  if (!swl::ffn_fused_shape_ok(c.d_model, c.d_ff)) return false;
+  return L->ffn_mode == SWITCH_FFN_FUSED;
 }
 
 switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
@@ -254,7 +272,9 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
   swl::Profiler* P = &L->prof;
   swl::prof_begin(P);
 
-  Routed r = enqueue_routing(L, x, nullptr, T, logits, expert_idx, gate, aux_loss, load, w, lo, s);
+  const bool ffn1 = T > 0 && fused_ffn(L, T, expert_out != nullptr);
+  Routed r = enqueue_routing(L, x, nullptr, T, logits, expert_idx, gate, aux_loss, load, w, lo, s,
+                             ffn1 ? swl::kFfnTileRows : swl::kWideTileRows);
   const int64_t Cb = r.Cb;
   void* xbuf = w + lo.xbuf;
   void* hbuf = w + lo.hbuf;
@@ -280,9 +300,21 @@ switch_status forward_impl(switch_layer* L, const void* x, int64_t T, void* out,
       swl::launch_dispatch_index(x, T, k, (int)(es * d), expert_idx, r.rank, r.offsets, N,
                                  r.chunk, Cb, position, drop_mask, tok, fused, out, s);
     }
+    if (ffn1) {
+      // both matmuls, the ReLU and the combine in one launch, H on chip
+      swl::prof_mark(P, s, "ffn_fused");
+      swl::launch_ffn_fused(x, L->W_in, L->W_out, r.nkept, r.tile_start, tok, gate, out, d, F,
+                            Cb, N, (int32_t*)(w + lo.yflag), (int32_t*)(w + lo.hflag), s);
+      swl::prof_end(P, s);
+      return hipGetLastError() == hipSuccess ? SWITCH_OK : SWITCH_E_HIP;
+    }
+    // the first matmul records in the workspace that hbuf holds H
+    swl::GemmIO io1 = io;
+    io1.yflag = (int32_t*)(w + lo.hflag);
+    io1.yflag_value = 1;
     swl::prof_mark(P, s, "gemm1_relu");
     swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
-                                 hbuf, Cb * F, r.nkept, N, Cb, d, F, io, s);
+                                 hbuf, Cb * F, r.nkept, N, Cb, d, F, io1, s);
     // GEMM2 runs on the same tiles with or without the fused combine, so both
     // paths give the same expert outputs (the tile list of 256-row tiles
     // applies when the wide kernel is chosen)
@@ -392,7 +424,7 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
                             float grad_aux, const float* logits, const int32_t* expert_idx,
                             const float* gate, const int32_t* position, const uint8_t* drop_mask,
                             const int32_t* load, void* grad_x, float* grad_W_r, float* grad_b_r,
-                            void* grad_W_in, void* grad_W_out, void* ws, const void* fwd_ws,
+                            void* grad_W_in, void* grad_W_out, void* ws, void* fwd_ws,
                             hipStream_t s) {
   const switch_config& c = L->cfg;
   const int N = c.n_experts, d = c.d_model, F = c.d_ff;
@@ -403,10 +435,13 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
   int32_t* tok = (int32_t*)(w + lo.tok);
   void* gs = w + lo.gs;
   // the forward call's H when its workspace is given (the same tiles computed
-  // it, so it equals the recomputation bit for bit); else recomputed here
+  // it, so it equals the recomputation bit for bit); else recomputed here.  A
+  // forward that ran the fused FFN left no H: its flag word says so, and the
+  // recomputation then writes H into that workspace (decided on the device)
   const bool have_h = fwd_ws != nullptr;
-  void* hbuf = have_h ? (void*)((const char*)fwd_ws + layout_of(L, T).hbuf)
-                      : (void*)(w + lo.hbuf);
+  void* hbuf = have_h ? (void*)((char*)fwd_ws + layout_of(L, T).hbuf) : (void*)(w + lo.hbuf);
+  const int32_t* hflag_fwd = have_h ? (const int32_t*)((const char*)fwd_ws + layout_of(L, T).hflag)
+                                    : nullptr;
   void* ybuf = w + lo.ybuf;
   // its expert outputs too, when it kept them (decided on the device: the flag
   // word the forward's second matmul wrote)
@@ -432,11 +467,11 @@ switch_status backward_impl(switch_layer* L, const void* x, int64_t T, const voi
     swl::GemmIO io_rows = io;
     io_rows.tile_start = tiles;
     if (Cb > 0) {
-      if (!have_h) {
-        swl::prof_mark(P, s, "recompute_h");
-        swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
-                                     hbuf, Cb * F, nkept, N, Cb, d, F, io_rows, s);
-      }
+      swl::prof_mark(P, s, "recompute_h");
+      swl::GemmIO ioh = io_rows;
+      ioh.yskip = hflag_fwd;   // the forward stored H: the blocks exit at once
+      swl::launch_expert_gemm_bf16(swl::kRowsGather, true, nullptr, 0, L->W_in, (int64_t)F * d,
+                                   hbuf, Cb * F, nkept, N, Cb, d, F, ioh, s);
       // Y again, unless the forward call whose workspace is given kept it (its
       // flag word; the kernel's blocks then exit at once)
       swl::prof_mark(P, s, "recompute_y");
@@ -640,7 +675,7 @@ switch_status switch_backward(switch_layer* L, const void* x, int64_t T, const v
                               const float* gate, const int32_t* position,
                               const uint8_t* drop_mask, const int32_t* load, void* grad_x,
                               float* grad_W_r, float* grad_b_r, void* grad_W_in,
-                              void* grad_W_out, void* ws, size_t ws_bytes, const void* fwd_ws,
+                              void* grad_W_out, void* ws, size_t ws_bytes, void* fwd_ws,
                               size_t fwd_ws_bytes, void* stream) {
   if (!L || T < 0 || T > L->cfg.t_max) return SWITCH_E_INVALID;
   const switch_config& c = L->cfg;
@@ -666,6 +701,17 @@ switch_status switch_backward(switch_layer* L, const void* x, int64_t T, const v
   return backward_impl(L, x, T, grad_out, grad_aux, logits, expert_idx, gate, position, drop_mask,
                        load, grad_x, grad_W_r, grad_b_r, grad_W_in, grad_W_out, ws, fwd_ws,
                        (hipStream_t)stream);
+}
+
+switch_status switch_set_ffn_mode(switch_layer* L, int mode) {
+  if (!L || (mode != SWITCH_FFN_AUTO && mode != SWITCH_FFN_UNFUSED && mode != SWITCH_FFN_FUSED))
+    return SWITCH_E_INVALID;
+  if (mode == SWITCH_FFN_FUSED &&
+      (L->cfg.act_dtype != SWITCH_BF16 || top_k(L->cfg) != 1 ||
+       !swl::ffn_fused_shape_ok(L->cfg.d_model, L->cfg.d_ff)))
+    return SWITCH_E_UNSUPPORTED;
+  L->ffn_mode = mode;
+  return SWITCH_OK;
 }
 
 switch_status switch_set_keep_expert_out(switch_layer* L, int keep) {

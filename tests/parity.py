@@ -134,6 +134,17 @@ def _check_out_rows(res, spec, x_host, out_ref, E_ref, rows, tag):
     err = np.abs(out - out_ref)
     tol = 1e-2 * (1 + np.abs(out_ref))
     assert (err <= tol).all(), f"{tag} out err {(err - tol).max()}"
+    # the stricter bound the expert-output check implies: with the expert output
+    # y within delta = 2^-6 (|E| + rms(E)) of E, out = bf16(x + g y) (one fp32 FMA,
+    # one rounding to bf16) is within (2^-8 + 2^-23) (|ref| + g delta) + g delta
+    kept = ~drop
+    if kept.any():
+        Ek = E_ref[kept]
+        g = np.asarray(res["gate"][rows][kept], dtype=np.float64)[:, None]
+        delta = 2.0 ** -6 * (np.abs(Ek) + np.sqrt(np.mean(Ek ** 2)) + 1e-30)
+        strict = (2.0 ** -8 + 2.0 ** -23) * (np.abs(out_ref[kept]) + g * delta) + g * delta
+        over = err[kept] > strict
+        assert not over.any(), f"{tag} out beyond the expert-output bound: {over.sum()} elements"
     if "expert_out" in res:
         kept = ~drop
         if kept.any():

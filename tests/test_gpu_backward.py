@@ -273,6 +273,30 @@ def test_backward_reads_forward_h(B, top_k, T, N, d, F, c, seed):
     assert st == B.SWITCH_E_INVALID
 
 
+@pytest.mark.parametrize("T,N,d,F,c,seed", [
+    (1000, 8, 256, 512, 1.0, 141),
+    (2100, 16, 768, 512, 1.0, 142),
+])
+def test_backward_after_fused_forward(B, T, N, d, F, c, seed):
+    """A forward on the fused FFN leaves no H in its workspace; a backward given that
+    workspace recomputes H into it (its flag word says so) and gives the gradients of
+    a backward without the workspace, bit for bit, then reads H from it the next time."""
+    spec = S.Spec(f"bwd-fused-{T}", T=T, d=d, F=F, N=N, c=c, seed=seed)
+    host, layer, x, G, fwd, grads, f, g, G_bits = _run(B, spec)
+    print(f"[case] backward after fused forward {spec.name}", flush=True)
+    B.switch_set_ffn_mode(layer.handle, B.SWITCH_FFN_FUSED)
+    fused = layer.alloc(T)
+    layer.forward(x, T, fused)
+    for k in ("expert_idx", "gate", "position", "drop_mask", "logits", "load"):
+        assert np.array_equal(B.from_device(fused[k]), f[k]), k
+    for rnd in range(2):
+        again = layer.alloc_backward(T)
+        layer.backward(x, T, G, 1.0, fused, again, reuse_forward=True)
+        torch.cuda.synchronize()
+        for k in ("grad_x", "grad_W_r", "grad_b_r", "grad_W_in", "grad_W_out"):
+            assert np.array_equal(B.from_device(again[k]), g[k]), (rnd, k)
+
+
 @pytest.mark.parametrize("top_k,T,N,d,F,c,seed", [
     (1, 4096, 8, 768, 3072, 1.25, 131),   # Switch-Base: split-K second matmul with the combine
     (1, 1000, 8, 256, 512, 1.0, 132),     # 128-row tiles
@@ -288,6 +312,10 @@ def test_backward_reads_kept_y(B, top_k, T, N, d, F, c, seed):
     spec = S.Spec(f"bwd-keep-y-{top_k}-{T}", T=T, d=d, F=F, N=N, c=c, seed=seed)
     host, layer, x, G, fwd, grads, f, g, G_bits = _run(B, spec, top_k=top_k)
     print(f"[case] kept Y {spec.name}", flush=True)
+    # the plain forward's outputs equal the training forward's bit for bit on the
+    # two-launch FFN (a training forward always runs it)
+    B.switch_set_ffn_mode(layer.handle, B.SWITCH_FFN_UNFUSED)
+    layer.forward(x, T, fwd)
     keys = ("out", "expert_idx", "gate", "position", "drop_mask", "aux_loss", "logits", "load")
     plain = {k: B.from_device(fwd[k]) for k in keys}
     B.switch_set_keep_expert_out(layer.handle, True)

@@ -85,12 +85,20 @@ def _check_large(B, spec, tag):
     host, layer = _device_layer(B, spec)
     res = layer.forward_host(host["x"], debug=True)
     print(f"[case] {tag}: forward done, kept={int((res['drop_mask'] == 0).sum())}", flush=True)
-    # the default entry point (combine fused into the second matmul) gives the same bits
+    # the two-launch default entry point (combine fused into the second matmul)
+    # gives the same bits as the debug entry point
+    B.switch_set_ffn_mode(layer.handle, B.SWITCH_FFN_UNFUSED)
     plain = layer.forward_host(host["x"])
     for k in ("out", "expert_idx", "gate", "position", "drop_mask", "logits", "load"):
         assert np.array_equal(plain[k], res[k]), f"default path differs in {k}"
     assert plain["aux_loss"] == res["aux_loss"]
     del plain
+    # the automatic choice (the fused FFN where it applies): same routing, outputs
+    # checked against the oracle below
+    B.switch_set_ffn_mode(layer.handle, B.SWITCH_FFN_AUTO)
+    auto = layer.forward_host(host["x"])
+    for k in ("expert_idx", "gate", "position", "drop_mask", "logits", "load"):
+        assert np.array_equal(auto[k], res[k]), f"automatic path differs in {k}"
     parity.check_routing_stage(res, spec, tag)
     rng = np.random.default_rng(spec.seed)
     xf = S.to_f32(host["x"], spec.act)
@@ -105,6 +113,10 @@ def _check_large(B, spec, tag):
                 S.to_f32(S.expert_slice(spec, S.TENSOR_WOUT, int(e)), "bf16"))
 
     parity.check_output_rows(res, spec, host["x"], out_rows, weights, tag)
+    auto_res = {k: v for k, v in res.items() if k != "expert_out"}
+    auto_res["out"] = auto["out"]
+    parity.check_output_rows(auto_res, spec, host["x"], out_rows, weights, tag + "-auto")
+    del auto, auto_res
     # every dropped token passes through bit for bit
     drop = res["drop_mask"].astype(bool)
     assert np.array_equal(res["out"][drop], host["x"][drop])

@@ -35,6 +35,9 @@ def same_as_default_path(layer, x, res):
 def _run(B, spec, host=None, debug=True):
     host = host or S.host_inputs(spec)
     layer = B.SwitchLayer.from_host(spec, host)
+    # the debug entry point always runs the two-launch FFN; the bit-for-bit
+    # comparison with the default path holds on that path
+    B.switch_set_ffn_mode(layer.handle, B.SWITCH_FFN_UNFUSED)
     print(f"[case] {spec.name} T={spec.T} d={spec.d} F={spec.F} N={spec.N} c={spec.c}", flush=True)
     res = layer.forward_host(host["x"], debug=debug)
     if debug:
@@ -98,6 +101,74 @@ def test_more_than_2048_experts(B):
     for k in ("expert_idx", "gate", "position", "drop_mask", "load"):
         assert np.array_equal(B.from_device(bufs[k]), res[k]), k
     assert float(bufs["aux_loss"].item()) == res["aux_loss"]
+
+
+# ---------------------------------------------------------------- fused expert FFN
+
+def _run_fused(B, spec, host=None):
+    """Forward with the fused expert FFN (H on chip); the profiler's stage names
+    show that it ran."""
+    host = host or S.host_inputs(spec)
+    layer = B.SwitchLayer.from_host(spec, host)
+    B.switch_set_ffn_mode(layer.handle, B.SWITCH_FFN_FUSED)
+    print(f"[case] fused {spec.name} T={spec.T} d={spec.d} F={spec.F} N={spec.N} c={spec.c}",
+          flush=True)
+    B.switch_profile_enable(layer.handle, 1)
+    res = layer.forward_host(host["x"])
+    stages = [n for n, _ in B.switch_profile_read(layer.handle)]
+    B.switch_profile_enable(layer.handle, 0)
+    if spec.T > 0 and res["drop_mask"].min() == 0:   # some token reaches an expert
+        assert "ffn_fused" in stages and "gemm1_relu" not in stages, stages
+    return host, layer, res
+
+
+@pytest.mark.parametrize("T,N,d,F,c,seed", [
+    (1000, 8, 256, 512, 1.0, 41),      # one output tile per wave, two hidden chunks, ragged rows
+    (777, 5, 512, 768, 1.25, 42),      # two output tiles per wave, three chunks, odd expert count
+    (2100, 16, 768, 256, 1.0, 43),     # three output tiles per wave (Switch-Base width), one chunk
+    (1500, 12, 1024, 512, 1.0, 44),    # four output tiles per wave (Switch-Large width)
+    (130, 16, 256, 256, 0.5, 45),      # heavy overflow: dropped rows copied by the slot kernel
+    (64, 1, 256, 256, 1.0, 46),        # one expert
+    (9, 32, 256, 256, 2.0, 47),        # T < N: most experts empty
+    (3000, 300, 256, 512, 1.0, 48),    # logits router: scan and slot kernels build the tile list
+])
+def test_fused_ffn_shapes(B, T, N, d, F, c, seed):
+    spec = S.Spec(f"fused-{T}-{N}-{d}", T=T, d=d, F=F, N=N, c=c, seed=seed)
+    host, _, res = _run_fused(B, spec)
+    _full_check(spec, host, res, spec.name)
+    if N == 1:
+        assert np.all(res["gate"] == 1.0)
+
+
+def test_fused_ffn_capacity_zero(B):
+    spec = S.Spec("fused-c0", T=300, d=256, F=256, N=4, c=0.0, seed=49)
+    host, _, res = _run_fused(B, spec)
+    assert np.all(res["drop_mask"] == 1)
+    assert np.array_equal(res["out"], host["x"])
+
+
+def test_fused_ffn_switch_base_and_zipf(B):
+    for cfg in (2, 3):
+        spec = S.CONFIGS[cfg]
+        host, layer, res = _run_fused(B, spec)
+        _full_check(spec, host, res, f"fused-{spec.name}")
+        # routing does not depend on the FFN variant
+        B.switch_set_ffn_mode(layer.handle, B.SWITCH_FFN_UNFUSED)
+        two = layer.forward_host(host["x"])
+        for k in ROUTE_KEYS:
+            assert np.array_equal(two[k], res[k]), k
+        assert np.array_equal(two["out"][res["drop_mask"] == 1], res["out"][res["drop_mask"] == 1])
+
+
+def test_ffn_mode_arguments(B):
+    spec = S.Spec("mode", T=64, d=128, F=256, N=4, c=1.0, seed=50)
+    host = S.host_inputs(spec)
+    layer = B.SwitchLayer.from_host(spec, host)
+    assert B.lib.switch_set_ffn_mode(layer.handle, 3) == B.SWITCH_E_INVALID
+    assert B.lib.switch_set_ffn_mode(None, 0) == B.SWITCH_E_INVALID
+    # d = 128 is not a multiple of 256: the fused kernel does not take it
+    assert B.lib.switch_set_ffn_mode(layer.handle, B.SWITCH_FFN_FUSED) == B.SWITCH_E_UNSUPPORTED
+    assert B.lib.switch_set_ffn_mode(layer.handle, B.SWITCH_FFN_UNFUSED) == B.SWITCH_OK
 
 
 def test_switch_base_config_full(B):
