@@ -19,6 +19,8 @@
 //
 // bf16 path: CDNA4 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation, the
 // result rounded to bf16 (after the ReLU for GEMM1).  fp32 path: plain FMA.
+#include <type_traits>
+
 #include "epilogue.hpp"
 
 namespace swl {
@@ -117,35 +119,48 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
   };
   const int fr = lane & 31, fk = (lane >> 5) * 8;
 
-  fetch(0);
-  for (int k0 = 0; k0 < K; k0 += GB_BK) {
-    __syncthreads();
+  // the K loop for a wave whose first TV row tiles of 32 hold kept rows (the
+  // MFMAs of row tiles wholly past n_kept are left out; every wave still loads
+  // and stores its share of the operand tiles)
+  auto kloop = [&](auto tv_const) {
+    constexpr int TV = decltype(tv_const)::value;
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += GB_BK) {
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < LA; ++j)
-      *reinterpret_cast<u32x4*>(&As[(lrow + 32 * j) * GB_LDK + lcol]) = ra[j];
+      for (int j = 0; j < LA; ++j)
+        *reinterpret_cast<u32x4*>(&As[(lrow + 32 * j) * GB_LDK + lcol]) = ra[j];
 #pragma unroll
-    for (int j = 0; j < LB; ++j)
-      *reinterpret_cast<u32x4*>(&Bs[(lrow + 32 * j) * GB_LDK + lcol]) = rb[j];
-    __syncthreads();
-    fetch(k0 + GB_BK);
+      for (int j = 0; j < LB; ++j)
+        *reinterpret_cast<u32x4*>(&Bs[(lrow + 32 * j) * GB_LDK + lcol]) = rb[j];
+      __syncthreads();
+      fetch(k0 + GB_BK);
+      if (TV == 0) continue;
 #pragma unroll
-    for (int ks = 0; ks < GB_BK; ks += 16) {
-      bf16x8 a[TI], b[TJ];
+      for (int ks = 0; ks < GB_BK; ks += 16) {
+        bf16x8 a[TI], b[TJ];
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(
-            &As[(wm * (BM / 2) + i * 32 + fr) * GB_LDK + ks + fk]);
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(
-            &Bs[(wn * (BN / 2) + j * 32 + fr) * GB_LDK + ks + fk]);
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
+        for (int i = 0; i < TV; ++i)
+          a[i] = *reinterpret_cast<const bf16x8*>(
+              &As[(wm * (BM / 2) + i * 32 + fr) * GB_LDK + ks + fk]);
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+          b[j] = *reinterpret_cast<const bf16x8*>(
+              &Bs[(wn * (BN / 2) + j * 32 + fr) * GB_LDK + ks + fk]);
+#pragma unroll
+        for (int i = 0; i < TV; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+      }
     }
-  }
+  };
+  int tv = (rows_e - (m0 + wm * (BM / 2)) + 31) / 32;
+  tv = tv < 0 ? 0 : (tv > TI ? TI : tv);
+  static_assert(TI == 1 || TI == 2, "row tiles per wave");
+  if (tv >= TI) kloop(std::integral_constant<int, TI>{});
+  else if (TI == 2 && tv == 1) kloop(std::integral_constant<int, (TI == 2 ? 1 : 0)>{});
+  else kloop(std::integral_constant<int, 0>{});
 
   __syncthreads();  // every wave is done with the LDS operand tiles
   if (MODE == kRowsCombine)
@@ -193,6 +208,34 @@ __device__ __forceinline__ void sched_substep() {
   __builtin_amdgcn_sched_group_barrier(0x200, NW / 2, 0);
   __builtin_amdgcn_sched_group_barrier(0x020, NL / 2, 0);
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// The same interleave for a wave that multiplies only part of its row tiles
+// (NM MFMAs and NR fragment reads per K sub-step): MFMA / read pairs while both
+// last, then the stores and loads split over the last two MFMAs.
+template <int NM, int NR, int NW, int NL>
+__device__ __forceinline__ void sched_substep_n() {
+  constexpr int P = NM - 2 < NR ? NM - 2 : NR;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+  }
+  if (NM >= 2) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, (NW + 1) / 2, 0);  // LDS write
+    __builtin_amdgcn_sched_group_barrier(0x020, (NL + 1) / 2, 0);  // global load
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, NW / 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, NL / 2, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int TV, int NW, int NL>
+__device__ __forceinline__ void sched_substep_tv() {
+  if constexpr (TV == 4) sched_substep<NW, NL>();
+  else sched_substep_n<2 * TV, (TV > 0 ? TV + 2 : 0), NW, NL>();
 }
 
 constexpr int GW_BM = 256, GW_BN = 256;
@@ -291,50 +334,71 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   const int fr = lane & 31, fk = (lane >> 5) * 8;
   bf16x8 fa[2][TI], fb[2][TJ];
-  auto frags = [&](int f, int buf, int ks) {
+
+  // The K loop for a wave whose first TV row tiles of 32 hold kept rows: the
+  // MFMAs (and fragment reads) of row tiles wholly past n_kept are left out, so
+  // the short last M tile of an expert costs MFMA time for its kept rows only;
+  // every wave still loads and stores its share of the operand tiles and meets
+  // every barrier.
+  auto kloop = [&](auto tv_const) {
+    constexpr int TV = decltype(tv_const)::value;
+    auto frags = [&](int f, int buf, int ks) {
+      if (TV == 0) return;
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
-      fa[f][i] = *reinterpret_cast<const bf16x8*>(
-          &wlds[buf * STAGE + (wm * 128 + i * 32 + fr) * LDK + ks * 16 + fk]);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-      fb[f][j] = *reinterpret_cast<const bf16x8*>(
-          &wlds[buf * STAGE + (BM + wn * 64 + j * 32 + fr) * LDK + ks * 16 + fk]);
-  };
-  auto mfmas = [&](int f) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
+      for (int i = 0; i < TV; ++i)
+        fa[f][i] = *reinterpret_cast<const bf16x8*>(
+            &wlds[buf * STAGE + (wm * 128 + i * 32 + fr) * LDK + ks * 16 + fk]);
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
-  };
+        fb[f][j] = *reinterpret_cast<const bf16x8*>(
+            &wlds[buf * STAGE + (BM + wn * 64 + j * 32 + fr) * LDK + ks * 16 + fk]);
+    };
+    auto mfmas = [&](int f) {
+#pragma unroll
+      for (int i = 0; i < TV; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
+    };
 
-  gload(0, NL, 0);
-  gstore(0, NL, 0);
-  gload(0, NL, 1);
-  __syncthreads();
-  frags(0, 0, 0);
-  for (int t = 0; t < nk; ++t) {
-    const int cur = t & 1, nxt = cur ^ 1;
-    // buffer nxt was last read in step t - 1, before the barrier that ended it
-    frags(1, cur, 1);
-    gstore(0, 3, nxt);
-    gload(0, 3, t + 2);
-    mfmas(0);
-    sched_substep<3, 3>();
-    frags(0, cur, 2);
-    gstore(3, 6, nxt);
-    gload(3, 6, t + 2);
-    mfmas(1);
-    sched_substep<3, 3>();
-    frags(1, cur, 3);
-    gstore(6, 8, nxt);
-    gload(6, 8, t + 2);
-    mfmas(0);
-    sched_substep<2, 2>();
-    mfmas(1);
+    gload(0, NL, 0);
+    gstore(0, NL, 0);
+    gload(0, NL, 1);
     __syncthreads();
-    frags(0, nxt, 0);
+    frags(0, 0, 0);
+    for (int t = 0; t < nk; ++t) {
+      const int cur = t & 1, nxt = cur ^ 1;
+      // buffer nxt was last read in step t - 1, before the barrier that ended it
+      frags(1, cur, 1);
+      gstore(0, 3, nxt);
+      gload(0, 3, t + 2);
+      mfmas(0);
+      sched_substep_tv<TV, 3, 3>();
+      frags(0, cur, 2);
+      gstore(3, 6, nxt);
+      gload(3, 6, t + 2);
+      mfmas(1);
+      sched_substep_tv<TV, 3, 3>();
+      frags(1, cur, 3);
+      gstore(6, 8, nxt);
+      gload(6, 8, t + 2);
+      mfmas(0);
+      sched_substep_tv<TV, 2, 2>();
+      mfmas(1);
+      __syncthreads();
+      frags(0, nxt, 0);
+    }
+  };
+  int tv = (rows_e - (m0 + wm * 128) + 31) / 32;
+  tv = tv < 0 ? 0 : (tv > TI ? TI : tv);
+  static_assert(TI == 4, "row tiles per wave");
+  switch (tv) {
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    default: kloop(std::integral_constant<int, 0>{}); break;
   }
 
   __syncthreads();  // every wave is done with the LDS operand buffers

@@ -132,11 +132,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 // Dispatch by index (bf16 path): the expert matmuls read the rows of x in
 // place, so dispatch only finalises the routing and records, for every kept
 // assignment, which token sits in slot (e, position): tok[e * C + position] = t.
-// One wave per 64 assignments: lane i finalises assignment 64 w + i (position
-// = chunk offset + in-chunk rank, drop = position >= C).  With the fused
-// combine (k = 1) a dropped token leaves the layer unchanged: the wave then
-// copies the row of each dropped token among its 64 from x to out, its 16-byte
-// pieces spread over the lanes, and the combine never touches it.
+// A block of four waves takes 64 assignments: in every wave lane i derives
+// assignment 64 b + i (position = chunk offset + in-chunk rank, drop =
+// position >= C), and wave 0 stores the results.  With the fused combine
+// (k = 1) a dropped token leaves the layer unchanged: its row is copied from x
+// to out here, the r-th dropped row of the 64 by wave r % 4, in 16-byte pieces
+// spread over the lanes, and the combine never touches it.
 __global__ __launch_bounds__(256) void dispatch_index_kernel(const uint4* __restrict__ x, int64_t T,
                                                              int k, int row_vec16,
                                                              const int32_t* __restrict__ expert_idx,
@@ -148,49 +149,32 @@ __global__ __launch_bounds__(256) void dispatch_index_kernel(const uint4* __rest
                                                              int32_t* __restrict__ tok,
                                                              bool copy_dropped,
                                                              uint4* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int64_t a0 = (((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6) * kWave;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t a0 = (int64_t)blockIdx.x * kWave;
   const int64_t a = a0 + lane;
+  if (w > 0 && !copy_dropped) return;   // uniform: only wave 0 has work then
   bool dropped = false;
   if (a < T * k) {
     const int64_t t = a / k;
     const int32_t e = expert_idx[a];
     const int32_t pos = offsets[(t / chunk) * N + e] + rank_local[a];
     dropped = (int64_t)pos >= C;
-    position[a] = pos;
-    drop_mask[a] = dropped ? 1 : 0;
-    if (!dropped) tok[(int64_t)e * C + pos] = (int32_t)t;
+    if (w == 0) {
+      position[a] = pos;
+      drop_mask[a] = dropped ? 1 : 0;
+      if (!dropped) tok[(int64_t)e * C + pos] = (int32_t)t;
+    }
   }
-  if (!copy_dropped) return;  // uniform: only with k = 1, where assignment a is token a
-  // the wave's dropped tokens, four rows at a time: every lane issues its loads
-  // of all four rows (16-byte pieces c = lane + 64 i) before any store
+  if (!copy_dropped) return;   // k = 1 from here on: assignment a is token a
   uint64_t m = __ballot(dropped);
-  while (m) {
-    int64_t row[4];
-    int n = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      row[j] = m ? (a0 + __builtin_ctzll(m)) * row_vec16 : 0;
-      n += m ? 1 : 0;
-      m &= m - 1;
-    }
-    for (int c0 = 0; c0 < row_vec16; c0 += 4 * kWave) {
-      uint4 v[4][4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = c0 + lane + kWave * i;
-          if (j < n && c < row_vec16) v[j][i] = x[row[j] + c];
-        }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = c0 + lane + kWave * i;
-          if (j < n && c < row_vec16) out[row[j] + c] = v[j][i];
-        }
-    }
+  for (int r = 0; m; ++r) {
+    const int64_t t = a0 + __builtin_ctzll(m);
+    m &= m - 1;
+    if ((r & 3) != w) continue;
+    const uint4* src = x + t * row_vec16;
+    uint4* dst = out + t * row_vec16;
+#pragma unroll 4
+    for (int c = lane; c < row_vec16; c += kWave) dst[c] = src[c];
   }
 }
 
@@ -229,8 +213,8 @@ void launch_dispatch_index(const void* x, int64_t T, int k, int row_bytes,
                            int32_t* position, uint8_t* drop_mask, int32_t* tok, bool copy_dropped,
                            void* out, hipStream_t s) {
   if (T == 0) return;
-  const int64_t waves = (T * k + kWave - 1) / kWave;
-  launch_k(dispatch_index_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
+  const int64_t groups = (T * k + kWave - 1) / kWave;   // 64 assignments per block
+  launch_k(dispatch_index_kernel, dim3((unsigned)groups), dim3(256), 0, s,
                      (const uint4*)x, T, k, row_bytes / 16, expert_idx, rank_local, offsets, N,
                      chunk, C, position, drop_mask, tok, copy_dropped && k == 1, (uint4*)out);
 }
