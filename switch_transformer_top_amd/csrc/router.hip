@@ -612,21 +612,34 @@ __global__ __launch_bounds__(64 * WAVES) void router_tok_kernel(
 // splits W into its three bf16 planes once and stores x and the planes to LDS
 // (double buffered, one barrier per step); every x fragment then serves three
 // MFMAs (one per plane) and every plane fragment four token tiles.  LDS rows
-// are 32 elements (64 bytes) with the 16-byte chunk c of row r stored at
-// c ^ ((r >> 2) & 3): the 16 rows one fragment read touches per chunk fall on
-// 16 distinct 16-byte slots of the 256-byte bank space.
+// hold the 32 elements of a step plus one 16-byte chunk of padding (80 bytes, an
+// odd number of chunks), so consecutive rows of one chunk fall on distinct bank
+// groups; the two buffers fill the 160 KiB of LDS.  (Unpadded 64-byte rows with
+// XOR-swizzled chunks measured bank conflicts in 92% of the LDS cycles.)
 // Tile order: block b takes expert tile b % n_et and token tile b / n_et, so
 // with 8 expert tiles each XCD (b % 8) keeps one 2 MB slice of W_r in its L2
 // while it walks the tokens.
 // ---------------------------------------------------------------------------
-constexpr int RG_BT = 256, RG_BE = 256, RG_BK = 32;
-constexpr int RG_XS = RG_BT * RG_BK;            // x tile (elements)
-constexpr int RG_PS = RG_BE * RG_BK;            // one weight plane
+constexpr int RG_BT = 256, RG_BE = 256, RG_BK = 32, RG_LD = RG_BK + 8;
+constexpr int RG_XS = RG_BT * RG_LD;            // x tile (elements)
+constexpr int RG_PS = RG_BE * RG_LD;            // one weight plane
 constexpr int RG_STAGE = RG_XS + 3 * RG_PS;     // one LDS buffer (elements)
-constexpr size_t kRouterGemmLds = (size_t)2 * RG_STAGE * sizeof(uint16_t);  // 128 KiB
+constexpr size_t kRouterGemmLds = (size_t)2 * RG_STAGE * sizeof(uint16_t);  // 160 KiB
 
-// element offset of 16-byte chunk c (0..3) of row r in a swizzled [rows][32] tile
-__device__ __forceinline__ int rg_at(int r, int c) { return r * RG_BK + ((c ^ ((r >> 2) & 3)) << 3); }
+// element offset of 16-byte chunk c (0..3) of row r in a [rows][32 + 8] tile
+__device__ __forceinline__ int rg_at(int r, int c) { return r * RG_LD + (c << 3); }
+
+// split3 on a pair of weights with the packed conversion (two values per
+// v_cvt_pk_bf16_f32): the same three pieces, as packed bf16 pairs (first value
+// in the low half)
+__device__ __forceinline__ void split3x2(float a, float b, uint32_t& hi, uint32_t& mid,
+                                         uint32_t& lo) {
+  hi = f32x2_to_bf16x2_bits(a, b);
+  const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xFFFF0000u);
+  mid = f32x2_to_bf16x2_bits(ra, rb);
+  const float qa = ra - __uint_as_float(mid << 16), qb = rb - __uint_as_float(mid & 0xFFFF0000u);
+  lo = f32x2_to_bf16x2_bits(qa, qb);
+}
 
 __global__ __launch_bounds__(512, 1) void router_gemm_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ W_r, const float* __restrict__ b_r,
@@ -644,8 +657,8 @@ __global__ __launch_bounds__(512, 1) void router_gemm_kernel(
   int64_t tr = t0 + lr;
   tr = tr < T ? tr : T - 1;  // rows past T: any valid row, never stored
   const uint16_t* xsrc = x + tr * d + lh * 16;
-  const bool wok = e0 + lr < N;
-  const float* wsrc = W_r + (int64_t)(wok ? e0 + lr : 0) * d + lh * 16;
+  // expert rows past N read row 0: their logits are computed and never stored
+  const float* wsrc = W_r + (int64_t)(e0 + lr < N ? e0 + lr : 0) * d + lh * 16;
   const int nk = d / RG_BK;
   // one register stage: step t + 1 waits in xr / wr while step t is multiplied
   u32x4 xr[2];
@@ -657,26 +670,24 @@ __global__ __launch_bounds__(512, 1) void router_gemm_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) wr[q] = *reinterpret_cast<const float4*>(wsrc + k + 4 * q);
   };
-  auto split_store = [&](int buf) {
-    uint16_t* xs = rlds + buf * RG_STAGE;
-    uint16_t* ps = xs + RG_XS;
+  // one half (q = 0, 1: 8 weights, one 16-byte chunk per plane) of the loaded
+  // step, split into its three planes and stored at row lr of buffer `pn`
+  auto split_half = [&](uint16_t* pn, int q) {
+    const float4 a = wr[2 * q], b = wr[2 * q + 1];
+    const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h4[4], m4[4], l4[4];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) *reinterpret_cast<u32x4*>(xs + rg_at(lr, 2 * lh + q)) = xr[q];
+    for (int i = 0; i < 4; ++i) split3x2(w[2 * i], w[2 * i + 1], h4[i], m4[i], l4[i]);
+    const u32x4 hi = {h4[0], h4[1], h4[2], h4[3]}, mid = {m4[0], m4[1], m4[2], m4[3]},
+                lo = {l4[0], l4[1], l4[2], l4[3]};
+    const int at = rg_at(lr, 2 * lh + q);
+    *reinterpret_cast<u32x4*>(pn + at) = hi;
+    *reinterpret_cast<u32x4*>(pn + RG_PS + at) = mid;
+    *reinterpret_cast<u32x4*>(pn + 2 * RG_PS + at) = lo;
+  };
+  auto store_x = [&](uint16_t* xn) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {   // 8 weights -> one 16-byte chunk per plane
-      const float4 a = wr[2 * q], b = wr[2 * q + 1];
-      float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      if (!wok) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = 0.f;
-      }
-      bf16x8 hi, mid, lo;
-      split3(w, hi, mid, lo);
-      const int at = rg_at(lr, 2 * lh + q);
-      *reinterpret_cast<bf16x8*>(ps + at) = hi;
-      *reinterpret_cast<bf16x8*>(ps + RG_PS + at) = mid;
-      *reinterpret_cast<bf16x8*>(ps + 2 * RG_PS + at) = lo;
-    }
+    for (int q = 0; q < 2; ++q) *reinterpret_cast<u32x4*>(xn + rg_at(lr, 2 * lh + q)) = xr[q];
   };
 
   floatx16 acc[2][4];
@@ -687,49 +698,85 @@ __global__ __launch_bounds__(512, 1) void router_gemm_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
   const int fr = lane & 31, fc = lane >> 5;
-  auto compute = [&](int buf) {
-    const uint16_t* xs = rlds + buf * RG_STAGE;
+  // the 24 MFMAs of K sub-step s (16 k) from buffer xs: x fragments of the
+  // wave's four token tiles, then per plane (smallest pieces first: lo, mid,
+  // hi) the fragments of its two expert tiles
+  auto substep = [&](const uint16_t* xs, int s) {
     const uint16_t* ps = xs + RG_XS;
+    const int c = 2 * s + fc;
+    bf16x8 xb[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int c = 2 * s + fc;
-      bf16x8 xb[4];
+    for (int i = 0; i < 4; ++i)
+      xb[i] = *reinterpret_cast<const bf16x8*>(xs + rg_at(wt * 128 + i * 32 + fr, c));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xb[i] = *reinterpret_cast<const bf16x8*>(xs + rg_at(wt * 128 + i * 32 + fr, c));
-      // smallest pieces first: lo, mid, hi
+    for (int p = 2; p >= 0; --p) {
+      bf16x8 wp[2];
 #pragma unroll
-      for (int p = 2; p >= 0; --p) {
-        bf16x8 wp[2];
+      for (int j = 0; j < 2; ++j)
+        wp[j] = *reinterpret_cast<const bf16x8*>(ps + p * RG_PS + rg_at(we * 64 + j * 32 + fr, c));
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          wp[j] = *reinterpret_cast<const bf16x8*>(ps + p * RG_PS +
-                                                   rg_at(we * 64 + j * 32 + fr, c));
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wp[j], xb[i], acc[j][i], 0, 0, 0);
-      }
+        for (int i = 0; i < 4; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wp[j], xb[i], acc[j][i], 0, 0, 0);
     }
+  };
+  // Issue order inside a sub-step: the x and lo-plane fragment reads, then each
+  // MFMA followed by two VALU instructions of the split of the next step's
+  // weights (which run while the matrix pipe works), the other planes'
+  // fragment reads ahead of their MFMAs, and the plane stores at the end.
+  auto schedule = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // LDS read: x, lo plane
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
+      }
+      if (p < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next plane's reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x200, 5, 0);   // LDS write
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   gload(0);
-  split_store(0);
+  store_x(rlds);
+  split_half(rlds + RG_XS, 0);
+  split_half(rlds + RG_XS, 1);
   gload(1);
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
-    // buffer (t + 1) & 1 was last read in step t - 1, before the barrier that
-    // ended it; the registers then take step t + 2
-    if (t + 1 < nk) split_store((t + 1) & 1);
+    // step t from buffer t & 1; step t + 1 (in the registers) into the other
+    // buffer, last read in step t - 1 before the barrier that ended it, its
+    // split interleaved with step t's MFMAs; then the registers take step t + 2
+    // (after the last step the copy goes to a buffer nobody reads)
+    const uint16_t* xs = rlds + (t & 1) * RG_STAGE;
+    uint16_t* xn = rlds + ((t + 1) & 1) * RG_STAGE;
+    store_x(xn);
+    substep(xs, 0);
+    split_half(xn + RG_XS, 0);
+    schedule();
+    substep(xs, 1);
+    split_half(xn + RG_XS, 1);
+    schedule();
     gload(t + 2);
-    compute(t & 1);
     __syncthreads();
   }
 
   // logits + bias: lane l of tile (j, i) holds token wt*128 + 32 i + l % 32 and
   // experts we*64 + 32 j + 8 q + 4 (l / 32) + (0..3), q < 4; vec: 16-byte stores
   // (h 16-byte aligned and N a multiple of 4)
+  float bias[2][4][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + we * 64 + j * 32 + 8 * q + 4 * fc + u;
+        bias[j][q][u] = (b_r && e < N) ? b_r[e] : 0.f;
+      }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t t = t0 + wt * 128 + i * 32 + fr;
@@ -742,8 +789,7 @@ __global__ __launch_bounds__(512, 1) void router_gemm_kernel(
         const int e = e0 + we * 64 + j * 32 + 8 * q + 4 * fc;
         float v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          v[u] = acc[j][i][4 * q + u] + ((b_r && e + u < N) ? b_r[e + u] : 0.f);
+        for (int u = 0; u < 4; ++u) v[u] = acc[j][i][4 * q + u] + bias[j][q][u];
         if (vec && e + 3 < N) {
           *reinterpret_cast<float4*>(hrow + e) = make_float4(v[0], v[1], v[2], v[3]);
         } else {
