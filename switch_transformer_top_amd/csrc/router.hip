@@ -886,6 +886,10 @@ __global__ __launch_bounds__(256) void route_rows_kernel(const float* __restrict
 // sums of p over the wave's rows (fp64).  The four waves' sums are then added
 // as (w0 + w2) + (w1 + w3).  Same statistics as route_rows_kernel; the P sums
 // are the same terms added in another fixed order.
+// word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
+// offsets checked against the record count
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 template <int NPL>
 __global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __restrict__ h,
                                                              int64_t T, int N, int k,
@@ -897,35 +901,52 @@ __global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __rest
   extern __shared__ double rr_red[];  // [2][N] partial sums, then N ints of counts
   __shared__ int32_t s_idx[RR_ROWS * kMaxTopK];
   int32_t* cnt = reinterpret_cast<int32_t*>(rr_red + 2 * N);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: row bases in SGPRs
   const int64_t t0 = (int64_t)blockIdx.x * RR_ROWS;
   const int rows = (int)((T - t0) < RR_ROWS ? (T - t0) : RR_ROWS);
   double pacc[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) pacc[i] = 0.0;
 
-  for (int r = wave; r < rows; r += 4) {
-    const float* row = h + (t0 + r) * N;
-    float v[NPL];
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + kWave * i;
-      v[i] = e < N ? row[e] : -__builtin_huge_valf();
-    }
-    float m = -__builtin_huge_valf();
-    int mi = 0x7fffffff;
+  // row r + 4 is loaded while row r is worked on: two register buffers, the loop
+  // taken twice per pass so that no copy between them waits for the loads
+  auto load_row = [&](float (&v)[NPL], int r) {
+    // buffer loads over the one row: a uniform base, one lane offset, and reads
+    // past the row's N values return 0 without touching memory
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(h + (t0 + r) * N), (short)0, N * 4, kBufferRsrcWord3);
+    // the lane's byte offset, kept opaque so that the compiler folds each
+    // element's 256 i into the instruction instead of holding NPL offsets live
+    int off = lane * 4;
+    asm volatile("" : "+v"(off));
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
-      if (lane + kWave * i < N && (v[i] > m || mi == 0x7fffffff)) {
-        m = v[i];
-        mi = lane + kWave * i;  // ascending within a lane: the first (lowest) index wins
-      }
-    wave_argmax(m, mi);
-    double sum = 0.0;
+      v[i] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rs, off + 256 * (i & 15), 4096 * (i >> 4), 0));
+  };
+  auto do_row = [&](float (&v)[NPL], float (&vn)[NPL], int r) {
+    load_row(vn, r + 4 < rows ? r + 4 : r);  // the last one reads its own row again
+    // experts past N (read as 0) out of every choice and sum; done here, not at
+    // the load, so that only this row's loads are waited for
+    if (N < kWave * NPL) {
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) sum += (double)expf(v[i] - m);
-    sum = wave_sum_f64(sum);
-    const double inv = 1.0 / sum;
+      for (int i = 0; i < NPL; ++i)
+        if (lane + kWave * i >= N) v[i] = -__builtin_huge_valf();
+    }
+    // lane maximum, the first (lowest) index among equals: a strict > over
+    // ascending i; a lane with no expert (lane >= N) offers -inf at index lane,
+    // which loses to every expert's index on a tie
+    float m = v[0];
+    int mi = 0;
+#pragma unroll
+    for (int i = 1; i < NPL; ++i)
+      if (v[i] > m) {
+        m = v[i];
+        mi = i;
+      }
+    mi = lane + kWave * mi;
+    wave_argmax(m, mi);
     float m2 = -__builtin_huge_valf();
     int mi2 = 0x7fffffff;
     if (k > 1) {
@@ -947,8 +968,18 @@ __global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __rest
         }
       }
     }
+    // each exponential once: the terms replace the logits (the same values, added
+    // in the same order, as evaluating them again for the sums of p)
+    double sum = 0.0;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) pacc[i] += (double)expf(v[i] - m) * inv;
+    for (int i = 0; i < NPL; ++i) {
+      v[i] = expf(v[i] - m);
+      sum += (double)v[i];
+    }
+    sum = wave_sum_f64(sum);
+    const double inv = 1.0 / sum;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) pacc[i] += (double)v[i] * inv;
     if (lane == 0) {
       expert_idx[(t0 + r) * k] = mi;
       gate[(t0 + r) * k] = (float)inv;
@@ -959,6 +990,13 @@ __global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __rest
         s_idx[r * k + 1] = mi2;
       }
     }
+  };
+  float va[NPL], vb[NPL];
+  if (wave < rows) load_row(va, wave);
+  for (int r = wave; r < rows; r += 8) {
+    do_row(va, vb, r);
+    if (r + 4 >= rows) break;
+    do_row(vb, va, r + 4);
   }
   // (w0 + w2) + (w1 + w3)
   if (wave >= 2) {

@@ -326,10 +326,24 @@ def test_backward_reads_kept_y(B, top_k, T, N, d, F, c, seed):
     for k in keys:
         assert np.array_equal(B.from_device(kept[k]), plain[k]), k
     again = layer.alloc_backward(T)
+    B.switch_profile_enable(layer.handle, 1)
     layer.backward(x, T, G, 1.0, kept, again, reuse_forward=True)
+    kept_stages = dict(B.switch_profile_read(layer.handle))
+    B.switch_profile_enable(layer.handle, 0)
     torch.cuda.synchronize()
     for k in ("grad_x", "grad_W_r", "grad_b_r", "grad_W_in", "grad_W_out"):
         assert np.array_equal(B.from_device(again[k]), g[k]), k
+    if top_k == 1 and T * d * F >= 4096 * 768 * 3072:
+        # the gradients are the same either way, so tell a read of the kept Y from
+        # a recomputation by time: the recomputation is a whole second matmul
+        # (tens of microseconds here), while with Y kept its blocks exit at once
+        layer.forward(x, T, fwd)   # keeps nothing: the shared workspace's flag is cleared
+        B.switch_profile_enable(layer.handle, 1)
+        layer.backward(x, T, G, 1.0, fwd, again, reuse_forward=True)
+        fresh_stages = dict(B.switch_profile_read(layer.handle))
+        B.switch_profile_enable(layer.handle, 0)
+        assert kept_stages["recompute_y"] < 0.5 * fresh_stages["recompute_y"], \
+            (kept_stages["recompute_y"], fresh_stages["recompute_y"])
     # the same workspace after a forward of another input that keeps nothing: its
     # buffer still holds the first input's Y, and the backward must recompute Y
     if top_k == 1:
