@@ -10,8 +10,9 @@ Switch layer, T=131072 tokens, d_model=2048, d_ff=6144, capacity factor 1.0
 (about 103 GB of bf16 expert weights).
 
 Timing: W untimed steps, then K steps each timed with HIP events on the
-library's stream after a 512 MiB write that evicts L2 and the Infinity Cache
-(cold caches); the value is T / the median step time.  Then K warm steps, a
+library's stream after a 512 MiB read that evicts L2 and the Infinity Cache
+(cold caches, and no dirty lines left to write back); the value is T / the
+median step time.  Then K warm steps, a
 profiled pass whose per-kernel event means give each kernel's roofline, a
 pass of the unfused path that times the stand-alone combine, the attainable
 peaks of the box (an MFMA loop and HBM streams), and the CPU oracle on the
@@ -110,7 +111,11 @@ def roofline_entry(stage: str, work: dict, ms: float) -> dict:
 STAGE_KERNEL = {"gemm1_relu": (r"gemm_bf16_\w+<(\d+, \d+, )?true, 1(, false)?>", "gemm.hip"),
                 "gemm2": (r"gemm_bf16_\w+<(\d+, \d+, )?false, 0(, false)?>", "gemm.hip"),
                 "gemm2_combine": (r"gemm_bf16_\w+<(\d+, \d+, )?false, 2(, false)?>", "gemm.hip"),
-                "router": (r"router_\w+(<.*>)?", "router.hip"),
+                "router": (r"router_(small|tok)_kernel(<.*>)?", "router.hip"),
+                "router_logits": (r"router_gemm_kernel", "router.hip"),
+                "route_rows": (r"route_rows\w*(<.*>)?", "router.hip"),
+                "route_scan": (r"route_scan_kernel", "assign.hip"),
+                "ffn_fused": (r"ffn_fused_kernel(<.*>)?", "ffn.hip"),
                 "dispatch": (r"dispatch_index_kernel", "move.hip"),
                 "assign": (r"assign_kernel", "assign.hip"),
                 "combine": (r"combine_kernel<.*>", "move.hip")}
@@ -250,6 +255,30 @@ def cpu_baseline(spec, host, budget_s: float, top_k: int = 1) -> dict:
 
 # ------------------------------------------------------------------ attainable peaks
 
+class CacheEvict:
+    """Reads a 512 MiB buffer that is never written (twice the Infinity Cache,
+    64x an XCD's L2) with the streaming read probe: what the next step reads
+    then comes from HBM, and no dirty line is left to be written back."""
+
+    def __init__(self, torch, dev, stream):
+        import ctypes
+        from switch_transformer_top_amd import build as lb
+        self.L = ctypes.CDLL(lb.PEAKS_LIB)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        self.L.peak_hbm_read.argtypes = [vp, i64, vp, vp]
+        self.L.peak_stream_blocks.restype = ctypes.c_int
+        self.nbytes = 512 << 20
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=dev)
+        self.sink = torch.empty(max(1, self.L.peak_stream_blocks()), dtype=torch.int32,
+                                device=dev)
+        self.stream = stream
+
+    def __call__(self):
+        if self.L.peak_hbm_read(self.buf.data_ptr(), self.nbytes, self.sink.data_ptr(),
+                                self.stream) != 0:
+            raise RuntimeError("cache-evicting read failed to launch")
+
+
 def attainable_peaks(torch, dev, stream) -> dict:
     """What the box reaches with plain probes (best of five launches each): bf16 MFMA
     (v_mfma_f32_32x32x16_bf16 loop, register operands), and HBM read, write and copy
@@ -294,8 +323,8 @@ def attainable_peaks(torch, dev, stream) -> dict:
             "hbm_write_gbs": round(nbytes / (t_write * 1e-3) / 1e9, 1),
             "hbm_copy_gbs": round(2 * half / (t_copy * 1e-3) / 1e9, 1),
             "probe": "best of 5 launches; MFMA: 8 blocks of 4 waves per CU, 4 independent "
-                     "32x32x16 bf16 chains per wave; HBM: 4 GiB streams (copy: 2 GiB read "
-                     "+ 2 GiB written, counted as 4 GiB)"}
+                     "32x32x16 bf16 chains per wave; HBM: 4 GiB streams, each XCD over its own "
+                     "contiguous eighth (copy: 2 GiB read + 2 GiB written, counted as 4 GiB)"}
 
 
 # stages whose HBM traffic is almost all reads (weights, tokens, logits): their
@@ -413,22 +442,23 @@ def main():
         print(json.dumps({"profile_steps": args.profile_steps, "workload": workload}), flush=True)
         return
 
-    # timed region: K steps, each after a 512 MiB write that evicts the weights, x
-    # and the workspace from L2 and the Infinity Cache; only the step is timed
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # timed region: K steps, each after a 512 MiB read that evicts the weights, x
+    # and the workspace from L2 and the Infinity Cache (a read leaves no dirty
+    # lines whose write-back would land inside the step); only the step is timed
+    evict = CacheEvict(torch, dev, sp)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for a, b in ev:
-        flush.fill_(1)
+        evict()
         a.record(stream)
         step()
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     cold = [a.elapsed_time(b) for a, b in ev]
-    del flush
+    del evict
 
     # warm: the same K steps back to back (weights and x may stay in the caches, as
     # between the layers of one model's forward), each timed alone
@@ -525,7 +555,7 @@ def main():
                    "n_experts": spec.N, "capacity_factor": spec.c, "capacity": C,
                    "router": "fp32", "experts": spec.expert, "parallelism": "single-gpu",
                    "ffn": "fused" if "ffn_fused" in stage_ms else "two launches",
-                   "timing": "median of K steps, each after a 512 MiB cache-evicting write "
+                   "timing": "median of K steps, each after a 512 MiB cache-evicting read "
                              "(cold caches)"},
         "roofline": rooflines[dominant],
         "cpu_baseline": None,
