@@ -75,6 +75,8 @@ def test_tiny_fp32_config(B):
     (8192, 256, 256, 256, 1.0, 30),    # capacity 32 with more tiles than CUs: 64-row tiles
     (1000, 520, 128, 256, 1.0, 31),    # logits router: three expert tiles (the last of 8), a
                                        # 256-token block whose second 128-token group is partial
+    (1300, 1500, 128, 128, 2.0, 35),   # 1024 < N < 2048: the 32-per-lane statistics with the
+                                       # experts past N masked, a ragged last expert tile
 ])
 def test_bf16_ragged_shapes(B, T, N, d, F, c, seed):
     spec = S.Spec(f"bf16-{T}-{N}", T=T, d=d, F=F, N=N, c=c, seed=seed)
