@@ -12,7 +12,8 @@ Switch layer, T=131072 tokens, d_model=2048, d_ff=6144, capacity factor 1.0
 Timing: W untimed steps, then K steps each timed with HIP events on the
 library's stream after a 512 MiB read that evicts L2 and the Infinity Cache
 (cold caches, and no dirty lines left to write back); the value is T / the
-median step time.  Then K warm steps, a
+median step time.  The same K steps after a 512 MiB write each are reported
+beside it.  Then K warm steps, a
 profiled pass whose per-kernel event means give each kernel's roofline, a
 pass of the unfused path that times the stand-alone combine, the attainable
 peaks of the box (an MFMA loop and HBM streams), and the CPU oracle on the
@@ -192,6 +193,31 @@ def _oracle_whole(oracle, spec, host, top_k, nt, budget_s):
             return reps, el
 
 
+def _oracle_prefix_single(oracle, spec, host, top_k, xf, r, tk, jk, ek, budget_s):
+    """Seconds per token of the prefix sample on one thread: the routing of up to
+    256 tokens and the FFN of the first experts' assignments, each within the budget."""
+    n1 = min(len(xf), 256)
+    t0 = time.perf_counter()
+    h = oracle.logits(xf[:n1], host["W_r"], host["b_r"], nthreads=1)
+    oracle.route_topk(h, top_k, spec.c, spec.capacity_override, spec.alpha, nthreads=1)
+    t_route = (time.perf_counter() - t0) / n1
+    n_ffn, t_ffn, i = 0, 0.0, 0
+    while i < len(tk) and t_ffn < budget_s:
+        j = i + 1
+        while j < len(tk) and ek[j] == ek[i] and j - i < 8:
+            j += 1
+        e = int(ek[i])
+        W_in = S.to_f32(S.expert_slice(spec, S.TENSOR_WIN, e), spec.expert)[None]
+        W_out = S.to_f32(S.expert_slice(spec, S.TENSOR_WOUT, e), spec.expert)[None]
+        t1 = time.perf_counter()
+        oracle.combine(xf[tk[i:j]], np.zeros(j - i, np.int32), r["gate"][tk[i:j], jk[i:j]],
+                       np.zeros(j - i, np.uint8), W_in, W_out, nthreads=1)
+        t_ffn += time.perf_counter() - t1
+        n_ffn += j - i
+        i = j
+    return t_route + top_k * t_ffn / max(1, n_ffn)
+
+
 def cpu_baseline(spec, host, budget_s: float, top_k: int = 1) -> dict:
     """The oracle as it stands on every host core the process may use, over a bounded
     sample; one thread as well for the workloads the oracle runs whole."""
@@ -244,7 +270,12 @@ def cpu_baseline(spec, host, budget_s: float, top_k: int = 1) -> dict:
         i = j
         del W_in, W_out
     per_token = t_route / n_r + top_k * t_ffn / n_ffn
+    single = None
+    if nt > 1:
+        single = round(1.0 / _oracle_prefix_single(oracle, spec, host, top_k, xf, r, tk, jk, ek,
+                                                   budget_s / 4), 2)
     return {"value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": nt,
+            "single_thread_value": single,
             "kind": "oracle",
             "sample": f"{spec.name}: logits and routing of the first {n_r} tokens "
                       f"({t_route:.1f} s) plus the expert FFN of {n_ffn} of their kept "
@@ -372,6 +403,15 @@ def spec_id_of(spec) -> int:
     return 0
 
 
+def load_summary(load, C: int) -> dict:
+    """The realised per-expert loads (assignments before the capacity cut)."""
+    load = np.asarray(load, dtype=np.int64)
+    return {"min": int(load.min()), "p50": float(np.percentile(load, 50)),
+            "p99": float(np.percentile(load, 99)), "max": int(load.max()),
+            "empty_experts": int((load == 0).sum()), "over_capacity": int((load > C).sum()),
+            "top8": [int(v) for v in np.sort(load)[::-1][:8]]}
+
+
 def median(v):
     return float(np.median(np.asarray(v, dtype=np.float64)))
 
@@ -459,6 +499,19 @@ def main():
     wall = time.perf_counter() - t_wall
     cold = [a.elapsed_time(b) for a, b in ev]
     del evict
+
+    # the same K steps, each after a 512 MiB write instead (the eviction the
+    # measurement plan names; the write-back of its dirty lines lands inside the
+    # step), reported beside the value
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for a, b in ev:
+        flush.fill_(1)
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    cold_write = [a.elapsed_time(b) for a, b in ev]
+    del flush
 
     # warm: the same K steps back to back (weights and x may stay in the caches, as
     # between the layers of one model's forward), each timed alone
@@ -566,6 +619,9 @@ def main():
         "warm": {"ms_per_step": round(warm_ms, 5),
                  "tokens_per_s": round(spec.T / (warm_ms * 1e-3), 1)},
         "step_ms_cold": {"min": round(min(cold), 5), "max": round(max(cold), 5)},
+        "step_ms_cold_write_evict": {"median": round(median(cold_write), 5),
+                                     "tokens_per_s": round(spec.T / (median(cold_write) * 1e-3), 1)},
+        "loads": load_summary(load, C),
         "expert_tflops": round(expert_tflops, 2),
         "expert_mfma_frac": round(expert_tflops / PEAK_BF16_TFLOPS, 4),
         "dispatch_hbm_frac": rooflines.get(slot_stage, {}).get("frac"),
