@@ -165,6 +165,19 @@ __device__ __forceinline__ void chunk_hist_rank(const int32_t* s_idx, int n, int
   for (int i = threadIdx.x; i < N; i += blockDim.x) hist_row[i] = cnt[i];
 }
 
+// The three-piece split of the routers below (w = hi + mid + lo, each piece the
+// round-to-nearest bf16 of what the earlier ones leave) for a pair of weights,
+// with the packed conversion (two values per v_cvt_pk_bf16_f32): the pieces as
+// packed bf16 pairs (first value in the low half)
+__device__ __forceinline__ void split3x2(float a, float b, uint32_t& hi, uint32_t& mid,
+                                         uint32_t& lo) {
+  hi = f32x2_to_bf16x2_bits(a, b);
+  const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xFFFF0000u);
+  mid = f32x2_to_bf16x2_bits(ra, rb);
+  const float qa = ra - __uint_as_float(mid << 16), qb = rb - __uint_as_float(mid & 0xFFFF0000u);
+  lo = f32x2_to_bf16x2_bits(qa, qb);
+}
+
 // ---------------------------------------------------------------------------
 // bf16 routers on MFMA with fp32 semantics.  x is bf16 (exact), and each fp32
 // router weight is split exactly into three bf16 pieces w = hi + mid + lo
@@ -181,17 +194,12 @@ __device__ __forceinline__ void chunk_hist_rank(const int32_t* s_idx, int n, int
 // reductions (row_stats below).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void split3(const float* w, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+  uint32_t h4[4], m4[4], l4[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint16_t h = f32_to_bf16_bits(w[i]);
-    const float r1 = w[i] - bf16_bits_to_f32(h);
-    const uint16_t m = f32_to_bf16_bits(r1);
-    const float r2 = r1 - bf16_bits_to_f32(m);
-    const uint16_t l = f32_to_bf16_bits(r2);
-    hi[i] = __builtin_bit_cast(__bf16, h);
-    mid[i] = __builtin_bit_cast(__bf16, m);
-    lo[i] = __builtin_bit_cast(__bf16, l);
-  }
+  for (int i = 0; i < 4; ++i) split3x2(w[2 * i], w[2 * i + 1], h4[i], m4[i], l4[i]);
+  hi = __builtin_bit_cast(bf16x8, u32x4{h4[0], h4[1], h4[2], h4[3]});
+  mid = __builtin_bit_cast(bf16x8, u32x4{m4[0], m4[1], m4[2], m4[3]});
+  lo = __builtin_bit_cast(bf16x8, u32x4{l4[0], l4[1], l4[2], l4[3]});
 }
 
 // Routing statistics of a block's logit tile st[BT][LD] (LDS, fp32, bias
@@ -417,6 +425,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(
                          rank_local);
 }
 
+
 // More experts (32 < N): a block of WAVES waves owns 16 * ROWT * WAVES tokens
 // and NPAD experts starting at e0 = blockIdx.y * NPAD; each wave takes
 // 16 * ROWT of the tokens and the whole K.  Every 32-wide K chunk of W_r is
@@ -504,20 +513,7 @@ __global__ __launch_bounds__(64 * WAVES) void router_tok_kernel(
                            wok[q] ? wq.w : 0.f};
       uint32_t hv[2], mv[2], lv[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint16_t hb[2], mb[2], lb[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float w = w4[2 * h + u];
-          hb[u] = f32_to_bf16_bits(w);
-          const float r1 = w - bf16_bits_to_f32(hb[u]);
-          mb[u] = f32_to_bf16_bits(r1);
-          lb[u] = f32_to_bf16_bits(r1 - bf16_bits_to_f32(mb[u]));
-        }
-        hv[h] = hb[0] | ((uint32_t)hb[1] << 16);
-        mv[h] = mb[0] | ((uint32_t)mb[1] << 16);
-        lv[h] = lb[0] | ((uint32_t)lb[1] << 16);
-      }
+      for (int h = 0; h < 2; ++h) split3x2(w4[2 * h], w4[2 * h + 1], hv[h], mv[h], lv[h]);
       const int off = (wr + WROWS * q) * WLD + wk;
       *reinterpret_cast<uint2*>(&wpl[buf][0][off]) = make_uint2(hv[0], hv[1]);
       *reinterpret_cast<uint2*>(&wpl[buf][1][off]) = make_uint2(mv[0], mv[1]);
@@ -629,17 +625,6 @@ constexpr size_t kRouterGemmLds = (size_t)2 * RG_STAGE * sizeof(uint16_t);  // 1
 // element offset of 16-byte chunk c (0..3) of row r in a [rows][32 + 8] tile
 __device__ __forceinline__ int rg_at(int r, int c) { return r * RG_LD + (c << 3); }
 
-// split3 on a pair of weights with the packed conversion (two values per
-// v_cvt_pk_bf16_f32): the same three pieces, as packed bf16 pairs (first value
-// in the low half)
-__device__ __forceinline__ void split3x2(float a, float b, uint32_t& hi, uint32_t& mid,
-                                         uint32_t& lo) {
-  hi = f32x2_to_bf16x2_bits(a, b);
-  const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xFFFF0000u);
-  mid = f32x2_to_bf16x2_bits(ra, rb);
-  const float qa = ra - __uint_as_float(mid << 16), qb = rb - __uint_as_float(mid & 0xFFFF0000u);
-  lo = f32x2_to_bf16x2_bits(qa, qb);
-}
 
 __global__ __launch_bounds__(512, 1) void router_gemm_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ W_r, const float* __restrict__ b_r,
