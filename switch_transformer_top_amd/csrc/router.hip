@@ -209,8 +209,10 @@ __device__ __forceinline__ void split3(const float* w, bf16x8& hi, bf16x8& mid, 
 // the other experts (lowest index on ties) and its probability
 // exp(h - max) / S.  Choices go to expert_idx / gate [t * k + j] and s_idx
 // [row * k + j].  Then thread e owns expert e and sums p_e over the chunk's
-// tokens in token order (fp64) for P_part; the logits leave in full coalesced
-// rows when requested.  Synchronises the block.
+// tokens in token order (fp64) for P_part (with at most 128 experts two
+// threads share an expert, each summing half of the tokens in order, and the
+// halves are added first + second); the logits leave in full coalesced rows
+// when requested.  Synchronises the block.
 //
 // With s_term (LDS, BT x NPAD doubles) each thread also stores its terms
 // exp(h_e - max) * (1 / S) there, so the P_part sums read them back instead of
@@ -291,12 +293,29 @@ __device__ __forceinline__ void block_stats(const float* st, int N, int k, int64
     }
   }
   __syncthreads();
+  if (!s_term && 2 * N <= 256) {
+    // two adjacent threads per expert, each over half of the rows in token
+    // order; the halves are added first + second
+    const int e = tid >> 1, g = tid & 1;
+    const int half = (n_tok + 1) >> 1;
+    const int r0 = g ? half : 0, r1 = g ? n_tok : half;
+    double acc = 0.0;
+    if (e < N) {
+#pragma unroll 4
+      for (int r = r0; r < r1; ++r) acc += (double)expf(st[r * LD + e] - s_m[r]) * s_inv[r];
+    }
+    const double other = shfl_xor_f64_w(acc, 1, 2);
+    if (e < N && g == 0) P_row[e] = (float)(acc + other);
+    return;
+  }
   for (int e = tid; e < N; e += 256) {
     double acc = 0.0;
-    if (s_term)
+    if (s_term) {
       for (int r = 0; r < n_tok; ++r) acc += s_term[r * NPAD + e];
-    else
+    } else {
+#pragma unroll 4
       for (int r = 0; r < n_tok; ++r) acc += (double)expf(st[r * LD + e] - s_m[r]) * s_inv[r];
+    }
     P_row[e] = (float)acc;
   }
 }
