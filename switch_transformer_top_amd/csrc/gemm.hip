@@ -34,10 +34,15 @@ namespace swl {
 //
 // Block: 256 threads = 4 waves in a 2 x 2 grid; each wave owns a
 // (BM/2) x (BN/2) sub-tile made of 32 x 32 MFMA tiles.  The launch bound asks
-// for three waves per SIMD (three blocks per CU share the LDS and MFMA pipes).  K advances 64 at a
+// for three waves per SIMD (three blocks per CU share the LDS and MFMA pipes).  K advances BK at a
 // time through one padded LDS buffer per operand; the next K tile is fetched
 // into registers (unconditionally: the last step re-reads its own tile) while
-// the current one is multiplied.
+// the current one is multiplied.  BK is 128 for 64-row tiles, which stream
+// weights with few rows to reuse them: twice the bytes in flight per block
+// (three blocks and 144 KB per CU) and 256 contiguous bytes of every weight
+// row per step; 128-row tiles keep BK = 64 (their registers would not allow
+// three blocks per CU at 128).  K is a multiple of 128 (the layer accepts
+// bf16 shapes with d and F multiples of 128 only).
 //
 // MFMA 32x32x16 operand layout (per lane l): first operand row (l % 32) with 8
 // consecutive k, second operand column (l % 32) with the same 8 k; the k group
@@ -55,13 +60,17 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
                                                         int Nout, int m_tiles, int n_tiles,
                                                         int tiles, GemmIO io, int64_t C) {
   if (y_prologue(io)) return;
-  constexpr int LA = BM / 32, LB = BN / 32;   // 16-byte loads per thread per operand
+  constexpr int BK = BM == 64 ? 128 : 64;
+  constexpr int LDK = BK + GB_PAD;            // LDS row stride (bf16 elements)
+  constexpr int TPR = BK / 8;                 // threads per row of a K tile (16 bytes each)
+  constexpr int RP = 256 / TPR;               // rows per load pass
+  constexpr int LA = BM / RP, LB = BN / RP;   // 16-byte loads per thread per operand
   constexpr int TI = BM / 64, TJ = BN / 64;   // MFMA tiles per wave
   // one buffer holding the A rows then the B rows; reused by the epilogue
-  __shared__ __attribute__((aligned(16))) uint16_t lds[(BM + BN) * GB_LDK];
-  static_assert(4 * (BM / 2) * (BN / 2 + 8) <= (BM + BN) * GB_LDK, "epilogue staging fits");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[(BM + BN) * LDK];
+  static_assert(4 * (BM / 2) * (BN / 2 + 8) <= (BM + BN) * LDK, "epilogue staging fits");
   uint16_t* As = lds;
-  uint16_t* Bs = lds + BM * GB_LDK;
+  uint16_t* Bs = lds + BM * LDK;
 
   const int per_xcd = (tiles + 7) >> 3;
   const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -83,18 +92,18 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid >> 3, lcol = (tid & 7) * 8;
+  const int lrow = tid / TPR, lcol = (tid % TPR) * 8;
 
   int64_t a_off[LA], b_off[LB];
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
-    int r = m0 + lrow + 32 * j;
+    int r = m0 + lrow + RP * j;
     r = r < rows_e ? r : rows_e - 1;  // rows past n_kept: any valid row, never stored
     const int64_t src = MODE == kRowsGather ? (int64_t)tok_e[r] : (int64_t)r;
     a_off[j] = src * K + lcol;
   }
 #pragma unroll
-  for (int j = 0; j < LB; ++j) b_off[j] = (int64_t)(lrow + 32 * j) * K + lcol;
+  for (int j = 0; j < LB; ++j) b_off[j] = (int64_t)(lrow + RP * j) * K + lcol;
 
   floatx16 acc[TI][TJ];
 #pragma unroll
@@ -104,7 +113,7 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int last = K - GB_BK;
+  const int last = K - BK;
   u32x4 ra[LA], rb[LB];
   // The scheduling barrier keeps the prefetch loads ahead of the MFMAs that
   // follow; without it the compiler sinks them to the end of the loop body,
@@ -125,28 +134,28 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
   auto kloop = [&](auto tv_const) {
     constexpr int TV = decltype(tv_const)::value;
     fetch(0);
-    for (int k0 = 0; k0 < K; k0 += GB_BK) {
+    for (int k0 = 0; k0 < K; k0 += BK) {
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < LA; ++j)
-        *reinterpret_cast<u32x4*>(&As[(lrow + 32 * j) * GB_LDK + lcol]) = ra[j];
+        *reinterpret_cast<u32x4*>(&As[(lrow + RP * j) * LDK + lcol]) = ra[j];
 #pragma unroll
       for (int j = 0; j < LB; ++j)
-        *reinterpret_cast<u32x4*>(&Bs[(lrow + 32 * j) * GB_LDK + lcol]) = rb[j];
+        *reinterpret_cast<u32x4*>(&Bs[(lrow + RP * j) * LDK + lcol]) = rb[j];
       __syncthreads();
-      fetch(k0 + GB_BK);
+      fetch(k0 + BK);
       if (TV == 0) continue;
 #pragma unroll
-      for (int ks = 0; ks < GB_BK; ks += 16) {
+      for (int ks = 0; ks < BK; ks += 16) {
         bf16x8 a[TI], b[TJ];
 #pragma unroll
         for (int i = 0; i < TV; ++i)
           a[i] = *reinterpret_cast<const bf16x8*>(
-              &As[(wm * (BM / 2) + i * 32 + fr) * GB_LDK + ks + fk]);
+              &As[(wm * (BM / 2) + i * 32 + fr) * LDK + ks + fk]);
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
           b[j] = *reinterpret_cast<const bf16x8*>(
-              &Bs[(wn * (BN / 2) + j * 32 + fr) * GB_LDK + ks + fk]);
+              &Bs[(wn * (BN / 2) + j * 32 + fr) * LDK + ks + fk]);
 #pragma unroll
         for (int i = 0; i < TV; ++i)
 #pragma unroll
