@@ -113,7 +113,7 @@ STAGE_KERNEL = {"gemm1_relu": (r"gemm_bf16_\w+<(\d+, \d+, )?true, 1(, false)?>",
                 "gemm2": (r"gemm_bf16_\w+<(\d+, \d+, )?false, 0(, false)?>", "gemm.hip"),
                 "gemm2_combine": (r"gemm_bf16_\w+<(\d+, \d+, )?false, 2(, false)?>", "gemm.hip"),
                 "router": (r"router_(small|tok)_kernel(<.*>)?", "router.hip"),
-                "router_logits": (r"router_gemm_kernel", "router.hip"),
+                "router_logits": (r"router_gemm_dma_kernel", "router.hip"),
                 "route_rows": (r"route_rows\w*(<.*>)?", "router.hip"),
                 "route_scan": (r"route_scan_kernel", "assign.hip"),
                 "ffn_fused": (r"ffn_fused_kernel(<.*>)?", "ffn.hip"),

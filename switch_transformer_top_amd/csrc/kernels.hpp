@@ -89,8 +89,9 @@ constexpr int kMaxTopK = 2;
 // router.hip
 bool router_fused_ok(bool x_bf16, int N);
 int64_t route_chunk_tokens(bool x_bf16, int N);
+// planes: workspace of 3 N d bf16 for the weight planes (bf16 x only)
 void launch_router_logits(const void* x, bool x_bf16, const float* W_r, const float* b_r,
-                          float* h, int64_t T, int d, int N, hipStream_t s);
+                          float* h, int64_t T, int d, int N, uint16_t* planes, hipStream_t s);
 void launch_router_fused(const uint16_t* x, const float* W_r, const float* b_r, int64_t T, int d,
                          int N, int k, float* logits, int32_t* expert_idx, float* gate,
                          float* P_part, int32_t* hist, int32_t* rank_local, hipStream_t s);

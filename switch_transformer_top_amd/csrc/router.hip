@@ -616,82 +616,112 @@ __global__ __launch_bounds__(64 * WAVES) void router_tok_kernel(
 // ---------------------------------------------------------------------------
 // Logits of many experts (N > 256, bf16 tokens): a dense fp32-exact GEMM
 // h[T, N] = x W_r^T + b on bf16 MFMA over the three-plane split of W_r (see
-// split3), written to memory for the statistics kernel below.
+// split3), written to memory for the statistics kernel below.  A pre-pass
+// writes hi, mid and lo of every W_r row (split3x2) to planes [3][N][d] bf16
+// once per call, and the logits kernel moves its x and plane tiles from memory
+// straight into LDS (global_load_lds_dwordx4: no registers and no VALU on the
+// way), so the data path of a step is eight load instructions per wave.
 //
 // Block: 512 threads = 8 waves, tile 256 tokens x 256 experts; waves in a
 // 2 x 4 grid (token half, expert quarter), each 128 tokens x 64 experts = 4 x 2
 // tiles of v_mfma_f32_32x32x16_bf16 with the weight plane as the first operand,
 // so lane l ends up holding token (l % 32) of a tile and 16 of its 32 experts:
 // rows 8 (v / 4) + 4 (l / 32) + (v % 4), which leave as four 16-byte stores.
-// K steps of 32: the block loads x [256][32] (bf16) and W_r [256][32] (fp32),
-// splits W into its three bf16 planes once and stores x and the planes to LDS
-// (double buffered, one barrier per step); every x fragment then serves three
-// MFMAs (one per plane) and every plane fragment four token tiles.  LDS rows
-// hold the 32 elements of a step plus one 16-byte chunk of padding (80 bytes, an
-// odd number of chunks), so consecutive rows of one chunk fall on distinct bank
-// groups; the two buffers fill the 160 KiB of LDS.  (Unpadded 64-byte rows with
-// XOR-swizzled chunks measured bank conflicts in 92% of the LDS cycles.)
-// Tile order: block b takes expert tile b % n_et and token tile b / n_et, so
-// with 8 expert tiles each XCD (b % 8) keeps one 2 MB slice of W_r in its L2
-// while it walks the tokens.
+// Every x fragment serves three MFMAs (one per plane) and every plane fragment
+// four token tiles.  K steps of 32; the tiles are [rows][32] bf16 (64-byte
+// rows): x tiles (16 KB) in a ring of four, the three plane tiles of a step
+// (48 KB) in a ring of two, 160 KB in all.  Tile order: block b takes expert
+// tile b % n_et and token tile b / n_et, so with 8 expert tiles XCD k (b % 8)
+// keeps its 256 experts' planes (3 MB) in its L2 and the planes are fetched one
+// step ahead; the x tiles come from beyond L2 (every XCD reads all of x once)
+// and are fetched three steps ahead.  Every load instruction fills 1 KB of LDS
+// (16 rows) with lane l writing bytes 16 l .. 16 l + 15, so the rows cannot be
+// padded; instead the 16-byte chunk c of row r sits at position
+// c ^ ((r >> 2) & 3) of its row, which puts the 16 rows one fragment read
+// touches (one chunk each) on 16 distinct groups of four banks (the counters
+// read no bank conflicts).  A lane of a load instruction therefore fetches row
+// R + l / 4, chunk (l % 4) ^ swizzle(row).
 // ---------------------------------------------------------------------------
-constexpr int RG_BT = 256, RG_BE = 256, RG_BK = 32, RG_LD = RG_BK + 8;
-constexpr int RG_XS = RG_BT * RG_LD;            // x tile (elements)
-constexpr int RG_PS = RG_BE * RG_LD;            // one weight plane
-constexpr int RG_STAGE = RG_XS + 3 * RG_PS;     // one LDS buffer (elements)
-constexpr size_t kRouterGemmLds = (size_t)2 * RG_STAGE * sizeof(uint16_t);  // 160 KiB
+constexpr int RD_BT = 256, RD_BE = 256, RD_BK = 32;
+constexpr int RD_XB = RD_BT * RD_BK * 2;          // bytes of the x tile
+constexpr int RD_PB = RD_BE * RD_BK * 2;          // bytes of one plane tile
+constexpr int RD_XRING = 4, RD_PRING = 2;         // x and plane stages
+constexpr int RD_POFF = RD_XRING * RD_XB;         // plane ring offset
+constexpr size_t kRouterDmaLds = (size_t)RD_POFF + RD_PRING * 3 * (size_t)RD_PB;  // 160 KiB
 
-// element offset of 16-byte chunk c (0..3) of row r in a [rows][32 + 8] tile
-__device__ __forceinline__ int rg_at(int r, int c) { return r * RG_LD + (c << 3); }
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
 
+// byte offset of logical 16-byte chunk c (0..3) of row r in a [rows][32] tile
+__device__ __forceinline__ int rd_at(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
-__global__ __launch_bounds__(512, 1) void router_gemm_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ W_r, const float* __restrict__ b_r,
-    float* __restrict__ h, int64_t T, int d, int N, int n_et, bool vec) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t rlds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wt = wave >> 2, we = wave & 3;
-  const int et = (int)(blockIdx.x % (unsigned)n_et);
-  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)n_et) * RG_BT;
-  const int e0 = et * RG_BE;
-
-  // loaders: thread -> row tid / 2, half (tid & 1) of the 32-wide K step: 16
-  // fp32 weights (four 16-byte loads) and 16 bf16 token values (two loads)
-  const int lr = tid >> 1, lh = tid & 1;
-  int64_t tr = t0 + lr;
-  tr = tr < T ? tr : T - 1;  // rows past T: any valid row, never stored
-  const uint16_t* xsrc = x + tr * d + lh * 16;
-  // expert rows past N read row 0: their logits are computed and never stored
-  const float* wsrc = W_r + (int64_t)(e0 + lr < N ? e0 + lr : 0) * d + lh * 16;
-  const int nk = d / RG_BK;
-  // one register stage: step t + 1 waits in xr / wr while step t is multiplied
-  u32x4 xr[2];
-  float4 wr[4];
-  auto gload = [&](int kc) {
-    const int k = (kc < nk ? kc : nk - 1) * RG_BK;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) xr[q] = *reinterpret_cast<const u32x4*>(xsrc + k + 8 * q);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) wr[q] = *reinterpret_cast<const float4*>(wsrc + k + 4 * q);
-  };
-  // one half (q = 0, 1: 8 weights, one 16-byte chunk per plane) of the loaded
-  // step, split into its three planes and stored at row lr of buffer `pn`
-  auto split_half = [&](uint16_t* pn, int q) {
-    const float4 a = wr[2 * q], b = wr[2 * q + 1];
+// planes[p][e][k] (p = 0 hi, 1 mid, 2 lo) of W_r [N][d]; n8 = N d / 8.
+__global__ __launch_bounds__(256) void router_planes_kernel(const float* __restrict__ W_r,
+                                                            uint16_t* __restrict__ planes,
+                                                            int64_t n8) {
+  const int64_t plane = n8 * 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float4 a = reinterpret_cast<const float4*>(W_r)[2 * i];
+    const float4 b = reinterpret_cast<const float4*>(W_r)[2 * i + 1];
     const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     uint32_t h4[4], m4[4], l4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) split3x2(w[2 * i], w[2 * i + 1], h4[i], m4[i], l4[i]);
-    const u32x4 hi = {h4[0], h4[1], h4[2], h4[3]}, mid = {m4[0], m4[1], m4[2], m4[3]},
-                lo = {l4[0], l4[1], l4[2], l4[3]};
-    const int at = rg_at(lr, 2 * lh + q);
-    *reinterpret_cast<u32x4*>(pn + at) = hi;
-    *reinterpret_cast<u32x4*>(pn + RG_PS + at) = mid;
-    *reinterpret_cast<u32x4*>(pn + 2 * RG_PS + at) = lo;
-  };
-  auto store_x = [&](uint16_t* xn) {
+    for (int j = 0; j < 4; ++j) split3x2(w[2 * j], w[2 * j + 1], h4[j], m4[j], l4[j]);
+    *reinterpret_cast<u32x4*>(planes + 8 * i) = u32x4{h4[0], h4[1], h4[2], h4[3]};
+    *reinterpret_cast<u32x4*>(planes + plane + 8 * i) = u32x4{m4[0], m4[1], m4[2], m4[3]};
+    *reinterpret_cast<u32x4*>(planes + 2 * plane + 8 * i) = u32x4{l4[0], l4[1], l4[2], l4[3]};
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void router_gemm_dma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
+    const float* __restrict__ b_r, float* __restrict__ h, int64_t T, int d, int N, int n_et,
+    bool vec) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t rlds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave >> 2, we = wave & 3;
+  const int et = (int)(blockIdx.x % (unsigned)n_et);
+  const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)n_et) * RD_BT;
+  const int e0 = et * RD_BE;
+
+  // wave w moves rows 32 w .. 32 w + 31 of the x tile (two instructions) and
+  // rows 96 w .. 96 w + 95 of the 768 plane rows [3][256] (six); token rows
+  // past T read row T - 1 and expert rows past N read row 0 (never stored)
+  const int lr = lane >> 2, pc = lane & 3;
+  const uint16_t* src[8];
+  int dst[8];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) *reinterpret_cast<u32x4*>(xn + rg_at(lr, 2 * lh + q)) = xr[q];
+  for (int j = 0; j < 2; ++j) {
+    const int row = 32 * wave + 16 * j + lr;
+    int64_t tr = t0 + row;
+    tr = tr < T ? tr : T - 1;
+    src[j] = x + tr * d + ((pc ^ ((row >> 2) & 3)) << 3);
+    dst[j] = (32 * wave + 16 * j) * 64;  // within an x stage
+  }
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    const int prow = 96 * wave + 16 * j + lr;
+    const int p = prow >> 8, r = prow & 255;
+    const int e = e0 + r < N ? e0 + r : 0;
+    src[2 + j] = planes + ((int64_t)p * N + e) * d + ((pc ^ ((r >> 2) & 3)) << 3);
+    dst[2 + j] = (96 * wave + 16 * j) * 64;  // within a plane stage
+  }
+  char* lds_bytes = reinterpret_cast<char*>(rlds);
+  auto dma_x = [&](int kc) {
+    char* stage = lds_bytes + (kc & (RD_XRING - 1)) * RD_XB;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(src[j] + kc * RD_BK),
+                                       (lds_void_ptr)(stage + dst[j]), 16, 0, 0);
+  };
+  auto dma_planes = [&](int kc) {
+    char* stage = lds_bytes + RD_POFF + (kc & (RD_PRING - 1)) * 3 * RD_PB;
+#pragma unroll
+    for (int j = 2; j < 8; ++j)
+      __builtin_amdgcn_global_load_lds((global_void_ptr)(src[j] + kc * RD_BK),
+                                       (lds_void_ptr)(stage + dst[j]), 16, 0, 0);
   };
 
   floatx16 acc[2][4];
@@ -702,75 +732,70 @@ __global__ __launch_bounds__(512, 1) void router_gemm_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.f;
   const int fr = lane & 31, fc = lane >> 5;
-  // the 24 MFMAs of K sub-step s (16 k) from buffer xs: x fragments of the
-  // wave's four token tiles, then per plane (smallest pieces first: lo, mid,
-  // hi) the fragments of its two expert tiles
-  auto substep = [&](const uint16_t* xs, int s) {
-    const uint16_t* ps = xs + RG_XS;
+  // fragments of K sub-step s (16 k): x of the wave's four token tiles and,
+  // per plane, its two expert tiles
+  struct Frags {
+    bf16x8 x[4], w[3][2];
+  };
+  auto read_frags = [&](Frags& f, const char* xst, const char* pst, int s) {
     const int c = 2 * s + fc;
-    bf16x8 xb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      xb[i] = *reinterpret_cast<const bf16x8*>(xs + rg_at(wt * 128 + i * 32 + fr, c));
+      f.x[i] = *reinterpret_cast<const bf16x8*>(xst + rd_at(wt * 128 + i * 32 + fr, c));
 #pragma unroll
-    for (int p = 2; p >= 0; --p) {
-      bf16x8 wp[2];
+    for (int p = 2; p >= 0; --p)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        wp[j] = *reinterpret_cast<const bf16x8*>(ps + p * RG_PS + rg_at(we * 64 + j * 32 + fr, c));
+        f.w[p][j] = *reinterpret_cast<const bf16x8*>(pst + p * RD_PB +
+                                                     rd_at(we * 64 + j * 32 + fr, c));
+  };
+  // the 24 MFMAs of a sub-step, smallest plane first
+  auto mfmas = [&](const Frags& f) {
+#pragma unroll
+    for (int p = 2; p >= 0; --p)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wp[j], xb[i], acc[j][i], 0, 0, 0);
-    }
-  };
-  // Issue order inside a sub-step: the x and lo-plane fragment reads, then each
-  // MFMA followed by two VALU instructions of the split of the next step's
-  // weights (which run while the matrix pipe works), the other planes'
-  // fragment reads ahead of their MFMAs, and the plane stores at the end.
-  auto schedule = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // LDS read: x, lo plane
-#pragma unroll
-    for (int p = 0; p < 3; ++p) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
-      }
-      if (p < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next plane's reads
-    }
-    __builtin_amdgcn_sched_group_barrier(0x200, 5, 0);   // LDS write
-    __builtin_amdgcn_sched_barrier(0);
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[p][j], f.x[i], acc[j][i], 0, 0, 0);
   };
 
-  gload(0);
-  store_x(rlds);
-  split_half(rlds + RG_XS, 0);
-  split_half(rlds + RG_XS, 1);
-  gload(1);
-  __syncthreads();
+  // Issue order: x 0, x 1, planes 0, x 2, then in step t planes t + 1 and
+  // x t + 3.  At the top of step t the last two load instructions of this wave
+  // are those of x t + 2 (while it exists), so waiting until at most two are
+  // outstanding completes x t, x t + 1 and planes t (the counter retires loads
+  // in issue order); the barrier then covers every wave's loads, and every
+  // wave has finished step t - 1, whose stages steps t + 1 and t + 3 refill.
+  // (A plain __syncthreads would wait for all outstanding loads.)
+  const int nk = d / RD_BK;
+  dma_x(0);
+  if (nk > 1) dma_x(1);
+  dma_planes(0);
+  if (nk > 2) dma_x(2);
   for (int t = 0; t < nk; ++t) {
-    // step t from buffer t & 1; step t + 1 (in the registers) into the other
-    // buffer, last read in step t - 1 before the barrier that ended it, its
-    // split interleaved with step t's MFMAs; then the registers take step t + 2
-    // (after the last step the copy goes to a buffer nobody reads)
-    const uint16_t* xs = rlds + (t & 1) * RG_STAGE;
-    uint16_t* xn = rlds + ((t + 1) & 1) * RG_STAGE;
-    store_x(xn);
-    substep(xs, 0);
-    split_half(xn + RG_XS, 0);
-    schedule();
-    substep(xs, 1);
-    split_half(xn + RG_XS, 1);
-    schedule();
-    gload(t + 2);
-    __syncthreads();
+    if (t + 2 < nk) asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 1 < nk) dma_planes(t + 1);
+    if (t + 3 < nk) dma_x(t + 3);
+    const char* xst = lds_bytes + (t & (RD_XRING - 1)) * RD_XB;
+    const char* pst = lds_bytes + RD_POFF + (t & (RD_PRING - 1)) * 3 * RD_PB;
+    // the second sub-step's fragment reads go out between the first
+    // sub-step's MFMAs (one read after every two MFMAs)
+    Frags f0, f1;
+    read_frags(f0, xst, pst, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f0);
+    read_frags(f1, xst, pst, 1);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1);
   }
 
-  // logits + bias: lane l of tile (j, i) holds token wt*128 + 32 i + l % 32 and
-  // experts we*64 + 32 j + 8 q + 4 (l / 32) + (0..3), q < 4; vec: 16-byte stores
-  // (h 16-byte aligned and N a multiple of 4)
   float bias[2][4][4];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -1034,7 +1059,6 @@ __global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __rest
 // ------------------------------------------------------------------ launchers
 
 constexpr int kTokRowt = 2;                 // router_tok_kernel: 128 tokens per block
-constexpr int kLogitRowt = 2, kLogitWaves = 8;  // logits only: 256 tokens per block
 
 bool router_fused_ok(bool x_bf16, int N) { return x_bf16 && N <= 256; }
 
@@ -1044,23 +1068,28 @@ int64_t route_chunk_tokens(bool x_bf16, int N) {
 }
 
 void launch_router_logits(const void* x, bool x_bf16, const float* W_r, const float* b_r,
-                          float* h, int64_t T, int d, int N, hipStream_t s) {
+                          float* h, int64_t T, int d, int N, uint16_t* planes, hipStream_t s) {
   if (T == 0) return;
   if (x_bf16) {
-    // MFMA logits in 256 x 256 tiles, statistics by route_rows_kernel
+    // the weight planes once per call, then MFMA logits in 256 x 256 tiles;
+    // statistics by route_rows_kernel
     static uint64_t set_on = 0;
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (dev < 64 && !(set_on >> dev & 1)) {
-      (void)hipFuncSetAttribute((const void*)router_gemm_kernel,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRouterGemmLds);
+      (void)hipFuncSetAttribute((const void*)router_gemm_dma_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRouterDmaLds);
       set_on |= 1ull << dev;
     }
-    const int n_et = (N + RG_BE - 1) / RG_BE;
-    const int64_t n_tt = (T + RG_BT - 1) / RG_BT;
+    const int64_t n8 = (int64_t)N * d / 8;
+    const int64_t pb = (n8 + 255) / 256;
+    launch_k(router_planes_kernel, dim3((unsigned)(pb < 4096 ? pb : 4096)), dim3(256), 0, s, W_r,
+             planes, n8);
+    const int n_et = (N + RD_BE - 1) / RD_BE;
+    const int64_t n_tt = (T + RD_BT - 1) / RD_BT;
     const bool vec = (N & 3) == 0 && ((uintptr_t)h & 15) == 0;
-    launch_k(router_gemm_kernel, dim3((unsigned)(n_tt * n_et)), dim3(512), kRouterGemmLds, s,
-             (const uint16_t*)x, W_r, b_r, h, T, d, N, n_et, vec);
+    launch_k(router_gemm_dma_kernel, dim3((unsigned)(n_tt * n_et)), dim3(512), kRouterDmaLds, s,
+             (const uint16_t*)x, (const uint16_t*)planes, b_r, h, T, d, N, n_et, vec);
     return;
   }
   dim3 grid((unsigned)((T + RT_BT - 1) / RT_BT), (unsigned)((N + RT_BE - 1) / RT_BE));

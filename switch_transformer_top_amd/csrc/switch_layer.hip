@@ -58,8 +58,8 @@ int64_t buffer_rows(const switch_config& c, int64_t T) {
 }
 
 struct Layout {
-  size_t logits, ppart, hist, rank, load, nkept, terms, tiles, tok, xbuf, hbuf, ybuf, yflag, hflag,
-      total;
+  size_t logits, planes, ppart, hist, rank, load, nkept, terms, tiles, tok, xbuf, hbuf, ybuf, yflag,
+      hflag, total;
 };
 
 // Chunks of the routing statistics: the fused router uses small chunks, the
@@ -80,6 +80,9 @@ Layout layout_of(const switch_layer* L, int64_t T) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes); return at; };
   lo.logits = take(sizeof(float) * (size_t)T * (size_t)N);
+  // the bf16 logits router of many experts splits W_r into three bf16 planes
+  const bool planes = c.act_dtype == SWITCH_BF16 && !swl::router_fused_ok(true, (int)N);
+  lo.planes = take(planes ? 3 * sizeof(uint16_t) * (size_t)N * (size_t)c.d_model : 0);
   lo.ppart = take(sizeof(float) * (size_t)nc * (size_t)N);
   lo.hist = take(sizeof(int32_t) * (size_t)nc * (size_t)N);
   lo.rank = take(sizeof(int32_t) * (size_t)T * (size_t)top_k(c));
@@ -200,7 +203,8 @@ Routed enqueue_routing(switch_layer* L, const void* x, const float* given_logits
       if (!h) {
         float* hw = logits_out ? logits_out : (float*)(ws + lo.logits);
         swl::prof_mark(P, s, "router_logits");
-        swl::launch_router_logits(x, bf16, L->W_r, L->b_r, hw, T, c.d_model, N, s);
+        swl::launch_router_logits(x, bf16, L->W_r, L->b_r, hw, T, c.d_model, N,
+                                  (uint16_t*)(ws + lo.planes), s);
         h = hw;
       }
       swl::prof_mark(P, s, "route_rows");
