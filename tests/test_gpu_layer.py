@@ -77,6 +77,10 @@ def test_tiny_fp32_config(B):
                                        # 256-token block whose second 128-token group is partial
     (1300, 1500, 128, 128, 2.0, 35),   # 1024 < N < 2048: the 32-per-lane statistics with the
                                        # experts past N masked, a ragged last expert tile
+    (1000, 600, 1024, 256, 1.0, 36),   # logits router over 32 K steps: the x ring refilled
+                                       # three steps ahead, a ragged last expert tile
+    (300, 300, 2048, 128, 1.0, 37),    # the 2048-wide rows of the 2048-expert share (64 K
+                                       # steps), one partial token tile
 ])
 def test_bf16_ragged_shapes(B, T, N, d, F, c, seed):
     spec = S.Spec(f"bf16-{T}-{N}", T=T, d=d, F=F, N=N, c=c, seed=seed)
