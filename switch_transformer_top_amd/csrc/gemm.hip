@@ -49,7 +49,7 @@ namespace swl {
 // is (l / 32).  Result: lane l holds column (l % 32) and rows
 // 8 (v / 4) + 4 (l / 32) + (v % 4), v < 16.  The first operand is the weight
 // fragment, so those result rows are output columns (see stage_tile_bf16).
-template <int BM, int BN, bool RELU, int MODE>
+template <int BM, int BN, bool RELU, int MODE, bool NTW = false>
 __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                         int64_t strideA,
                                                         const uint16_t* __restrict__ B,
@@ -123,7 +123,9 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
 #pragma unroll
     for (int j = 0; j < LA; ++j) ra[j] = *reinterpret_cast<const u32x4*>(Ae + a_off[j] + k);
 #pragma unroll
-    for (int j = 0; j < LB; ++j) rb[j] = *reinterpret_cast<const u32x4*>(Be + b_off[j] + k);
+    for (int j = 0; j < LB; ++j)
+      rb[j] = NTW ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Be + b_off[j] + k))
+                  : *reinterpret_cast<const u32x4*>(Be + b_off[j] + k);
     __builtin_amdgcn_sched_barrier(0);
   };
   const int fr = lane & 31, fk = (lane >> 5) * 8;
@@ -1037,6 +1039,11 @@ void launch_plain(GemmRows mode, bool relu, const uint16_t* a, int64_t strideA,
   launch_k((gemm_bf16_kernel<BM, BN, RL, MD>), dim3(grid), dim3(256), 0, s, a, strideA, b,    \
            strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C)
   if (mode == kRowsGather && relu) SWL_PLAIN(true, kRowsGather);
+  else if (mode == kRowsCombine && mt == 1)
+    // every expert's weights are read once: non-temporal loads keep them from
+    // pushing H (read by all N tiles of an expert) out of L2
+    launch_k((gemm_bf16_kernel<BM, BN, false, kRowsCombine, true>), dim3(grid), dim3(256), 0, s,
+             a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
   else if (mode == kRowsCombine) SWL_PLAIN(false, kRowsCombine);
   else if (mode == kRowsMask) SWL_PLAIN(false, kRowsMask);
   else if (relu) SWL_PLAIN(true, kRowsDense);
