@@ -737,11 +737,14 @@ __global__ __launch_bounds__(512, 1) void router_gemm_dma_kernel(
   struct Frags {
     bf16x8 x[4], w[3][2];
   };
-  auto read_frags = [&](Frags& f, const char* xst, const char* pst, int s) {
+  auto read_x = [&](Frags& f, const char* xst, int s) {
     const int c = 2 * s + fc;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       f.x[i] = *reinterpret_cast<const bf16x8*>(xst + rd_at(wt * 128 + i * 32 + fr, c));
+  };
+  auto read_w = [&](Frags& f, const char* pst, int s) {
+    const int c = 2 * s + fc;
 #pragma unroll
     for (int p = 2; p >= 0; --p)
 #pragma unroll
@@ -772,20 +775,30 @@ __global__ __launch_bounds__(512, 1) void router_gemm_dma_kernel(
   if (nk > 1) dma_x(1);
   dma_planes(0);
   if (nk > 2) dma_x(2);
-  for (int t = 0; t < nk; ++t) {
+  auto xstage = [&](int kc) { return lds_bytes + (kc & (RD_XRING - 1)) * RD_XB; };
+  auto step_barrier = [&](int t) {
     if (t + 2 < nk) asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  // The first sub-step's x fragments of step t are read during step t - 1 (x
+  // t is complete at that step's barrier); the second sub-step's fragment
+  // reads go out between the first sub-step's MFMAs and the next step's first
+  // x fragments between the second sub-step's (one read after every two
+  // MFMAs), so after a barrier a wave waits only for its six plane fragments.
+  Frags f0, f1;
+  step_barrier(0);
+  read_x(f0, xstage(0), 0);
+  for (int t = 0; t < nk; ++t) {
+    if (t > 0) step_barrier(t);
     if (t + 1 < nk) dma_planes(t + 1);
     if (t + 3 < nk) dma_x(t + 3);
-    const char* xst = lds_bytes + (t & (RD_XRING - 1)) * RD_XB;
+    const char* xst = xstage(t);
     const char* pst = lds_bytes + RD_POFF + (t & (RD_PRING - 1)) * 3 * RD_PB;
-    // the second sub-step's fragment reads go out between the first
-    // sub-step's MFMAs (one read after every two MFMAs)
-    Frags f0, f1;
-    read_frags(f0, xst, pst, 0);
+    read_w(f0, pst, 0);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(f0);
-    read_frags(f1, xst, pst, 1);
+    read_x(f1, xst, 1);
+    read_w(f1, pst, 1);
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
@@ -794,6 +807,14 @@ __global__ __launch_bounds__(512, 1) void router_gemm_dma_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(f1);
+    read_x(f0, xstage(t + 1 < nk ? t + 1 : t), 0);  // the last step re-reads its own
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   float bias[2][4][4];
