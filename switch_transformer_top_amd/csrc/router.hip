@@ -776,29 +776,20 @@ __global__ __launch_bounds__(512, 1) void router_gemm_dma_kernel(
   dma_planes(0);
   if (nk > 2) dma_x(2);
   auto xstage = [&](int kc) { return lds_bytes + (kc & (RD_XRING - 1)) * RD_XB; };
+  auto pstage = [&](int kc) { return lds_bytes + RD_POFF + (kc & (RD_PRING - 1)) * 3 * RD_PB; };
+  // The wait before step t's barrier also completes this wave's fragment
+  // reads (lgkmcnt 0): the loads issued after the barrier refill the stages
+  // that step t - 1 read.
   auto step_barrier = [&](int t) {
-    if (t + 2 < nk) asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 2 < nk) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  // The first sub-step's x fragments of step t are read during step t - 1 (x
-  // t is complete at that step's barrier); the second sub-step's fragment
-  // reads go out between the first sub-step's MFMAs and the next step's first
-  // x fragments between the second sub-step's (one read after every two
-  // MFMAs), so after a barrier a wave waits only for its six plane fragments.
-  Frags f0, f1;
-  step_barrier(0);
-  read_x(f0, xstage(0), 0);
-  for (int t = 0; t < nk; ++t) {
-    if (t > 0) step_barrier(t);
-    if (t + 1 < nk) dma_planes(t + 1);
-    if (t + 3 < nk) dma_x(t + 3);
-    const char* xst = xstage(t);
-    const char* pst = lds_bytes + RD_POFF + (t & (RD_PRING - 1)) * 3 * RD_PB;
-    read_w(f0, pst, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(f0);
-    read_x(f1, xst, 1);
-    read_w(f1, pst, 1);
+  // MFMAs of `f` with the ten fragment reads of `g` (sub-step s of step kc)
+  // spread between them, one read after every two MFMAs
+  auto mfmas_reading = [&](const Frags& f, Frags& g, int kc, int s) {
+    mfmas(f);
+    read_x(g, xstage(kc), s);
+    read_w(g, pstage(kc), s);
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
@@ -806,16 +797,28 @@ __global__ __launch_bounds__(512, 1) void router_gemm_dma_kernel(
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(f1);
-    read_x(f0, xstage(t + 1 < nk ? t + 1 : t), 0);  // the last step re-reads its own
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+  };
+  // Software pipeline across the barrier: after step t's barrier the MFMAs of
+  // step t - 1's second sub-step (its fragments already in registers) run
+  // while step t's first fragments arrive, then step t's first sub-step runs
+  // while its second sub-step's fragments arrive.
+  Frags f0, f1;
+  step_barrier(0);
+  if (nk > 1) dma_planes(1);
+  if (nk > 3) dma_x(3);
+  read_x(f0, xstage(0), 0);
+  read_w(f0, pstage(0), 0);
+  __builtin_amdgcn_sched_barrier(0);
+  mfmas_reading(f0, f1, 0, 1);
+  for (int t = 1; t < nk; ++t) {
+    step_barrier(t);
+    if (t + 1 < nk) dma_planes(t + 1);
+    if (t + 3 < nk) dma_x(t + 3);
     __builtin_amdgcn_sched_barrier(0);
+    mfmas_reading(f1, f0, t, 0);
+    mfmas_reading(f0, f1, t, 1);
   }
+  mfmas(f1);
 
   float bias[2][4][4];
 #pragma unroll
