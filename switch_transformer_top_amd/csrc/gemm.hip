@@ -243,6 +243,19 @@ __device__ __forceinline__ void sched_substep_n() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// After a K step's barrier: the previous sub-step's MFMAs with this step's
+// first fragment reads (TV + 2 of them) between them.
+template <int TV>
+__device__ __forceinline__ void sched_tail_tv() {
+  constexpr int NM = 2 * TV, NR = TV > 0 ? TV + 2 : 0;
+#pragma unroll
+  for (int i = 0; i < (NM < NR ? NM : NR); ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int TV, int NW, int NL>
 __device__ __forceinline__ void sched_substep_tv() {
   if constexpr (TV == 4) sched_substep<NW, NL>();
@@ -396,9 +409,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
       gload(6, 8, t + 2);
       mfmas(0);
       sched_substep_tv<TV, 2, 2>();
-      mfmas(1);
+      // the last sub-step's MFMAs go after the barrier (their fragments are in
+      // registers), so the matrix pipe has work while the next step's first
+      // fragments arrive
       __syncthreads();
       frags(0, nxt, 0);
+      mfmas(1);
+      sched_tail_tv<TV>();
     }
   };
   int tv = (rows_e - (m0 + wm * 128) + 31) / 32;
