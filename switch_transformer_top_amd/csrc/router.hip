@@ -936,31 +936,36 @@ __global__ __launch_bounds__(256) void route_rows_kernel(const float* __restrict
 // Statistics from logits with each row read once (N <= 64 NPL): a wave takes
 // rows w, w + 4, ... of the block's 64; lane l holds experts l + 64 i of the row
 // in registers for the max, the sum, the second choice and its own running
-// sums of p over the wave's rows (fp64).  The four waves' sums are then added
-// as (w0 + w2) + (w1 + w3).  Same statistics as route_rows_kernel; the P sums
-// are the same terms added in another fixed order.
+// sums of p over the wave's 16 rows (fp32: at most 16 terms of at most 1).
+// The four waves' sums are then added in fp64 as (w0 + w2) + (w1 + w3) through
+// two LDS rows of N doubles, which the chunk's counts reuse afterwards.  Same statistics as route_rows_kernel; the P sums
+// are the same terms added in another fixed order.  K (choices per token) and
+// FULL (N == 64 NPL: no padded experts) are compile-time, so that no per-expert
+// masks or indices stay live: with at most 128 registers four blocks share a
+// CU (32 KB of LDS each at N = 2048), twice the waves of the register-bound
+// form, which hides the row loads behind the other waves' arithmetic.
 // word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
 // offsets checked against the record count
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
-template <int NPL>
-__global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __restrict__ h,
-                                                             int64_t T, int N, int k,
-                                                             int32_t* __restrict__ expert_idx,
-                                                             float* __restrict__ gate,
-                                                             float* __restrict__ P_part,
-                                                             int32_t* __restrict__ hist,
-                                                             int32_t* __restrict__ rank_local) {
-  extern __shared__ double rr_red[];  // [2][N] partial sums, then N ints of counts
+template <int NPL, int K, bool FULL>
+__global__ __launch_bounds__(256, 4) void route_rows_reg_kernel(const float* __restrict__ h,
+                                                                int64_t T, int N,
+                                                                int32_t* __restrict__ expert_idx,
+                                                                float* __restrict__ gate,
+                                                                float* __restrict__ P_part,
+                                                                int32_t* __restrict__ hist,
+                                                                int32_t* __restrict__ rank_local) {
+  extern __shared__ double rr_red[];  // [2][N] partial sums, later N ints of counts
   __shared__ int32_t s_idx[RR_ROWS * kMaxTopK];
-  int32_t* cnt = reinterpret_cast<int32_t*>(rr_red + 2 * N);
+  int32_t* cnt = reinterpret_cast<int32_t*>(rr_red);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: row bases in SGPRs
   const int64_t t0 = (int64_t)blockIdx.x * RR_ROWS;
   const int rows = (int)((T - t0) < RR_ROWS ? (T - t0) : RR_ROWS);
-  double pacc[NPL];
+  float pacc[NPL];
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) pacc[i] = 0.0;
+  for (int i = 0; i < NPL; ++i) pacc[i] = 0.0f;
 
   // row r + 4 is loaded while row r is worked on: two register buffers, the loop
   // taken twice per pass so that no copy between them waits for the loads
@@ -982,7 +987,7 @@ __global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __rest
     load_row(vn, r + 4 < rows ? r + 4 : r);  // the last one reads its own row again
     // experts past N (read as 0) out of every choice and sum; done here, not at
     // the load, so that only this row's loads are waited for
-    if (N < kWave * NPL) {
+    if (!FULL) {
 #pragma unroll
       for (int i = 0; i < NPL; ++i)
         if (lane + kWave * i >= N) v[i] = -__builtin_huge_valf();
@@ -1002,11 +1007,11 @@ __global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __rest
     wave_argmax(m, mi);
     float m2 = -__builtin_huge_valf();
     int mi2 = 0x7fffffff;
-    if (k > 1) {
+    if (K > 1) {
 #pragma unroll
       for (int i = 0; i < NPL; ++i) {
         const int e = lane + kWave * i;
-        if (e < N && e != mi && (v[i] > m2 || mi2 == 0x7fffffff)) {
+        if ((FULL || e < N) && e != mi && (v[i] > m2 || mi2 == 0x7fffffff)) {
           m2 = v[i];
           mi2 = e;
         }
@@ -1031,16 +1036,17 @@ __global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __rest
     }
     sum = wave_sum_f64(sum);
     const double inv = 1.0 / sum;
+    const float invf = (float)inv;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) pacc[i] += (double)v[i] * inv;
+    for (int i = 0; i < NPL; ++i) pacc[i] = fmaf(v[i], invf, pacc[i]);
     if (lane == 0) {
-      expert_idx[(t0 + r) * k] = mi;
-      gate[(t0 + r) * k] = (float)inv;
-      s_idx[r * k] = mi;
-      if (k > 1) {
-        expert_idx[(t0 + r) * k + 1] = mi2;
-        gate[(t0 + r) * k + 1] = (float)((double)expf(m2 - m) * inv);
-        s_idx[r * k + 1] = mi2;
+      expert_idx[(t0 + r) * K] = mi;
+      gate[(t0 + r) * K] = (float)inv;
+      s_idx[r * K] = mi;
+      if (K > 1) {
+        expert_idx[(t0 + r) * K + 1] = mi2;
+        gate[(t0 + r) * K + 1] = (float)((double)expf(m2 - m) * inv);
+        s_idx[r * K + 1] = mi2;
       }
     }
   };
@@ -1051,33 +1057,29 @@ __global__ __launch_bounds__(256) void route_rows_reg_kernel(const float* __rest
     if (r + 4 >= rows) break;
     do_row(vb, va, r + 4);
   }
-  // (w0 + w2) + (w1 + w3)
+  // (w0 + w2) + (w1 + w3) in fp64: waves 2 and 3 leave their sums in two LDS
+  // rows, waves 0 and 1 add theirs in place, then wave 0 adds the two rows
   if (wave >= 2) {
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
-      if (lane + kWave * i < N) rr_red[(wave - 2) * N + lane + kWave * i] = pacc[i];
+      if (FULL || lane + kWave * i < N) rr_red[(wave - 2) * N + lane + kWave * i] = (double)pacc[i];
   }
   __syncthreads();
   if (wave < 2) {
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
-      if (lane + kWave * i < N) pacc[i] += rr_red[wave * N + lane + kWave * i];
-  }
-  __syncthreads();
-  if (wave == 1) {
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      if (lane + kWave * i < N) rr_red[lane + kWave * i] = pacc[i];
+      if (FULL || lane + kWave * i < N) rr_red[wave * N + lane + kWave * i] += (double)pacc[i];
   }
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
       const int e = lane + kWave * i;
-      if (e < N) P_part[(int64_t)blockIdx.x * N + e] = (float)(pacc[i] + rr_red[e]);
+      if (FULL || e < N) P_part[(int64_t)blockIdx.x * N + e] = (float)(rr_red[e] + rr_red[N + e]);
     }
   }
-  chunk_hist_rank(s_idx, rows * k, t0 * k, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
+  __syncthreads();  // the counts below reuse the rows
+  chunk_hist_rank(s_idx, rows * K, t0 * K, N, cnt, hist + (int64_t)blockIdx.x * N, rank_local);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -1146,10 +1148,18 @@ void launch_route_rows(const float* h, int64_t T, int N, int k, int32_t* expert_
                        float* P_part, int32_t* hist, int32_t* rank_local, hipStream_t s) {
   if (T == 0) return;
   const dim3 grid((unsigned)((T + RR_ROWS - 1) / RR_ROWS));
-  const size_t lds = (2 * sizeof(double) + sizeof(int32_t)) * (size_t)N;
+  const size_t lds = 2 * sizeof(double) * (size_t)N;
+#define SWL_RR3(NPL, K, FULL)                                                                    \
+  launch_k((route_rows_reg_kernel<NPL, K, FULL>), grid, dim3(256), lds, s, h, T, N, expert_idx, \
+           gate, P_part, hist, rank_local)
 #define SWL_RR(NPL)                                                                              \
-  launch_k(route_rows_reg_kernel<NPL>, grid, dim3(256), lds, s, h, T, N, k, expert_idx, \
-                     gate, P_part, hist, rank_local)
+  do {                                                                                           \
+    const bool full = N == kWave * NPL;                                                          \
+    if (k == 1 && full) SWL_RR3(NPL, 1, true);                                                   \
+    else if (k == 1) SWL_RR3(NPL, 1, false);                                                     \
+    else if (full) SWL_RR3(NPL, 2, true);                                                        \
+    else SWL_RR3(NPL, 2, false);                                                                 \
+  } while (0)
   if (N <= 4 * kWave) SWL_RR(4);
   else if (N <= 8 * kWave) SWL_RR(8);
   else if (N <= 16 * kWave) SWL_RR(16);
@@ -1158,6 +1168,7 @@ void launch_route_rows(const float* h, int64_t T, int N, int k, int32_t* expert_
     launch_k(route_rows_kernel, grid, dim3(256), sizeof(int32_t) * (size_t)N, s, h, T,
                        N, k, expert_idx, gate, P_part, hist, rank_local);
 #undef SWL_RR
+#undef SWL_RR3
 }
 
 }  // namespace swl

@@ -81,6 +81,9 @@ def test_tiny_fp32_config(B):
                                        # three steps ahead, a ragged last expert tile
     (300, 300, 2048, 128, 1.0, 37),    # the 2048-wide rows of the 2048-expert share (64 K
                                        # steps), one partial token tile
+    (700, 2048, 128, 128, 1.0, 38),    # N = 2048: full 32-per-lane statistics rows, a ragged
+                                       # last chunk of 60 tokens
+    (640, 512, 128, 128, 1.0, 39),     # N = 512: full 8-per-lane rows, whole chunks only
 ])
 def test_bf16_ragged_shapes(B, T, N, d, F, c, seed):
     spec = S.Spec(f"bf16-{T}-{N}", T=T, d=d, F=F, N=N, c=c, seed=seed)
