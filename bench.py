@@ -109,9 +109,11 @@ def roofline_entry(stage: str, work: dict, ms: float) -> dict:
 
 # stage of the forward call -> (regular expression over the kernel's name in the
 # hardware-counter profiles, its source file)
-STAGE_KERNEL = {"gemm1_relu": (r"gemm_bf16_\w+<(\d+, \d+, )?true, 1(, (false|true))?>", "gemm.hip"),
-                "gemm2": (r"gemm_bf16_\w+<(\d+, \d+, )?false, 0(, (false|true))?>", "gemm.hip"),
-                "gemm2_combine": (r"gemm_bf16_\w+<(\d+, \d+, )?false, 2(, (false|true))?>",
+STAGE_KERNEL = {"gemm1_relu": (r"gemm_bf16_\w+<(\d+, \d+, )?true, 1(, (false|true)(, \d+)?)?>",
+                               "gemm.hip"),
+                "gemm2": (r"gemm_bf16_\w+<(\d+, \d+, )?false, 0(, (false|true)(, \d+)?)?>",
+                          "gemm.hip"),
+                "gemm2_combine": (r"gemm_bf16_\w+<(\d+, \d+, )?false, 2(, (false|true)(, \d+)?)?>",
                                   "gemm.hip"),
                 "router": (r"router_(small|tok)_kernel(<.*>)?", "router.hip"),
                 "router_logits": (r"router_gemm_dma_kernel", "router.hip"),

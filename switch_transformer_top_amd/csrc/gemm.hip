@@ -49,7 +49,7 @@ namespace swl {
 // is (l / 32).  Result: lane l holds column (l % 32) and rows
 // 8 (v / 4) + 4 (l / 32) + (v % 4), v < 16.  The first operand is the weight
 // fragment, so those result rows are output columns (see stage_tile_bf16).
-template <int BM, int BN, bool RELU, int MODE, bool NTW = false>
+template <int BM, int BN, bool RELU, int MODE, bool NTW = false, int BKT = 0>
 __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                         int64_t strideA,
                                                         const uint16_t* __restrict__ B,
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
                                                         int Nout, int m_tiles, int n_tiles,
                                                         int tiles, GemmIO io, int64_t C) {
   if (y_prologue(io)) return;
-  constexpr int BK = BM == 64 ? 128 : 64;
+  constexpr int BK = BKT ? BKT : (BM == 64 ? 128 : 64);
   constexpr int LDK = BK + GB_PAD;            // LDS row stride (bf16 elements)
   constexpr int TPR = BK / 8;                 // threads per row of a K tile (16 bytes each)
   constexpr int RP = 256 / TPR;               // rows per load pass
@@ -1042,30 +1042,47 @@ void launch_t_sized(GemmRows mode, bool relu, bool a_ko, bool b_ko, const uint16
 // 64 rows take 64-row tiles: the same weight traffic as 128 rows with half the
 // LDS, registers and MFMA work, so more blocks share a CU and more loads are in
 // flight (at the 2048-expert share, capacity 64, the two matmuls stream their
-// weights 7-16% faster).
+// weights 7-16% faster).  Where the output width splits into 256-column tiles
+// they are 64 x 256 with 64-wide K steps: half the tiles (half the prologues)
+// and half the re-reads of the A rows of 64 x 128 with 128-wide steps, with the
+// same 40 KB of operands in flight and three blocks per CU (at the 2048-expert
+// share: GEMM2 with the combine 2.4% and GEMM1 0.7% faster, same process).
+template <int BM, int BN, int BKT>
+void launch_plain_tiles(GemmRows mode, bool relu, const uint16_t* a, int64_t strideA,
+                        const uint16_t* b, int64_t strideB, uint16_t* c, int64_t strideC,
+                        const int32_t* rows, int n_experts, int64_t C, int K, int Nout,
+                        const GemmIO& io, hipStream_t s) {
+  const int mt = (int)((C + BM - 1) / BM), nt = Nout / BN;
+  const int tiles = mt * nt * n_experts;
+  const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
+#define SWL_PLAIN(RL, MD, NT)                                                                  \
+  launch_k((gemm_bf16_kernel<BM, BN, RL, MD, NT, BKT>), dim3(grid), dim3(256), 0, s, a,       \
+           strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C)
+  if (mode == kRowsGather && relu) SWL_PLAIN(true, kRowsGather, false);
+  // every expert's weights are read once: non-temporal loads keep them from
+  // pushing H (read by all N tiles of an expert) out of L2
+  else if (mode == kRowsCombine && mt == 1) SWL_PLAIN(false, kRowsCombine, true);
+  else if (mode == kRowsCombine) SWL_PLAIN(false, kRowsCombine, false);
+  else if (mode == kRowsMask) SWL_PLAIN(false, kRowsMask, false);
+  else if (relu) SWL_PLAIN(true, kRowsDense, false);
+  else SWL_PLAIN(false, kRowsDense, false);
+#undef SWL_PLAIN
+}
+
 template <int BM>
 void launch_plain(GemmRows mode, bool relu, const uint16_t* a, int64_t strideA,
                   const uint16_t* b, int64_t strideB, uint16_t* c, int64_t strideC,
                   const int32_t* rows, int n_experts, int64_t C, int K, int Nout,
                   const GemmIO& io, hipStream_t s) {
-  constexpr int BN = 128;
-  const int mt = (int)((C + BM - 1) / BM), nt = Nout / BN;
-  const int tiles = mt * nt * n_experts;
-  const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
-#define SWL_PLAIN(RL, MD)                                                                      \
-  launch_k((gemm_bf16_kernel<BM, BN, RL, MD>), dim3(grid), dim3(256), 0, s, a, strideA, b,    \
-           strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C)
-  if (mode == kRowsGather && relu) SWL_PLAIN(true, kRowsGather);
-  else if (mode == kRowsCombine && mt == 1)
-    // every expert's weights are read once: non-temporal loads keep them from
-    // pushing H (read by all N tiles of an expert) out of L2
-    launch_k((gemm_bf16_kernel<BM, BN, false, kRowsCombine, true>), dim3(grid), dim3(256), 0, s,
-             a, strideA, b, strideB, c, strideC, rows, K, Nout, mt, nt, tiles, io, C);
-  else if (mode == kRowsCombine) SWL_PLAIN(false, kRowsCombine);
-  else if (mode == kRowsMask) SWL_PLAIN(false, kRowsMask);
-  else if (relu) SWL_PLAIN(true, kRowsDense);
-  else SWL_PLAIN(false, kRowsDense);
-#undef SWL_PLAIN
+  if constexpr (BM == 64) {
+    if (Nout % 256 == 0) {
+      launch_plain_tiles<64, 256, 64>(mode, relu, a, strideA, b, strideB, c, strideC, rows,
+                                      n_experts, C, K, Nout, io, s);
+      return;
+    }
+  }
+  launch_plain_tiles<BM, 128, 0>(mode, relu, a, strideA, b, strideB, c, strideC, rows,
+                                 n_experts, C, K, Nout, io, s);
 }
 
 }  // namespace
