@@ -820,37 +820,50 @@ __global__ __launch_bounds__(512, 1) void router_gemm_dma_kernel(
   }
   mfmas(f1);
 
-  float bias[2][4][4];
+  // Epilogue: each wave stages two of its four 32-token tiles at a time in its
+  // own 20 KB of the (now free) LDS, rows of 64 logits padded to 68, and reads
+  // them back row-major, so that every store instruction writes four whole
+  // 256-byte row pieces (the accumulator layout alone gives 32-byte pieces of
+  // 32 rows, whose lines can be written back before they are complete).
+  __syncthreads();  // every wave is done with the operand rings
+  constexpr int SP = 68;                                 // staged row pitch (floats)
+  float* wst = reinterpret_cast<float*>(rlds) + wave * (20480 / 4);
+  const int rc = lane & 15, rr = lane >> 4;              // read-back: chunk, row within 4
+  const int eb = e0 + we * 64 + 4 * rc;                  // first expert of the lane's chunk
+  float bias[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int u = 0; u < 4; ++u) bias[u] = (b_r && eb + u < N) ? b_r[eb + u] : 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + we * 64 + j * 32 + 8 * q + 4 * fc + u;
-        bias[j][q][u] = (b_r && e < N) ? b_r[e] : 0.f;
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * half + ii;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(wst + (ii * 32 + fr) * SP + j * 32 + 8 * q + 4 * fc) =
+              make_float4(acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                          acc[j][i][4 * q + 3]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = 4 * it + rr;                       // 0..63: two token tiles
+      const int64_t t = t0 + wt * 128 + half * 64 + row;
+      const float4 v4 = *reinterpret_cast<const float4*>(wst + row * SP + 4 * rc);
+      if (t >= T) continue;
+      float v[4] = {v4.x + bias[0], v4.y + bias[1], v4.z + bias[2], v4.w + bias[3]};
+      float* hrow = h + t * N;
+      if (vec && eb + 3 < N) {
+        *reinterpret_cast<float4*>(hrow + eb) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (eb + u < N) hrow[eb + u] = v[u];
       }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = t0 + wt * 128 + i * 32 + fr;
-    if (t >= T) continue;
-    float* hrow = h + t * N;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = e0 + we * 64 + j * 32 + 8 * q + 4 * fc;
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = acc[j][i][4 * q + u] + bias[j][q][u];
-        if (vec && e + 3 < N) {
-          *reinterpret_cast<float4*>(hrow + e) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (e + u < N) hrow[e + u] = v[u];
-        }
-      }
+    }
+    __syncthreads();  // the second half reuses the staging rows
   }
 }
 
