@@ -37,12 +37,13 @@ namespace swl {
 // for three waves per SIMD (three blocks per CU share the LDS and MFMA pipes).  K advances BK at a
 // time through one padded LDS buffer per operand; the next K tile is fetched
 // into registers (unconditionally: the last step re-reads its own tile) while
-// the current one is multiplied.  BK is 128 for 64-row tiles, which stream
+// the current one is multiplied.  BK is 128 for 64 x 128 tiles, which stream
 // weights with few rows to reuse them: twice the bytes in flight per block
 // (three blocks and 144 KB per CU) and 256 contiguous bytes of every weight
-// row per step; 128-row tiles keep BK = 64 (their registers would not allow
-// three blocks per CU at 128).  K is a multiple of 128 (the layer accepts
-// bf16 shapes with d and F multiples of 128 only).
+// row per step; 64 x 256 tiles (BKT = 64) move the same bytes per step over
+// twice the columns, and 128-row tiles keep BK = 64 (their registers would not
+// allow three blocks per CU at 128).  K is a multiple of 128 (the layer
+// accepts bf16 shapes with d and F multiples of 128 only).
 //
 // MFMA 32x32x16 operand layout (per lane l): first operand row (l % 32) with 8
 // consecutive k, second operand column (l % 32) with the same 8 k; the k group

@@ -112,6 +112,18 @@ def test_more_than_2048_experts(B):
     assert float(bufs["aux_loss"].item()) == res["aux_loss"]
 
 
+def test_logits_router_bias_odd_width(B):
+    """N = 777 with a router bias: the many-expert logits router stores rows whose width is
+    not a multiple of 4 (element stores past each 4-wide piece's end are left out), adds the
+    bias in its staged epilogue, and ends in a partial expert tile (9 experts) and a
+    partial token tile (132 tokens); the statistics kernel masks the experts past N."""
+    spec = S.Spec("bf16-900-777-bias", T=900, d=128, F=128, N=777, c=1.25, seed=64,
+                  zipf=(1.1, 0.12))
+    host, _, res = _run(B, spec)
+    assert host["b_r"] is not None
+    _full_check(spec, host, res, spec.name)
+
+
 # ---------------------------------------------------------------- fused expert FFN
 
 def _run_fused(B, spec, host=None):
