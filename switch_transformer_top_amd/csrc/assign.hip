@@ -22,7 +22,7 @@
 namespace swl {
 
 // Chunk scan.  A block of 1024 threads takes EG consecutive experts (EG a power
-// of two: N rounded up when one block covers all experts, 64 otherwise); the
+// of two: N rounded up when one block covers all experts, 32 otherwise); the
 // G = 1024 / EG threads of an expert split the chunk range into contiguous
 // pieces.  Each thread sums its piece (counts and
 // probability sums); a log-step scan over the pieces (in LDS) gives each
@@ -329,7 +329,9 @@ void launch_route_scan(int32_t* hist, const float* P_part, int64_t nc, int N, in
                        k, C, alpha, load, n_kept, nullptr, aux, tile_start, tile_rows);
     return;
   }
-  constexpr int EG = 64;
+  // 32 experts per block: each row piece a thread group reads and rewrites is
+  // one whole 128-byte line, with twice the blocks of 64 (64 at N = 2048)
+  constexpr int EG = 32;
   launch_k(route_scan_kernel, dim3((unsigned)((N + EG - 1) / EG)), dim3(1024), 0, s,
                      hist, P_part, nc, N, EG, T, k, C, alpha, load, n_kept, terms, aux, nullptr,
                      tile_rows);
