@@ -810,13 +810,19 @@ __global__ __launch_bounds__(512, 1) void router_gemm_dma_kernel(
   read_w(f0, pstage(0), 0);
   __builtin_amdgcn_sched_barrier(0);
   mfmas_reading(f0, f1, 0, 1);
+  // Each wave raises its issue priority for its MFMA and fragment-read section and
+  // drops it before the next barrier, so that on a SIMD a wave in that section
+  // issues ahead of one between sections (1% faster at the 2048-expert share,
+  // same process).
   for (int t = 1; t < nk; ++t) {
     step_barrier(t);
     if (t + 1 < nk) dma_planes(t + 1);
     if (t + 3 < nk) dma_x(t + 3);
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
     mfmas_reading(f1, f0, t, 0);
     mfmas_reading(f0, f1, t, 1);
+    __builtin_amdgcn_s_setprio(0);
   }
   mfmas(f1);
 
