@@ -132,12 +132,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 // Dispatch by index (bf16 path): the expert matmuls read the rows of x in
 // place, so dispatch only finalises the routing and records, for every kept
 // assignment, which token sits in slot (e, position): tok[e * C + position] = t.
-// A block of four waves takes 64 assignments: in every wave lane i derives
+// A block of four waves takes 64 assignments: in wave 0 lane i derives
 // assignment 64 b + i (position = chunk offset + in-chunk rank, drop =
-// position >= C), and wave 0 stores the results.  With the fused combine
-// (k = 1) a dropped token leaves the layer unchanged: its row is copied from x
-// to out here, the r-th dropped row of the 64 by wave r % 4, in 16-byte pieces
-// spread over the lanes, and the combine never touches it.
+// position >= C) and stores the results.  With the fused combine (k = 1) a
+// dropped token leaves the layer unchanged: wave 0 leaves the block's drop
+// mask in LDS, and the r-th dropped row of the 64 is copied from x to out by
+// wave r % 4, in 16-byte pieces spread over the lanes; the combine never
+// touches it.  (Every wave deriving the mask itself took four times the
+// gathers of chunk offsets.)
 __global__ __launch_bounds__(256) void dispatch_index_kernel(const uint4* __restrict__ x, int64_t T,
                                                              int k, int row_vec16,
                                                              const int32_t* __restrict__ expert_idx,
@@ -149,24 +151,28 @@ __global__ __launch_bounds__(256) void dispatch_index_kernel(const uint4* __rest
                                                              int32_t* __restrict__ tok,
                                                              bool copy_dropped,
                                                              uint4* __restrict__ out) {
+  __shared__ uint64_t s_drops;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t a0 = (int64_t)blockIdx.x * kWave;
   const int64_t a = a0 + lane;
   if (w > 0 && !copy_dropped) return;   // uniform: only wave 0 has work then
-  bool dropped = false;
-  if (a < T * k) {
-    const int64_t t = a / k;
-    const int32_t e = expert_idx[a];
-    const int32_t pos = offsets[(t / chunk) * N + e] + rank_local[a];
-    dropped = (int64_t)pos >= C;
-    if (w == 0) {
+  if (w == 0) {
+    bool dropped = false;
+    if (a < T * k) {
+      const int64_t t = a / k;
+      const int32_t e = expert_idx[a];
+      const int32_t pos = offsets[(t / chunk) * N + e] + rank_local[a];
+      dropped = (int64_t)pos >= C;
       position[a] = pos;
       drop_mask[a] = dropped ? 1 : 0;
       if (!dropped) tok[(int64_t)e * C + pos] = (int32_t)t;
     }
+    const uint64_t m0 = __ballot(dropped);
+    if (lane == 0) s_drops = m0;
   }
-  if (!copy_dropped) return;   // k = 1 from here on: assignment a is token a
-  uint64_t m = __ballot(dropped);
+  if (!copy_dropped) return;   // uniform; k = 1 from here on: assignment a is token a
+  __syncthreads();
+  uint64_t m = s_drops;
   for (int r = 0; m; ++r) {
     const int64_t t = a0 + __builtin_ctzll(m);
     m &= m - 1;
