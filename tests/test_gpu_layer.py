@@ -84,6 +84,7 @@ def test_tiny_fp32_config(B):
     (700, 2048, 128, 128, 1.0, 38),    # N = 2048: full 32-per-lane statistics rows, a ragged
                                        # last chunk of 60 tokens
     (640, 512, 128, 128, 1.0, 39),     # N = 512: full 8-per-lane rows, whole chunks only
+    (600, 1024, 128, 256, 1.0, 41),    # N = 1024: full 16-per-lane rows
 ])
 def test_bf16_ragged_shapes(B, T, N, d, F, c, seed):
     spec = S.Spec(f"bf16-{T}-{N}", T=T, d=d, F=F, N=N, c=c, seed=seed)

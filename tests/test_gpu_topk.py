@@ -90,6 +90,7 @@ def _check_output(res, spec, host, tag):
     (700, 48, 128, 256, 1.0, 58, "bf16"),  # 32 < N <= 256: the token-split router
     (500, 1024, 128, 128, 2.0, 62, "bf16"),  # N = 1024: full 16-per-lane statistics rows
     (300, 1500, 128, 128, 2.0, 63, "bf16"),  # 1024 < N < 2048: 32 per lane, experts past N masked
+    (400, 2048, 128, 128, 2.0, 65, "bf16"),  # N = 2048: full 32-per-lane rows with two choices
 ])
 def test_top2_shapes(B, T, N, d, F, c, seed, act):
     spec = S.Spec(f"top2-{T}-{N}", T=T, d=d, F=F, N=N, c=c, seed=seed, act=act, expert=act)
