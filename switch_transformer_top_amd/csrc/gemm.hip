@@ -96,6 +96,16 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
   const int lrow = tid / TPR, lcol = (tid % TPR) * 8;
 
   int64_t a_off[LA], b_off[LB];
+  u32x4 ra[LA], rb[LB];
+  // the first K step's weight rows are requested before the slot-table reads
+  // that the gathered A rows wait on
+#pragma unroll
+  for (int j = 0; j < LB; ++j) b_off[j] = (int64_t)(lrow + RP * j) * K + lcol;
+#pragma unroll
+  for (int j = 0; j < LB; ++j)
+    rb[j] = NTW ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Be + b_off[j]))
+                : *reinterpret_cast<const u32x4*>(Be + b_off[j]);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
     int r = m0 + lrow + RP * j;
@@ -103,8 +113,6 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
     const int64_t src = MODE == kRowsGather ? (int64_t)tok_e[r] : (int64_t)r;
     a_off[j] = src * K + lcol;
   }
-#pragma unroll
-  for (int j = 0; j < LB; ++j) b_off[j] = (int64_t)(lrow + RP * j) * K + lcol;
 
   floatx16 acc[TI][TJ];
 #pragma unroll
@@ -115,7 +123,6 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int last = K - BK;
-  u32x4 ra[LA], rb[LB];
   // The scheduling barrier keeps the prefetch loads ahead of the MFMAs that
   // follow; without it the compiler sinks them to the end of the loop body,
   // where nothing is left to hide their latency.
@@ -136,7 +143,9 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(const uint16_t* __res
   // and stores its share of the operand tiles)
   auto kloop = [&](auto tv_const) {
     constexpr int TV = decltype(tv_const)::value;
-    fetch(0);
+#pragma unroll
+    for (int j = 0; j < LA; ++j) ra[j] = *reinterpret_cast<const u32x4*>(Ae + a_off[j]);
+    __builtin_amdgcn_sched_barrier(0);  // (rb holds step 0 already)
     for (int k0 = 0; k0 < K; k0 += BK) {
       __syncthreads();
 #pragma unroll
@@ -326,17 +335,24 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
   const int lrow = tid >> 3, lcol = (tid & 7) * 8;  // 64 rows per pass of 512 threads
 
   int64_t go[NL];  // element offsets: A rows (j < 4) from Ae, B rows (j >= 4) from Be
+  u32x4 g[NL];
+  // the first K step's weight rows are requested before the slot-table reads
+  // that the gathered A rows wait on (1-4% off the matmuls at the Switch-Base
+  // and Switch-Large shapes, same bits)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) go[4 + j] = (int64_t)(lrow + 64 * j) * K + lcol;
+#pragma unroll
+  for (int j = 4; j < NL; ++j) g[j] = *reinterpret_cast<const u32x4*>(Be + go[j]);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     int r = m0 + lrow + 64 * j;
     r = r < rows_e ? r : rows_e - 1;  // rows past n_kept: any valid row, never stored
     const int64_t src = MODE == kRowsGather ? (int64_t)tok_e[r] : (int64_t)r;
     go[j] = src * K + lcol;
-    go[4 + j] = (int64_t)(lrow + 64 * j) * K + lcol;
   }
   const int lbase = lrow * LDK + lcol;
   const int nk = K / BK;
-  u32x4 g[NL];
   auto gload = [&](int j0, int j1, int t) {
     t = t < nk ? t : nk - 1;
     const int k = t * BK;
@@ -387,7 +403,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_wide_kernel(
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
     };
 
-    gload(0, NL, 0);
+    gload(0, 4, 0);  // the weight rows of step 0 are already on their way
     gstore(0, NL, 0);
     gload(0, NL, 1);
     __syncthreads();
